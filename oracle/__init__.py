@@ -1,0 +1,25 @@
+"""CPU oracle for the speculative verify step -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct NumPy (fp64) implementations of what the verify
+path computes, written from the pages:
+
+  * model.py   -- the target model's forward over B sequences x T verify rows
+                  (chain or tree), cached context plus speculative suffix;
+  * accept.py  -- Leviathan et al.'s speculative-sampling accept / residual
+                  resample / bonus (chain and token tree, sampled and greedy)
+                  and the pending-token KV commit;
+  * philox.py  -- Philox4x64-10 (Salmon et al., SC'11), the uniforms' source;
+  * metrics.py -- the closed forms the pages give (beta, tokens per round,
+                  speedup, compute increase, accept-rate metrics);
+  * numerics.py -- bf16 decoding and round-to-nearest-even.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package.  It shares no code with the HIP path and imports nothing from it.
+
+Parity unpinned: the absolute logit values of the random-init 8B-shaped model
+have no external reference; they are pinned only through the component checks
+in tests/test_oracle_model.py (closed forms, library special cases, causal and
+prefill/decode consistency).  The sibling order of a token tree has no printed
+example; enumeration and sampling pin only losslessness.
+"""
+from . import philox, numerics, model, accept, metrics  # noqa: F401

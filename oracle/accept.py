@@ -1,0 +1,205 @@
+"""Speculative-sampling accept / resample / bonus, fp64.  Test infrastructure.
+
+Chain (CS349E Lecture 6, "Optimizing Autoregressive Decode", section 6.2,
+Leviathan et al.'s Algorithm 1, steps 3-5):
+  for i = 1 .. gamma: accept x_i when u_i < p_i(x_i) / q_i(x_i), else stop;
+  n = number accepted; if n < gamma draw the extra token from
+  norm(max(0, p_{n+1} - q_{n+1})), otherwise take a bonus token from p_{gamma+1};
+  emit x_1 .. x_n and the extra token.
+The test u < p/q is evaluated as u * q < p (the Kimi-K3 tuning page, "What
+SGLang actually runs": a uniform times the draft probability under the target
+probability), which avoids the division.
+
+Sampling settings (section 7.3): p_i = softmax(z_i / T).  q arrives already
+adjusted by the draft side.  Greedy (section 7.4, T = 0): accept x_i iff it
+equals argmax z_i; the extra token is argmax z_{n+1}, the only positive term of
+the residual of two one-hot distributions.
+
+Token tree (section 10.3 gives only greedy trees; the sampled walk is the
+reading taken here, exact for any draft distribution by section 7.3's remark
+that the proof holds whatever q is): at node v with target r = p_v and the
+distribution q' its children were drawn from, test the children in their
+order; a rejected child replaces r by norm(max(0, r - q')) and, for children
+drawn without replacement, removes that token from q' and renormalises.  All
+children rejected: draw from r.  Reached a leaf: bonus from p_leaf.  Greedy:
+descend into the child whose token is argmax p_v, else emit that argmax.
+
+Readings where the pages say nothing:
+  * inverse-CDF sampling in token-id order with a strict test,
+    token = min{x : sum_{y<=x} r(y) > u * sum(r)};
+  * greedy ties resolve to the lowest token id;
+  * a residual whose mass is zero in floating point falls back to the
+    distribution it was taken from (p for the chain);
+  * uniforms come from Philox4x64-10 (see philox.py for slot assignment).
+
+Each function also returns a trace of the margins of the decisions it took, so
+a test can tell a genuine mismatch from a near-tie: accept tests record
+|u - min(1, p/q)|, draws record the distance of u * R to the nearest CDF
+boundary divided by R, argmax decisions the top-2 gap over max |z|.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def softmax(z: np.ndarray, temperature: float) -> np.ndarray:
+    s = np.asarray(z, dtype=np.float64) / temperature
+    s = s - s.max()
+    e = np.exp(s)
+    return e / e.sum()
+
+
+def argmax_lowest(z: np.ndarray) -> int:
+    """Index of the maximum; ties go to the lowest index."""
+    return int(np.argmax(np.asarray(z)))
+
+
+def top2_margin(z: np.ndarray) -> float:
+    z = np.asarray(z, dtype=np.float64)
+    if z.size < 2:
+        return np.inf
+    part = np.partition(z, -2)
+    scale = max(np.abs(z).max(), 1e-300)
+    return float((part[-1] - part[-2]) / scale)
+
+
+def inverse_cdf(r: np.ndarray, u: float):
+    """Smallest x with cumsum(r)[x] > u * R, R = cumsum(r)[-1].  Returns
+    (token, margin)."""
+    c = np.cumsum(np.asarray(r, dtype=np.float64))
+    R = c[-1]
+    t = u * R
+    x = int(np.argmax(c > t))
+    lo = c[x - 1] if x > 0 else 0.0
+    margin = min(t - lo, c[x] - t) / R
+    return x, float(margin)
+
+
+def accept_chain_one(z, q, tokens, temperature, u, _variant="residual"):
+    """One sequence.  z [gamma+1, V] target logits for the window rows;
+    q [gamma, V] draft probabilities (row j: distribution draft j+1 came from);
+    tokens [gamma+1] = [pending, x_1 .. x_gamma]; u(slot) -> uniform.
+    Returns (n_accepted, emitted tokens [n+1], margins).
+
+    _variant plants one of the two wrong implementations of section 7.5 for
+    negative-control tests only: "resample_from_p" draws the extra token from p
+    after a rejection; "deterministic" rejects whenever q > p."""
+    gamma = len(tokens) - 1
+    margins = []
+    if temperature == 0.0:
+        n = 0
+        while n < gamma:
+            am = argmax_lowest(z[n])
+            margins.append(top2_margin(z[n]))
+            if int(tokens[n + 1]) != am:
+                break
+            n += 1
+        margins.append(top2_margin(z[n]))
+        extra = argmax_lowest(z[n])
+        return n, [int(t) for t in tokens[1:n + 1]] + [extra], margins
+
+    n = 0
+    for i in range(gamma):
+        p = softmax(z[i], temperature)
+        x = int(tokens[i + 1])
+        ui = u(i)
+        margins.append(abs(ui - min(1.0, p[x] / q[i][x])) if q[i][x] > 0 else np.inf)
+        ok = (q[i][x] <= p[x]) if _variant == "deterministic" else (ui * q[i][x] < p[x])
+        if ok:
+            n += 1
+        else:
+            break
+    p = softmax(z[n], temperature)
+    if n < gamma and _variant != "resample_from_p":
+        r = np.maximum(0.0, p - np.asarray(q[n], dtype=np.float64))
+        if not (r.sum() > 0.0):
+            r = p
+    else:
+        r = p
+    extra, m = inverse_cdf(r, u(gamma))
+    margins.append(m)
+    return n, [int(t) for t in tokens[1:n + 1]] + [extra], margins
+
+
+def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _variant="residual"):
+    """One sequence with a token tree.  z [T, V] logits per node; q [T, V] the
+    draft distribution each node's children were drawn from; tokens [T] node
+    tokens (node 0 = pending token); parent [T] (root -1).  u(slot) -> uniform.
+    Returns (path node ids from the root, emitted tokens, margins)."""
+    T = len(tokens)
+    children = [[] for _ in range(T)]
+    for c in range(1, T):
+        children[int(parent[c])].append(c)
+    margins = []
+    v = 0
+    path = [0]
+
+    if temperature == 0.0:
+        while True:
+            am = argmax_lowest(z[v])
+            margins.append(top2_margin(z[v]))
+            nxt = [c for c in children[v] if int(tokens[c]) == am]
+            if not nxt:
+                return path, [int(tokens[c]) for c in path[1:]] + [am], margins
+            v = nxt[0]
+            path.append(v)
+
+    while True:
+        r = softmax(z[v], temperature)
+        if not children[v]:
+            extra, m = inverse_cdf(r, u(T - 1))
+            margins.append(m)
+            return path, [int(tokens[c]) for c in path[1:]] + [extra], margins
+        qp = np.asarray(q[v], dtype=np.float64).copy()
+        accepted = None
+        for c in children[v]:
+            x = int(tokens[c])
+            uc = u(c - 1)
+            margins.append(abs(uc - min(1.0, r[x] / qp[x])) if qp[x] > 0 else np.inf)
+            if uc * qp[x] < r[x]:
+                accepted = c
+                break
+            if _variant == "resample_from_p":
+                continue
+            res = np.maximum(0.0, r - qp)
+            if res.sum() > 0.0:
+                r = res / res.sum()
+            if not replacement:
+                qp[x] = 0.0
+                s = qp.sum()
+                if s > 0.0:
+                    qp = qp / s
+        if accepted is None:
+            extra, m = inverse_cdf(r, u(T - 1))
+            margins.append(m)
+            return path, [int(tokens[c]) for c in path[1:]] + [extra], margins
+        v = accepted
+        path.append(v)
+
+
+def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replacement=False,
+           _variant="residual"):
+    """Batch driver.  logits [B, T, V]; q [B, T-1, V] (chain) or [B, T, V] (tree);
+    tokens [B, T]; uniforms(b, slot) -> float.
+    Returns dict with n_accepted [B], out_tokens [B, T] (-1 padded), paths,
+    margins (list per sequence)."""
+    logits = np.asarray(logits)
+    B, T = np.asarray(tokens).shape
+    n_acc = np.zeros(B, dtype=np.int64)
+    out = np.full((B, T), -1, dtype=np.int64)
+    paths, margins = [], []
+    for b in range(B):
+        ub = (lambda s, b=b: uniforms(b, s))
+        if tree_parent is None:
+            n, toks, m = accept_chain_one(logits[b], None if q is None else q[b], tokens[b],
+                                          temperature, ub, _variant)
+            path = list(range(n + 1))
+        else:
+            path, toks, m = accept_tree_one(logits[b], None if q is None else q[b], tokens[b],
+                                            tree_parent[b], temperature, ub, replacement, _variant)
+            n = len(path) - 1
+        n_acc[b] = n
+        out[b, : len(toks)] = toks
+        paths.append(path)
+        margins.append(m)
+    return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins}
