@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative verify step on one MI355X.
+
+Workload (default): Llama-3-8B-shaped decoder with random-init bf16 weights,
+B = 1, synthetic bf16 KV context of 2048 tokens, chain verify at gamma = 3
+(T = 4 rows), noisy-target drafts with logit noise sigma = 1.0, temperature 1.
+
+One timed step = spec_verify_step (T = gamma + 1 rows, all weights streamed
+once) + spec_accept (accept / residual resample / bonus) + the commit of
+kv_len, on device-resident inputs.  R pre-drafted rounds from the same cache
+state are cycled so acceptance varies; the commit writes to a separate length
+buffer so every step sees the same context.
+
+Printed JSON line:
+  value         accepted tokens / s = sum_b (n_b + 1) over the timed steps / time
+  c_verify      T_verify(gamma+1) / T_decode(1): the same spec_verify_step at
+                T = gamma+1 and at T = 1 (same B, context), whole-step times
+  roofline      the gate/up GEMM launch class (the largest weight stream):
+                algorithmic bytes per launch / mean launch time from HIP events
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--ctx", type=int, default=2048)
+    ap.add_argument("--gamma", type=int, default=3)
+    ap.add_argument("--sigma", type=float, default=1.0)
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--rounds", type=int, default=8, help="distinct pre-drafted rounds cycled")
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
+    ap.add_argument("--profile-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the verify step of this build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import speculative_decoding_verify_spec_amd as S
+    from speculative_decoding_verify_spec_amd.engine import VerifyEngine
+
+    S.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    sh = synth.LLAMA8B
+    B, ctx, gamma, T = a.batch, a.ctx, a.gamma, a.gamma + 1
+    max_ctx = ((ctx + T + 63) // 64) * 64
+    log(f"workload: {sh.n_layers}L d={sh.d_model} V={sh.vocab} B={B} ctx={ctx} gamma={gamma}")
+
+    t0 = time.time()
+    names, w = synth.make_weights(sh, device=dev)
+    cache = synth.make_kv_cache(sh, B, max_ctx, ctx, device=dev, poison_tail=False)
+    eng = VerifyEngine(sh, w, cache, B, max_ctx, max(T, 1))
+    torch.cuda.synchronize()
+    log(f"weights + cache ready in {time.time() - t0:.1f}s")
+
+    kv_len = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    kv_out = torch.empty_like(kv_len)
+    pending = synth.make_tokens(B, 1, sh.vocab, seed=synth.SEED_PROMPT, device=dev)
+
+    # ---- pre-draft R rounds from the same state: gamma sequential T=1 decodes
+    # give the target logits z_i of each drafted prefix; q_i = softmax(z_i + eps)
+    rounds = []
+    z1 = torch.empty((B, 1, sh.vocab), device=dev)
+    for r in range(a.rounds):
+        toks = [pending[:, 0]]
+        qs = []
+        for i in range(gamma):
+            tok = toks[-1][:, None].contiguous().to(torch.int32)
+            eng.step(tok, kv_len + i, z1)
+            q, zn = synth.noisy_draft_dist(z1[:, 0], a.sigma, synth.SEED_NOISE * 1000 + r * 16 + i,
+                                           a.temperature if a.temperature > 0 else 1.0)
+            if a.temperature > 0:
+                x = synth.sample_from(q, synth.SEED_DRAFT * 1000 + r * 16 + i)[:, 0]
+            else:
+                x = zn.argmax(-1).to(torch.int32)
+            toks.append(x)
+            qs.append(q)
+        tokens = torch.stack(toks, 1).to(torch.int32).contiguous()
+        qt = torch.stack(qs, 1).contiguous() if gamma else torch.empty((B, 0, sh.vocab), device=dev)
+        rounds.append((tokens, qt))
+    torch.cuda.synchronize()
+    log(f"{a.rounds} draft rounds ready")
+
+    logits = torch.empty((B, T, sh.vocab), device=dev)
+    out = torch.empty((B, T), dtype=torch.int32, device=dev)
+    nacc_hist = torch.zeros((a.steps + a.warmup, B), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(k):
+        tokens, qt = rounds[k % len(rounds)]
+        eng.step(tokens, kv_len, logits)
+        eng.accept(logits, qt if gamma else None, tokens, out, nacc_hist[k], kv_len, kv_out,
+                   temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
+
+    for k in range(a.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for k in range(a.warmup, a.warmup + a.steps):
+        one_step(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    n_timed = nacc_hist[a.warmup:].cpu().numpy()
+    tokens_out = int((n_timed + 1).sum())
+    value = tokens_out / wall
+    ms_per_step = wall * 1000.0 / a.steps
+    alpha_hat = float(n_timed.mean()) / gamma if gamma else 0.0
+    assert eng.device_errors() == 0
+    log(f"timed {a.steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / a.steps:.3f}), "
+        f"{tokens_out} tokens, {value:.1f} tok/s")
+
+    # ---- c = T_verify(gamma+1) / T_decode(1), whole-step times
+    def time_forward(Tn, iters):
+        tok = rounds[0][0][:, :Tn].contiguous()
+        lg = torch.empty((B, Tn, sh.vocab), device=dev)
+        for _ in range(3):
+            eng.step(tok, kv_len, lg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            eng.step(tok, kv_len, lg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    iters = max(10, a.steps // 2)
+    t_verify = time_forward(T, iters)
+    t_decode = time_forward(1, iters)
+    c_v = t_verify / t_decode
+    log(f"T_verify({T}) {t_verify:.3f} ms, T_decode(1) {t_decode:.3f} ms, c = {c_v:.3f}")
+
+    # ---- per-kernel event timing (a separate profiled pass)
+    S.spec_profile_enable(eng.handle, True)
+    for k in range(a.profile_steps):
+        one_step(k)
+    torch.cuda.synchronize()
+    stats = S.spec_profile_read(eng.handle, reset=True)
+    S.spec_profile_enable(eng.handle, False)
+    kernels = {}
+    for name, st in stats.items():
+        if st["launches"]:
+            avg_ms = st["total_ms"] / st["launches"]
+            gbs = st["algo_bytes"] / (st["total_ms"] * 1e-3) / 1e9 if st["total_ms"] > 0 else 0.0
+            kernels[name] = {"launches_per_step": st["launches"] / a.profile_steps,
+                             "avg_us": avg_ms * 1e3, "algo_GBps": round(gbs, 1)}
+    gu = stats["gemm_gate_up"]
+    gu_bytes = gu["algo_bytes"] / gu["launches"]
+    gu_avg_s = gu["total_ms"] / gu["launches"] * 1e-3
+    gemm_names = [k for k in stats if k.startswith("gemm_")]
+    g_bytes = sum(stats[k]["algo_bytes"] for k in gemm_names)
+    g_ms = sum(stats[k]["total_ms"] for k in gemm_names)
+    roofline = {"bound": "hbm", "kernel": "gemm_gate_up (skinny-M weight stream + SiLU*up)",
+                "achieved": round(gu_bytes / gu_avg_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_bytes / gu_avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                "algo_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2),
+                "traffic": None,
+                "all_gemms_GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                "all_gemms_frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"gate/up GEMM {roofline['achieved']} GB/s, all GEMMs {roofline['all_gemms_GBps']} GB/s")
+
+    result = {
+        "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
+        "value": round(value, 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (bf16 weights, fp32 activations/accum)",
+        "data": "synthetic (random-init weights, random bf16 KV context, noisy-target drafts)",
+        "config": {"workload": f"llama3-8b-shape chain verify B={B} ctx={ctx} gamma={gamma} "
+                               f"sigma={a.sigma} T={a.temperature}",
+                   "B": B, "ctx": ctx, "gamma": gamma, "sigma": a.sigma, "temperature": a.temperature,
+                   "parallelism": "single GPU"},
+        "c_verify": round(c_v, 4), "t_verify_ms": round(t_verify, 4), "t_decode_ms": round(t_decode, 4),
+        "mean_accepted": round(float(n_timed.mean()), 4), "alpha_hat": round(alpha_hat, 4),
+        "tokens_per_round": round(float((n_timed + 1).mean()), 4),
+        "kernels": kernels, "roofline": roofline,
+    }
+
+    if a.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a, kv_len)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
+    """One verify round (forward over the T rows + accept) of the same workload
+    in the CPU oracle, on this host's cores."""
+    import numpy as np
+
+    import synth
+    from oracle import accept as OA
+    from oracle import model as OM
+    from oracle import philox
+
+    log("cpu baseline: copying weights and cache to host")
+    Wn = OM.Weights(names, [synth.to_numpy_raw(t) for t in w])
+    k, v = synth.kv_views(cache, sh, B, max_ctx)
+    kc, vc = synth.to_numpy_raw(k), synth.to_numpy_raw(v)
+    tokens, qt = round0
+    tok = tokens.cpu().numpy()
+    qn = qt.double().cpu().numpy()
+    cores = len(os.sched_getaffinity(0))
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    log(f"cpu baseline: oracle round on {cores} cores")
+    t0 = time.perf_counter()
+    z, _, _ = OM.forward(sh, Wn, tok, np.full(B, ctx), kc, vc)
+    res = OA.accept(z, qn, tok, a.temperature, philox.Uniforms(synth.SEED_ACCEPT, 0))
+    dt = time.perf_counter() - t0
+    toks = int((res["n_accepted"] + 1).sum())
+    log(f"cpu baseline: {dt:.1f}s for one round, {toks} tokens")
+    return {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores,
+            "kind": "oracle", "sample": f"one verify round (B={B}, T={a.gamma + 1}, ctx {ctx}, 32 layers, "
+                                        f"accept) of the same workload; {dt:.1f} s",
+            "round_seconds": round(dt, 2), "host_cores_visible": cores}
+
+
+if __name__ == "__main__":
+    main()

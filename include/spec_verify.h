@@ -1,0 +1,201 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X speculative verify step.
+ *
+ * One call of spec_verify_step runs the target model's forward over B
+ * sequences x T verify rows, streaming every weight matrix from HBM once for
+ * all B*T rows; spec_accept then applies speculative sampling to the logits
+ * and commits the accepted prefix to the KV cache.
+ *
+ * What the calls compute, and where it is defined:
+ *   - the verify forward yields p_1 .. p_{gamma+1} in one target pass
+ *     (CS349E Lecture 6 "Optimizing Autoregressive Decode", section 6.2,
+ *     Leviathan et al.'s Algorithm 1, step 2);
+ *   - accept / residual resample / bonus: the same section, steps 3-5, with
+ *     the test u * q(x) < p(x) (Kimi-K3 tuning page, "What SGLang actually
+ *     runs"); greedy acceptance as argmax match (section 7.4);
+ *   - tree verification with an ancestor-only mask (section 10.3);
+ *   - the cache commit under the pending-token invariant (section 6.2, KV
+ *     handling): after a round the cache holds the confirmed sequence minus its
+ *     last token;
+ *   - acceptance is per sequence and accept counts differ between sequences
+ *     (section 11; the Kimi-K3 tuning page on accept length vs batch).
+ *
+ * Conventions for every call:
+ *   - d_* arguments are device pointers (HIP device memory of the GPU current
+ *     when the handle was created); everything else lives on the host.
+ *   - `stream` is a hipStream_t passed as void*.  Work is enqueued on it
+ *     asynchronously; outputs are valid once the stream has synchronised.
+ *     No call synchronises the host except spec_device_errors.
+ *   - The caller owns every buffer (weights, KV cache, workspace, inputs,
+ *     outputs).  The handle only borrows them; they must outlive it.  The
+ *     library never allocates or frees device memory.
+ *   - Host-detectable errors return a negative spec_status before anything is
+ *     enqueued.  Data errors visible only on the device (token id outside
+ *     [0, V), bad tree parent, cache overflow) set bits in a sticky flag word
+ *     read by spec_device_errors; the kernels clamp or skip the offending
+ *     access instead of faulting.  Nothing aborts or throws across the ABI.
+ *   - A handle is not thread-safe; calls on one handle must be serialised.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t spec_status;
+#define SPEC_OK 0
+#define SPEC_ERR_INVALID_ARG (-1) /* null pointer, bad enum, bad temperature   */
+#define SPEC_ERR_SHAPE (-2)       /* model shape this build does not support   */
+#define SPEC_ERR_CAPACITY (-3)    /* B, T or a buffer beyond what init sized   */
+#define SPEC_ERR_UNSUPPORTED (-4) /* dtype or device architecture              */
+#define SPEC_ERR_DEVICE (-5)      /* a HIP runtime call failed                 */
+#define SPEC_ERR_STATE (-6)       /* handle misuse                             */
+#define SPEC_ERR_DATA (-7)        /* device-side data error flagged            */
+
+#define SPEC_DTYPE_F32 0
+#define SPEC_DTYPE_BF16 1
+
+/* Device-side error flag bits (spec_device_errors). */
+#define SPEC_FLAG_TOKEN_RANGE 1u  /* a token id outside [0, vocab)              */
+#define SPEC_FLAG_TREE 2u         /* parent[0] != -1 or parent[i] not in [0,i)   */
+#define SPEC_FLAG_KV_OVERFLOW 4u  /* kv_len < 0 or kv_len + T > max_ctx          */
+
+/* Model shape and capacities, fixed at init.
+ *   Llama-style decoder: RMSNorm, rotary embedding (rotate-half, theta),
+ *   grouped-query attention (n_heads % n_kv_heads == 0), SiLU-gated FFN,
+ *   untied LM head, no biases.
+ *   weight_dtype: SPEC_DTYPE_BF16 or SPEC_DTYPE_F32 for every matrix (the
+ *   embedding and LM head included); norm gains are always fp32.
+ *   max_batch, max_ctx, max_rows_per_seq bound B, the cache length and T.
+ *   Supported: head_dim 64 or 128; d_model, d_ffn multiples of 64;
+ *   max_rows_per_seq <= 128; max_ctx a multiple of 64 (the cache is laid out
+ *   with this stride). */
+typedef struct spec_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype;
+  int32_t max_batch, max_ctx, max_rows_per_seq;
+} spec_config;
+
+/* Sampling for one accept call.
+ *   temperature > 0: p = softmax(z / temperature), speculative sampling.
+ *   temperature == 0: greedy (argmax match, argmax extra token).
+ *   seed, round: the Philox4x64-10 key is (seed, 0) and the counter is
+ *   (slot, sequence, round, 0); u = (word0 >> 40) * 2^-24.
+ *   tree_replacement: 0 if each node's children were drawn from its draft
+ *   distribution without replacement (the rejected token is removed from q'
+ *   and q' renormalised), 1 if drawn with replacement (q' unchanged). */
+typedef struct spec_sampling {
+  float temperature;
+  uint32_t tree_replacement;
+  uint64_t seed;
+  uint64_t round;
+} spec_sampling;
+
+typedef struct spec_handle spec_handle;
+
+/* Bytes of device workspace spec_verify_init needs (scratch activations,
+ * attention partials, accept partials, rotary tables, flag word).
+ * Returns 0 for an invalid config. */
+size_t spec_workspace_bytes(const spec_config* cfg);
+
+/* Bytes of the bf16 KV cache: [L][2][max_batch][Hkv][max_ctx * D].
+ * The K half stores each head's keys as [max_ctx][D] (row per position,
+ * keys already rotated); the V half stores each head's values transposed,
+ * [D][max_ctx].  Returns 0 for an invalid config. */
+size_t spec_kv_cache_bytes(const spec_config* cfg);
+
+/* Create a handle.
+ *   d_weights: n_weights = 1 + 6 * n_layers + 2 device pointers, row-major
+ *     [out, in]: embed [V, d]; per layer attn_norm [d], w_qkv [(Hq+2Hkv)D, d]
+ *     (q rows, then k rows, then v rows), w_o [d, Hq D], ffn_norm [d],
+ *     w_gate_up [2F, d] (gate rows, then up rows), w_down [d, F];
+ *     final_norm [d], lm_head [V, d].  Pointers must be 16-byte aligned.
+ *   d_kv_cache: spec_kv_cache_bytes(cfg) bytes.
+ *   d_workspace: workspace_bytes >= spec_workspace_bytes(cfg), 256-byte aligned.
+ *   The rotary tables are computed on the host in double precision and copied
+ *   into the workspace on `stream` (the only host-to-device copy); init waits
+ *   for that copy before returning.
+ *   Errors: INVALID_ARG (null), SHAPE, CAPACITY (workspace too small),
+ *   UNSUPPORTED (device is not gfx950), DEVICE. */
+spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weights, size_t n_weights,
+                             void* d_kv_cache, void* d_workspace, size_t workspace_bytes,
+                             void* stream, spec_handle** out);
+
+/* The verify forward: logits for B sequences x T rows in one pass.
+ *   d_tokens [B, T] int32: row 0 is the sequence's pending token (the last
+ *     confirmed token, not yet cached), rows 1.. its drafts; for a tree, node
+ *     ids in an order where every parent precedes its children.
+ *   d_kv_len [B] int32: committed cache length of each sequence.
+ *   d_tree_parent: NULL for chain verify (row i sees cached rows and rows
+ *     0..i, at position kv_len + i); else [B, T] int32 parent ids, root -1
+ *     (node i sees cached rows, itself and its ancestors, at position
+ *     kv_len + depth(i)).
+ *   d_logits [B, T, vocab] fp32 output.
+ *   Side effect: every row's K/V (rounded to bf16) is written to cache slot
+ *   kv_len[b] + i.  Slots beyond the length spec_accept commits are left as
+ *   they are (a position-indexed cache abandons a rejected tail for free).
+ *   Errors: INVALID_ARG, CAPACITY (B > max_batch, T > max_rows_per_seq,
+ *   T < 1), DEVICE.  Flags: TOKEN_RANGE, TREE, KV_OVERFLOW. */
+spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
+                             const int32_t* d_kv_len, const int32_t* d_tree_parent,
+                             float* d_logits, void* stream);
+
+/* Speculative-sampling accept and cache commit.
+ *   d_logits [B, T, vocab] fp32 from spec_verify_step.
+ *   d_q: draft probabilities, fp32, rows summing to 1.  Chain: [B, T-1, vocab],
+ *     row j = the distribution draft j+1 was sampled from.  Tree: [B, T, vocab],
+ *     row v = the distribution node v's children were drawn from (rows of
+ *     leaves are not read).  May be NULL when temperature == 0 or for a chain
+ *     with T == 1 (no drafts).
+ *   d_tokens [B, T]: the same tokens given to spec_verify_step.
+ *   d_tree_parent: NULL (chain) or the same parent array.
+ *   d_out_tokens [B, T] int32 output: the n accepted draft tokens followed by
+ *     the resampled / bonus token, then -1 padding.
+ *   d_num_accepted [B] int32 output: n (accepted drafts, bonus excluded).
+ *   d_kv_len [B] input lengths; d_kv_len_out [B] output lengths
+ *     kv_len + n + 1 (may alias d_kv_len).  With a tree, the accepted path's
+ *     K/V are also copied to slots kv_len + 0 .. n.  Pass d_kv_len_out = NULL
+ *     to skip the commit.
+ *   Errors: INVALID_ARG (null where required, temperature < 0 or not finite),
+ *   CAPACITY, DEVICE.  Flags: TOKEN_RANGE (a draft token outside [0, V)),
+ *   TREE. */
+spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_logits,
+                        const float* d_q, const int32_t* d_tokens, const int32_t* d_tree_parent,
+                        const spec_sampling* sampling, int32_t* d_out_tokens,
+                        int32_t* d_num_accepted, const int32_t* d_kv_len, int32_t* d_kv_len_out,
+                        void* stream);
+
+/* Synchronise `stream`, return the sticky device flag word (SPEC_FLAG_*) in
+ * *flags and clear it.  Returns SPEC_OK, or DEVICE if a HIP call failed. */
+spec_status spec_device_errors(spec_handle* h, uint32_t* flags, void* stream);
+
+/* Per-kernel timing with HIP events on the launch stream, for measurement.
+ * When enabled, every launch of each kernel class is bracketed by events;
+ * spec_profile_read synchronises and reports, per class, the launch count,
+ * total milliseconds and the algorithmic bytes those launches had to move
+ * (weights, activations, KV, logits and q, each counted once).  Class names:
+ * "gemm", "attention", "attn_combine", "norm", "embed", "prep", "accept". */
+typedef struct spec_kernel_stat {
+  char name[24];
+  int64_t launches;
+  double total_ms;
+  double algo_bytes;
+} spec_kernel_stat;
+spec_status spec_profile_enable(spec_handle* h, int32_t enable);
+int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out, int32_t reset);
+
+/* Release the handle (host memory and events only). */
+void spec_verify_destroy(spec_handle* h);
+
+/* Static string for a status code. */
+const char* spec_status_str(spec_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,197 @@
+"""Python binding of the MI355X speculative verify step (C ABI in
+include/spec_verify.h).
+
+Argument marshalling only: every function below forwards to the symbol of the
+same name in libspec_verify.so.  Device buffers may be passed as torch tensors
+(their data_ptr() is used) or as raw integer addresses; streams as
+torch.cuda.Stream or raw handles.  Importing the package does not load the
+library; the first call does, and raises if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspec_verify.so")
+
+SPEC_OK = 0
+SPEC_ERR_INVALID_ARG = -1
+SPEC_ERR_SHAPE = -2
+SPEC_ERR_CAPACITY = -3
+SPEC_ERR_UNSUPPORTED = -4
+SPEC_ERR_DEVICE = -5
+SPEC_ERR_STATE = -6
+SPEC_ERR_DATA = -7
+
+SPEC_DTYPE_F32 = 0
+SPEC_DTYPE_BF16 = 1
+
+SPEC_FLAG_TOKEN_RANGE = 1
+SPEC_FLAG_TREE = 2
+SPEC_FLAG_KV_OVERFLOW = 4
+
+EXPORTED = [
+    "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
+    "spec_accept", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
+    "spec_verify_destroy", "spec_status_str",
+]
+
+
+class spec_config(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32),
+                ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_ctx", C.c_int32),
+                ("max_rows_per_seq", C.c_int32)]
+
+
+class spec_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("tree_replacement", C.c_uint32),
+                ("seed", C.c_uint64), ("round", C.c_uint64)]
+
+
+class spec_kernel_stat(C.Structure):
+    _fields_ = [("name", C.c_char * 24), ("launches", C.c_int64), ("total_ms", C.c_double),
+                ("algo_bytes", C.c_double)]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({spec_status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libspec_verify.so (once).  Raises if it is missing: there is no
+    fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not built; run __graft_entry__.build() or "
+                          "python -m speculative_decoding_verify_spec_amd.build")
+    L = C.CDLL(LIB_PATH)
+    vp, sz, i32 = C.c_void_p, C.c_size_t, C.c_int32
+    L.spec_workspace_bytes.argtypes = [C.POINTER(spec_config)]
+    L.spec_workspace_bytes.restype = sz
+    L.spec_kv_cache_bytes.argtypes = [C.POINTER(spec_config)]
+    L.spec_kv_cache_bytes.restype = sz
+    L.spec_verify_init.argtypes = [C.POINTER(spec_config), C.POINTER(vp), sz, vp, vp, sz, vp,
+                                   C.POINTER(vp)]
+    L.spec_verify_init.restype = i32
+    L.spec_verify_step.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
+    L.spec_verify_step.restype = i32
+    L.spec_accept.argtypes = [vp, i32, i32, vp, vp, vp, vp, C.POINTER(spec_sampling), vp, vp, vp, vp, vp]
+    L.spec_accept.restype = i32
+    L.spec_device_errors.argtypes = [vp, C.POINTER(C.c_uint32), vp]
+    L.spec_device_errors.restype = i32
+    L.spec_profile_enable.argtypes = [vp, i32]
+    L.spec_profile_enable.restype = i32
+    L.spec_profile_read.argtypes = [vp, C.POINTER(spec_kernel_stat), i32, i32]
+    L.spec_profile_read.restype = i32
+    L.spec_verify_destroy.argtypes = [vp]
+    L.spec_verify_destroy.restype = None
+    L.spec_status_str.argtypes = [i32]
+    L.spec_status_str.restype = C.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn, st):
+    if st != SPEC_OK:
+        raise SpecError(fn, st)
+
+
+def make_config(shape, max_batch, max_ctx, max_rows_per_seq) -> spec_config:
+    """spec_config from any object with the model-shape attributes."""
+    return spec_config(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                       shape.d_ffn, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
+                       SPEC_DTYPE_BF16 if shape.weight_dtype == "bf16" else SPEC_DTYPE_F32,
+                       int(max_batch), int(max_ctx), int(max_rows_per_seq))
+
+
+def spec_status_str(status: int) -> str:
+    return lib().spec_status_str(int(status)).decode()
+
+
+def spec_workspace_bytes(cfg: spec_config) -> int:
+    return int(lib().spec_workspace_bytes(C.byref(cfg)))
+
+
+def spec_kv_cache_bytes(cfg: spec_config) -> int:
+    return int(lib().spec_kv_cache_bytes(C.byref(cfg)))
+
+
+def spec_verify_init(cfg: spec_config, weights, kv_cache, workspace, workspace_bytes: int, stream=None,
+                     check: bool = True):
+    """Returns the handle (int), or (status, None) when check=False and it fails."""
+    arr = (C.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    h = C.c_void_p()
+    st = lib().spec_verify_init(C.byref(cfg), arr, len(weights), _ptr(kv_cache), _ptr(workspace),
+                                int(workspace_bytes), _stream(stream), C.byref(h))
+    if check:
+        _check("spec_verify_init", st)
+        return h.value
+    return st, h.value
+
+
+def spec_verify_step(h, B, T, tokens, kv_len, tree_parent, logits, stream=None, check=True):
+    st = lib().spec_verify_step(h, int(B), int(T), _ptr(tokens), _ptr(kv_len), _ptr(tree_parent),
+                                _ptr(logits), _stream(stream))
+    if check:
+        _check("spec_verify_step", st)
+    return st
+
+
+def spec_accept(h, B, T, logits, q, tokens, tree_parent, sampling: spec_sampling, out_tokens,
+                num_accepted, kv_len, kv_len_out, stream=None, check=True):
+    st = lib().spec_accept(h, int(B), int(T), _ptr(logits), _ptr(q), _ptr(tokens), _ptr(tree_parent),
+                           C.byref(sampling), _ptr(out_tokens), _ptr(num_accepted), _ptr(kv_len),
+                           _ptr(kv_len_out), _stream(stream))
+    if check:
+        _check("spec_accept", st)
+    return st
+
+
+def spec_device_errors(h, stream=None) -> int:
+    v = C.c_uint32(0)
+    _check("spec_device_errors", lib().spec_device_errors(h, C.byref(v), _stream(stream)))
+    return int(v.value)
+
+
+def spec_profile_enable(h, enable: bool):
+    _check("spec_profile_enable", lib().spec_profile_enable(h, 1 if enable else 0))
+
+
+def spec_profile_read(h, reset: bool = True):
+    arr = (spec_kernel_stat * 32)()
+    n = lib().spec_profile_read(h, arr, 32, 1 if reset else 0)
+    if n < 0:
+        raise SpecError("spec_profile_read", SPEC_ERR_DEVICE)
+    return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms),
+                                   "algo_bytes": float(arr[i].algo_bytes)} for i in range(n)}
+
+
+def spec_verify_destroy(h):
+    if h:
+        lib().spec_verify_destroy(h)

@@ -1,0 +1,556 @@
+// Speculative-sampling accept, residual resample, bonus token and KV commit.
+//
+// CS349E Lecture 6 ("Optimizing Autoregressive Decode"), section 6.2 steps
+// 3-5: accept draft x_i when u_i < p_i(x_i)/q_i(x_i) (evaluated as
+// u_i * q_i(x_i) < p_i(x_i), the form the Kimi-K3 tuning page describes), stop
+// at the first rejection, then draw from norm(max(0, p_{n+1} - q_{n+1})) or,
+// when every draft survived, a bonus token from p_{gamma+1}.  Greedy
+// (section 7.4): longest prefix where draft == argmax, then that argmax.
+// Token trees (section 10.3): walk from the root, testing each node's children
+// in order against a running residual (see accept_tree_sampled_kernel).
+//
+// The vocabulary is cut into chunks of CH entries so a handful of rows still
+// fills the GPU:
+//   1. rowstats  (grid chunks x rows): per-chunk max and sum of exp (or argmax)
+//   2. residual  (grid chunks x sequences): every workgroup combines the row
+//      statistics, replays the accept tests (cheap: gamma lookups), and sums
+//      the residual over its chunk
+//   3. sample    (one workgroup per sequence): inverse CDF over chunk sums,
+//      then a scan inside the chosen chunk; writes tokens and the commit.
+// Sampling is inverse CDF in token-id order: the token is the smallest x with
+// sum_{y<=x} r(y) > u * R.  Greedy ties go to the lowest id.  A residual with
+// no mass in floating point falls back to p.
+#include "common.h"
+#include "launch.h"
+
+namespace sv {
+
+constexpr int CH = 4096;
+int accept_chunks(int V) { return (V + CH - 1) / CH; }
+
+// Block-wide sum / max for blockDim.x a multiple of 64 (<= 1024).
+template <typename Tv>
+DEVI Tv block_sum(Tv v, Tv* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  Tv t = 0;
+  for (int i = 0; i < nw; ++i) t += sh[i];
+  return t;
+}
+DEVI float block_max(float v, float* sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, sh[i]);
+  return t;
+}
+
+DEVI bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+// ---------------------------------------------------------------- pass 1
+template <bool GREEDY>
+__global__ __launch_bounds__(256) void accept_rowstats_kernel(AcceptParams p) {
+  __shared__ float shf[16];
+  __shared__ int shi[16];
+  const int c = blockIdx.x, row = blockIdx.y;
+  const float* z = p.logits + (size_t)row * p.V;
+  const int y0 = c * CH, y1 = min(p.V, y0 + CH);
+  float* out = p.rowstat + ((size_t)row * p.nch + c) * 2;
+  if (GREEDY) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int y = y0 + threadIdx.x; y < y1; y += 256) {
+      const float v = z[y];
+      if (better(v, y, bv, bi)) { bv = v; bi = y; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if ((threadIdx.x & 63) == 0) { shf[threadIdx.x >> 6] = bv; shi[threadIdx.x >> 6] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float v0 = shf[0];
+      int i0 = shi[0];
+      for (int i = 1; i < 4; ++i)
+        if (better(shf[i], shi[i], v0, i0)) { v0 = shf[i]; i0 = shi[i]; }
+      out[0] = v0;
+      out[1] = __int_as_float(i0);
+    }
+    return;
+  }
+  const float Tt = p.temperature;
+  float mx = -INFINITY;
+  for (int y = y0 + threadIdx.x; y < y1; y += 256) mx = fmaxf(mx, z[y] / Tt);
+  mx = block_max(mx, shf);
+  float s = 0.f;
+  for (int y = y0 + threadIdx.x; y < y1; y += 256) s += expf(z[y] / Tt - mx);
+  s = block_sum(s, shf);
+  if (threadIdx.x == 0) { out[0] = mx; out[1] = s; }
+}
+
+// Combine the chunk statistics of one row: M = max, S = sum exp(z/T - M).
+DEVI void row_ms(const AcceptParams& p, int row, float& M, float& S) {
+  const float* st = p.rowstat + (size_t)row * p.nch * 2;
+  M = -INFINITY;
+  for (int c = 0; c < p.nch; ++c) M = fmaxf(M, st[2 * c]);
+  S = 0.f;
+  for (int c = 0; c < p.nch; ++c) S += st[2 * c + 1] * expf(st[2 * c] - M);
+}
+DEVI void row_argmax(const AcceptParams& p, int row, int& idx) {
+  const float* st = p.rowstat + (size_t)row * p.nch * 2;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int c = 0; c < p.nch; ++c) {
+    const float v = st[2 * c];
+    const int i = __float_as_int(st[2 * c + 1]);
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  idx = bi;
+}
+
+DEVI int clamp_token(const AcceptParams& p, int x, bool& bad) {
+  bad = (x < 0 || x >= p.V);
+  if (bad) atomicOr(p.flags, FLAG_TOKEN_RANGE);
+  return x < 0 ? 0 : (x >= p.V ? p.V - 1 : x);
+}
+
+// ---------------------------------------------------------------- chain, pass 2
+__global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams p) {
+  __shared__ float sM[128], sS[128];
+  __shared__ int sn;
+  __shared__ float shf[16];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int T = p.T, gamma = T - 1;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    float M, S;
+    row_ms(p, b * T + i, M, S);
+    sM[i] = M;
+    sS[i] = S;
+    if (c == 0) { p.rowms[2 * (b * T + i)] = M; p.rowms[2 * (b * T + i) + 1] = S; }
+  }
+  __syncthreads();
+  const float Tt = p.temperature;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int i = 0; i < gamma; ++i) {
+      bool bad;
+      const int x = clamp_token(p, p.tokens[b * T + i + 1], bad);
+      if (bad) break;
+      const float pz = expf(p.logits[((size_t)(b * T + i)) * p.V + x] / Tt - sM[i]) / sS[i];
+      const float qx = p.q[((size_t)(b * gamma + i)) * p.V + x];
+      const float u = philox_uniform(p.seed, p.round, b, i);
+      if (u * qx < pz) ++n;
+      else break;
+    }
+    sn = n;
+    if (c == 0) p.nacc[b] = n;
+  }
+  __syncthreads();
+  const int n = sn;
+  const float* z = p.logits + ((size_t)(b * T + n)) * p.V;
+  const float* q = (n < gamma) ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
+  const float M = sM[n], S = sS[n];
+  const int y0 = c * CH, y1 = min(p.V, y0 + CH);
+  float acc = 0.f;
+  for (int y = y0 + threadIdx.x; y < y1; y += 256) {
+    const float pv = expf(z[y] / Tt - M) / S;
+    acc += q ? fmaxf(0.f, pv - q[y]) : pv;
+  }
+  acc = block_sum(acc, shf);
+  if (threadIdx.x == 0) p.rsum[(size_t)b * p.nch + c] = acc;
+}
+
+// Write the sequence's outputs: n accepted drafts, the extra token, -1 padding,
+// and the chain commit kv_len + n + 1.
+DEVI void write_chain_outputs(const AcceptParams& p, int b, int n, int extra) {
+  const int T = p.T;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    int v = -1;
+    if (i < n) v = p.tokens[b * T + i + 1];
+    else if (i == n) v = extra;
+    p.out_tokens[b * T + i] = v;
+  }
+  if (threadIdx.x == 0) {
+    p.num_accepted[b] = n;
+    if (p.kv_len_out) p.kv_len_out[b] = p.kv_len[b] + n + 1;
+  }
+}
+
+// ---------------------------------------------------------------- chain, pass 3
+__global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p) {
+  constexpr int PER = CH / 256;
+  __shared__ double shd[16];
+  __shared__ int s_c, s_deg, s_tok;
+  __shared__ double s_base, s_t;
+  const int b = blockIdx.x;
+  const int T = p.T, gamma = T - 1;
+  const int n = p.nacc[b];
+  const int row = b * T + n;
+  const float M = p.rowms[2 * row], S = p.rowms[2 * row + 1];
+  const float Tt = p.temperature;
+  if (threadIdx.x == 0) {
+    double R = 0.0;
+    for (int c = 0; c < p.nch; ++c) R += (double)p.rsum[(size_t)b * p.nch + c];
+    int deg = !(R > 0.0);
+    const float* st = p.rowstat + (size_t)row * p.nch * 2;
+    if (deg) {
+      R = 0.0;
+      for (int c = 0; c < p.nch; ++c) R += (double)(st[2 * c + 1] * expf(st[2 * c] - M) / S);
+    }
+    const double t = (double)philox_uniform(p.seed, p.round, b, gamma) * R;
+    double cum = 0.0;
+    int cs = p.nch - 1;
+    double base = 0.0;
+    for (int c = 0; c < p.nch; ++c) {
+      const double v = deg ? (double)(st[2 * c + 1] * expf(st[2 * c] - M) / S)
+                           : (double)p.rsum[(size_t)b * p.nch + c];
+      if (cum + v > t) { cs = c; base = cum; break; }
+      cum += v;
+      base = cum;
+    }
+    s_c = cs; s_deg = deg; s_base = base; s_t = t; s_tok = 0x7fffffff;
+  }
+  __syncthreads();
+  const int c = s_c;
+  const bool use_res = (n < gamma) && !s_deg;
+  const float* z = p.logits + (size_t)row * p.V;
+  const float* q = use_res ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
+  const int y0 = c * CH + threadIdx.x * PER;
+  float r[PER];
+  float loc = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + e;
+    float v = 0.f;
+    if (y < p.V) {
+      const float pv = expf(z[y] / Tt - M) / S;
+      v = q ? fmaxf(0.f, pv - q[y]) : pv;
+    }
+    r[e] = v;
+    loc += v;
+  }
+  // exclusive scan of the per-thread sums (double)
+  __shared__ double scan[256];
+  scan[threadIdx.x] = (double)loc;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    double add = threadIdx.x >= o ? scan[threadIdx.x - o] : 0.0;
+    __syncthreads();
+    scan[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const double excl = scan[threadIdx.x] - (double)loc;
+  const double t = s_t;
+  double run = s_base + excl;
+  if (run <= t && run + (double)loc > t) {
+    int found = -1;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      run += (double)r[e];
+      if (found < 0 && run > t) found = y0 + e;
+    }
+    if (found >= 0) atomicMin(&s_tok, found);
+  }
+  __syncthreads();
+  if (s_tok == 0x7fffffff) {
+    // rounding left the crossing past the chunk's recomputed total: the last
+    // token of the chunk with positive mass is the answer
+    int last = -1;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (r[e] > 0.f && y0 + e < p.V) last = y0 + e;
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = -1;
+    __syncthreads();
+    if (last >= 0) atomicMax(&s_last, last);
+    __syncthreads();
+    if (threadIdx.x == 0) s_tok = s_last >= 0 ? s_last : c * CH;
+    __syncthreads();
+  }
+  write_chain_outputs(p, b, n, s_tok);
+}
+
+// ---------------------------------------------------------------- chain, greedy
+__global__ __launch_bounds__(128) void accept_chain_greedy_kernel(AcceptParams p) {
+  __shared__ int am[128];
+  __shared__ int s_n;
+  const int b = blockIdx.x, T = p.T, gamma = T - 1;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, b * T + i, am[i]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < gamma) {
+      bool bad;
+      const int x = clamp_token(p, p.tokens[b * T + n + 1], bad);
+      if (bad || x != am[n]) break;
+      ++n;
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  write_chain_outputs(p, b, s_n, am[s_n]);
+}
+
+// ---------------------------------------------------------------- tree
+// Validate the parent array and build child lists (children in ascending id).
+DEVI void build_tree(const AcceptParams& p, int b, int* first_child, int* next_sib) {
+  const int T = p.T;
+  const int32_t* par = p.parent + (size_t)b * T;
+  for (int v = 0; v < T; ++v) { first_child[v] = -1; next_sib[v] = -1; }
+  bool bad = par[0] != -1;
+  for (int c = T - 1; c >= 1; --c) {
+    int pc = par[c];
+    if (pc < 0 || pc >= c) { bad = true; pc = c - 1; }
+    next_sib[c] = first_child[pc];
+    first_child[pc] = c;
+  }
+  if (bad) atomicOr(p.flags, FLAG_TREE);
+}
+
+// Copy the accepted path's K/V (path[j] -> slot kv_len + j) in ascending j;
+// node path[j] >= j, so no copy overwrites a slot a later copy still reads.
+DEVI void tree_commit(const AcceptParams& p, int b, const int* path, int plen) {
+  if (!p.kv_len_out) return;
+  const int base = p.kv_len[b];
+  if (threadIdx.x == 0) p.kv_len_out[b] = base + plen;
+  if (base < 0 || base + p.T > p.max_ctx) return;
+  const size_t per = (size_t)p.maxB * p.Hkv * p.max_ctx * p.D;  // one K or V region
+  const int nel = p.L * p.Hkv * p.D;
+  for (int e = threadIdx.x; e < nel; e += blockDim.x) {
+    const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
+    uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per + ((size_t)b * p.Hkv + hk) * p.max_ctx * p.D + d;
+    uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per + (((size_t)b * p.Hkv + hk) * p.D + d) * p.max_ctx;
+    for (int j = 1; j < plen; ++j) {
+      const int src = path[j];
+      if (src == j) continue;
+      kreg[(size_t)(base + j) * p.D] = kreg[(size_t)(base + src) * p.D];
+      vreg[base + j] = vreg[base + src];
+    }
+  }
+}
+
+DEVI void write_tree_outputs(const AcceptParams& p, int b, const int* path, int plen, int extra) {
+  const int T = p.T;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    int v = -1;
+    if (i < plen - 1) v = p.tokens[b * T + path[i + 1]];
+    else if (i == plen - 1) v = extra;
+    p.out_tokens[b * T + i] = v;
+  }
+  if (threadIdx.x == 0) p.num_accepted[b] = plen - 1;
+}
+
+__global__ __launch_bounds__(128) void accept_tree_greedy_kernel(AcceptParams p) {
+  __shared__ int first_child[128], next_sib[128], path[128], am[128];
+  __shared__ int s_plen, s_extra;
+  const int b = blockIdx.x, T = p.T;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, b * T + i, am[i]);
+  if (threadIdx.x == 0) build_tree(p, b, first_child, next_sib);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int v = 0, plen = 1;
+    path[0] = 0;
+    while (true) {
+      int nxt = -1;
+      for (int c = first_child[v]; c >= 0; c = next_sib[c]) {
+        bool bad;
+        const int x = clamp_token(p, p.tokens[b * T + c], bad);
+        if (!bad && x == am[v]) { nxt = c; break; }
+      }
+      if (nxt < 0) break;
+      v = nxt;
+      path[plen++] = v;
+    }
+    s_plen = plen;
+    s_extra = am[v];
+  }
+  __syncthreads();
+  write_tree_outputs(p, b, path, s_plen, s_extra);
+  tree_commit(p, b, path, s_plen);
+}
+
+// Sampled tree walk, one workgroup per sequence.  At node v the running target
+// r starts as p_v and the draft q' as q_v.  Child c (token x, uniform slot
+// c - 1) is accepted when u * q'(x) < r(x).  A rejection replaces r by
+// norm(max(0, r - q')) (a pass over the vocabulary into one of two ping-pong
+// buffers) and, without replacement, removes x from q' and renormalises.  No
+// child accepted: draw from r; a leaf reached: bonus from p_leaf (slot T - 1).
+__global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams p) {
+  __shared__ int first_child[128], next_sib[128], path[128], removed[128];
+  __shared__ double shd[16];
+  __shared__ float s_M, s_S, s_Zr, s_qmass, s_qtot;
+  __shared__ int s_cur, s_acc, s_nrem, s_tok;
+  __shared__ double s_t;
+  const int b = blockIdx.x, T = p.T, V = p.V;
+  const float Tt = p.temperature;
+  float* rb0 = p.rbuf + (size_t)b * V;
+  float* rb1 = p.rbuf + ((size_t)p.B + b) * V;
+  if (threadIdx.x == 0) build_tree(p, b, first_child, next_sib);
+  __syncthreads();
+  int v = 0, plen = 1;
+  if (threadIdx.x == 0) path[0] = 0;
+  while (true) {
+    const int row = b * T + v;
+    const float* z = p.logits + (size_t)row * V;
+    const float* qv = p.q + (size_t)row * V;
+    if (threadIdx.x == 0) {
+      float M, S;
+      row_ms(p, row, M, S);
+      s_M = M; s_S = S; s_cur = -1; s_Zr = 1.f; s_nrem = 0; s_qmass = 0.f; s_qtot = -1.f;
+    }
+    __syncthreads();
+    int c = first_child[v];
+    int accepted = -1;
+    while (c >= 0) {
+      if (threadIdx.x == 0) {
+        bool bad;
+        const int x = clamp_token(p, p.tokens[b * T + c], bad);
+        const float u = philox_uniform(p.seed, p.round, b, c - 1);
+        const float rx = (s_cur < 0) ? expf(z[x] / Tt - s_M) / s_S : (s_cur == 0 ? rb0 : rb1)[x] / s_Zr;
+        float qx = qv[x];
+        if (!p.replacement && s_nrem > 0) {
+          bool gone = false;
+          for (int i = 0; i < s_nrem; ++i) gone |= removed[i] == x;
+          qx = gone ? 0.f : qx / (s_qtot - s_qmass);
+        }
+        s_acc = (!bad && u * qx < rx) ? 1 : 0;
+        removed[s_nrem] = x;  // recorded now, counted only after a rejection
+      }
+      __syncthreads();
+      if (s_acc) { accepted = c; break; }
+      // rejection: r <- max(0, r - q') into the other buffer
+      const int cur = s_cur;
+      const float* src = cur == 1 ? rb1 : rb0;
+      float* dst = cur == 0 ? rb1 : rb0;
+      const float M = s_M, S = s_S, Zr = s_Zr;
+      const int nrem = s_nrem;
+      const float qscale = (!p.replacement && nrem > 0) ? 1.0f / (s_qtot - s_qmass) : 1.0f;
+      double zs = 0.0, qs = 0.0;
+      for (int y = threadIdx.x; y < V; y += blockDim.x) {
+        const float ry = cur < 0 ? expf(z[y] / Tt - M) / S : src[y] / Zr;
+        float qy = qv[y];
+        qs += (double)qy;
+        if (!p.replacement) {
+          bool gone = false;
+          for (int i = 0; i < nrem; ++i) gone |= removed[i] == y;
+          if (gone) qy = 0.f;
+        }
+        const float d = fmaxf(0.f, ry - qy * qscale);
+        dst[y] = d;
+        zs += (double)d;
+      }
+      zs = block_sum(zs, shd);
+      qs = block_sum(qs, shd);
+      if (threadIdx.x == 0) {
+        if (zs > 0.0) { s_cur = (cur == 0) ? 1 : 0; s_Zr = (float)zs; }
+        if (!p.replacement) {
+          if (s_qtot < 0.f) s_qtot = (float)qs;
+          s_qmass += qv[removed[s_nrem]];
+          s_nrem = s_nrem + 1;
+        }
+      }
+      __syncthreads();
+      c = next_sib[c];
+    }
+    if (accepted < 0) break;
+    v = accepted;
+    if (threadIdx.x == 0) path[plen] = v;
+    ++plen;
+    if (first_child[v] < 0) {
+      // leaf: bonus from p_leaf
+      if (threadIdx.x == 0) {
+        float M, S;
+        row_ms(p, b * T + v, M, S);
+        s_M = M; s_S = S; s_cur = -1; s_Zr = 1.f;
+      }
+      __syncthreads();
+      break;
+    }
+  }
+  // final draw from r (s_cur, s_Zr) or p_v (s_cur < 0) at node v, slot T - 1
+  {
+    const int row = b * T + v;
+    const float* z = p.logits + (size_t)row * V;
+    const int cur = s_cur;
+    const float* src = cur == 1 ? rb1 : rb0;
+    const float M = s_M, S = s_S;
+    const int per = (V + blockDim.x - 1) / blockDim.x;
+    const int y0 = threadIdx.x * per, y1 = min(V, y0 + per);
+    double loc = 0.0;
+    for (int y = y0; y < y1; ++y) loc += (double)(cur < 0 ? expf(z[y] / Tt - M) / S : src[y]);
+    __shared__ double scan[1024];
+    scan[threadIdx.x] = loc;
+    if (threadIdx.x == 0) s_tok = 0x7fffffff;
+    __syncthreads();
+    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+      double add = threadIdx.x >= o ? scan[threadIdx.x - o] : 0.0;
+      __syncthreads();
+      scan[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const double R = scan[blockDim.x - 1];
+    if (threadIdx.x == 0) s_t = (double)philox_uniform(p.seed, p.round, b, T - 1) * R;
+    __syncthreads();
+    const double t = s_t;
+    double run = scan[threadIdx.x] - loc;
+    if (run <= t && run + loc > t) {
+      for (int y = y0; y < y1; ++y) {
+        run += (double)(cur < 0 ? expf(z[y] / Tt - M) / S : src[y]);
+        if (run > t) { atomicMin(&s_tok, y); break; }
+      }
+    }
+    __syncthreads();
+    if (s_tok == 0x7fffffff) {
+      // rounding: take the last token with positive mass
+      int last = -1;
+      for (int y = y0; y < y1; ++y)
+        if ((cur < 0 ? expf(z[y] / Tt - M) / S : src[y]) > 0.f) last = y;
+      __shared__ int s_last;
+      if (threadIdx.x == 0) s_last = -1;
+      __syncthreads();
+      if (last >= 0) atomicMax(&s_last, last);
+      __syncthreads();
+      if (threadIdx.x == 0) s_tok = s_last >= 0 ? s_last : 0;
+      __syncthreads();
+    }
+  }
+  write_tree_outputs(p, b, path, plen, s_tok);
+  tree_commit(p, b, path, plen);
+}
+
+hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
+  const bool greedy = p.temperature == 0.f;
+  dim3 g1(p.nch, p.B * p.T);
+  if (greedy)
+    accept_rowstats_kernel<true><<<g1, 256, 0, s>>>(p);
+  else
+    accept_rowstats_kernel<false><<<g1, 256, 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.parent) {
+    if (greedy) accept_tree_greedy_kernel<<<p.B, 128, 0, s>>>(p);
+    else accept_tree_sampled_kernel<<<p.B, 1024, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  if (greedy) {
+    accept_chain_greedy_kernel<<<p.B, 128, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  accept_chain_residual_kernel<<<dim3(p.nch, p.B), 256, 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  accept_chain_sample_kernel<<<p.B, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,83 @@
+// Device helpers shared by the verify-step kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define DEVI __device__ __forceinline__
+
+// --- bf16 -----------------------------------------------------------------
+// A dword holding two bf16 values: low half is element 0, high half element 1.
+DEVI float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+DEVI float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+DEVI float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+DEVI uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 significant bits,
+// relative error <= 2^-17.  Used to feed fp32 activations to bf16 MFMA.
+DEVI void split_bf16(float x, short& hi, short& lo) {
+  uint32_t h = f32_to_bf16_rne(x);
+  float r = x - __uint_as_float(h << 16);
+  hi = (short)h;
+  lo = (short)f32_to_bf16_rne(r);
+}
+
+// --- MFMA -----------------------------------------------------------------
+// D(16x16, fp32) += A(16x16, bf16) * B(16x16, bf16).
+// Lane l holds A[l%16][4(l/16) + e], B[4(l/16) + e][l%16] (e = 0..3) and
+// D[4(l/16) + e][l%16].
+DEVI floatx4 mfma16x16x16(shortx4 a, shortx4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// --- wave reductions ------------------------------------------------------
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEVI float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// --- Philox4x64-10 (Salmon et al., SC'11) -----------------------------------
+// Key (seed, 0), counter (slot, sequence, round, 0); the accept uniform is
+// u = (word0 >> 40) * 2^-24.
+DEVI uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                               uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+DEVI float philox_uniform(uint64_t seed, uint64_t round, int b, int slot) {
+  uint64_t w = philox4x64_word0((uint64_t)slot, (uint64_t)b, round, 0ull, seed, 0ull);
+  return (float)(w >> 40) * 0x1p-24f;
+}
+
+#define FLAG_TOKEN_RANGE 1u
+#define FLAG_TREE 2u
+#define FLAG_KV_OVERFLOW 4u

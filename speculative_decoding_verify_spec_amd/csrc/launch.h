@@ -1,0 +1,117 @@
+// Internal interface between the runtime (runtime.hip) and the kernel files.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+// ---------------------------------------------------------------- prep / embed / norm
+struct PrepParams {
+  const int32_t* tokens;  // [B, T]
+  const int32_t* kv_len;  // [B]
+  const int32_t* parent;  // [B, T] or null (chain)
+  int32_t* tok;           // [M] clamped token ids
+  int32_t* pos;           // [M] rotary position
+  int32_t* slot;          // [M] cache slot, -1 when it would overflow
+  uint64_t* anc;          // [M][2] ancestor-or-self bitmask (tree only)
+  uint32_t* flags;
+  int B, T, vocab, max_ctx;
+};
+hipError_t launch_prep(const PrepParams& p, hipStream_t s);
+
+hipError_t launch_embed(const void* E, int wdtype, const int32_t* tok, float* x, int M, int d,
+                        hipStream_t s);
+
+// h[m] = x[m] / sqrt(mean(x[m]^2) + eps) * g
+hipError_t launch_rmsnorm(const float* x, const float* g, float* h, int M, int d, float eps,
+                          hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+
+struct GemmParams {
+  const void* W;  // [N][K], bf16 or fp32
+  int wdtype;     // 0 fp32, 1 bf16
+  const float* X; // [M][ldx] fp32
+  int ldx;
+  int M, N, K;    // N = output rows of W used by the epilogue mapping
+  int epi;
+  float* out;     // STORE / RESID / SWIGLU: [M][ldo]
+  int ldo;
+  int F;          // SWIGLU: gate rows [0,F), up rows [F,2F)
+  // QKV epilogue
+  int m0;                   // global row offset of this launch (row chunking)
+  const int32_t* pos;       // [M_total]
+  const int32_t* slot;      // [M_total]
+  const float* rope_cos;    // [max_ctx][D/2]
+  const float* rope_sin;
+  float* q_out;             // [M_total][Hq][D]
+  float* k_out;             // [M_total][Hkv][D]
+  float* v_out;
+  uint16_t* kcache;         // this layer's K region [maxB][Hkv][max_ctx][D]
+  uint16_t* vcache;         // this layer's V region [maxB][Hkv][D][max_ctx]
+  int T, Hq, Hkv, D, max_ctx;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnParams {
+  const float* q;          // [M][Hq][D] rotated queries
+  const uint16_t* kc;      // layer K region
+  const uint16_t* vc;      // layer V region
+  const int32_t* kv_len;   // [B]
+  float* part_o;           // [nsplit][B][Hkv][nq][D]
+  float* part_ml;          // [nsplit][B][Hkv][nq][2]
+  int B, T, Hq, Hkv, D, max_ctx;
+  int splits;              // workgroups per (sequence, kv head, query group)
+  float scale;
+};
+// number of partial slots per query the context kernel writes
+int attn_nsplit(int splits);
+int attn_query_tiles_per_wave(int nq);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_ml;
+  int nsplit;
+  const float* q;          // [M][Hq][D]
+  const float* k_suf;      // [M][Hkv][D]
+  const float* v_suf;
+  const uint64_t* anc;     // [M][2] or null for chain
+  float* out;              // [M][Hq][D]
+  int B, T, Hq, Hkv, D;
+  float scale;
+};
+hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- accept
+struct AcceptParams {
+  const float* logits;     // [B][T][V]
+  const float* q;          // chain [B][T-1][V], tree [B][T][V]
+  const int32_t* tokens;   // [B][T]
+  const int32_t* parent;   // [B][T] or null
+  float temperature;
+  int replacement;
+  uint64_t seed, round;
+  int32_t* out_tokens;     // [B][T]
+  int32_t* num_accepted;   // [B]
+  const int32_t* kv_len;   // [B]
+  int32_t* kv_len_out;     // [B] or null
+  // scratch
+  float* rowstat;          // [B*T][nch][2]
+  float* rowms;            // [B*T][2]
+  float* rsum;             // [B][nch]
+  int32_t* nacc;           // [B]
+  float* rbuf;             // [2][B][V]
+  uint32_t* flags;
+  // cache for the tree commit
+  uint16_t* kv_cache;
+  int L, maxB, Hkv, D, max_ctx;
+  int B, T, V, nch;
+};
+int accept_chunks(int V);
+hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
+
+}  // namespace sv

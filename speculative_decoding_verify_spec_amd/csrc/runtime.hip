@@ -1,0 +1,436 @@
+// Host runtime behind the C ABI: validation, workspace carving, the launch
+// sequence of one verify step, accept dispatch and per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/spec_verify.h"
+#include "launch.h"
+
+using namespace sv;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) & ~(ALIGN - 1); }
+
+bool valid_config(const spec_config* c) {
+  if (!c) return false;
+  if (c->n_layers < 1 || c->d_model < 64 || c->n_heads < 1 || c->n_kv_heads < 1 || c->d_ffn < 64 ||
+      c->vocab < 2)
+    return false;
+  if (c->n_heads % c->n_kv_heads) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->d_model % 64 || c->d_ffn % 64 || (c->n_heads * c->head_dim) % 64) return false;
+  if (c->weight_dtype != SPEC_DTYPE_F32 && c->weight_dtype != SPEC_DTYPE_BF16) return false;
+  if (c->max_batch < 1 || c->max_rows_per_seq < 1 || c->max_rows_per_seq > 128) return false;
+  if (c->max_ctx < 64 || c->max_ctx % 64 || c->max_ctx < c->max_rows_per_seq) return false;
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return false;
+  return true;
+}
+
+// Attention workgroups per (sequence, KV head, query group): about 256 keys
+// each, capped so the grid stays near 2048 workgroups.
+int attn_splits(const spec_config& c, int B, int T) {
+  const int nq = (c.n_heads / c.n_kv_heads) * T;
+  const int QT = attn_query_tiles_per_wave(nq);
+  const int nqg = (nq + 16 * QT - 1) / (16 * QT);
+  const int units = B * c.n_kv_heads * nqg;
+  int s = (c.max_ctx + 255) / 256;
+  const int cap = std::max(1, (2048 + units - 1) / units);
+  s = std::min(s, cap);
+  return std::max(1, std::min(s, 64));
+}
+
+struct Layout {
+  size_t x, h, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
+  size_t tok, pos, slot, anc, rowstat, rowms, rsum, nacc, rbuf, flags, total;
+};
+
+Layout plan(const spec_config& c) {
+  Layout L{};
+  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
+  const size_t D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  size_t part = 0;
+  for (int B = 1; B <= c.max_batch; ++B)
+    for (int T = 1; T <= c.max_rows_per_seq; ++T) {
+      const size_t n = (size_t)attn_nsplit(attn_splits(c, B, T)) * B * Hq * T;
+      part = std::max(part, n);
+    }
+  const int nch = accept_chunks(c.vocab);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.x = take(Mmax * c.d_model * 4);
+  L.h = take(Mmax * c.d_model * 4);
+  L.q = take(Mmax * Hq * D * 4);
+  L.ksuf = take(Mmax * Hkv * D * 4);
+  L.vsuf = take(Mmax * Hkv * D * 4);
+  L.attn = take(Mmax * Hq * D * 4);
+  L.act = take(Mmax * c.d_ffn * 4);
+  L.part_o = take(part * D * 4);
+  L.part_ml = take(part * 2 * 4);
+  L.rope_cos = take((size_t)c.max_ctx * (D / 2) * 4);
+  L.rope_sin = take((size_t)c.max_ctx * (D / 2) * 4);
+  L.tok = take(Mmax * 4);
+  L.pos = take(Mmax * 4);
+  L.slot = take(Mmax * 4);
+  L.anc = take(Mmax * 2 * 8);
+  L.rowstat = take(Mmax * nch * 2 * 4);
+  L.rowms = take(Mmax * 2 * 4);
+  L.rsum = take((size_t)c.max_batch * nch * 4);
+  L.nacc = take((size_t)c.max_batch * 4);
+  L.rbuf = take(2 * (size_t)c.max_batch * c.vocab * 4);
+  L.flags = take(256);
+  L.total = off;
+  return L;
+}
+
+const char* kClassNames[] = {"prep", "embed", "rmsnorm", "gemm_qkv", "attention", "attn_combine",
+                             "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head", "accept"};
+enum KClass { K_PREP, K_EMBED, K_NORM, K_QKV, K_ATTN, K_COMB, K_O, K_GU, K_DOWN, K_LM, K_ACC, K_N };
+
+}  // namespace
+
+struct spec_handle {
+  spec_config cfg;
+  int device = 0;
+  std::vector<const void*> w;
+  uint16_t* kv = nullptr;
+  char* ws = nullptr;
+  Layout lay{};
+  // profiling
+  bool prof = false;
+  struct Rec {
+    int cls;
+    hipEvent_t a, b;
+    double bytes;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[K_N] = {};
+  double ms[K_N] = {};
+  double bytes[K_N] = {};
+
+  template <typename P>
+  P* at(size_t off) const { return (P*)(ws + off); }
+  const void* W(size_t i) const { return w[i]; }
+  size_t layer_w(int l, int k) const { return 1 + 6 * (size_t)l + k; }
+
+  hipEvent_t ev() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+// Bracket one launch with events when profiling is on.
+template <typename F>
+hipError_t timed(spec_handle* h, int cls, double bytes, hipStream_t s, F&& launch) {
+  if (!h->prof) return launch();
+  hipEvent_t a = h->ev(), b = h->ev();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipEventRecord(a, s);
+  hipError_t e = launch();
+  hipEventRecord(b, s);
+  h->recs.push_back({cls, a, b, bytes});
+  return e;
+}
+
+spec_status dev(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_DEVICE; }
+
+// GEMM over M rows in launches of at most 8 activation rows.
+hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
+  const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
+  size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    GemmParams q = p;
+    q.M = std::min(8, M - m0);
+    q.X = p.X + (size_t)m0 * p.ldx;
+    q.m0 = m0;
+    if (p.out) q.out = p.out + (size_t)m0 * p.ldo;
+    const size_t out_cols = (p.epi == EPI_SWIGLU) ? p.F : (p.epi == EPI_QKV ? p.N : p.N);
+    double bytes = (double)q.M * p.K * 4 + (double)q.M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
+    if (m0 == 0) bytes += (double)nrows * p.K * wbytes;  // weights count once per GEMM
+    hipError_t e = timed(h, cls, bytes, s, [&] { return launch_gemm(q, s); });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_str(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_INVALID_ARG: return "invalid argument";
+    case SPEC_ERR_SHAPE: return "unsupported model shape";
+    case SPEC_ERR_CAPACITY: return "beyond the capacity given at init";
+    case SPEC_ERR_UNSUPPORTED: return "unsupported dtype or device";
+    case SPEC_ERR_DEVICE: return "HIP runtime error";
+    case SPEC_ERR_STATE: return "invalid handle state";
+    case SPEC_ERR_DATA: return "device-side data error";
+    default: return "unknown status";
+  }
+}
+
+size_t spec_workspace_bytes(const spec_config* cfg) {
+  if (!valid_config(cfg)) return 0;
+  return plan(*cfg).total;
+}
+
+size_t spec_kv_cache_bytes(const spec_config* c) {
+  if (!valid_config(c)) return 0;
+  return (size_t)c->n_layers * 2 * c->max_batch * c->n_kv_heads * (size_t)c->max_ctx * c->head_dim * 2;
+}
+
+spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weights, size_t n_weights,
+                             void* d_kv_cache, void* d_workspace, size_t workspace_bytes,
+                             void* stream, spec_handle** out) {
+  if (!cfg || !d_weights || !d_kv_cache || !d_workspace || !out) return SPEC_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!valid_config(cfg)) return SPEC_ERR_SHAPE;
+  const size_t nw = 1 + 6 * (size_t)cfg->n_layers + 2;
+  if (n_weights != nw) return SPEC_ERR_INVALID_ARG;
+  for (size_t i = 0; i < nw; ++i)
+    if (!d_weights[i] || ((uintptr_t)d_weights[i] & 15)) return SPEC_ERR_INVALID_ARG;
+  if ((uintptr_t)d_workspace & (ALIGN - 1)) return SPEC_ERR_INVALID_ARG;
+  Layout L = plan(*cfg);
+  if (workspace_bytes < L.total) return SPEC_ERR_CAPACITY;
+
+  int devid = 0;
+  if (hipGetDevice(&devid) != hipSuccess) return SPEC_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, devid) != hipSuccess) return SPEC_ERR_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SPEC_ERR_UNSUPPORTED;
+
+  spec_handle* h = new spec_handle();
+  h->cfg = *cfg;
+  h->device = devid;
+  h->w.assign(d_weights, d_weights + nw);
+  h->kv = (uint16_t*)d_kv_cache;
+  h->ws = (char*)d_workspace;
+  h->lay = L;
+
+  // rotary tables: angle = pos * theta^(-2i/D), evaluated in double
+  const int D = cfg->head_dim, half = D / 2;
+  std::vector<float> cs((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
+  for (int ps = 0; ps < cfg->max_ctx; ++ps)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)cfg->rope_theta, -(2.0 * i) / D);
+      const double a = (double)ps * inv;
+      cs[(size_t)ps * half + i] = (float)std::cos(a);
+      sn[(size_t)ps * half + i] = (float)std::sin(a);
+    }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(h->at<float>(L.rope_cos), cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->at<float>(L.rope_sin), sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemsetAsync(h->at<uint32_t>(L.flags), 0, 256, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete h;
+    return SPEC_ERR_DEVICE;
+  }
+  *out = h;
+  return SPEC_OK;
+}
+
+spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
+                             const int32_t* d_kv_len, const int32_t* d_tree_parent, float* d_logits,
+                             void* stream) {
+  if (!h || !d_tokens || !d_kv_len || !d_logits) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& L = h->lay;
+  const int M = B * T, d = c.d_model, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn;
+  const int V = c.vocab;
+  const size_t wb = c.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
+  float* x = h->at<float>(L.x);
+  float* hb = h->at<float>(L.h);
+  float* q = h->at<float>(L.q);
+  float* ks = h->at<float>(L.ksuf);
+  float* vs = h->at<float>(L.vsuf);
+  float* at = h->at<float>(L.attn);
+  float* act = h->at<float>(L.act);
+  int32_t* tok = h->at<int32_t>(L.tok);
+  int32_t* pos = h->at<int32_t>(L.pos);
+  int32_t* slot = h->at<int32_t>(L.slot);
+  uint64_t* anc = h->at<uint64_t>(L.anc);
+  uint32_t* flags = h->at<uint32_t>(L.flags);
+  hipError_t e;
+
+  PrepParams pp{d_tokens, d_kv_len, d_tree_parent, tok, pos, slot, anc, flags, B, T, V, c.max_ctx};
+  e = timed(h, K_PREP, 0, s, [&] { return launch_prep(pp, s); });
+  if (e != hipSuccess) return SPEC_ERR_DEVICE;
+  e = timed(h, K_EMBED, (double)M * d * (wb + 4), s,
+            [&] { return launch_embed(h->W(0), c.weight_dtype, tok, x, M, d, s); });
+  if (e != hipSuccess) return SPEC_ERR_DEVICE;
+
+  const size_t per_region = (size_t)c.max_batch * Hkv * c.max_ctx * D;  // elements of one K or V region
+  const int splits = attn_splits(c, B, T);
+  const int nsplit = attn_nsplit(splits);
+  const float scale = 1.0f / std::sqrt((float)D);
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const float* g1 = (const float*)h->W(h->layer_w(l, 0));
+    const void* wqkv = h->W(h->layer_w(l, 1));
+    const void* wo = h->W(h->layer_w(l, 2));
+    const float* g2 = (const float*)h->W(h->layer_w(l, 3));
+    const void* wgu = h->W(h->layer_w(l, 4));
+    const void* wdn = h->W(h->layer_w(l, 5));
+    uint16_t* kreg = h->kv + (size_t)(2 * l) * per_region;
+    uint16_t* vreg = h->kv + (size_t)(2 * l + 1) * per_region;
+
+    e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, g1, hb, M, d, c.rms_eps, s); });
+    if (e != hipSuccess) return SPEC_ERR_DEVICE;
+
+    GemmParams gq{};
+    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = hb; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
+    gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
+    gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
+    gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
+    if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
+
+    AttnParams ap{q, kreg, vreg, d_kv_len, h->at<float>(L.part_o), h->at<float>(L.part_ml),
+                  B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
+    e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
+    if (e != hipSuccess) return SPEC_ERR_DEVICE;
+    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, q, ks, vs,
+                     d_tree_parent ? anc : nullptr, at, B, T, Hq, Hkv, D, scale};
+    e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
+    if (e != hipSuccess) return SPEC_ERR_DEVICE;
+
+    GemmParams go{};
+    go.W = wo; go.wdtype = c.weight_dtype; go.X = at; go.ldx = Hq * D; go.N = d; go.K = Hq * D;
+    go.epi = EPI_RESID; go.out = x; go.ldo = d;
+    if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
+
+    e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, g2, hb, M, d, c.rms_eps, s); });
+    if (e != hipSuccess) return SPEC_ERR_DEVICE;
+
+    GemmParams gg{};
+    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = hb; gg.ldx = d; gg.N = 2 * F; gg.K = d;
+    gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
+    if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
+
+    GemmParams gd{};
+    gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
+    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
+    if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
+  }
+  const float* gf = (const float*)h->W(1 + 6 * (size_t)c.n_layers);
+  e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, gf, hb, M, d, c.rms_eps, s); });
+  if (e != hipSuccess) return SPEC_ERR_DEVICE;
+  GemmParams gl{};
+  gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = hb; gl.ldx = d; gl.N = V;
+  gl.K = d; gl.epi = EPI_STORE; gl.out = d_logits; gl.ldo = V;
+  if ((e = gemm_rows(h, K_LM, gl, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
+  return SPEC_OK;
+}
+
+spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_logits, const float* d_q,
+                        const int32_t* d_tokens, const int32_t* d_tree_parent,
+                        const spec_sampling* sampling, int32_t* d_out_tokens, int32_t* d_num_accepted,
+                        const int32_t* d_kv_len, int32_t* d_kv_len_out, void* stream) {
+  if (!h || !d_logits || !d_tokens || !sampling || !d_out_tokens || !d_num_accepted)
+    return SPEC_ERR_INVALID_ARG;
+  const float temp = sampling->temperature;
+  if (!(temp >= 0.f) || !std::isfinite(temp)) return SPEC_ERR_INVALID_ARG;
+  if (temp > 0.f && !d_q && (d_tree_parent || T > 1)) return SPEC_ERR_INVALID_ARG;
+  if (d_kv_len_out && !d_kv_len) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  const Layout& L = h->lay;
+  AcceptParams ap{};
+  ap.logits = d_logits; ap.q = d_q; ap.tokens = d_tokens; ap.parent = d_tree_parent;
+  ap.temperature = temp; ap.replacement = sampling->tree_replacement ? 1 : 0;
+  ap.seed = sampling->seed; ap.round = sampling->round;
+  ap.out_tokens = d_out_tokens; ap.num_accepted = d_num_accepted; ap.kv_len = d_kv_len;
+  ap.kv_len_out = d_kv_len_out;
+  ap.rowstat = h->at<float>(L.rowstat); ap.rowms = h->at<float>(L.rowms); ap.rsum = h->at<float>(L.rsum);
+  ap.nacc = h->at<int32_t>(L.nacc); ap.rbuf = h->at<float>(L.rbuf); ap.flags = h->at<uint32_t>(L.flags);
+  ap.kv_cache = h->kv; ap.L = c.n_layers; ap.maxB = c.max_batch; ap.Hkv = c.n_kv_heads; ap.D = c.head_dim;
+  ap.max_ctx = c.max_ctx; ap.B = B; ap.T = T; ap.V = c.vocab; ap.nch = accept_chunks(c.vocab);
+  hipStream_t s = (hipStream_t)stream;
+  const int nq_rows = d_tree_parent ? T : T - 1;
+  const double bytes = (double)B * T * c.vocab * 4 + (temp > 0 ? (double)B * nq_rows * c.vocab * 4 : 0.0);
+  return dev(timed(h, K_ACC, bytes, s, [&] { return launch_accept(ap, s); }));
+}
+
+spec_status spec_device_errors(spec_handle* h, uint32_t* flags, void* stream) {
+  if (!h || !flags) return SPEC_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t v = 0;
+  uint32_t* d = h->at<uint32_t>(h->lay.flags);
+  if (hipMemcpyAsync(&v, d, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return SPEC_ERR_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return SPEC_ERR_DEVICE;
+  if (hipMemsetAsync(d, 0, 4, s) != hipSuccess) return SPEC_ERR_DEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return SPEC_ERR_DEVICE;
+  *flags = v;
+  return SPEC_OK;
+}
+
+spec_status spec_profile_enable(spec_handle* h, int32_t enable) {
+  if (!h) return SPEC_ERR_INVALID_ARG;
+  h->prof = enable != 0;
+  return SPEC_OK;
+}
+
+int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out, int32_t reset) {
+  if (!h) return -1;
+  for (auto& r : h->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return -1;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return -1;
+    h->launches[r.cls] += 1;
+    h->ms[r.cls] += t;
+    h->bytes[r.cls] += r.bytes;
+    h->pool.push_back(r.a);
+    h->pool.push_back(r.b);
+  }
+  h->recs.clear();
+  int n = 0;
+  for (int k = 0; k < K_N && n < max_out; ++k) {
+    if (!out) break;
+    std::memset(&out[n], 0, sizeof(spec_kernel_stat));
+    std::snprintf(out[n].name, sizeof(out[n].name), "%s", kClassNames[k]);
+    out[n].launches = h->launches[k];
+    out[n].total_ms = h->ms[k];
+    out[n].algo_bytes = h->bytes[k];
+    ++n;
+  }
+  if (reset)
+    for (int k = 0; k < K_N; ++k) h->launches[k] = 0, h->ms[k] = 0, h->bytes[k] = 0;
+  return n;
+}
+
+void spec_verify_destroy(spec_handle* h) {
+  if (!h) return;
+  for (auto& r : h->recs) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (auto e : h->pool) hipEventDestroy(e);
+  delete h;
+}
+
+}  // extern "C"

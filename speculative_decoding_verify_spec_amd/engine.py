@@ -1,0 +1,53 @@
+"""Buffer plumbing around the C ABI: allocates the workspace with torch, keeps
+the weights and cache alive for the handle's lifetime and forwards calls.
+No computation happens here."""
+from __future__ import annotations
+
+import torch
+
+from . import (make_config, spec_accept, spec_device_errors, spec_kv_cache_bytes, spec_sampling,
+               spec_verify_destroy, spec_verify_init, spec_verify_step, spec_workspace_bytes)
+
+
+class VerifyEngine:
+    def __init__(self, shape, weights, kv_cache: torch.Tensor, max_batch: int, max_ctx: int,
+                 max_rows_per_seq: int, stream=None):
+        self.shape = shape
+        self.cfg = make_config(shape, max_batch, max_ctx, max_rows_per_seq)
+        self.weights = list(weights)
+        self.kv_cache = kv_cache
+        need = spec_kv_cache_bytes(self.cfg)
+        have = kv_cache.numel() * kv_cache.element_size()
+        if have < need:
+            raise ValueError(f"kv cache has {have} bytes, needs {need}")
+        self.ws_bytes = spec_workspace_bytes(self.cfg)
+        dev = kv_cache.device
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.handle = spec_verify_init(self.cfg, self.weights, self.kv_cache, self.workspace,
+                                       self.ws_bytes, self.stream)
+
+    def step(self, tokens, kv_len, logits, tree_parent=None):
+        B, T = tokens.shape
+        return spec_verify_step(self.handle, B, T, tokens, kv_len, tree_parent, logits, self.stream)
+
+    def accept(self, logits, q, tokens, out_tokens, num_accepted, kv_len, kv_len_out=None,
+               tree_parent=None, temperature=1.0, seed=0, round_=0, replacement=False):
+        B, T = tokens.shape
+        smp = spec_sampling(float(temperature), 1 if replacement else 0, int(seed), int(round_))
+        return spec_accept(self.handle, B, T, logits, q, tokens, tree_parent, smp, out_tokens,
+                           num_accepted, kv_len, kv_len_out, self.stream)
+
+    def device_errors(self) -> int:
+        return spec_device_errors(self.handle, self.stream)
+
+    def close(self):
+        if self.handle:
+            spec_verify_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

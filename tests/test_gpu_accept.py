@@ -1,0 +1,180 @@
+"""Parity of spec_accept with the oracle's accept on the same synthetic logits,
+draft distributions, draft tokens and Philox uniforms.  Token ids and accept
+counts must be bit-exact apart from counted near-ties (|u - min(1, p/q)| or
+the CDF boundary distance below 1e-4, measured on the oracle's fp64 p, q)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import accept as OA
+from oracle import philox
+from tests.gpu_util import compare_decisions, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _accept_shape(V):
+    return synth.ModelShape(n_layers=1, d_model=64, n_heads=1, n_kv_heads=1, head_dim=64, d_ffn=64,
+                            vocab=V, rms_eps=1e-5, rope_theta=10000.0, weight_dtype="f32")
+
+
+_engines = {}
+
+
+def _engine(V, max_batch, max_rows, max_ctx=256):
+    key = (V, max_batch, max_rows, max_ctx)
+    if key not in _engines:
+        from speculative_decoding_verify_spec_amd.engine import VerifyEngine
+        sh = _accept_shape(V)
+        _, w = synth.make_weights(sh, device=dev())
+        cache = synth.make_kv_cache(sh, max_batch, max_ctx, max_ctx // 2, device=dev(), poison_tail=False)
+        _engines[key] = VerifyEngine(sh, w, cache, max_batch, max_ctx, max_rows)
+    return _engines[key]
+
+
+def _chain_inputs(B, gamma, V, temperature, sigma, seed):
+    T = gamma + 1
+    z = synth.random_logits((B, T), V, seed=seed, device=dev())
+    tokens = synth.make_tokens(B, T, V, seed=seed + 1, device=dev())
+    if temperature > 0:
+        q, _ = synth.noisy_draft_dist(z[:, :gamma], sigma, seed + 2, temperature)
+        if gamma:
+            tokens[:, 1:] = synth.sample_from(q, seed + 3)[..., 0]
+    else:
+        q = None
+        _, zn = synth.noisy_draft_dist(z[:, :gamma], sigma, seed + 2, 0.0)
+        if gamma:
+            tokens[:, 1:] = zn.argmax(-1).to(torch.int32)
+    return z, q, tokens
+
+
+CHAIN_CASES = [
+    # V, B, gamma, temperature, sigma
+    (8, 4, 3, 1.0, 1.0),
+    (8, 4, 1, 1.0, 3.0),
+    (4099, 3, 4, 1.0, 1.0),
+    (4099, 3, 7, 0.7, 0.5),
+    (4099, 2, 0, 1.0, 1.0),
+    (128256, 2, 3, 1.0, 1.0),
+    (128256, 1, 7, 1.0, 0.5),
+    (8, 4, 3, 0.0, 1.0),
+    (4099, 3, 5, 0.0, 0.3),
+    (128256, 2, 3, 0.0, 0.5),
+]
+
+
+@pytest.mark.parametrize("V,B,gamma,temp,sigma", CHAIN_CASES)
+def test_chain_accept_matches_oracle(V, B, gamma, temp, sigma):
+    print(f"[chain accept] V={V} B={B} gamma={gamma} T={temp} sigma={sigma}", flush=True)
+    T = gamma + 1
+    eng = _engine(V, 4, 8)
+    near, rounds, n_total = 0, 6, 0
+    for r in range(rounds):
+        seed = 1000 * V % 9973 + 17 * r + gamma
+        z, q, tokens = _chain_inputs(B, gamma, V, temp, sigma, seed)
+        kv_len = torch.arange(5, 5 + B, dtype=torch.int32, device=dev())
+        kv_out = torch.full((B,), -7, dtype=torch.int32, device=dev())
+        out = torch.full((B, T), -5, dtype=torch.int32, device=dev())
+        nacc = torch.full((B,), -5, dtype=torch.int32, device=dev())
+        qq = q if q is not None else None
+        eng.accept(z, qq, tokens, out, nacc, kv_len, kv_out, temperature=temp, seed=42 + r, round_=r)
+        torch.cuda.synchronize()
+        zn = z.double().cpu().numpy()
+        qn = q.double().cpu().numpy() if q is not None else None
+        orc = OA.accept(zn, qn, tokens.cpu().numpy(), temp, philox.Uniforms(42 + r, r))
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        assert np.array_equal(kv_out.cpu().numpy(), kv_len.cpu().numpy() + nacc.cpu().numpy() + 1)
+        n_total += B
+        assert eng.device_errors() == 0
+    print(f"  near-ties {near}/{n_total}", flush=True)
+    assert near <= max(1, n_total // 20)
+
+
+def _tree_inputs(B, branching, V, temperature, sigma, seed, replacement):
+    parent = synth.random_tree(branching, B).to(dev())
+    T = parent.shape[1]
+    z = synth.random_logits((B, T), V, seed=seed, device=dev())
+    tokens = synth.make_tokens(B, T, V, seed=seed + 1, device=dev())
+    q, zn = synth.noisy_draft_dist(z, sigma, seed + 2, temperature if temperature > 0 else 1.0)
+    ch = synth.tree_children(parent[0].cpu().tolist())
+    g = torch.Generator(device="cpu").manual_seed(seed + 3)
+    tok = tokens.cpu()
+    for b in range(B):
+        for v in range(T):
+            kids = ch[v]
+            if not kids:
+                continue
+            if temperature > 0:
+                picks = torch.multinomial(q[b, v].double().cpu(), len(kids), replacement=replacement, generator=g)
+            else:
+                picks = torch.topk(zn[b, v].cpu(), len(kids)).indices
+            for c, x in zip(kids, picks.tolist()):
+                tok[b, c] = x
+    return z, q, tok.to(torch.int32).to(dev()), parent
+
+
+TREE_CASES = [
+    # V, B, branching, temperature, replacement
+    (16, 3, [2, 2], 1.0, False),
+    (4099, 2, [4, 2, 2], 1.0, False),
+    (4099, 2, [3, 2], 1.0, True),
+    (128256, 1, [4, 4, 2, 2], 1.0, False),
+    (4099, 2, [4, 2, 2], 0.0, False),
+    (128256, 2, [2, 2, 1], 0.0, False),
+]
+
+
+@pytest.mark.parametrize("V,B,branching,temp,repl", TREE_CASES)
+def test_tree_accept_matches_oracle(V, B, branching, temp, repl):
+    print(f"[tree accept] V={V} B={B} branching={branching} T={temp} replacement={repl}", flush=True)
+    max_rows = 1 + sum(int(np.prod(branching[:i + 1])) for i in range(len(branching)))
+    eng = _engine(V, 4, 128, max_ctx=512)
+    near, n_total = 0, 0
+    for r in range(4):
+        seed = 31 * V % 7919 + 13 * r
+        z, q, tokens, parent = _tree_inputs(B, branching, V, temp, 0.8, seed, repl)
+        T = parent.shape[1]
+        assert T == max_rows
+        kv_len = torch.full((B,), 100, dtype=torch.int32, device=dev())
+        kv_out = torch.zeros((B,), dtype=torch.int32, device=dev())
+        out = torch.full((B, T), -5, dtype=torch.int32, device=dev())
+        nacc = torch.full((B,), -5, dtype=torch.int32, device=dev())
+        k_before, v_before = synth.kv_views(eng.kv_cache.clone(), _accept_shape(V), 4, 512)
+        eng.accept(z, q if temp > 0 else None, tokens, out, nacc, kv_len, kv_out, tree_parent=parent,
+                   temperature=temp, seed=7 + r, round_=r, replacement=repl)
+        torch.cuda.synchronize()
+        orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy() if temp > 0 else None,
+                        tokens.cpu().numpy(), temp, philox.Uniforms(7 + r, r),
+                        tree_parent=parent.cpu().numpy(), replacement=repl)
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        n_total += B
+        assert eng.device_errors() == 0
+        # commit: the accepted path's K/V now sit at slots kv_len + 0..n
+        k_after, v_after = synth.kv_views(eng.kv_cache, _accept_shape(V), 4, 512)
+        n = nacc.cpu().numpy()
+        assert np.array_equal(kv_out.cpu().numpy(), 100 + n + 1)
+        for b in range(B):
+            path = orc["paths"][b]
+            if int(n[b]) != len(path) - 1:
+                continue  # a near-tie took another path
+            for j, node in enumerate(path):
+                assert torch.equal(k_after[:, b, :, 100 + j], k_before[:, b, :, 100 + node])
+                assert torch.equal(v_after[:, b, :, :, 100 + j], v_before[:, b, :, :, 100 + node])
+    print(f"  near-ties {near}/{n_total}", flush=True)
+    assert near <= max(1, n_total // 10)
+
+
+def test_accept_flags_bad_draft_token():
+    V, B, gamma = 4099, 2, 3
+    eng = _engine(V, 4, 8)
+    z, q, tokens = _chain_inputs(B, gamma, V, 1.0, 1.0, 5)
+    tokens[0, 2] = V + 5
+    kv_len = torch.zeros((B,), dtype=torch.int32, device=dev())
+    out = torch.zeros((B, gamma + 1), dtype=torch.int32, device=dev())
+    nacc = torch.zeros((B,), dtype=torch.int32, device=dev())
+    eng.accept(z, q, tokens, out, nacc, kv_len, None, temperature=1.0, seed=1, round_=0)
+    torch.cuda.synchronize()
+    flags = eng.device_errors()
+    assert flags & 1
+    assert int(nacc[0]) <= 1  # the bad draft is never accepted
