@@ -165,33 +165,10 @@ def main():
     log(f"T_verify({T}) {t_verify:.3f} ms, T_decode(1) {t_decode:.3f} ms, c = {c_v:.3f}")
 
     # ---- per-kernel event timing (a separate profiled pass)
-    S.spec_profile_enable(eng.handle, True)
-    for k in range(a.profile_steps):
-        one_step(k)
-    torch.cuda.synchronize()
-    stats = S.spec_profile_read(eng.handle, reset=True)
-    S.spec_profile_enable(eng.handle, False)
-    kernels = {}
-    for name, st in stats.items():
-        if st["launches"]:
-            avg_ms = st["total_ms"] / st["launches"]
-            gbs = st["algo_bytes"] / (st["total_ms"] * 1e-3) / 1e9 if st["total_ms"] > 0 else 0.0
-            kernels[name] = {"launches_per_step": st["launches"] / a.profile_steps,
-                             "avg_us": avg_ms * 1e3, "algo_GBps": round(gbs, 1)}
-    gu = stats["gemm_gate_up"]
-    gu_bytes = gu["algo_bytes"] / gu["launches"]
-    gu_avg_s = gu["total_ms"] / gu["launches"] * 1e-3
-    gemm_names = [k for k in stats if k.startswith("gemm_")]
-    g_bytes = sum(stats[k]["algo_bytes"] for k in gemm_names)
-    g_ms = sum(stats[k]["total_ms"] for k in gemm_names)
-    roofline = {"bound": "hbm", "kernel": "gemm_gate_up (skinny-M weight stream + SiLU*up)",
-                "achieved": round(gu_bytes / gu_avg_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_bytes / gu_avg_s / 1e9 / HBM_PEAK_GBS, 4),
-                "algo_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2),
-                "traffic": None,
-                "all_gemms_GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
-                "all_gemms_frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"gate/up GEMM {roofline['achieved']} GB/s, all GEMMs {roofline['all_gemms_GBps']} GB/s")
+    kernels, roofline = {}, None
+    if a.profile_steps > 0:
+        kernels, roofline = profile_pass(S, eng, one_step, a.profile_steps)
+        log(f"gate/up GEMM {roofline['achieved']} GB/s, all GEMMs {roofline['all_gemms_GBps']} GB/s")
 
     result = {
         "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
@@ -212,6 +189,40 @@ def main():
     if a.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a, kv_len)
     print(json.dumps(result), flush=True)
+
+
+def profile_pass(S, eng, one_step, steps):
+    """Per-kernel-class HIP-event timing over `steps` steps; roofline of the
+    gate/up GEMM class (algorithmic bytes per launch / mean launch time)."""
+    import torch
+
+    S.spec_profile_enable(eng.handle, True)
+    for k in range(steps):
+        one_step(k)
+    torch.cuda.synchronize()
+    stats = S.spec_profile_read(eng.handle, reset=True)
+    S.spec_profile_enable(eng.handle, False)
+    kernels = {}
+    for name, st in stats.items():
+        if st["launches"]:
+            avg_ms = st["total_ms"] / st["launches"]
+            gbs = st["algo_bytes"] / (st["total_ms"] * 1e-3) / 1e9 if st["total_ms"] > 0 else 0.0
+            kernels[name] = {"launches_per_step": st["launches"] / steps,
+                             "avg_us": round(avg_ms * 1e3, 3), "algo_GBps": round(gbs, 1)}
+    gu = stats["gemm_gate_up"]
+    gu_bytes = gu["algo_bytes"] / gu["launches"]
+    gu_avg_s = gu["total_ms"] / gu["launches"] * 1e-3
+    gemm_names = [k for k in stats if k.startswith("gemm_")]
+    g_bytes = sum(stats[k]["algo_bytes"] for k in gemm_names)
+    g_ms = sum(stats[k]["total_ms"] for k in gemm_names)
+    roofline = {"bound": "hbm", "kernel": "gemm_gate_up (skinny-M weight stream + SiLU*up)",
+                "achieved": round(gu_bytes / gu_avg_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_bytes / gu_avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                "algo_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2),
+                "traffic": None,
+                "all_gemms_GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                "all_gemms_frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return kernels, roofline
 
 
 def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):

@@ -178,8 +178,11 @@ spec_status spec_device_errors(spec_handle* h, uint32_t* flags, void* stream);
  * When enabled, every launch of each kernel class is bracketed by events;
  * spec_profile_read synchronises and reports, per class, the launch count,
  * total milliseconds and the algorithmic bytes those launches had to move
- * (weights, activations, KV, logits and q, each counted once).  Class names:
- * "gemm", "attention", "attn_combine", "norm", "embed", "prep", "accept". */
+ * (weights and activations for the GEMMs, logits and q for accept; each
+ * counted once).  Class names: "prep_embed", "gemm_qkv", "attention",
+ * "attn_combine", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head",
+ * "accept".  Attention's bytes depend on the device-side kv_len and are
+ * reported as 0. */
 typedef struct spec_kernel_stat {
   char name[24];
   int64_t launches;

@@ -5,8 +5,9 @@
 // vectors) read that head's cached keys once, inside one wave, so the
 // gamma+1 rows of a sequence share one KV read (CS349E Lecture 6, section 9.2).
 // The context of a (sequence, KV head) is cut into `splits` workgroups of 4
-// waves; each wave keeps its own online-softmax state (flash-decoding style)
-// and writes a partial (max, sum, unnormalised output) per query.  The
+// waves; each wave keeps its own online-softmax state (flash-decoding style),
+// the four states are merged in LDS and the workgroup writes one partial
+// (max, sum, unnormalised output) per query.  The
 // products run on bf16 MFMA 16x16x16: S^T = K Q^T with K exact in bf16 and
 // the fp32 queries split into bf16 hi + lo, then O^T += V^T P^T with the fp32
 // probabilities split the same way; accumulation is fp32.  V is stored
@@ -14,8 +15,8 @@
 // contiguous.
 //
 // Combine part (attn_combine_kernel), one wave per (row, query head): merges
-// the partials, adds the suffix keys in fp32 (chain: rows 0..i; tree: the
-// node and its ancestors) and normalises.  Keys beyond a wave's range are
+// the split partials, adds the suffix keys in fp32 (chain: rows 0..i; tree:
+// the node and its ancestors) and normalises.  Keys beyond a wave's range are
 // loaded as zeros and masked, so nothing past kv_len is ever used.
 #include "common.h"
 #include "launch.h"
@@ -23,7 +24,7 @@
 namespace sv {
 
 int attn_query_tiles_per_wave(int nq) { return nq > 16 ? 2 : 1; }
-int attn_nsplit(int splits) { return splits * 4; }
+int attn_nsplit(int splits) { return splits; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
 // 4g..4g+3 of both tiles cover keys kb + 8g .. kb + 8g + 7, so one 16-byte
@@ -184,24 +185,51 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
     }
   }
 
-  // ---- write this wave's partial state
-  const int split_id = s * 4 + w;
+  // ---- merge the four waves' states in LDS and write one partial per query
+  constexpr int QN = QT * 16;
+  constexpr int OS = D + 4;  // padded row stride of the staged outputs
+  __shared__ float s_m[4][QN];
+  __shared__ float s_l[4][QN];
+  __shared__ float s_o[4][QN * OS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float l = lrun[qt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int qi = (qg * QT + qt) * 16 + j;
-    if (qi >= nq) continue;
-    const size_t base = (((size_t)split_id * p.B + b) * p.Hkv + kvh) * nq + qi;
-    if (g == 0) {
-      p.part_ml[2 * base] = mrun[qt];
-      p.part_ml[2 * base + 1] = l;
-    }
-    float* dst = p.part_o + base * D;
+    lrun[qt] = l;
+    if (g == 0) s_m[w][qt * 16 + j] = mrun[qt];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qq = qt * 16 + j;
+    const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+    // a wave that saw no key has m = -inf and contributes nothing
+    const float f = (mrun[qt] == -INFINITY) ? 0.f : __expf(mrun[qt] - mall);
+    if (g == 0) s_l[w][qq] = lrun[qt] * f;
+    float* dst = &s_o[w][qq * OS];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *(float4*)(dst + dt * 16 + 4 * g) = make_float4(o[qt][dt][0], o[qt][dt][1], o[qt][dt][2], o[qt][dt][3]);
+      *(float4*)(dst + dt * 16 + 4 * g) =
+          make_float4(o[qt][dt][0] * f, o[qt][dt][1] * f, o[qt][dt][2] * f, o[qt][dt][3] * f);
+  }
+  __syncthreads();
+  const size_t pbase = (((size_t)s * p.B + b) * p.Hkv + kvh) * nq;
+  for (int e = threadIdx.x; e < QN * D; e += 256) {
+    const int qq = e / D, dd = e % D;
+    const int qi = (qg * QT) * 16 + qq;
+    if (qi >= nq) continue;
+    const int o2 = qq * OS + dd;
+    p.part_o[(pbase + qi) * D + dd] = s_o[0][o2] + s_o[1][o2] + s_o[2][o2] + s_o[3][o2];
+  }
+  if (threadIdx.x < QN) {
+    const int qq = threadIdx.x;
+    const int qi = (qg * QT) * 16 + qq;
+    if (qi < nq) {
+      const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+      p.part_ml[2 * (pbase + qi)] = mall;
+      p.part_ml[2 * (pbase + qi) + 1] = s_l[0][qq] + s_l[1][qq] + s_l[2][qq] + s_l[3][qq];
+    }
   }
 }
 
@@ -220,33 +248,69 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One wave per (row i, query head, sequence).
+// One workgroup per (row i, KV head, sequence); wave g handles query head
+// kvh * G + g.  The split statistics are read by all lanes at once, the
+// weighted sum of the split outputs keeps every load in flight, then the
+// suffix keys (chain: rows 0..i; tree: the node and its ancestors) are added
+// in fp32 and the result normalised.
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   constexpr int PL = D / 64;  // dims per lane
-  const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  constexpr int MAXS = 128;
+  __shared__ float s_w[8][MAXS];
+  const int i = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, gg = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
-  const int kvh = hq / G, gg = hq % G;
+  const int hq = kvh * G + gg;
   const int nq = G * p.T;
   const int qi = i * G + gg;
   const int m = b * p.T + i;
+  const int ns = p.nsplit;
 
+  // split statistics: M = max over splits with mass, weights exp(m_s - M)
+  float mloc = -INFINITY;
+  for (int sp = lane; sp < ns; sp += 64) {
+    const size_t base = (((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi;
+    if (p.part_ml[2 * base + 1] > 0.f) mloc = fmaxf(mloc, p.part_ml[2 * base]);
+  }
+  const float mstar = wave_max(mloc);
+  float lloc = 0.f;
+  for (int sp = lane; sp < ns; sp += 64) {
+    const size_t base = (((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi;
+    const float ls = p.part_ml[2 * base + 1];
+    const float wgt = (ls > 0.f) ? expf(p.part_ml[2 * base] - mstar) : 0.f;
+    s_w[gg][sp] = wgt;
+    lloc += wgt * ls;
+  }
+  float l = wave_sum(lloc);
+  __syncthreads();
   float acc[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-  float mcur = -INFINITY, l = 0.f;
-  for (int sp = 0; sp < p.nsplit; ++sp) {
-    const size_t base = (((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi;
-    const float ms = p.part_ml[2 * base], ls = p.part_ml[2 * base + 1];
-    if (!(ls > 0.f)) continue;
-    const float mnew = fmaxf(mcur, ms);
-    const float f1 = expf(mcur - mnew), f2 = expf(ms - mnew);
-    const float* src = p.part_o + base * D;
+  float mcur = mstar;
+  if (l > 0.f) {
+    int sp = 0;
+    for (; sp + 8 <= ns; sp += 8) {
+      float v[8][PL];
 #pragma unroll
-    for (int e = 0; e < PL; ++e) acc[e] = acc[e] * f1 + f2 * src[lane + 64 * e];
-    l = l * f1 + f2 * ls;
-    mcur = mnew;
+      for (int u = 0; u < 8; ++u) {
+        const float* src = p.part_o + ((((size_t)(sp + u) * p.B + b) * p.Hkv + kvh) * nq + qi) * D;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) v[u][e] = src[lane + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < PL; ++e) acc[e] += s_w[gg][sp + u] * v[u][e];
+    }
+    for (; sp < ns; ++sp) {
+      const float* src = p.part_o + ((((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi) * D;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] += s_w[gg][sp] * src[lane + 64 * e];
+    }
+  } else {
+    mcur = -INFINITY;
+    l = 0.f;
   }
   // suffix keys in fp32
   float qv[PL];
@@ -263,16 +327,16 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
     }
     if (!vis) continue;
     const int mj = b * p.T + jj;
-    const float* ks = p.k_suf + ((size_t)mj * p.Hkv + kvh) * D;
+    const float* ksp = p.k_suf + ((size_t)mj * p.Hkv + kvh) * D;
     float d = 0.f;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) d += qv[e] * ks[lane + 64 * e];
+    for (int e = 0; e < PL; ++e) d += qv[e] * ksp[lane + 64 * e];
     const float sc = wave_sum(d) * p.scale;
     const float mnew = fmaxf(mcur, sc);
     const float f1 = expf(mcur - mnew), ee = expf(sc - mnew);
-    const float* vs = p.v_suf + ((size_t)mj * p.Hkv + kvh) * D;
+    const float* vsp = p.v_suf + ((size_t)mj * p.Hkv + kvh) * D;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) acc[e] = acc[e] * f1 + ee * vs[lane + 64 * e];
+    for (int e = 0; e < PL; ++e) acc[e] = acc[e] * f1 + ee * vsp[lane + 64 * e];
     l = l * f1 + ee;
     mcur = mnew;
   }
@@ -283,11 +347,13 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s) {
-  dim3 grid(p.T, p.Hq, p.B);
+  const int G = p.Hq / p.Hkv;
+  if (G > 8 || p.nsplit > 128) return hipErrorInvalidValue;
+  dim3 grid(p.T, p.Hkv, p.B);
   if (p.D == 128)
-    attn_combine_kernel<128><<<grid, 64, 0, s>>>(p);
+    attn_combine_kernel<128><<<grid, 64 * G, 0, s>>>(p);
   else
-    attn_combine_kernel<64><<<grid, 64, 0, s>>>(p);
+    attn_combine_kernel<64><<<grid, 64 * G, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -6,7 +6,7 @@
 
 namespace sv {
 
-// ---------------------------------------------------------------- prep / embed / norm
+// ---------------------------------------------------------------- prep + embedding
 struct PrepParams {
   const int32_t* tokens;  // [B, T]
   const int32_t* kv_len;  // [B]
@@ -16,16 +16,12 @@ struct PrepParams {
   int32_t* slot;          // [M] cache slot, -1 when it would overflow
   uint64_t* anc;          // [M][2] ancestor-or-self bitmask (tree only)
   uint32_t* flags;
-  int B, T, vocab, max_ctx;
+  const void* embed;      // [V][d] embedding table (weight dtype)
+  int wdtype;             // 0 fp32, 1 bf16
+  float* x;               // [M][d] residual stream, written with the rows' embeddings
+  int B, T, vocab, max_ctx, d;
 };
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
-
-hipError_t launch_embed(const void* E, int wdtype, const int32_t* tok, float* x, int M, int d,
-                        hipStream_t s);
-
-// h[m] = x[m] / sqrt(mean(x[m]^2) + eps) * g
-hipError_t launch_rmsnorm(const float* x, const float* g, float* h, int M, int d, float eps,
-                          hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
@@ -40,6 +36,8 @@ struct GemmParams {
   float* out;     // STORE / RESID / SWIGLU: [M][ldo]
   int ldo;
   int F;          // SWIGLU: gate rows [0,F), up rows [F,2F)
+  const float* norm_g;  // non-null: RMSNorm the activation rows (gain g, eps) first
+  float eps;
   // QKV epilogue
   int m0;                   // global row offset of this launch (row chunking)
   const int32_t* pos;       // [M_total]

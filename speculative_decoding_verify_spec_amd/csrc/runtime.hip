@@ -33,21 +33,22 @@ bool valid_config(const spec_config* c) {
   return true;
 }
 
-// Attention workgroups per (sequence, KV head, query group): about 256 keys
-// each, capped so the grid stays near 2048 workgroups.
+// Attention workgroups per (sequence, KV head, query group): about 128 keys
+// each (one 32-key block per wave), capped so the grid stays near 4096
+// workgroups and the combine merges at most 128 partials.
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
   const int QT = attn_query_tiles_per_wave(nq);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int units = B * c.n_kv_heads * nqg;
-  int s = (c.max_ctx + 255) / 256;
-  const int cap = std::max(1, (2048 + units - 1) / units);
+  int s = (c.max_ctx + 127) / 128;
+  const int cap = std::max(1, (4096 + units - 1) / units);
   s = std::min(s, cap);
-  return std::max(1, std::min(s, 64));
+  return std::max(1, std::min(s, 128));
 }
 
 struct Layout {
-  size_t x, h, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
+  size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
   size_t tok, pos, slot, anc, rowstat, rowms, rsum, nacc, rbuf, flags, total;
 };
 
@@ -69,7 +70,6 @@ Layout plan(const spec_config& c) {
     return o;
   };
   L.x = take(Mmax * c.d_model * 4);
-  L.h = take(Mmax * c.d_model * 4);
   L.q = take(Mmax * Hq * D * 4);
   L.ksuf = take(Mmax * Hkv * D * 4);
   L.vsuf = take(Mmax * Hkv * D * 4);
@@ -93,9 +93,9 @@ Layout plan(const spec_config& c) {
   return L;
 }
 
-const char* kClassNames[] = {"prep", "embed", "rmsnorm", "gemm_qkv", "attention", "attn_combine",
-                             "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head", "accept"};
-enum KClass { K_PREP, K_EMBED, K_NORM, K_QKV, K_ATTN, K_COMB, K_O, K_GU, K_DOWN, K_LM, K_ACC, K_N };
+const char* kClassNames[] = {"prep_embed", "gemm_qkv", "attention", "attn_combine", "gemm_o",
+                             "gemm_gate_up", "gemm_down", "gemm_lm_head", "accept"};
+enum KClass { K_PREP, K_QKV, K_ATTN, K_COMB, K_O, K_GU, K_DOWN, K_LM, K_ACC, K_N };
 
 }  // namespace
 
@@ -264,7 +264,6 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
   const int V = c.vocab;
   const size_t wb = c.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   float* x = h->at<float>(L.x);
-  float* hb = h->at<float>(L.h);
   float* q = h->at<float>(L.q);
   float* ks = h->at<float>(L.ksuf);
   float* vs = h->at<float>(L.vsuf);
@@ -277,11 +276,9 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
   uint32_t* flags = h->at<uint32_t>(L.flags);
   hipError_t e;
 
-  PrepParams pp{d_tokens, d_kv_len, d_tree_parent, tok, pos, slot, anc, flags, B, T, V, c.max_ctx};
-  e = timed(h, K_PREP, 0, s, [&] { return launch_prep(pp, s); });
-  if (e != hipSuccess) return SPEC_ERR_DEVICE;
-  e = timed(h, K_EMBED, (double)M * d * (wb + 4), s,
-            [&] { return launch_embed(h->W(0), c.weight_dtype, tok, x, M, d, s); });
+  PrepParams pp{d_tokens, d_kv_len, d_tree_parent, tok, pos, slot, anc, flags, h->W(0), c.weight_dtype, x,
+                B, T, V, c.max_ctx, d};
+  e = timed(h, K_PREP, (double)M * d * (wb + 4), s, [&] { return launch_prep(pp, s); });
   if (e != hipSuccess) return SPEC_ERR_DEVICE;
 
   const size_t per_region = (size_t)c.max_batch * Hkv * c.max_ctx * D;  // elements of one K or V region
@@ -299,11 +296,9 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
     uint16_t* kreg = h->kv + (size_t)(2 * l) * per_region;
     uint16_t* vreg = h->kv + (size_t)(2 * l + 1) * per_region;
 
-    e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, g1, hb, M, d, c.rms_eps, s); });
-    if (e != hipSuccess) return SPEC_ERR_DEVICE;
-
     GemmParams gq{};
-    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = hb; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = x; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    gq.norm_g = g1; gq.eps = c.rms_eps;
     gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
     gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
     gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
@@ -324,11 +319,9 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
     go.epi = EPI_RESID; go.out = x; go.ldo = d;
     if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
 
-    e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, g2, hb, M, d, c.rms_eps, s); });
-    if (e != hipSuccess) return SPEC_ERR_DEVICE;
-
     GemmParams gg{};
-    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = hb; gg.ldx = d; gg.N = 2 * F; gg.K = d;
+    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = x; gg.ldx = d; gg.N = 2 * F; gg.K = d;
+    gg.norm_g = g2; gg.eps = c.rms_eps;
     gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
     if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
 
@@ -338,11 +331,10 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
   }
   const float* gf = (const float*)h->W(1 + 6 * (size_t)c.n_layers);
-  e = timed(h, K_NORM, (double)M * d * 8, s, [&] { return launch_rmsnorm(x, gf, hb, M, d, c.rms_eps, s); });
-  if (e != hipSuccess) return SPEC_ERR_DEVICE;
   GemmParams gl{};
-  gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = hb; gl.ldx = d; gl.N = V;
+  gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = x; gl.ldx = d; gl.N = V;
   gl.K = d; gl.epi = EPI_STORE; gl.out = d_logits; gl.ldo = V;
+  gl.norm_g = gf; gl.eps = c.rms_eps;
   if ((e = gemm_rows(h, K_LM, gl, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
   return SPEC_OK;
 }
