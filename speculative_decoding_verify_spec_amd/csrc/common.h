@@ -50,6 +50,17 @@ DEVI float wave_max(float v) {
   return v;
 }
 
+// --- workgroup barrier for LDS traffic only -------------------------------
+// __syncthreads() also orders global memory, which makes every wave wait for
+// all of its outstanding global loads at the barrier.  Kernels that keep
+// weight loads in flight across an LDS reduction use this barrier instead: it
+// orders LDS accesses only, so the loads stay outstanding.
+DEVI void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // --- Philox4x64-10 (Salmon et al., SC'11) -----------------------------------
 // Key (seed, 0), counter (slot, sequence, round, 0); the accept uniform is
 // u = (word0 >> 40) * 2^-24.

@@ -90,6 +90,36 @@ DEVI void load_w8<float>(const float* __restrict__ W, size_t off, float (&w)[8])
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
+// Eight weights of one row as loaded, widened to fp32 only where they are
+// used, so a prefetched row group costs 4 registers per 8 bf16 weights.
+template <typename WT>
+struct WRaw;
+template <>
+struct WRaw<uint16_t> {
+  u32x4 v;
+  DEVI void load(const uint16_t* __restrict__ W, size_t off) {
+    v = __builtin_nontemporal_load((const u32x4*)(W + off));
+  }
+  DEVI void widen(float (&w)[8]) const {
+    w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x);
+    w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+    w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z);
+    w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
+  }
+};
+template <>
+struct WRaw<float> {
+  f32x4 a, b;
+  DEVI void load(const float* __restrict__ W, size_t off) {
+    a = __builtin_nontemporal_load((const f32x4*)(W + off));
+    b = __builtin_nontemporal_load((const f32x4*)(W + off + 4));
+  }
+  DEVI void widen(float (&w)[8]) const {
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+};
+
 // Halving exchange across the 64 lanes, unrolled at compile time: at offset
 // O a lane keeps half of the CNT values it holds (the upper half when its bit
 // O is set, else the lower half), adds the partner's copy of that half and
@@ -129,20 +159,20 @@ DEVI void fma_rows(float* acc, const float (&w)[8], const float (&x)[MT][8], int
 
 // Fold one row group's partial sums over lanes and waves; returns with the
 // YT*MT sums in tot[] (all threads synchronised).
-template <int MT>
+template <int MT, bool LDS_ONLY = false>
 DEVI void reduce_group(float* acc, int lane, int w, int nwaves, float (*red)[MaxPow2<MT>::v], float* tot) {
   constexpr int NV = YT * MT;
   constexpr int NVP = MaxPow2<MT>::v;
   constexpr int SH = (NVP == 8) ? 3 : (NVP == 16) ? 2 : (NVP == 32) ? 1 : 0;
   lane_fold<NVP, 32>(acc, lane);
   if ((lane & ((1 << SH) - 1)) == 0) red[w][lane >> SH] = acc[0];
-  __syncthreads();
+  if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();
   if (threadIdx.x < NV) {
     float t = 0.f;
     for (int i = 0; i < nwaves; ++i) t += red[i][threadIdx.x];
     tot[threadIdx.x] = t;
   }
-  __syncthreads();
+  if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();
 }
 
 // Epilogue for row group rg from the finished sums tot[y * MT + m].
@@ -229,20 +259,40 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
   const WT* __restrict__ W = (const WT*)p.W;
   const int nsteps = (p.K + 511) >> 9;
 
-  // ---- this wave's activation slice, kept in registers
-  float xr[SPW][MT][8];
+  // ---- this wave's K steps.  A lane with no k in range loads from the start
+  // of the row (always in bounds) and multiplies it by zero activations, so
+  // the loads need no branches.
   int kofs[SPW];
-  bool sact[SPW];
+  bool kok[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
     const int s = w + i * KSTAT_WAVES;
     const int kraw = s * 512 + lane * 8;
-    const bool kok = (s < nsteps) && (kraw < p.K);
-    sact[i] = s < nsteps;  // wave-uniform: is there a step at all
-    kofs[i] = kok ? kraw : 0;
+    kok[i] = (s < nsteps) && (kraw < p.K);
+    kofs[i] = kok[i] ? kraw : 0;
+  }
+  const int ngroups = gemm_groups<EPI>(p);
+  WRaw<WT> wr[SPW][YT];
+  auto load_group = [&](int g_) {
+#pragma unroll
+    for (int y = 0; y < YT; ++y) {
+      int r = gemm_row<EPI>(p, g_, y);
+      r = r < p.N ? r : 0;  // the LM head's last group may be short; those rows are never stored
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) wr[i][y].load(W, (size_t)r * p.K + kofs[i]);
+    }
+  };
+  // the first row group's loads go out before the activation prologue
+  int rg = blockIdx.x;
+  if (rg < ngroups) load_group(rg);
+
+  // ---- this wave's activation slice, kept in registers
+  float xr[SPW][MT][8];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const bool ok = kok && (m < p.M);
+      const bool ok = kok[i] && (m < p.M);
       const float* xs = p.X + (size_t)(m < p.M ? m : 0) * p.ldx + kofs[i];
       const float4 a = *(const float4*)xs;
       const float4 b = *(const float4*)(xs + 4);
@@ -264,7 +314,7 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
       ss = wave_sum(ss);
       if (lane == 0) ssq[w][m] = ss;
     }
-    __syncthreads();
+    lds_barrier();
     float inv[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -285,31 +335,31 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
     }
   }
 
-  const int ngroups = gemm_groups<EPI>(p);
-  for (int rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
+  for (; rg < ngroups; rg += gridDim.x) {
+    // Each weight register is refilled with the next row group's weights as
+    // soon as its current contents are consumed, so those loads are in flight
+    // during the rest of this group's products, its reduction and epilogue.
+    const int nx = rg + gridDim.x;
+    const bool more = nx < ngroups;
+    size_t rnext[YT];
+#pragma unroll
+    for (int y = 0; y < YT; ++y) {
+      const int r = gemm_row<EPI>(p, more ? nx : rg, y);
+      rnext[y] = (size_t)(r < p.N ? r : 0) * p.K;
+    }
     float acc[NVP];
 #pragma unroll
     for (int i = 0; i < NVP; ++i) acc[i] = 0.f;
-    int rows[YT];
-#pragma unroll
-    for (int y = 0; y < YT; ++y) {
-      const int r = gemm_row<EPI>(p, rg, y);
-      rows[y] = r < p.N ? r : 0;  // the LM head's last group may be short; its extra rows are never stored
-    }
-    float wv[SPW][YT][8];
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
-      if (sact[i]) {
 #pragma unroll
-        for (int y = 0; y < YT; ++y) load_w8<WT>(W, (size_t)rows[y] * p.K + kofs[i], wv[i][y]);
+      for (int y = 0; y < YT; ++y) {
+        float wf[8];
+        wr[i][y].widen(wf);
+        if (more) wr[i][y].load(W, rnext[y] + kofs[i]);
+        fma_rows<MT>(acc, wf, xr[i], y);
       }
-#pragma unroll
-    for (int i = 0; i < SPW; ++i)
-      if (sact[i]) {
-#pragma unroll
-        for (int y = 0; y < YT; ++y) fma_rows<MT>(acc, wv[i][y], xr[i], y);
-      }
-    reduce_group<MT>(acc, lane, w, KSTAT_WAVES, red, tot);
+    reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot);
     epilogue<MT, EPI>(p, rg, tot);
   }
 }
@@ -378,8 +428,13 @@ template <int MT, int EPI>
 static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
   const int groups = gemm_groups<EPI>(p);
   if (gemm_is_kstat(p.K)) {
-    // persistent workgroups: up to 4 per CU, each looping over row groups
-    const int grid = std::min(groups, 4 * device_cus());
+    // persistent workgroups, at most two per CU, each looping over row
+    // groups; the grid is sized so that every workgroup gets the same number
+    // of groups (up to one), which keeps the last round from running on a
+    // fraction of the chip
+    const int slots = 2 * device_cus();
+    const int rounds = (groups + slots - 1) / slots;
+    const int grid = (groups + rounds - 1) / rounds;
     if (p.wdtype == 1) {
       if (p.norm_g) gemm_kstat_kernel<MT, uint16_t, EPI, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
       else gemm_kstat_kernel<MT, uint16_t, EPI, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
