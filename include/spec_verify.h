@@ -192,6 +192,21 @@ typedef struct spec_kernel_stat {
 spec_status spec_profile_enable(spec_handle* h, int32_t enable);
 int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out, int32_t reset);
 
+/* Back-to-back timing of one GEMM class, for measurement: the class's GEMM
+ * of every layer is launched in layer order, `iters` times over, on `stream`
+ * with `rows` activation rows, between one pair of HIP events; no event sits
+ * between the launches.  Returns the elapsed milliseconds and the algorithmic
+ * bytes of all those launches (each weight matrix once per launch, plus the
+ * activation rows read and written).  cls: "gemm_o", "gemm_gate_up" or
+ * "gemm_down".  The launches read and overwrite the workspace's activation
+ * buffers and touch neither the KV cache nor caller memory; call it between
+ * verify steps, never while one is in flight on another stream.
+ * Errors: SPEC_ERR_INVALID_ARG (null pointer, unknown class, iters < 1),
+ * SPEC_ERR_CAPACITY (rows outside [1, max_batch * max_rows_per_seq]),
+ * SPEC_ERR_DEVICE (a HIP call failed). */
+spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int32_t iters, void* stream,
+                              double* ms_out, double* bytes_out);
+
 /* Release the handle (host memory and events only). */
 void spec_verify_destroy(spec_handle* h);
 

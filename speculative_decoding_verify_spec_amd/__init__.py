@@ -34,7 +34,7 @@ SPEC_FLAG_KV_OVERFLOW = 4
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_accept", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_verify_destroy", "spec_status_str",
+    "spec_profile_gemm", "spec_verify_destroy", "spec_status_str",
 ]
 
 
@@ -93,6 +93,9 @@ def lib():
     L.spec_profile_enable.restype = i32
     L.spec_profile_read.argtypes = [vp, C.POINTER(spec_kernel_stat), i32, i32]
     L.spec_profile_read.restype = i32
+    L.spec_profile_gemm.argtypes = [vp, C.c_char_p, i32, i32, vp, C.POINTER(C.c_double),
+                                    C.POINTER(C.c_double)]
+    L.spec_profile_gemm.restype = i32
     L.spec_verify_destroy.argtypes = [vp]
     L.spec_verify_destroy.restype = None
     L.spec_status_str.argtypes = [i32]
@@ -190,6 +193,15 @@ def spec_profile_read(h, reset: bool = True):
         raise SpecError("spec_profile_read", SPEC_ERR_DEVICE)
     return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms),
                                    "algo_bytes": float(arr[i].algo_bytes)} for i in range(n)}
+
+
+def spec_profile_gemm(h, cls: str, rows: int, iters: int, stream=None):
+    """(milliseconds, algorithmic bytes) of `iters` back-to-back passes of one
+    GEMM class over all layers."""
+    ms, nbytes = C.c_double(0.0), C.c_double(0.0)
+    _check("spec_profile_gemm", lib().spec_profile_gemm(h, cls.encode(), int(rows), int(iters),
+                                                        _stream(stream), C.byref(ms), C.byref(nbytes)))
+    return ms.value, nbytes.value
 
 
 def spec_verify_destroy(h):

@@ -415,6 +415,68 @@ int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out
   return n;
 }
 
+spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int32_t iters, void* stream,
+                              double* ms_out, double* bytes_out) {
+  if (!h || !cls || !ms_out || !bytes_out || iters < 1) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (rows < 1 || rows > c.max_batch * c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  int k;
+  if (!std::strcmp(cls, "gemm_o")) k = K_O;
+  else if (!std::strcmp(cls, "gemm_gate_up")) k = K_GU;
+  else if (!std::strcmp(cls, "gemm_down")) k = K_DOWN;
+  else return SPEC_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& L = h->lay;
+  const int d = c.d_model, F = c.d_ffn, HD = c.n_heads * c.head_dim;
+  const size_t wb = c.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
+  float* x = h->at<float>(L.x);
+  float* at = h->at<float>(L.attn);
+  float* act = h->at<float>(L.act);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) return SPEC_ERR_DEVICE;
+  if (hipEventCreate(&b) != hipSuccess) {
+    hipEventDestroy(a);
+    return SPEC_ERR_DEVICE;
+  }
+  const bool prof = h->prof;
+  h->prof = false;  // one event pair around the whole sequence, none per launch
+  spec_status st = SPEC_OK;
+  double bytes = 0;
+  if (hipEventRecord(a, s) != hipSuccess) st = SPEC_ERR_DEVICE;
+  for (int it = 0; it < iters && st == SPEC_OK; ++it) {
+    for (int l = 0; l < c.n_layers && st == SPEC_OK; ++l) {
+      GemmParams g{};
+      g.wdtype = c.weight_dtype;
+      if (k == K_O) {
+        g.W = h->W(h->layer_w(l, 2)); g.X = at; g.ldx = HD; g.N = d; g.K = HD;
+        g.epi = EPI_RESID; g.out = x; g.ldo = d;
+        bytes += (double)d * HD * wb + (double)rows * (HD + 2.0 * d) * 4;
+      } else if (k == K_GU) {
+        g.W = h->W(h->layer_w(l, 4)); g.X = x; g.ldx = d; g.N = 2 * F; g.K = d;
+        g.norm_g = (const float*)h->W(h->layer_w(l, 3)); g.eps = c.rms_eps;
+        g.epi = EPI_SWIGLU; g.out = act; g.ldo = F; g.F = F;
+        bytes += 2.0 * F * d * wb + (double)rows * (d + F) * 4;
+      } else {
+        g.W = h->W(h->layer_w(l, 5)); g.X = act; g.ldx = F; g.N = d; g.K = F;
+        g.epi = EPI_RESID; g.out = x; g.ldo = d;
+        bytes += (double)d * F * wb + (double)rows * (F + 2.0 * d) * 4;
+      }
+      if (gemm_rows(h, k, g, rows, s) != hipSuccess) st = SPEC_ERR_DEVICE;
+    }
+  }
+  if (st == SPEC_OK && hipEventRecord(b, s) != hipSuccess) st = SPEC_ERR_DEVICE;
+  float ms = 0.f;
+  if (st == SPEC_OK && (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess))
+    st = SPEC_ERR_DEVICE;
+  h->prof = prof;
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  if (st != SPEC_OK) return st;
+  *ms_out = ms;
+  *bytes_out = bytes;
+  return SPEC_OK;
+}
+
 void spec_verify_destroy(spec_handle* h) {
   if (!h) return;
   for (auto& r : h->recs) {

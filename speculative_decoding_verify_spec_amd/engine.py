@@ -5,8 +5,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (make_config, spec_accept, spec_device_errors, spec_kv_cache_bytes, spec_sampling,
-               spec_verify_destroy, spec_verify_init, spec_verify_step, spec_workspace_bytes)
+from . import (make_config, spec_accept, spec_device_errors, spec_kv_cache_bytes, spec_profile_gemm,
+               spec_sampling, spec_verify_destroy, spec_verify_init, spec_verify_step,
+               spec_workspace_bytes)
 
 
 class VerifyEngine:
@@ -37,6 +38,11 @@ class VerifyEngine:
         smp = spec_sampling(float(temperature), 1 if replacement else 0, int(seed), int(round_))
         return spec_accept(self.handle, B, T, logits, q, tokens, tree_parent, smp, out_tokens,
                            num_accepted, kv_len, kv_len_out, self.stream)
+
+    def profile_gemm(self, cls: str, rows: int, iters: int):
+        """(ms, algorithmic bytes) of `iters` back-to-back passes of one GEMM
+        class over all layers; overwrites the workspace activations."""
+        return spec_profile_gemm(self.handle, cls, rows, iters, self.stream)
 
     def device_errors(self) -> int:
         return spec_device_errors(self.handle, self.stream)
