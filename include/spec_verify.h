@@ -139,6 +139,14 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
  *   Side effect: every row's K/V (rounded to bf16) is written to cache slot
  *   kv_len[b] + i.  Slots beyond the length spec_accept commits are left as
  *   they are (a position-indexed cache abandons a rejected tail for free).
+ *   Launches: a prep kernel, the per-layer kernels, the LM head.  The
+ *   per-layer kernels read only weights, cache and workspace, so for each
+ *   (B, T, chain or tree) their launch sequence is recorded once as a HIP
+ *   graph on a private stream of the handle and replayed on `stream` (at most
+ *   32 shapes are kept; the least recently used is dropped).  When `stream`
+ *   is itself being captured by the caller, or graphs are switched off with
+ *   spec_graph_enable, the kernels are launched directly instead.  The HIP
+ *   runtime may allocate internal memory when a shape is first recorded.
  *   Errors: INVALID_ARG, CAPACITY (B > max_batch, T > max_rows_per_seq,
  *   T < 1), DEVICE.  Flags: TOKEN_RANGE, TREE, KV_OVERFLOW. */
 spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
@@ -207,7 +215,15 @@ int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out
 spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int32_t iters, void* stream,
                               double* ms_out, double* bytes_out);
 
-/* Release the handle (host memory and events only). */
+/* Replay the recorded per-layer launch sequence (enable != 0, the default)
+ * or launch every kernel directly (enable == 0).  Both run the same kernels
+ * with the same arguments, so the results are identical; replay saves the
+ * per-launch dispatch overhead of ~190 kernels per step.
+ * Errors: INVALID_ARG (null handle). */
+spec_status spec_graph_enable(spec_handle* h, int32_t enable);
+
+/* Release the handle: host memory, events, recorded graphs and the private
+ * recording stream (waits for the device first when graphs exist). */
 void spec_verify_destroy(spec_handle* h);
 
 /* Static string for a status code. */

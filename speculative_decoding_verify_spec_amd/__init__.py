@@ -34,7 +34,7 @@ SPEC_FLAG_KV_OVERFLOW = 4
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_accept", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_profile_gemm", "spec_verify_destroy", "spec_status_str",
+    "spec_profile_gemm", "spec_graph_enable", "spec_verify_destroy", "spec_status_str",
 ]
 
 
@@ -96,6 +96,8 @@ def lib():
     L.spec_profile_gemm.argtypes = [vp, C.c_char_p, i32, i32, vp, C.POINTER(C.c_double),
                                     C.POINTER(C.c_double)]
     L.spec_profile_gemm.restype = i32
+    L.spec_graph_enable.argtypes = [vp, i32]
+    L.spec_graph_enable.restype = i32
     L.spec_verify_destroy.argtypes = [vp]
     L.spec_verify_destroy.restype = None
     L.spec_status_str.argtypes = [i32]
@@ -202,6 +204,10 @@ def spec_profile_gemm(h, cls: str, rows: int, iters: int, stream=None):
     _check("spec_profile_gemm", lib().spec_profile_gemm(h, cls.encode(), int(rows), int(iters),
                                                         _stream(stream), C.byref(ms), C.byref(nbytes)))
     return ms.value, nbytes.value
+
+
+def spec_graph_enable(h, enable: bool):
+    _check("spec_graph_enable", lib().spec_graph_enable(h, 1 if enable else 0))
 
 
 def spec_verify_destroy(h):

@@ -4,7 +4,10 @@
 
 namespace sv {
 
-// One workgroup per sequence.  Validates tokens, cache room and the tree;
+// One workgroup per sequence.  Copies kv_len into the workspace (the later
+// kernels of the step read only the workspace, weights and cache, so their
+// launch sequence can be recorded once and replayed); validates tokens, cache
+// room and the tree;
 // writes each row's clamped token, rotary position (kv_len + i for a chain,
 // kv_len + depth for a tree node), cache slot (kv_len + i), for a tree the
 // ancestor-or-self bitmask used by the attention mask, and gathers the rows'
@@ -18,6 +21,7 @@ __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
   __shared__ int stok[128];
   const int kv = p.kv_len[b];
   if (threadIdx.x == 0) {
+    p.kv_copy[b] = kv;
     if (kv < 0 || kv > p.max_ctx - T) atomicOr(p.flags, FLAG_KV_OVERFLOW);
     if (p.parent) {
       const int32_t* par = p.parent + (size_t)b * T;

@@ -19,6 +19,7 @@ struct PrepParams {
   const void* embed;      // [V][d] embedding table (weight dtype)
   int wdtype;             // 0 fp32, 1 bf16
   float* x;               // [M][d] residual stream, written with the rows' embeddings
+  int32_t* kv_copy;       // [B] copy of kv_len for the later kernels of the step
   int B, T, vocab, max_ctx, d;
 };
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);

@@ -49,7 +49,7 @@ int attn_splits(const spec_config& c, int B, int T) {
 
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, rowstat, rowms, rsum, nacc, rbuf, flags, total;
+  size_t tok, pos, slot, anc, kvw, rowstat, rowms, rsum, nacc, rbuf, flags, total;
 };
 
 Layout plan(const spec_config& c) {
@@ -83,6 +83,7 @@ Layout plan(const spec_config& c) {
   L.pos = take(Mmax * 4);
   L.slot = take(Mmax * 4);
   L.anc = take(Mmax * 2 * 8);
+  L.kvw = take((size_t)c.max_batch * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
@@ -92,6 +93,8 @@ Layout plan(const spec_config& c) {
   L.total = off;
   return L;
 }
+
+constexpr size_t kMaxGraphs = 32;  // recorded shapes kept per handle
 
 const char* kClassNames[] = {"prep_embed", "gemm_qkv", "attention", "attn_combine", "gemm_o",
                              "gemm_gate_up", "gemm_down", "gemm_lm_head", "accept"};
@@ -115,6 +118,17 @@ struct spec_handle {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
+  // recorded layer sequences, one per (B, T, tree) shape, replayed as HIP graphs
+  struct Graph {
+    int B, T;
+    bool tree;
+    hipGraphExec_t exec;
+    uint64_t used;
+  };
+  bool graphs = true;
+  hipStream_t cap = nullptr;  // private stream used only to record
+  std::vector<Graph> gcache;
+  uint64_t gclock = 0;
   int64_t launches[K_N] = {};
   double ms[K_N] = {};
   double bytes[K_N] = {};
@@ -170,6 +184,135 @@ hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+namespace {
+
+// The per-layer kernels of a step.  They read only the weights, the cache and
+// the workspace (kv_len through its copy made by the prep kernel), so for a
+// given (B, T, chain/tree) the launch sequence is fixed and can be recorded.
+hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s) {
+  const spec_config& c = h->cfg;
+  const Layout& L = h->lay;
+  const int M = B * T, d = c.d_model, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn;
+  float* x = h->at<float>(L.x);
+  float* q = h->at<float>(L.q);
+  float* ks = h->at<float>(L.ksuf);
+  float* vs = h->at<float>(L.vsuf);
+  float* at = h->at<float>(L.attn);
+  float* act = h->at<float>(L.act);
+  int32_t* pos = h->at<int32_t>(L.pos);
+  int32_t* slot = h->at<int32_t>(L.slot);
+  uint64_t* anc = h->at<uint64_t>(L.anc);
+  const int32_t* kvw = h->at<int32_t>(L.kvw);
+  hipError_t e;
+  const size_t per_region = (size_t)c.max_batch * Hkv * c.max_ctx * D;  // elements of one K or V region
+  const int splits = attn_splits(c, B, T);
+  const int nsplit = attn_nsplit(splits);
+  const float scale = 1.0f / std::sqrt((float)D);
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const float* g1 = (const float*)h->W(h->layer_w(l, 0));
+    const void* wqkv = h->W(h->layer_w(l, 1));
+    const void* wo = h->W(h->layer_w(l, 2));
+    const float* g2 = (const float*)h->W(h->layer_w(l, 3));
+    const void* wgu = h->W(h->layer_w(l, 4));
+    const void* wdn = h->W(h->layer_w(l, 5));
+    uint16_t* kreg = h->kv + (size_t)(2 * l) * per_region;
+    uint16_t* vreg = h->kv + (size_t)(2 * l + 1) * per_region;
+
+    GemmParams gq{};
+    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = x; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    gq.norm_g = g1; gq.eps = c.rms_eps;
+    gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
+    gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
+    gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
+    gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
+    if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return e;
+
+    AttnParams ap{q, kreg, vreg, kvw, h->at<float>(L.part_o), h->at<float>(L.part_ml),
+                  B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
+    e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
+    if (e != hipSuccess) return e;
+    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, q, ks, vs,
+                     tree ? anc : nullptr, at, B, T, Hq, Hkv, D, scale};
+    e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
+    if (e != hipSuccess) return e;
+
+    GemmParams go{};
+    go.W = wo; go.wdtype = c.weight_dtype; go.X = at; go.ldx = Hq * D; go.N = d; go.K = Hq * D;
+    go.epi = EPI_RESID; go.out = x; go.ldo = d;
+    if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return e;
+
+    GemmParams gg{};
+    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = x; gg.ldx = d; gg.N = 2 * F; gg.K = d;
+    gg.norm_g = g2; gg.eps = c.rms_eps;
+    gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
+    if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return e;
+
+    GemmParams gd{};
+    gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
+    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
+    if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Replay of the recorded layer sequence for this shape, recorded on first use
+// on the handle's private stream (recording runs nothing).  Returns null when
+// recording or instantiation fails.
+hipGraphExec_t layer_graph(spec_handle* h, int B, int T, bool tree) {
+  for (auto& g : h->gcache)
+    if (g.B == B && g.T == T && g.tree == tree) {
+      g.used = ++h->gclock;
+      return g.exec;
+    }
+  if (!h->cap && hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess) {
+    h->cap = nullptr;
+    return nullptr;
+  }
+  if (hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
+  const hipError_t le = launch_layers(h, B, T, tree, h->cap);
+  hipGraph_t graph = nullptr;
+  const hipError_t ce = hipStreamEndCapture(h->cap, &graph);
+  if (le != hipSuccess || ce != hipSuccess || !graph) {
+    if (graph) hipGraphDestroy(graph);
+    return nullptr;
+  }
+  hipGraphExec_t ex = nullptr;
+  const hipError_t ie = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
+  hipGraphDestroy(graph);
+  if (ie != hipSuccess) return nullptr;
+  if (h->gcache.size() >= kMaxGraphs) {
+    // evict the least recently used shape; it may still be running
+    size_t old = 0;
+    for (size_t i = 1; i < h->gcache.size(); ++i)
+      if (h->gcache[i].used < h->gcache[old].used) old = i;
+    if (hipDeviceSynchronize() != hipSuccess) {
+      hipGraphExecDestroy(ex);
+      return nullptr;
+    }
+    hipGraphExecDestroy(h->gcache[old].exec);
+    h->gcache.erase(h->gcache.begin() + old);
+  }
+  h->gcache.push_back({B, T, tree, ex, ++h->gclock});
+  return ex;
+}
+
+spec_status run_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s) {
+  if (h->graphs && !h->prof) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SPEC_ERR_DEVICE;
+    if (cs == hipStreamCaptureStatusNone) {
+      // the caller is not recording: replay our own recording
+      hipGraphExec_t ex = layer_graph(h, B, T, tree);
+      if (!ex) return SPEC_ERR_DEVICE;
+      return dev(hipGraphLaunch(ex, s));
+    }
+  }
+  return dev(launch_layers(h, B, T, tree, s));
 }
 
 }  // namespace
@@ -260,15 +403,10 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
   if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
   const Layout& L = h->lay;
-  const int M = B * T, d = c.d_model, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn;
+  const int M = B * T, d = c.d_model;
   const int V = c.vocab;
   const size_t wb = c.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   float* x = h->at<float>(L.x);
-  float* q = h->at<float>(L.q);
-  float* ks = h->at<float>(L.ksuf);
-  float* vs = h->at<float>(L.vsuf);
-  float* at = h->at<float>(L.attn);
-  float* act = h->at<float>(L.act);
   int32_t* tok = h->at<int32_t>(L.tok);
   int32_t* pos = h->at<int32_t>(L.pos);
   int32_t* slot = h->at<int32_t>(L.slot);
@@ -277,59 +415,13 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
   hipError_t e;
 
   PrepParams pp{d_tokens, d_kv_len, d_tree_parent, tok, pos, slot, anc, flags, h->W(0), c.weight_dtype, x,
-                B, T, V, c.max_ctx, d};
+                h->at<int32_t>(L.kvw), B, T, V, c.max_ctx, d};
   e = timed(h, K_PREP, (double)M * d * (wb + 4), s, [&] { return launch_prep(pp, s); });
   if (e != hipSuccess) return SPEC_ERR_DEVICE;
 
-  const size_t per_region = (size_t)c.max_batch * Hkv * c.max_ctx * D;  // elements of one K or V region
-  const int splits = attn_splits(c, B, T);
-  const int nsplit = attn_nsplit(splits);
-  const float scale = 1.0f / std::sqrt((float)D);
+  spec_status st = run_layers(h, B, T, d_tree_parent != nullptr, s);
+  if (st != SPEC_OK) return st;
 
-  for (int l = 0; l < c.n_layers; ++l) {
-    const float* g1 = (const float*)h->W(h->layer_w(l, 0));
-    const void* wqkv = h->W(h->layer_w(l, 1));
-    const void* wo = h->W(h->layer_w(l, 2));
-    const float* g2 = (const float*)h->W(h->layer_w(l, 3));
-    const void* wgu = h->W(h->layer_w(l, 4));
-    const void* wdn = h->W(h->layer_w(l, 5));
-    uint16_t* kreg = h->kv + (size_t)(2 * l) * per_region;
-    uint16_t* vreg = h->kv + (size_t)(2 * l + 1) * per_region;
-
-    GemmParams gq{};
-    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = x; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
-    gq.norm_g = g1; gq.eps = c.rms_eps;
-    gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
-    gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
-    gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
-    gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
-    if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
-
-    AttnParams ap{q, kreg, vreg, d_kv_len, h->at<float>(L.part_o), h->at<float>(L.part_ml),
-                  B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
-    e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
-    if (e != hipSuccess) return SPEC_ERR_DEVICE;
-    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, q, ks, vs,
-                     d_tree_parent ? anc : nullptr, at, B, T, Hq, Hkv, D, scale};
-    e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
-    if (e != hipSuccess) return SPEC_ERR_DEVICE;
-
-    GemmParams go{};
-    go.W = wo; go.wdtype = c.weight_dtype; go.X = at; go.ldx = Hq * D; go.N = d; go.K = Hq * D;
-    go.epi = EPI_RESID; go.out = x; go.ldo = d;
-    if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
-
-    GemmParams gg{};
-    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = x; gg.ldx = d; gg.N = 2 * F; gg.K = d;
-    gg.norm_g = g2; gg.eps = c.rms_eps;
-    gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
-    if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
-
-    GemmParams gd{};
-    gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
-    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
-    if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
-  }
   const float* gf = (const float*)h->W(1 + 6 * (size_t)c.n_layers);
   GemmParams gl{};
   gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = x; gl.ldx = d; gl.N = V;
@@ -484,7 +576,16 @@ void spec_verify_destroy(spec_handle* h) {
     hipEventDestroy(r.b);
   }
   for (auto e : h->pool) hipEventDestroy(e);
+  if (!h->gcache.empty()) hipDeviceSynchronize();  // a replay may still be running
+  for (auto& g : h->gcache) hipGraphExecDestroy(g.exec);
+  if (h->cap) hipStreamDestroy(h->cap);
   delete h;
+}
+
+spec_status spec_graph_enable(spec_handle* h, int32_t enable) {
+  if (!h) return SPEC_ERR_INVALID_ARG;
+  h->graphs = enable != 0;
+  return SPEC_OK;
 }
 
 }  // extern "C"

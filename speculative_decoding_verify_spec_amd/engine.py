@@ -5,9 +5,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (make_config, spec_accept, spec_device_errors, spec_kv_cache_bytes, spec_profile_gemm,
-               spec_sampling, spec_verify_destroy, spec_verify_init, spec_verify_step,
-               spec_workspace_bytes)
+from . import (make_config, spec_accept, spec_device_errors, spec_graph_enable, spec_kv_cache_bytes,
+               spec_profile_gemm, spec_sampling, spec_verify_destroy, spec_verify_init,
+               spec_verify_step, spec_workspace_bytes)
 
 
 class VerifyEngine:
@@ -43,6 +43,10 @@ class VerifyEngine:
         """(ms, algorithmic bytes) of `iters` back-to-back passes of one GEMM
         class over all layers; overwrites the workspace activations."""
         return spec_profile_gemm(self.handle, cls, rows, iters, self.stream)
+
+    def graphs(self, enable: bool):
+        """Replay the recorded per-layer launches (default) or launch directly."""
+        spec_graph_enable(self.handle, enable)
 
     def device_errors(self) -> int:
         return spec_device_errors(self.handle, self.stream)
