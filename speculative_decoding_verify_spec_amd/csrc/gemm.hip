@@ -158,9 +158,13 @@ DEVI void fma_rows(float* acc, const float (&w)[8], const float (&x)[MT][8], int
 }
 
 // Fold one row group's partial sums over lanes and waves; returns with the
-// YT*MT sums in tot[] (all threads synchronised).
+// YT*MT sums in tot[] (all threads synchronised).  With `ssq` (per-wave sums
+// of x^2 of the activation rows, [nwaves][MT] in LDS) the sums are scaled by
+// the rows' RMSNorm factor 1/sqrt(mean(x^2) + eps): the norm's gain was
+// applied to the activations, its row factor is applied here.
 template <int MT, bool LDS_ONLY = false>
-DEVI void reduce_group(float* acc, int lane, int w, int nwaves, float (*red)[MaxPow2<MT>::v], float* tot) {
+DEVI void reduce_group(float* acc, int lane, int w, int nwaves, float (*red)[MaxPow2<MT>::v], float* tot,
+                       const float (*ssq)[MT] = nullptr, float inv_k = 0.f, float eps = 0.f) {
   constexpr int NV = YT * MT;
   constexpr int NVP = MaxPow2<MT>::v;
   constexpr int SH = (NVP == 8) ? 3 : (NVP == 16) ? 2 : (NVP == 32) ? 1 : 0;
@@ -170,6 +174,12 @@ DEVI void reduce_group(float* acc, int lane, int w, int nwaves, float (*red)[Max
   if (threadIdx.x < NV) {
     float t = 0.f;
     for (int i = 0; i < nwaves; ++i) t += red[i][threadIdx.x];
+    if (ssq) {
+      const int m = threadIdx.x % MT;
+      float q = 0.f;
+      for (int i = 0; i < nwaves; ++i) q += ssq[i][m];
+      t *= 1.0f / sqrtf(q * inv_k + eps);
+    }
     tot[threadIdx.x] = t;
   }
   if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();
@@ -303,7 +313,9 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
     }
   }
   if constexpr (NORM) {
-    // RMSNorm of the activation rows: the workgroup's waves hold them whole
+    // RMSNorm of the activation rows: the gain multiplies the registers now;
+    // the row factor needs every wave's sum of squares and is applied to the
+    // finished sums (reduce_group), so no barrier sits in front of the loop
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       float ss = 0.f;
@@ -314,15 +326,6 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
       ss = wave_sum(ss);
       if (lane == 0) ssq[w][m] = ss;
     }
-    lds_barrier();
-    float inv[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < KSTAT_WAVES; ++i) t += ssq[i][m];
-      inv[m] = 1.0f / sqrtf(t / (float)p.K + p.eps);
-    }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const float4 ga = *(const float4*)(p.norm_g + kofs[i]);
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xr[i][m][e] = xr[i][m][e] * inv[m] * g[e];
+        for (int e = 0; e < 8; ++e) xr[i][m][e] *= g[e];
     }
   }
 
@@ -359,7 +362,175 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
         if (more) wr[i][y].load(W, rnext[y] + kofs[i]);
         fma_rows<MT>(acc, wf, xr[i], y);
       }
-    reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot);
+    if constexpr (NORM)
+      reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot, ssq, 1.0f / (float)p.K, p.eps);
+    else
+      reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot);
+    epilogue<MT, EPI>(p, rg, tot);
+  }
+}
+
+// ---------------------------------------------------------------- matrix cores
+// The same k-stationary scheme on the 4x4x4 bf16 matrix instruction with 16
+// blocks (v_mfma_f32_4x4x4_16b_bf16).  Lane l = 4*blk + r: in each 128-k chunk,
+// block blk covers k = 8*blk .. 8*blk+7.  For the weights (A operand) lane l
+// holds row r of a 4-row set at those 8 k (one 16-byte load; a wave reads 4
+// rows x 256 contiguous bytes); for the activations (B operand) it holds
+// activation row r (4*mg + r for the second set of 4 rows) at the same k,
+// split into bf16 hi + lo so the fp32 activations keep ~2^-16 relative
+// accuracy.  Each instruction accumulates a 4x4 (weight row x activation row)
+// tile per block; the 16 blocks' tiles are summed across lanes at the end of
+// a row group.  Against the vector-ALU kernel this removes the widening of
+// the weights and three quarters of the multiply-add issue, which is what
+// makes the cost of a group grow with M there.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int MT, int EPI, bool NORM, int CPW>
+__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int MG = (MT + 3) / 4;  // sets of 4 activation rows
+  constexpr int RG = YT / 4;        // sets of 4 weight rows per group
+  constexpr int NV = YT * MT;
+  __shared__ float red[KSTAT_WAVES][YT][4 * MG];
+  __shared__ float tot[64];
+  __shared__ float ssq[KSTAT_WAVES][4 * MG];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 3, blk = lane >> 2;
+  const uint16_t* __restrict__ W = (const uint16_t*)p.W;
+  const int nch = p.K >> 7;
+  // chunks w, w+4, ... of 128 k; a chunk past K is read at chunk 0 (in
+  // bounds) and multiplied by zero activations
+  int kofs[CPW];
+  bool cok[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = w + KSTAT_WAVES * i;
+    cok[i] = c < nch;
+    kofs[i] = (cok[i] ? c : 0) * 128 + 8 * blk;
+  }
+  const int ngroups = gemm_groups<EPI>(p);
+  const int G = gridDim.x;
+  auto row_off = [&](int g_, int a) {
+    const int row = gemm_row<EPI>(p, g_, 4 * a + r);
+    return (size_t)(row < p.N ? row : 0) * p.K;
+  };
+  // first group's weights before the activation prologue; a workgroup with
+  // no group reads the head of row 0 and never uses it
+  u32x4 wr[RG][CPW];
+  int rg = blockIdx.x;
+#pragma unroll
+  for (int a = 0; a < RG; ++a) {
+    const size_t ro = rg < ngroups ? row_off(rg, a) : 0;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) wr[a][i] = __builtin_nontemporal_load((const u32x4*)(W + ro + kofs[i]));
+  }
+  // activations (times the norm gain), split into bf16 hi + lo
+  shortx4 xh[CPW][MG][2], xl[CPW][MG][2];
+  float ss[MG];
+#pragma unroll
+  for (int mg = 0; mg < MG; ++mg) ss[mg] = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    float g[8];
+    if constexpr (NORM) {
+      const float4 ga = *(const float4*)(p.norm_g + kofs[i]);
+      const float4 gb = *(const float4*)(p.norm_g + kofs[i] + 4);
+      g[0] = ga.x; g[1] = ga.y; g[2] = ga.z; g[3] = ga.w; g[4] = gb.x; g[5] = gb.y; g[6] = gb.z; g[7] = gb.w;
+    }
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      const int m = 4 * mg + r;
+      const bool ok = cok[i] && m < p.M;
+      const float* xs = p.X + (size_t)(m < p.M ? m : 0) * p.ldx + kofs[i];
+      const float4 x0 = *(const float4*)xs, x1 = *(const float4*)(xs + 4);
+      float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xv[e] = ok ? xv[e] : 0.f;
+        if constexpr (NORM) {
+          ss[mg] += xv[e] * xv[e];
+          xv[e] *= g[e];
+        }
+        short hi, lo;
+        split_bf16(xv[e], hi, lo);
+        xh[i][mg][e >> 2][e & 3] = hi;
+        xl[i][mg][e >> 2][e & 3] = lo;
+      }
+    }
+  }
+  if constexpr (NORM) {
+    // per-wave sums of x^2 of each activation row (lanes with the same r)
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+      float t = ss[mg];
+      t += __shfl_xor(t, 4, 64);
+      t += __shfl_xor(t, 8, 64);
+      t += __shfl_xor(t, 16, 64);
+      t += __shfl_xor(t, 32, 64);
+      if (blk == 0) ssq[w][4 * mg + r] = t;
+    }
+  }
+
+  for (; rg < ngroups; rg += G) {
+    // the weight registers are refilled with the next group's rows as soon
+    // as the products have read them; a workgroup without a next group reads
+    // the head of row 0 again (in bounds, cached, never used)
+    const int nx = rg + G;
+    size_t rn[RG];
+#pragma unroll
+    for (int a = 0; a < RG; ++a) rn[a] = nx < ngroups ? row_off(nx, a) : 0;
+    floatx4 acc[RG][MG];
+#pragma unroll
+    for (int a = 0; a < RG; ++a)
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) acc[a][mg] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int a = 0; a < RG; ++a)
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const u32x4 v = wr[a][i];
+        const shortx4 w0 = __builtin_bit_cast(shortx4, u32x2{v.x, v.y});
+        const shortx4 w1 = __builtin_bit_cast(shortx4, u32x2{v.z, v.w});
+        wr[a][i] = __builtin_nontemporal_load((const u32x4*)(W + rn[a] + kofs[i]));
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) {
+          acc[a][mg] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(w0, xh[i][mg][0], acc[a][mg], 0, 0, 0);
+          acc[a][mg] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(w0, xl[i][mg][0], acc[a][mg], 0, 0, 0);
+          acc[a][mg] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(w1, xh[i][mg][1], acc[a][mg], 0, 0, 0);
+          acc[a][mg] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(w1, xl[i][mg][1], acc[a][mg], 0, 0, 0);
+        }
+      }
+    // lane (blk, r) holds rows 4a + v (v = 0..3) x activation row 4mg + r of
+    // its block; sum the 16 blocks: halving over lane bits 5 and 4 (which
+    // also spreads the 4 rows over the lanes), plain adds over bits 3 and 2
+#pragma unroll
+    for (int a = 0; a < RG; ++a)
+#pragma unroll
+      for (int mg = 0; mg < MG; ++mg) {
+        const float v0 = acc[a][mg][0], v1 = acc[a][mg][1], v2 = acc[a][mg][2], v3 = acc[a][mg][3];
+        const bool u5 = (lane & 32) != 0;
+        float k0 = u5 ? v2 : v0, k1 = u5 ? v3 : v1;
+        const float s0 = u5 ? v0 : v2, s1 = u5 ? v1 : v3;
+        k0 += __shfl_xor(s0, 32, 64);
+        k1 += __shfl_xor(s1, 32, 64);
+        const bool u4 = (lane & 16) != 0;
+        float kk = u4 ? k1 : k0;
+        const float sk = u4 ? k0 : k1;
+        kk += __shfl_xor(sk, 16, 64);
+        kk += __shfl_xor(kk, 8, 64);
+        kk += __shfl_xor(kk, 4, 64);
+        if ((lane & 12) == 0) red[w][4 * a + ((lane >> 4) & 3)][4 * mg + r] = kk;
+      }
+    lds_barrier();
+    if (threadIdx.x < NV) {
+      const int y = threadIdx.x / MT, m = threadIdx.x % MT;
+      float t = red[0][y][m] + red[1][y][m] + red[2][y][m] + red[3][y][m];
+      if constexpr (NORM) {
+        const float q = ssq[0][m] + ssq[1][m] + ssq[2][m] + ssq[3][m];
+        t *= 1.0f / sqrtf(q / (float)p.K + p.eps);
+      }
+      tot[threadIdx.x] = t;
+    }
+    lds_barrier();
     epilogue<MT, EPI>(p, rg, tot);
   }
 }
@@ -424,17 +595,41 @@ static int device_cus() {
 
 bool gemm_is_kstat(int K) { return K <= KSTAT_WAVES * KSTAT_SPW * 512; }
 
+// Matrix cores or vector ALUs for an M-row launch.  Measured on the 8B layer
+// shapes (back-to-back launches): the matrix-core kernel is flat in M (gate/up
+// 38.9 / 39.4 / 41.0 us at M = 1 / 2 / 4, 63 us at M = 8 against 73 for the
+// vector kernel) but slower on small matrices and at M <= 2 (QKV 18.8 vs
+// 16.9 us and O 12.2 vs 10.7 us at M = 4), where its activation prologue is
+// not amortised.  So: matrix cores from M = 5 on, and from M = 3 on for
+// matrices of at least 64 Mi weights (gate/up, LM head).
+bool gemm_use_mfma(const GemmParams& p, int rows) {
+  if (p.wdtype != 1 || (p.K & 127) || p.K > KSTAT_WAVES * 8 * 128) return false;
+  const double elems = (double)(p.epi == EPI_SWIGLU ? 2 * p.F : p.N) * p.K;
+  return rows >= 5 || (rows >= 3 && elems >= 64.0 * 1024 * 1024);
+}
+
+template <int MT, int EPI, int CPW>
+static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
+  if (p.norm_g) gemm_mfma_kernel<MT, EPI, true, CPW><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI, false, CPW><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+}
+
 template <int MT, int EPI>
 static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
   const int groups = gemm_groups<EPI>(p);
-  if (gemm_is_kstat(p.K)) {
-    // persistent workgroups, at most two per CU, each looping over row
-    // groups; the grid is sized so that every workgroup gets the same number
-    // of groups (up to one), which keeps the last round from running on a
-    // fraction of the chip
-    const int slots = 2 * device_cus();
-    const int rounds = (groups + slots - 1) / slots;
-    const int grid = (groups + rounds - 1) / rounds;
+  // persistent workgroups, at most two per CU, each looping over row
+  // groups; the grid is sized so that every workgroup gets the same number
+  // of groups (up to one), which keeps the last round from running on a
+  // fraction of the chip
+  const int slots = 2 * device_cus();
+  const int rounds = (groups + slots - 1) / slots;
+  const int grid = (groups + rounds - 1) / rounds;
+  if (gemm_use_mfma(p, p.M)) {
+    const int cpw = ((p.K >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
+    if (cpw <= 2) launch_mfma_cpw<MT, EPI, 2>(p, grid, s);
+    else if (cpw <= 4) launch_mfma_cpw<MT, EPI, 4>(p, grid, s);
+    else launch_mfma_cpw<MT, EPI, 8>(p, grid, s);
+  } else if (gemm_is_kstat(p.K)) {
     if (p.wdtype == 1) {
       if (p.norm_g) gemm_kstat_kernel<MT, uint16_t, EPI, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
       else gemm_kstat_kernel<MT, uint16_t, EPI, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
