@@ -7,29 +7,136 @@
 // The context of a (sequence, KV head) is cut into `splits` workgroups of 4
 // waves; each wave keeps its own online-softmax state (flash-decoding style),
 // the four states are merged in LDS and the workgroup writes one partial
-// (max, sum, unnormalised output) per query.  The
-// products run on bf16 MFMA 16x16x16: S^T = K Q^T with K exact in bf16 and
-// the fp32 queries split into bf16 hi + lo, then O^T += V^T P^T with the fp32
-// probabilities split the same way; accumulation is fp32.  V is stored
-// transposed in the cache so the key index (the contraction of P V) is
-// contiguous.
+// (max, sum, unnormalised output) per query.  The products run on bf16 MFMA
+// 16x16x16: S^T = K Q^T with K exact in bf16 and the fp32 queries split into
+// bf16 hi + lo, then O^T += V^T P^T with the fp32 probabilities split the
+// same way; accumulation is fp32.  V is stored transposed in the cache so the
+// key index (the contraction of P V) is contiguous.  A wave's first key block
+// is requested before the queries are prepared, so the cache reads and the
+// query reads overlap.
+//
+// Suffix part: 4*QT more workgroups per (sequence, KV head, query group), one
+// wave per query, attend to the step's own keys in fp32 (chain: rows 0..i;
+// tree: the node and its ancestors) and write their partials in the slot
+// after the context splits, so the suffix runs beside the context instead of
+// after it.
 //
 // Combine part (attn_combine_kernel), one wave per (row, query head): merges
-// the split partials, adds the suffix keys in fp32 (chain: rows 0..i; tree:
-// the node and its ancestors) and normalises.  Keys beyond a wave's range are
-// loaded as zeros and masked, so nothing past kv_len is ever used.
+// the nsplit partials of a query and normalises.  Keys at or beyond kv_len
+// are loaded as zeros and masked, so nothing past kv_len is ever used.
 #include "common.h"
 #include "launch.h"
 
 namespace sv {
 
 int attn_query_tiles_per_wave(int nq) { return nq > 16 ? 2 : 1; }
-int attn_nsplit(int splits) { return splits; }
+int attn_nsplit(int splits) { return splits + 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
 // 4g..4g+3 of both tiles cover keys kb + 8g .. kb + 8g + 7, so one 16-byte
 // load of V^T feeds both tiles.
 DEVI int blk_key(int kb, int kt, int r) { return kb + 8 * (r >> 2) + 4 * kt + (r & 3); }
+
+// The step's own keys, in fp32, for four queries of one (sequence, KV head,
+// query group): suffix workgroup sw takes queries 4*sw .. 4*sw+3 of the
+// group, one per wave.  The queries are staged in LDS, the keys and values
+// come through LDS in chunks of KC rows shared by the four waves; scores are
+// lane-parallel over the chunk's keys, the value sum lane-parallel over
+// dimensions.  `smem` must hold 4*D + 2*KC*(D+4) floats.
+template <int D, int QT>
+DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float* smem) {
+  constexpr int PL = D / 64;
+  constexpr int QN = QT * 16;
+  constexpr int KC = 16;       // keys per chunk
+  constexpr int KS = D + 4;    // padded key-row stride
+  float* s_q = smem;           // [4][D]
+  float* s_k = s_q + 4 * D;    // [KC][KS]
+  float* s_v = s_k + KC * KS;  // [KC][KS]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int G = p.Hq / p.Hkv;
+  const int nq = G * p.T;
+  const int qi = qg * QN + 4 * sw + w;
+  const bool qok = qi < nq;  // wave-uniform
+  const int i = qok ? qi / G : 0;
+  // staging loads are issued before the LDS stores (float4 granules, loops
+  // fully unrolled), so each stage costs one memory latency
+  constexpr int KV = KC * D / 4 / 256;  // key (and value) float4s per thread
+  static_assert(KV * 256 * 4 == KC * D && D / 4 <= 64, "staging granules");
+  if (lane < D / 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qok) v = *(const float4*)(p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * G + qi % G) * D + 4 * lane);
+    *(float4*)(s_q + w * D + 4 * lane) = make_float4(v.x * p.scale, v.y * p.scale, v.z * p.scale, v.w * p.scale);
+  }
+  float mq = -INFINITY, lq = 0.f, oq[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) oq[e] = 0.f;
+  for (int c0 = 0; c0 < p.T; c0 += KC) {
+    {
+      float4 kv[KV], vv[KV];
+#pragma unroll
+      for (int r = 0; r < KV; ++r) {
+        const int e4 = threadIdx.x + 256 * r;
+        const int t = e4 / (D / 4), d4 = e4 % (D / 4);
+        const int jj = c0 + t;
+        kv[r] = vv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (jj < p.T) {
+          const size_t src = ((size_t)(b * p.T + jj) * p.Hkv + kvh) * D + 4 * d4;
+          kv[r] = *(const float4*)(p.k_suf + src);
+          vv[r] = *(const float4*)(p.v_suf + src);
+        }
+      }
+      __syncthreads();  // the previous chunk is consumed
+#pragma unroll
+      for (int r = 0; r < KV; ++r) {
+        const int e4 = threadIdx.x + 256 * r;
+        const int t = e4 / (D / 4), d4 = e4 % (D / 4);
+        *(float4*)(s_k + t * KS + 4 * d4) = kv[r];
+        *(float4*)(s_v + t * KS + 4 * d4) = vv[r];
+      }
+      __syncthreads();
+    }
+    if (!qok) continue;  // wave-uniform; the barriers above are shared by all
+    const int jj = c0 + lane;
+    bool vis = lane < KC && jj < p.T;
+    if (vis) vis = p.anc ? (((p.anc[2 * (b * p.T + i) + (jj >> 6)] >> (jj & 63)) & 1ull) != 0) : (jj <= i);
+    float sc = -INFINITY;
+    if (vis) {
+      const float* qr = s_q + w * D;
+      const float* kr = s_k + lane * KS;
+      float t = 0.f;
+#pragma unroll 8
+      for (int d4 = 0; d4 < D; d4 += 4) {
+        const float4 a = *(const float4*)(qr + d4);
+        const float4 k = *(const float4*)(kr + d4);
+        t += a.x * k.x + a.y * k.y + a.z * k.z + a.w * k.w;
+      }
+      sc = t;
+    }
+    const float cm = wave_max(sc);
+    if (cm == -INFINITY) continue;  // no visible key in this chunk
+    const float mn = fmaxf(mq, cm);
+    const float f = (mq == -INFINITY) ? 0.f : __expf(mq - mn);
+    const float pe = vis ? __expf(sc - mn) : 0.f;
+    lq = lq * f + wave_sum(pe);
+    mq = mn;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) oq[e] *= f;
+#pragma unroll
+    for (int t = 0; t < KC; ++t) {
+      const float pt = __shfl(pe, t, 64);
+#pragma unroll
+      for (int e = 0; e < PL; ++e) oq[e] += pt * s_v[t * KS + lane + 64 * e];
+    }
+  }
+  if (!qok) return;
+  const size_t slot = (((size_t)p.splits * p.B + b) * p.Hkv + kvh) * nq;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) p.part_o[(slot + qi) * D + lane + 64 * e] = oq[e];
+  if (lane == 0) {
+    p.part_ml[2 * (slot + qi)] = mq;
+    p.part_ml[2 * (slot + qi) + 1] = lq;
+  }
+}
 
 template <int D, int QT>
 __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
@@ -44,12 +151,48 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   const int G = p.Hq / p.Hkv;
   const int nq = G * p.T;
 
+  constexpr int QN = QT * 16;
+  constexpr int OS = D + 4;  // padded row stride of the staged outputs
+  __shared__ float s_m[4][QN];
+  __shared__ float s_l[4][QN];
+  __shared__ float s_o[4][QN * OS];
+  static_assert(4 * D + 2 * 16 * (D + 4) <= 4 * QN * OS, "suffix staging must fit the output stage");
+  if (s >= p.splits) {  // the step's own keys; the output stage is its scratch
+    attn_suffix<D, QT>(p, kvh, qg, b, s - p.splits, &s_o[0][0]);
+    return;
+  }
   int L = p.kv_len[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   int chunk = (L + p.splits - 1) / p.splits;
   chunk = (chunk + 127) & ~127;
   const int kbeg = s * chunk;
   const int kend = min(L, kbeg + chunk);
+
+  // ---- raw cache loads of one 32-key block, issued before they are needed:
+  // K rows of the block's two key tiles and the V^T columns of its keys;
+  // keys at or past kend read as zeros
+  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.max_ctx * D;
+  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)D * p.max_ctx;
+  uint4 kraw[2][DG / 8];
+  uint4 vraw[DT];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = blk_key(kb, kt, j);
+      const bool ok = key < kend;
+      const uint16_t* src = kbase + (size_t)(ok ? key : 0) * D + g * DG;
+#pragma unroll
+      for (int e = 0; e < DG / 8; ++e) kraw[kt][e] = ok ? *(const uint4*)(src + 8 * e) : make_uint4(0, 0, 0, 0);
+    }
+    const int k8 = kb + 8 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* src = vbase + (size_t)(dt * 16 + j) * p.max_ctx + (k8 < kend ? k8 : 0);
+      vraw[dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
+    }
+  };
+  int kb = kbeg + 32 * w;
+  if (kb < kend) load_block(kb);
 
   // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
   // g*DG + 4*ks + e for k-step ks.
@@ -93,27 +236,20 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.max_ctx * D;
-  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)D * p.max_ctx;
-
-  for (int kb = kbeg + 32 * w; kb < kend; kb += 128) {
+  for (; kb < kend; kb += 128) {
     // ---- K operand (A of S^T): lane row j of tile kt is key blk_key(kb, kt, j)
     shortx4 ka[2][KSTEPS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = blk_key(kb, kt, j);
-      const bool ok = key < kend;
-      const uint16_t* src = kbase + (size_t)key * D + g * DG;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < DG; e += 8) {
-        uint4 v = ok ? *(const uint4*)(src + e) : make_uint4(0, 0, 0, 0);
-        const int ks = e / 4;
+      for (int e = 0; e < DG / 8; ++e) {
+        const uint4 v = kraw[kt][e];
+        const int ks = 2 * e;
         ka[kt][ks][0] = (short)(v.x & 0xffff); ka[kt][ks][1] = (short)(v.x >> 16);
         ka[kt][ks][2] = (short)(v.y & 0xffff); ka[kt][ks][3] = (short)(v.y >> 16);
         ka[kt][ks + 1][0] = (short)(v.z & 0xffff); ka[kt][ks + 1][1] = (short)(v.z >> 16);
         ka[kt][ks + 1][2] = (short)(v.w & 0xffff); ka[kt][ks + 1][3] = (short)(v.w >> 16);
       }
-    }
     // ---- V^T operand (A of O^T += V^T P^T): lane row j of dim tile dt is
     // dim dt*16 + j; its k index 4g + e in key tile kt is key kb + 8g + 4kt + e.
     shortx4 va[DT][2];
@@ -121,8 +257,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
       const int k8 = kb + 8 * g;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* src = vbase + (size_t)(dt * 16 + j) * p.max_ctx + k8;
-        uint4 v = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
+        const uint4 v = vraw[dt];
         uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -183,14 +318,13 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
         }
       }
     }
+    // the wave's next block (long contexts) is requested once this one's
+    // operands are consumed, which keeps the raw and converted copies from
+    // being live together
+    if (kb + 128 < kend) load_block(kb + 128);
   }
 
   // ---- merge the four waves' states in LDS and write one partial per query
-  constexpr int QN = QT * 16;
-  constexpr int OS = D + 4;  // padded row stride of the staged outputs
-  __shared__ float s_m[4][QN];
-  __shared__ float s_l[4][QN];
-  __shared__ float s_o[4][QN * OS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float l = lrun[qt];
@@ -237,7 +371,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nq = (p.Hq / p.Hkv) * p.T;
   const int QT = attn_query_tiles_per_wave(nq);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
-  dim3 grid(p.splits, p.Hkv * nqg, p.B);
+  if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
+  // + QT*4 suffix workgroups of four queries each
+  dim3 grid(p.splits + 4 * QT, p.Hkv * nqg, p.B);
   if (p.D == 128) {
     if (QT == 1) attn_ctx_kernel<128, 1><<<grid, 256, 0, s>>>(p);
     else attn_ctx_kernel<128, 2><<<grid, 256, 0, s>>>(p);
@@ -248,99 +384,71 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One workgroup per (row i, KV head, sequence); wave g handles query head
-// kvh * G + g.  The split statistics are read by all lanes at once, the
-// weighted sum of the split outputs keeps every load in flight, then the
-// suffix keys (chain: rows 0..i; tree: the node and its ancestors) are added
-// in fp32 and the result normalised.
+// One workgroup per (row i, KV head, sequence); wave gg handles query head
+// kvh * G + gg.  Lanes read the split statistics in parallel (two splits per
+// lane); every split's output is requested before any is weighted, and the
+// weights reach the lanes by shuffles, so the only waits are the loads.
 template <int D>
 __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   constexpr int PL = D / 64;  // dims per lane
-  constexpr int MAXS = 128;
-  __shared__ float s_w[8][MAXS];
+  constexpr int U = 8;        // splits whose outputs are in flight at once
   const int i = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, gg = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
-  const int hq = kvh * G + gg;
   const int nq = G * p.T;
   const int qi = i * G + gg;
   const int m = b * p.T + i;
   const int ns = p.nsplit;
+  const size_t stride = (size_t)p.B * p.Hkv * nq;  // between splits, in queries
+  const size_t q0 = ((size_t)b * p.Hkv + kvh) * nq + qi;
 
-  // split statistics: M = max over splits with mass, weights exp(m_s - M)
+  float ms[2], ls[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int sp = lane + 64 * c;
+    ms[c] = -INFINITY;
+    ls[c] = 0.f;
+    if (sp < ns) {
+      ms[c] = p.part_ml[2 * (sp * stride + q0)];
+      ls[c] = p.part_ml[2 * (sp * stride + q0) + 1];
+    }
+  }
   float mloc = -INFINITY;
-  for (int sp = lane; sp < ns; sp += 64) {
-    const size_t base = (((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi;
-    if (p.part_ml[2 * base + 1] > 0.f) mloc = fmaxf(mloc, p.part_ml[2 * base]);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    if (ls[c] > 0.f) mloc = fmaxf(mloc, ms[c]);
+  const float mstar = wave_max(mloc);  // the suffix split always has mass
+  float wt[2], lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    wt[c] = (ls[c] > 0.f) ? __expf(ms[c] - mstar) : 0.f;
+    lsum += wt[c] * ls[c];
   }
-  const float mstar = wave_max(mloc);
-  float lloc = 0.f;
-  for (int sp = lane; sp < ns; sp += 64) {
-    const size_t base = (((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi;
-    const float ls = p.part_ml[2 * base + 1];
-    const float wgt = (ls > 0.f) ? expf(p.part_ml[2 * base] - mstar) : 0.f;
-    s_w[gg][sp] = wgt;
-    lloc += wgt * ls;
-  }
-  float l = wave_sum(lloc);
-  __syncthreads();
+  const float l = wave_sum(lsum);
+
   float acc[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-  float mcur = mstar;
-  if (l > 0.f) {
-    int sp = 0;
-    for (; sp + 8 <= ns; sp += 8) {
-      float v[8][PL];
+  for (int sp0 = 0; sp0 < ns; sp0 += U) {
+    float v[U][PL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* src = p.part_o + ((((size_t)(sp + u) * p.B + b) * p.Hkv + kvh) * nq + qi) * D;
+    for (int u = 0; u < U; ++u) {
+      const int sp = sp0 + u < ns ? sp0 + u : ns - 1;
+      const float* src = p.part_o + (sp * stride + q0) * D;
 #pragma unroll
-        for (int e = 0; e < PL; ++e) v[u][e] = src[lane + 64 * e];
+      for (int e = 0; e < PL; ++e) v[u][e] = src[lane + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = sp0 + u;
+      const float wsp = __shfl(sp < 64 ? wt[0] : wt[1], sp & 63, 64);
+      if (sp < ns) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) acc[e] += wsp * v[u][e];
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < PL; ++e) acc[e] += s_w[gg][sp + u] * v[u][e];
     }
-    for (; sp < ns; ++sp) {
-      const float* src = p.part_o + ((((size_t)sp * p.B + b) * p.Hkv + kvh) * nq + qi) * D;
-#pragma unroll
-      for (int e = 0; e < PL; ++e) acc[e] += s_w[gg][sp] * src[lane + 64 * e];
-    }
-  } else {
-    mcur = -INFINITY;
-    l = 0.f;
   }
-  // suffix keys in fp32
-  float qv[PL];
-  const float* qsrc = p.q + ((size_t)m * p.Hq + hq) * D;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) qv[e] = qsrc[lane + 64 * e];
-  for (int jj = 0; jj < p.T; ++jj) {
-    bool vis;
-    if (p.anc) {
-      const uint64_t word = p.anc[2 * m + (jj >> 6)];
-      vis = (word >> (jj & 63)) & 1ull;
-    } else {
-      vis = jj <= i;
-    }
-    if (!vis) continue;
-    const int mj = b * p.T + jj;
-    const float* ksp = p.k_suf + ((size_t)mj * p.Hkv + kvh) * D;
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) d += qv[e] * ksp[lane + 64 * e];
-    const float sc = wave_sum(d) * p.scale;
-    const float mnew = fmaxf(mcur, sc);
-    const float f1 = expf(mcur - mnew), ee = expf(sc - mnew);
-    const float* vsp = p.v_suf + ((size_t)mj * p.Hkv + kvh) * D;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) acc[e] = acc[e] * f1 + ee * vsp[lane + 64 * e];
-    l = l * f1 + ee;
-    mcur = mnew;
-  }
-  float* dst = p.out + ((size_t)m * p.Hq + hq) * D;
+  float* dst = p.out + ((size_t)m * p.Hq + kvh * G + gg) * D;
   const float inv = 1.0f / l;
 #pragma unroll
   for (int e = 0; e < PL; ++e) dst[lane + 64 * e] = acc[e] * inv;

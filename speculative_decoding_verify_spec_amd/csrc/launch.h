@@ -60,13 +60,17 @@ struct AttnParams {
   const uint16_t* kc;      // layer K region
   const uint16_t* vc;      // layer V region
   const int32_t* kv_len;   // [B]
+  const float* k_suf;      // [M][Hkv][D] the step's own keys, fp32
+  const float* v_suf;
+  const uint64_t* anc;     // [M][2] ancestor-or-self bits, or null for chain
   float* part_o;           // [nsplit][B][Hkv][nq][D]
   float* part_ml;          // [nsplit][B][Hkv][nq][2]
   int B, T, Hq, Hkv, D, max_ctx;
-  int splits;              // workgroups per (sequence, kv head, query group)
+  int splits;              // context workgroups per (sequence, kv head, query group)
   float scale;
 };
-// number of partial slots per query the context kernel writes
+// number of partial slots per query the attention kernel writes: the context
+// splits plus one for the step's own (suffix) keys
 int attn_nsplit(int splits);
 int attn_query_tiles_per_wave(int nq);
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
@@ -75,13 +79,8 @@ struct CombineParams {
   const float* part_o;
   const float* part_ml;
   int nsplit;
-  const float* q;          // [M][Hq][D]
-  const float* k_suf;      // [M][Hkv][D]
-  const float* v_suf;
-  const uint64_t* anc;     // [M][2] or null for chain
   float* out;              // [M][Hq][D]
   int B, T, Hq, Hkv, D;
-  float scale;
 };
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
 

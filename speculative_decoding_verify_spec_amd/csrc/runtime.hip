@@ -35,7 +35,7 @@ bool valid_config(const spec_config* c) {
 
 // Attention workgroups per (sequence, KV head, query group): about 128 keys
 // each (one 32-key block per wave), capped so the grid stays near 4096
-// workgroups and the combine merges at most 128 partials.
+// workgroups and the combine merges at most 128 partials (with the suffix's).
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
   const int QT = attn_query_tiles_per_wave(nq);
@@ -44,7 +44,7 @@ int attn_splits(const spec_config& c, int B, int T) {
   int s = (c.max_ctx + 127) / 128;
   const int cap = std::max(1, (4096 + units - 1) / units);
   s = std::min(s, cap);
-  return std::max(1, std::min(s, 128));
+  return std::max(1, std::min(s, 127));
 }
 
 struct Layout {
@@ -232,12 +232,11 @@ hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s)
     gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
     if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return e;
 
-    AttnParams ap{q, kreg, vreg, kvw, h->at<float>(L.part_o), h->at<float>(L.part_ml),
-                  B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
+    AttnParams ap{q, kreg, vreg, kvw, ks, vs, tree ? anc : nullptr, h->at<float>(L.part_o),
+                  h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
     e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
     if (e != hipSuccess) return e;
-    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, q, ks, vs,
-                     tree ? anc : nullptr, at, B, T, Hq, Hkv, D, scale};
+    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D};
     e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
     if (e != hipSuccess) return e;
 
