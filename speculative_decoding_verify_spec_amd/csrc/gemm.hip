@@ -385,27 +385,32 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
 // makes the cost of a group grow with M there.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int MT, int EPI, bool NORM, int CPW>
+template <int MT, int EPI, bool NORM, int CPW, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
   constexpr int MG = (MT + 3) / 4;  // sets of 4 activation rows
   constexpr int RG = YT / 4;        // sets of 4 weight rows per group
   constexpr int NV = YT * MT;
+  static_assert(!SPLIT || (!NORM && EPI == EPI_RESID), "K is split only for residual GEMMs");
   __shared__ float red[KSTAT_WAVES][YT][4 * MG];
   __shared__ float tot[64];
   __shared__ float ssq[KSTAT_WAVES][4 * MG];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 3, blk = lane >> 2;
   const uint16_t* __restrict__ W = (const uint16_t*)p.W;
-  const int nch = p.K >> 7;
-  // chunks w, w+4, ... of 128 k; a chunk past K is read at chunk 0 (in
-  // bounds) and multiplied by zero activations
+  // SPLIT: workgroup row blockIdx.y takes K slice blockIdx.y of GEMM_KSPLIT
+  // equal slices and writes its partial sums to p.part
+  const int kext = SPLIT ? p.K / GEMM_KSPLIT : p.K;
+  const int kbase = SPLIT ? (int)blockIdx.y * kext : 0;
+  const int nch = kext >> 7;
+  // chunks w, w+4, ... of 128 k; a chunk past the range is read at its first
+  // chunk (in bounds) and multiplied by zero activations
   int kofs[CPW];
   bool cok[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int c = w + KSTAT_WAVES * i;
     cok[i] = c < nch;
-    kofs[i] = (cok[i] ? c : 0) * 128 + 8 * blk;
+    kofs[i] = kbase + (cok[i] ? c : 0) * 128 + 8 * blk;
   }
   const int ngroups = gemm_groups<EPI>(p);
   const int G = gridDim.x;
@@ -531,8 +536,27 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
       tot[threadIdx.x] = t;
     }
     lds_barrier();
-    epilogue<MT, EPI>(p, rg, tot);
+    if constexpr (SPLIT) {
+      if (threadIdx.x < NV) {
+        const int y = threadIdx.x / MT, m = threadIdx.x % MT;
+        const int n = gemm_row<EPI>(p, rg, y);
+        if (m < p.M && n < p.N) p.part[((size_t)blockIdx.y * 8 + m) * p.ldo + n] = tot[threadIdx.x];
+      }
+    } else {
+      epilogue<MT, EPI>(p, rg, tot);
+    }
   }
+}
+
+// out[m][n] += sum over the K slices of the split partials, slice order fixed
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmParams p) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.M * p.N) return;
+  const int m = e / p.N, n = e % p.N;
+  float t = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < GEMM_KSPLIT; ++sl) t += p.part[((size_t)sl * 8 + m) * p.ldo + n];
+  p.out[(size_t)m * p.ldo + n] += t;
 }
 
 // ---------------------------------------------------------------- streaming
@@ -610,8 +634,34 @@ bool gemm_use_mfma(const GemmParams& p, int rows) {
 
 template <int MT, int EPI, int CPW>
 static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
-  if (p.norm_g) gemm_mfma_kernel<MT, EPI, true, CPW><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else gemm_mfma_kernel<MT, EPI, false, CPW><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  if (p.norm_g) gemm_mfma_kernel<MT, EPI, true, CPW, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI, false, CPW, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+}
+
+// A residual GEMM over a long K (the down projection) at M >= 3: the
+// streaming kernel re-reads the activation rows for every row group, and at
+// 4 rows that traffic equals the weight traffic.  Instead GEMM_KSPLIT slices
+// of K, each held in registers by the matrix-core kernel (7 chunks of 128 per
+// wave for K = 14336), write partial sums, and a small kernel adds them to
+// the residual in a fixed order.
+bool gemm_use_split(const GemmParams& p) {
+  if (!p.part || p.epi != EPI_RESID || p.norm_g || p.wdtype != 1 || p.M < 3) return false;
+  if (p.K <= KSTAT_WAVES * 8 * 128 || p.K % (GEMM_KSPLIT * 128)) return false;
+  return p.K / GEMM_KSPLIT <= KSTAT_WAVES * 8 * 128;
+}
+
+template <int MT>
+static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
+  const int groups = gemm_groups<EPI_RESID>(p);
+  const int slots = 2 * device_cus() / GEMM_KSPLIT;
+  const int rounds = (groups + slots - 1) / slots;
+  const dim3 grid((groups + rounds - 1) / rounds, GEMM_KSPLIT);
+  const int cpw = ((p.K / GEMM_KSPLIT >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
+  if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  gemm_split_reduce_kernel<<<(p.M * p.N + 255) / 256, 256, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 template <int MT, int EPI>
@@ -624,6 +674,9 @@ static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
   const int slots = 2 * device_cus();
   const int rounds = (groups + slots - 1) / slots;
   const int grid = (groups + rounds - 1) / rounds;
+  if constexpr (EPI == EPI_RESID) {
+    if (gemm_use_split(p)) return launch_split<MT>(p, s);
+  }
   if (gemm_use_mfma(p, p.M)) {
     const int cpw = ((p.K >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
     if (cpw <= 2) launch_mfma_cpw<MT, EPI, 2>(p, grid, s);

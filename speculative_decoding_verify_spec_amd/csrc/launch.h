@@ -51,7 +51,11 @@ struct GemmParams {
   uint16_t* kcache;         // this layer's K region [maxB][Hkv][max_ctx][D]
   uint16_t* vcache;         // this layer's V region [maxB][Hkv][D][max_ctx]
   int T, Hq, Hkv, D, max_ctx;
+  // split-K scratch for a residual GEMM over a long K: [GEMM_KSPLIT][8][ldo]
+  // floats, or null (then the GEMM never splits K)
+  float* part;
 };
+constexpr int GEMM_KSPLIT = 4;
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- attention

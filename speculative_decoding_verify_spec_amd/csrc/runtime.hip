@@ -49,7 +49,7 @@ int attn_splits(const spec_config& c, int B, int T) {
 
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, rowstat, rowms, rsum, nacc, rbuf, flags, total;
+  size_t tok, pos, slot, anc, kvw, gpart, rowstat, rowms, rsum, nacc, rbuf, flags, total;
 };
 
 Layout plan(const spec_config& c) {
@@ -84,6 +84,7 @@ Layout plan(const spec_config& c) {
   L.slot = take(Mmax * 4);
   L.anc = take(Mmax * 2 * 8);
   L.kvw = take((size_t)c.max_batch * 4);
+  L.gpart = take((size_t)GEMM_KSPLIT * 8 * c.d_model * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
@@ -253,7 +254,7 @@ hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s)
 
     GemmParams gd{};
     gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
-    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
+    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d; gd.part = h->at<float>(L.gpart);
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -549,7 +550,7 @@ spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int
         bytes += 2.0 * F * d * wb + (double)rows * (d + F) * 4;
       } else {
         g.W = h->W(h->layer_w(l, 5)); g.X = act; g.ldx = F; g.N = d; g.K = F;
-        g.epi = EPI_RESID; g.out = x; g.ldo = d;
+        g.epi = EPI_RESID; g.out = x; g.ldo = d; g.part = h->at<float>(L.gpart);
         bytes += (double)d * F * wb + (double)rows * (F + 2.0 * d) * 4;
       }
       if (gemm_rows(h, k, g, rows, s) != hipSuccess) st = SPEC_ERR_DEVICE;

@@ -85,6 +85,12 @@ MINI8B = ModelShape(n_layers=2, d_model=4096, n_heads=32, n_kv_heads=8, head_dim
                     d_ffn=1024, vocab=8192, rms_eps=1e-5, rope_theta=500000.0,
                     weight_dtype="bf16")
 
+# The 8B layer at full width (FFN 14336) with two layers and a small vocab:
+# exercises the long-K down projection at real size.
+FFN8B = ModelShape(n_layers=2, d_model=4096, n_heads=32, n_kv_heads=8, head_dim=128,
+                   d_ffn=14336, vocab=8192, rms_eps=1e-5, rope_theta=500000.0,
+                   weight_dtype="bf16")
+
 WEIGHT_STD = 0.02
 # Synthetic cached K/V: the scale x.W has for unit-RMS x at d=4096.
 KV_STD = WEIGHT_STD * math.sqrt(4096.0)

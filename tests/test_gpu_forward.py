@@ -145,6 +145,44 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
     assert eng.device_errors() == 0
 
 
+FFN_CASES = [
+    # B, T, ctx lengths: M = 1, 4 (split-K down, matrix-core gate/up), 8 (all matrix cores), 12
+    (1, 1, [700]),
+    (1, 4, [700]),
+    (2, 4, [700, 33]),
+    (3, 4, [5, 700, 129]),
+]
+
+
+@pytest.mark.parametrize("B,T,ctx", FFN_CASES)
+def test_full_width_ffn_step_matches_oracle(B, T, ctx):
+    """The 8B layer at full width (FFN 14336, K = 14336 for the down
+    projection) with two layers: every GEMM path the 8B model takes at these
+    row counts, against the oracle's logits and cache."""
+    sh = synth.FFN8B
+    print(f"[ffn] B={B} T={T} ctx={ctx}", flush=True)
+    max_ctx = 768
+    eng, names, w, cache = build_engine(sh, 3, max_ctx, 8, ctx_len=ctx + [0] * (3 - B))
+    W = oracle_weights(names, w)
+    kc, vc = oracle_cache(cache, sh, 3, max_ctx)
+    tokens = synth.make_tokens(B, T, sh.vocab, seed=91 + T, device=dev())
+    kv = torch.tensor(ctx, dtype=torch.int32, device=dev())
+    zg = _run_step(eng, tokens, kv)
+    assert torch.isfinite(zg).all()
+    zo, kn, vn = OM.forward(sh, W, tokens.cpu().numpy(), np.array(ctx), kc[:, :B], vc[:, :B])
+    err = logits_rel_err(zg.cpu().numpy(), zo)
+    print(f"  logits rel err max {err.max():.2e} median {np.median(err):.2e}", flush=True)
+    assert err.max() < 1e-3
+    kg, vg = oracle_cache(cache, sh, 3, max_ctx)
+    ko, vo = kc.copy(), vc.copy()
+    OM.write_suffix(ko[:, :B], vo[:, :B], kn, vn, np.array(ctx))
+    for b in range(B):
+        s0, s1 = ctx[b], ctx[b] + T
+        _bf16_close(kg[:, b, :, s0:s1], ko[:, b, :, s0:s1])
+        _bf16_close(vg[:, b, :, :, s0:s1], vo[:, b, :, :, s0:s1])
+    assert eng.device_errors() == 0
+
+
 def test_step_flags_bad_inputs_without_faulting():
     sh = synth.MINI8B
     max_ctx = 128
