@@ -185,9 +185,36 @@ DEVI void reduce_group(float* acc, int lane, int w, int nwaves, float (*red)[Max
   if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();
 }
 
-// Epilogue for row group rg from the finished sums tot[y * MT + m].
+// Per-row inputs of the QKV epilogue (cache slot, rotary cos/sin at the
+// row's position), staged in LDS by the prologue so that the epilogue of
+// every row group reads LDS instead of two dependent global loads.
+template <int MT>
+struct QkvStage {
+  int slot[MT];
+  float cs[MT][64];
+  float sn[MT][64];
+};
+
+template <int MT>
+DEVI void stage_qkv(const GemmParams& p, QkvStage<MT>* st) {
+  const int half = p.D / 2;
+  for (int t = threadIdx.x; t < MT * 64; t += blockDim.x) {
+    const int m = t / 64, i = t % 64;
+    if (m >= p.M) continue;
+    const int mg = p.m0 + m;
+    if (i < half) {
+      const int ps = p.pos[mg];
+      st->cs[m][i] = p.rope_cos[(size_t)ps * half + i];
+      st->sn[m][i] = p.rope_sin[(size_t)ps * half + i];
+    }
+    if (i == 0) st->slot[m] = p.slot[mg];
+  }
+}
+
+// Epilogue for row group rg from the finished sums tot[y * MT + m].  `st`:
+// the QKV stage in LDS, or null to read those inputs from global memory.
 template <int MT, int EPI>
-DEVI void epilogue(const GemmParams& p, int rg, const float* tot) {
+DEVI void epilogue(const GemmParams& p, int rg, const float* tot, const QkvStage<MT>* st = nullptr) {
   constexpr int NV = YT * MT;
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     if (threadIdx.x < NV) {
@@ -219,9 +246,17 @@ DEVI void epilogue(const GemmParams& p, int rg, const float* tot) {
       const int hh = r0 / D, i = r0 % D;  // i < D/2
       const int mg = p.m0 + m;            // global row
       const int bseq = mg / p.T;
+      const int sl = st ? st->slot[m] : p.slot[mg];
       if (hh < p.Hq + p.Hkv) {
-        const int ps = p.pos[mg];
-        const float c = p.rope_cos[(size_t)ps * half + i], s = p.rope_sin[(size_t)ps * half + i];
+        float c, s;
+        if (st) {
+          c = st->cs[m][i];
+          s = st->sn[m][i];
+        } else {
+          const int ps = p.pos[mg];
+          c = p.rope_cos[(size_t)ps * half + i];
+          s = p.rope_sin[(size_t)ps * half + i];
+        }
         const float ra = a * c - b * s, rb = b * c + a * s;
         if (hh < p.Hq) {
           float* q = p.q_out + ((size_t)mg * p.Hq + hh) * D;
@@ -232,7 +267,6 @@ DEVI void epilogue(const GemmParams& p, int rg, const float* tot) {
           float* k = p.k_out + ((size_t)mg * p.Hkv + hk) * D;
           k[i] = ra;
           k[i + half] = rb;
-          const int sl = p.slot[mg];
           if (sl >= 0) {
             uint16_t* kc = p.kcache + (((size_t)bseq * p.Hkv + hk) * p.max_ctx + sl) * D;
             kc[i] = (uint16_t)f32_to_bf16_rne(ra);
@@ -244,7 +278,6 @@ DEVI void epilogue(const GemmParams& p, int rg, const float* tot) {
         float* v = p.v_out + ((size_t)mg * p.Hkv + hv) * D;
         v[i] = a;
         v[i + half] = b;
-        const int sl = p.slot[mg];
         if (sl >= 0) {
           uint16_t* vc = p.vcache + ((size_t)bseq * p.Hkv + hv) * D * (size_t)p.max_ctx;
           vc[(size_t)i * p.max_ctx + sl] = (uint16_t)f32_to_bf16_rne(a);
@@ -263,6 +296,7 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
   __shared__ float red[KSTAT_WAVES][NVP];
   __shared__ float tot[NVP];
   __shared__ float ssq[KSTAT_WAVES][MT];
+  __shared__ QkvStage<(EPI == EPI_QKV) ? MT : 1> qst;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -295,6 +329,8 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
   // the first row group's loads go out before the activation prologue
   int rg = blockIdx.x;
   if (rg < ngroups) load_group(rg);
+
+  if constexpr (EPI == EPI_QKV) stage_qkv<MT>(p, &qst);
 
   // ---- this wave's activation slice, kept in registers
   float xr[SPW][MT][8];
@@ -366,7 +402,8 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
       reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot, ssq, 1.0f / (float)p.K, p.eps);
     else
       reduce_group<MT, true>(acc, lane, w, KSTAT_WAVES, red, tot);
-    epilogue<MT, EPI>(p, rg, tot);
+    if constexpr (EPI == EPI_QKV) epilogue<MT, EPI>(p, rg, tot, &qst);
+    else epilogue<MT, EPI>(p, rg, tot);
   }
 }
 
@@ -394,6 +431,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
   __shared__ float red[KSTAT_WAVES][YT][4 * MG];
   __shared__ float tot[64];
   __shared__ float ssq[KSTAT_WAVES][4 * MG];
+  __shared__ QkvStage<(EPI == EPI_QKV) ? MT : 1> qst;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 3, blk = lane >> 2;
   const uint16_t* __restrict__ W = (const uint16_t*)p.W;
@@ -428,6 +466,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) wr[a][i] = __builtin_nontemporal_load((const u32x4*)(W + ro + kofs[i]));
   }
+  if constexpr (EPI == EPI_QKV) stage_qkv<MT>(p, &qst);
   // activations (times the norm gain), split into bf16 hi + lo
   shortx4 xh[CPW][MG][2], xl[CPW][MG][2];
   float ss[MG];
@@ -542,6 +581,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
         const int n = gemm_row<EPI>(p, rg, y);
         if (m < p.M && n < p.N) p.part[((size_t)blockIdx.y * 8 + m) * p.ldo + n] = tot[threadIdx.x];
       }
+    } else if constexpr (EPI == EPI_QKV) {
+      epilogue<MT, EPI>(p, rg, tot, &qst);
     } else {
       epilogue<MT, EPI>(p, rg, tot);
     }

@@ -8,4 +8,4 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the HIP library)")
-    config.addinivalue_line("markers", "slow: long CPU-only test")
+    config.addinivalue_line("markers", "slow: long test (minutes)")

@@ -5,6 +5,7 @@ import torch
 
 import synth
 from oracle import model as OM
+from oracle.numerics import bf16_bits_to_f64
 from speculative_decoding_verify_spec_amd.engine import VerifyEngine
 
 NEAR_TIE = 1e-4      # decisions this close to their boundary may differ
@@ -55,3 +56,19 @@ def compare_decisions(gpu_out, gpu_n, orc, label=""):
                               f"n={orc['n_accepted'][b]} out={list(orc['out_tokens'][b])}, min margin {m}")
         near += 1
     return near
+
+
+def bf16_close(a_bits, b_bits, max_frac=2e-2, noise=1e-4):
+    """bf16 rounding of the GPU's K/V vs the oracle's: the two sides round
+    values that differ by the forward's numerical noise (about 1e-5 of the
+    values' RMS after a layer with d=4096, growing with depth), so a few
+    tenths of a percent of elements straddle a rounding boundary.  Bound: at
+    most one bf16 ulp (2^-7 |x|) plus `noise` times the RMS, on under
+    `max_frac` of the elements.  A wrong row would be off by about the RMS."""
+    diff = np.asarray(a_bits) != np.asarray(b_bits)
+    assert diff.mean() < max_frac, diff.mean()
+    fa, fb = bf16_bits_to_f64(a_bits), bf16_bits_to_f64(b_bits)
+    rms = np.sqrt(np.mean(fb * fb))
+    tol = 2.0 ** -7 * np.maximum(np.abs(fa), np.abs(fb)) + noise * rms
+    worst = np.abs(fa - fb) - tol
+    assert np.all(worst <= 0), f"bf16 values apart beyond one ulp + {noise} rms: {worst.max()}"

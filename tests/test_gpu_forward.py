@@ -14,25 +14,11 @@ from oracle import accept as OA
 from oracle import model as OM
 from oracle import philox
 from oracle.numerics import bf16_bits_to_f64
-from tests.gpu_util import (LOGIT_RTOL, build_engine, compare_decisions, dev, logits_rel_err,
-                            oracle_cache, oracle_weights)
+from tests.gpu_util import LOGIT_RTOL, build_engine, compare_decisions, dev, logits_rel_err
+from tests.gpu_util import bf16_close as _bf16_close
+from tests.gpu_util import oracle_cache, oracle_weights
 
 pytestmark = pytest.mark.gpu
-
-
-def _bf16_close(a_bits, b_bits, max_frac=2e-2):
-    """bf16 rounding of the GPU's K/V vs the oracle's: the two sides round
-    values that differ by the forward's numerical noise (about 1e-5 of the
-    values' RMS after a layer with d=4096), so a few tenths of a percent of
-    elements straddle a rounding boundary.  Bound: at most one bf16 ulp
-    (2^-7 |x|) plus 1e-4 of the RMS, on under 2% of elements."""
-    diff = np.asarray(a_bits) != np.asarray(b_bits)
-    assert diff.mean() < max_frac, diff.mean()
-    fa, fb = bf16_bits_to_f64(a_bits), bf16_bits_to_f64(b_bits)
-    rms = np.sqrt(np.mean(fb * fb))
-    tol = 2.0 ** -7 * np.maximum(np.abs(fa), np.abs(fb)) + 1e-4 * rms
-    worst = np.abs(fa - fb) - tol
-    assert np.all(worst <= 0), f"bf16 values apart beyond one ulp + 1e-4 rms: {worst.max()}"
 
 
 def _run_step(eng, tokens, kv_len, parent=None):
