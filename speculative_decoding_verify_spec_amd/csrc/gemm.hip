@@ -45,8 +45,6 @@ struct MaxPow2 {
   static constexpr int v = (YT * MT <= 8) ? 8 : (YT * MT <= 16) ? 16 : (YT * MT <= 32) ? 32 : 64;
 };
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Weight row handled by slot y of row group rg.
 template <int EPI>
@@ -420,8 +418,6 @@ __global__ __launch_bounds__(64 * KSTAT_WAVES) void gemm_kstat_kernel(GemmParams
 // a row group.  Against the vector-ALU kernel this removes the widening of
 // the weights and three quarters of the multiply-add issue, which is what
 // makes the cost of a group grow with M there.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 template <int MT, int EPI, bool NORM, int CPW, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
   constexpr int MG = (MT + 3) / 4;  // sets of 4 activation rows
@@ -686,7 +682,7 @@ static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
 // wave for K = 14336), write partial sums, and a small kernel adds them to
 // the residual in a fixed order.
 bool gemm_use_split(const GemmParams& p) {
-  if (!p.part || p.epi != EPI_RESID || p.norm_g || p.wdtype != 1 || p.M < 3) return false;
+  if (!p.part || p.part_floats < (size_t)GEMM_KSPLIT * 8 * p.ldo || p.epi != EPI_RESID || p.norm_g || p.wdtype != 1 || p.M < 3) return false;
   if (p.K <= KSTAT_WAVES * 8 * 128 || p.K % (GEMM_KSPLIT * 128)) return false;
   return p.K / GEMM_KSPLIT <= KSTAT_WAVES * 8 * 128;
 }
@@ -752,6 +748,7 @@ static hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  if (gemm_tiled_ok(p)) return launch_gemm_tiled(p, s);
   if (p.M <= 1) return launch_mt<1>(p, s);
   if (p.M <= 2) return launch_mt<2>(p, s);
   if (p.M <= 4) return launch_mt<4>(p, s);

@@ -51,12 +51,20 @@ struct GemmParams {
   uint16_t* kcache;         // this layer's K region [maxB][Hkv][max_ctx][D]
   uint16_t* vcache;         // this layer's V region [maxB][Hkv][D][max_ctx]
   int T, Hq, Hkv, D, max_ctx;
-  // split-K scratch for a residual GEMM over a long K: [GEMM_KSPLIT][8][ldo]
-  // floats, or null (then the GEMM never splits K)
+  // split-K scratch for partial sums, or null (then no launch splits K)
   float* part;
+  size_t part_floats;
+  // tiled kernel: bf16 hi/lo planes of the activations ([2][M][K], xs_elems
+  // elements available) and their rows' sums of squares [M]
+  uint16_t* xs;
+  size_t xs_elems;
+  float* xs_ssq;
 };
-constexpr int GEMM_KSPLIT = 4;
+constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
+bool gemm_tiled_ok(const GemmParams& p);
+hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnParams {

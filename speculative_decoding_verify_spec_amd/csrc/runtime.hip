@@ -47,9 +47,25 @@ int attn_splits(const spec_config& c, int B, int T) {
   return std::max(1, std::min(s, 127));
 }
 
+// Split-K scratch of the GEMMs: the skinny residual GEMM's [4][8][d] and the
+// tiled GEMM's [S <= 8][M <= 64][pairs][2] partial sums (the tiled kernel
+// splits only launches of at most 64 rows, and only while they fit).
+size_t gemm_part_floats(const spec_config& c) {
+  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
+  const size_t pairs = std::max<size_t>((size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim / 2, c.d_model);
+  return std::max((size_t)GEMM_KSPLIT * 8 * c.d_model, 8 * std::min<size_t>(Mmax, 64) * pairs * 2);
+}
+
+// bf16 hi/lo planes of the widest activation rows the tiled GEMM splits
+size_t gemm_xs_elems(const spec_config& c) {
+  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
+  const size_t K = std::max<size_t>(std::max<size_t>(c.d_model, c.d_ffn), (size_t)c.n_heads * c.head_dim);
+  return Mmax >= 5 ? 2 * Mmax * K : 0;
+}
+
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, gpart, rowstat, rowms, rsum, nacc, rbuf, flags, total;
+  size_t tok, pos, slot, anc, kvw, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, flags, total;
 };
 
 Layout plan(const spec_config& c) {
@@ -84,7 +100,9 @@ Layout plan(const spec_config& c) {
   L.slot = take(Mmax * 4);
   L.anc = take(Mmax * 2 * 8);
   L.kvw = take((size_t)c.max_batch * 4);
-  L.gpart = take((size_t)GEMM_KSPLIT * 8 * c.d_model * 4);
+  L.gpart = take(gemm_part_floats(c) * 4);
+  L.gxs = take(gemm_xs_elems(c) * 2);
+  L.gssq = take(Mmax * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
@@ -171,14 +189,29 @@ spec_status dev(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_DEVI
 // GEMM over M rows in launches of at most 8 activation rows.
 hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
   const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
-  size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
+  const size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
+  const size_t out_cols = (p.epi == EPI_SWIGLU) ? p.F : p.N;
+  p.part = h->at<float>(h->lay.gpart);
+  p.part_floats = gemm_part_floats(h->cfg);
+  p.xs = h->at<uint16_t>(h->lay.gxs);
+  p.xs_elems = gemm_xs_elems(h->cfg);
+  p.xs_ssq = h->at<float>(h->lay.gssq);
+  {
+    GemmParams q = p;
+    q.M = M;
+    if (gemm_tiled_ok(q)) {
+      // many rows: one tiled launch reads the weights once per 128 rows
+      const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
+                           (double)M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
+      return timed(h, cls, bytes, s, [&] { return launch_gemm(q, s); });
+    }
+  }
   for (int m0 = 0; m0 < M; m0 += 8) {
     GemmParams q = p;
     q.M = std::min(8, M - m0);
     q.X = p.X + (size_t)m0 * p.ldx;
     q.m0 = m0;
     if (p.out) q.out = p.out + (size_t)m0 * p.ldo;
-    const size_t out_cols = (p.epi == EPI_SWIGLU) ? p.F : (p.epi == EPI_QKV ? p.N : p.N);
     double bytes = (double)q.M * p.K * 4 + (double)q.M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
     if (m0 == 0) bytes += (double)nrows * p.K * wbytes;  // weights count once per GEMM
     hipError_t e = timed(h, cls, bytes, s, [&] { return launch_gemm(q, s); });
@@ -254,7 +287,7 @@ hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s)
 
     GemmParams gd{};
     gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
-    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d; gd.part = h->at<float>(L.gpart);
+    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -550,7 +583,7 @@ spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int
         bytes += 2.0 * F * d * wb + (double)rows * (d + F) * 4;
       } else {
         g.W = h->W(h->layer_w(l, 5)); g.X = act; g.ldx = F; g.N = d; g.K = F;
-        g.epi = EPI_RESID; g.out = x; g.ldo = d; g.part = h->at<float>(L.gpart);
+        g.epi = EPI_RESID; g.out = x; g.ldo = d;
         bytes += (double)d * F * wb + (double)rows * (F + 2.0 * d) * 4;
       }
       if (gemm_rows(h, k, g, rows, s) != hipSuccess) st = SPEC_ERR_DEVICE;
