@@ -29,7 +29,7 @@
 
 namespace sv {
 
-int attn_query_tiles_per_wave(int nq) { return nq > 16 ? 2 : 1; }
+int attn_query_tiles_per_wave(int nq) { return 1; }
 int attn_nsplit(int splits) { return splits + 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
@@ -145,11 +145,25 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   constexpr int DT = D / 16;  // output dim tiles
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y % p.Hkv, qg = blockIdx.y / p.Hkv;
-  const int b = blockIdx.z;
   const int G = p.Hq / p.Hkv;
   const int nq = G * p.T;
+  // Workgroup placement.  Workgroups are dispatched round-robin over the 8
+  // XCDs (each with its own L2), in launch order.  The query groups of one
+  // (sequence, KV head, split) read the same keys and values, so they are
+  // given ids that land on the same XCD one after another: unit u = (split,
+  // kv head, sequence) goes to XCD u % 8, and its query groups take
+  // consecutive places in that XCD's sequence.
+  const int ncol = p.splits + 4 * QT;            // context splits + suffix workgroups
+  const int nqg = (nq + 16 * QT - 1) / (16 * QT);
+  const int units = ncol * p.Hkv * p.B;
+  const int id = blockIdx.x;
+  const int n = id / 8;
+  const int u = (n / nqg) * 8 + id % 8;
+  if (u >= units) return;  // padding of the last XCD round
+  const int qg = n % nqg;
+  const int s = u % ncol;
+  const int kvh = (u / ncol) % p.Hkv;
+  const int b = u / (ncol * p.Hkv);
 
   constexpr int QN = QT * 16;
   constexpr int OS = D + 4;  // padded row stride of the staged outputs
@@ -372,8 +386,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int QT = attn_query_tiles_per_wave(nq);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
-  // + QT*4 suffix workgroups of four queries each
-  dim3 grid(p.splits + 4 * QT, p.Hkv * nqg, p.B);
+  // (context splits + QT*4 suffix workgroups) per (kv head, sequence), each
+  // repeated per query group, laid out XCD by XCD (see the kernel)
+  const int units = (p.splits + 4 * QT) * p.Hkv * p.B;
+  const dim3 grid(((units + 7) / 8) * 8 * nqg);
   if (p.D == 128) {
     if (QT == 1) attn_ctx_kernel<128, 1><<<grid, 256, 0, s>>>(p);
     else attn_ctx_kernel<128, 2><<<grid, 256, 0, s>>>(p);
