@@ -1,8 +1,11 @@
-// Tiled GEMM for many activation rows (M > 8): Y[m][n] = sum_k X[m][k] W[n][k]
+// Tiled GEMM for many activation rows (5 or more for the QKV, gate/up and LM
+// head projections, more than 8 for the residual ones):
+// Y[m][n] = sum_k X[m][k] W[n][k]
 // on the 16x16x16 bf16 matrix instruction, with the fp32 activations split
 // into bf16 hi + lo (two products per tile) so they keep ~2^-16 relative
 // accuracy, fp32 accumulation.  This is the regime where the skinny kernels
-// would stream the weights once per 8 rows: the 32-row verify window of 8
+// run out of vector or matrix throughput, or stream the weights once per 8
+// rows: the 32-row verify window of 8
 // sequences, 117-row token trees, 128-row long-context batches.
 //
 // A first kernel splits the activation rows into bf16 hi and lo planes (times
