@@ -10,8 +10,13 @@ The test u < p/q is evaluated as u * q < p (the Kimi-K3 tuning page, "What
 SGLang actually runs": a uniform times the draft probability under the target
 probability), which avoids the division.
 
-Sampling settings (section 7.3): p_i = softmax(z_i / T).  q arrives already
-adjusted by the draft side.  Greedy (section 7.4, T = 0): accept x_i iff it
+Sampling settings (section 7.3): every setting is sampling from an adjusted
+distribution, and speculative sampling on the adjusted p and q yields the
+adjusted p.  p_i = softmax(z_i / T), then top-k keeps the k most likely tokens
+(the rest set to zero, as logits of -inf) and renormalises, then top-p keeps
+the nucleus (the shortest run of most likely tokens whose renormalised mass
+reaches top_p) and renormalises (see `adjust`).  q arrives already adjusted by
+the draft side, the same way.  Greedy (section 7.4, T = 0): accept x_i iff it
 equals argmax z_i; the extra token is argmax z_{n+1}, the only positive term of
 the residual of two one-hot distributions.
 
@@ -30,7 +35,13 @@ Readings where the pages say nothing:
   * greedy ties resolve to the lowest token id;
   * a residual whose mass is zero in floating point falls back to the
     distribution it was taken from (p for the chain);
-  * uniforms come from Philox4x64-10 (see philox.py for slot assignment).
+  * uniforms come from Philox4x64-10 (see philox.py for slot assignment);
+  * "most likely" orders tokens by logit, largest first, equal logits by
+    lower id; top-k is applied before top-p (the order an engine's verify
+    calls its two renormalisations in, Kimi-K3 tuning page); the nucleus
+    is the shortest such prefix with cumulative mass >= top_p; top_k = 0
+    and top_p = 1 switch them off; greedy ignores both (the argmax is
+    always kept).
 
 Each function also returns a trace of the margins of the decisions it took, so
 a test can tell a genuine mismatch from a near-tie: accept tests record
@@ -47,6 +58,40 @@ def softmax(z: np.ndarray, temperature: float) -> np.ndarray:
     s = s - s.max()
     e = np.exp(s)
     return e / e.sum()
+
+
+def likelihood_order(z: np.ndarray) -> np.ndarray:
+    """Token ids from most to least likely: descending logit, equal logits by
+    ascending id."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.lexsort((np.arange(z.size), -z))
+
+
+def adjust(z: np.ndarray, temperature: float, top_k: int = 0, top_p: float = 1.0):
+    """Adjusted target distribution (section 7.3): softmax(z / T) restricted to
+    the top-k tokens, renormalised, then to the top-p nucleus, renormalised.
+    Returns (p, margin): margin is the distance of the nucleus' cumulative
+    mass to top_p at the cut (how far the boundary decision is from flipping),
+    inf when top-p is off."""
+    p = softmax(z, temperature)
+    V = p.size
+    margin = np.inf
+    if not (0 < top_k < V) and not (top_p < 1.0):
+        return p, margin
+    order = likelihood_order(z)
+    kept = order[:top_k] if 0 < top_k < V else order
+    if top_p < 1.0:
+        pk = p[kept] / p[kept].sum()
+        c = np.cumsum(pk)
+        hit = np.nonzero(c >= top_p)[0]
+        n = int(hit[0]) if hit.size else kept.size - 1
+        margin = float(c[n] - top_p) if hit.size else np.inf
+        if n > 0:
+            margin = min(margin, float(top_p - c[n - 1]))
+        kept = kept[:n + 1]
+    r = np.zeros(V)
+    r[kept] = p[kept]
+    return r / r.sum(), margin
 
 
 def argmax_lowest(z: np.ndarray) -> int:
@@ -75,10 +120,11 @@ def inverse_cdf(r: np.ndarray, u: float):
     return x, float(margin)
 
 
-def accept_chain_one(z, q, tokens, temperature, u, _variant="residual"):
+def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0, top_p=1.0):
     """One sequence.  z [gamma+1, V] target logits for the window rows;
     q [gamma, V] draft probabilities (row j: distribution draft j+1 came from);
-    tokens [gamma+1] = [pending, x_1 .. x_gamma]; u(slot) -> uniform.
+    tokens [gamma+1] = [pending, x_1 .. x_gamma]; u(slot) -> uniform;
+    top_k / top_p adjust the target (see `adjust`).
     Returns (n_accepted, emitted tokens [n+1], margins).
 
     _variant plants one of the two wrong implementations of section 7.5 for
@@ -100,7 +146,8 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual"):
 
     n = 0
     for i in range(gamma):
-        p = softmax(z[i], temperature)
+        p, am = adjust(z[i], temperature, top_k, top_p)
+        margins.append(am)
         x = int(tokens[i + 1])
         ui = u(i)
         margins.append(abs(ui - min(1.0, p[x] / q[i][x])) if q[i][x] > 0 else np.inf)
@@ -109,7 +156,8 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual"):
             n += 1
         else:
             break
-    p = softmax(z[n], temperature)
+    p, am = adjust(z[n], temperature, top_k, top_p)
+    margins.append(am)
     if n < gamma and _variant != "resample_from_p":
         r = np.maximum(0.0, p - np.asarray(q[n], dtype=np.float64))
         if not (r.sum() > 0.0):
@@ -121,7 +169,8 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual"):
     return n, [int(t) for t in tokens[1:n + 1]] + [extra], margins
 
 
-def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _variant="residual"):
+def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _variant="residual",
+                    top_k=0, top_p=1.0):
     """One sequence with a token tree.  z [T, V] logits per node; q [T, V] the
     draft distribution each node's children were drawn from; tokens [T] node
     tokens (node 0 = pending token); parent [T] (root -1).  u(slot) -> uniform.
@@ -145,7 +194,8 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
             path.append(v)
 
     while True:
-        r = softmax(z[v], temperature)
+        r, am = adjust(z[v], temperature, top_k, top_p)
+        margins.append(am)
         if not children[v]:
             extra, m = inverse_cdf(r, u(T - 1))
             margins.append(m)
@@ -178,9 +228,9 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
 
 
 def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replacement=False,
-           _variant="residual"):
+           _variant="residual", top_k=0, top_p=1.0):
     """Batch driver.  logits [B, T, V]; q [B, T-1, V] (chain) or [B, T, V] (tree);
-    tokens [B, T]; uniforms(b, slot) -> float.
+    tokens [B, T]; uniforms(b, slot) -> float; top_k / top_p as in `adjust`.
     Returns dict with n_accepted [B], out_tokens [B, T] (-1 padded), paths,
     margins (list per sequence)."""
     logits = np.asarray(logits)
@@ -192,11 +242,12 @@ def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replaceme
         ub = (lambda s, b=b: uniforms(b, s))
         if tree_parent is None:
             n, toks, m = accept_chain_one(logits[b], None if q is None else q[b], tokens[b],
-                                          temperature, ub, _variant)
+                                          temperature, ub, _variant, top_k, top_p)
             path = list(range(n + 1))
         else:
             path, toks, m = accept_tree_one(logits[b], None if q is None else q[b], tokens[b],
-                                            tree_parent[b], temperature, ub, replacement, _variant)
+                                            tree_parent[b], temperature, ub, replacement, _variant,
+                                            top_k, top_p)
             n = len(path) - 1
         n_acc[b] = n
         out[b, : len(toks)] = toks

@@ -40,13 +40,19 @@ class _Tables:
                 self.q[pre] = _random_dist(rng, V, zeros=1 if (len(pre) % 2) else 0)
 
 
-def _enumerate_chain(tab, gamma, variant="residual"):
+def _enumerate_chain(tab, gamma, variant="residual", ztab=None, temperature=1.0, adj=None):
     """Exact distribution of the oracle's emitted tokens, extended to gamma+1
     tokens with the target's own conditionals.  Draft tuples are enumerated
     with weight prod q; every uniform's range is split at the decision
     boundaries implied by the pages' rule (accept iff u < p/q; inverse CDF of
-    the residual) and the oracle is called at each cell's midpoint."""
+    the residual) and the oracle is called at each cell's midpoint.
+
+    With `ztab` the oracle receives log ztab.p as logits, with `temperature`
+    and the sampling adjustments `adj`, while the cells come from tab.p: the
+    adjusted target the oracle should be sampling."""
     V = tab.V
+    ztab = tab if ztab is None else ztab
+    adj = adj or {}
     joint = {}
     for xs in itertools.product(range(V), repeat=gamma):
         w_draft = 1.0
@@ -54,7 +60,7 @@ def _enumerate_chain(tab, gamma, variant="residual"):
             w_draft *= tab.q[xs[:i]][xs[i]]
         if w_draft == 0.0:
             continue
-        z = np.stack([np.log(np.maximum(tab.p[xs[:i]], 1e-300)) for i in range(gamma + 1)])
+        z = np.stack([np.log(np.maximum(ztab.p[xs[:i]], 1e-300)) for i in range(gamma + 1)])
         qrows = np.stack([tab.q[xs[:i]] for i in range(gamma)])
         tokens = [0] + list(xs)
         # walk the accept cells: n accepted, then the final draw
@@ -93,7 +99,8 @@ def _enumerate_chain(tab, gamma, variant="residual"):
                     continue
                 lo = c[y - 1] if y else 0.0
                 us[gamma] = (lo + r[y] / 2.0) / R
-                ny, out, _ = acc.accept_chain_one(z, qrows, tokens, 1.0, lambda s: us[s], _variant=variant)
+                ny, out, _ = acc.accept_chain_one(z, qrows, tokens, temperature, lambda s: us[s],
+                                                  _variant=variant, **adj)
                 cell_w = w_draft * w * r[y] / R
                 key = tuple(out)
                 joint[key] = joint.get(key, 0.0) + cell_w
@@ -278,11 +285,14 @@ def test_tree_all_ones_is_chain():
         assert out_t == out_c
 
 
-def _tree_round_sample(rng, tab, branching, replacement, variant="residual"):
+def _tree_round_sample(rng, tab, branching, replacement, variant="residual", ztab=None, adj=None):
     """Draw one token tree from the draft tables (children of a node drawn from
     q(.|path) with or without replacement), run the oracle's tree accept with
-    fresh uniforms, return the first two emitted tokens."""
+    fresh uniforms, return the first two emitted tokens.  With `ztab` / `adj`
+    as in _enumerate_chain (tab.p is then the adjusted target)."""
     V = tab.V
+    ztab = tab if ztab is None else ztab
+    adj = adj or {}
     parents, toks, ctx = [-1], [0], [()]
     level = [0]
     for k in branching:
@@ -302,11 +312,11 @@ def _tree_round_sample(rng, tab, branching, replacement, variant="residual"):
                 nxt.append(len(parents) - 1)
         level = nxt
     T = len(parents)
-    z = np.stack([np.log(np.maximum(tab.p[c], 1e-300)) if c in tab.p else np.zeros(V) for c in ctx])
+    z = np.stack([np.log(np.maximum(ztab.p[c], 1e-300)) if c in ztab.p else np.zeros(V) for c in ctx])
     q = np.stack([tab.q[c] if c in tab.q else np.full(V, 1.0 / V) for c in ctx])
     us = rng.random(T)
     path, out, _ = acc.accept_tree_one(z, q, toks, parents, 1.0, lambda s: us[s],
-                                       replacement=replacement, _variant=variant)
+                                       replacement=replacement, _variant=variant, **adj)
     # continue with the target's own conditionals if only one token came out
     if len(out) < 2:
         out = out + [int(rng.choice(V, p=tab.p[tuple(out)]))]
@@ -481,3 +491,114 @@ def test_bf16_round_nearest_even():
     assert round_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
     bits = f64_to_bf16_bits(np.array([1.5, -2.0, 0.0]))
     assert np.array_equal(bf16_bits_to_f64(bits), [1.5, -2.0, 0.0])
+
+
+# ----------------------------------------------------------------------------
+# sampling adjustments: temperature, top-k, top-p (CS349E Lecture 6, section 7.3)
+# ----------------------------------------------------------------------------
+
+def _brute_adjust(p, temperature=1.0, top_k=0, top_p=1.0):
+    """Independent statement of the adjusted distribution for tiny V: tempered
+    p ~ p^(1/T); top-k keeps the tokens with fewer than k tokens ranked above
+    them (higher probability, or equal probability and lower id); the nucleus
+    is, among all subsets of the kept tokens whose renormalised mass reaches
+    top_p, one of minimum size, and of those the heaviest."""
+    p = np.asarray(p, dtype=np.float64) ** (1.0 / temperature)
+    p = p / p.sum()
+    V = p.size
+    keep = np.ones(V, bool)
+    if 0 < top_k < V:
+        for x in range(V):
+            above = sum(1 for y in range(V) if p[y] > p[x] or (p[y] == p[x] and y < x))
+            keep[x] = above < top_k
+    if top_p < 1.0:
+        cand = [x for x in range(V) if keep[x]]
+        mass = p[cand].sum()
+        best = None
+        for size in range(1, len(cand) + 1):
+            for sub in itertools.combinations(cand, size):
+                m = p[list(sub)].sum() / mass
+                if m >= top_p and (best is None or m > best[0]):
+                    best = (m, sub)
+            if best is not None:
+                break
+        keep[:] = False
+        keep[list(best[1])] = True
+    r = np.where(keep, p, 0.0)
+    return r / r.sum()
+
+
+ADJ_CASES = [(1.0, 3, 1.0), (1.0, 0, 0.7), (0.7, 5, 0.85), (1.3, 2, 0.95), (1.0, 1, 1.0), (1.0, 0, 0.05)]
+
+
+@pytest.mark.parametrize("temperature,top_k,top_p", ADJ_CASES)
+def test_adjust_matches_subset_brute_force(temperature, top_k, top_p):
+    """The oracle's top-k / nucleus agree with the subset definition on random
+    distributions (V = 8)."""
+    rng = np.random.default_rng(int(100 * temperature) + 7 * top_k + int(100 * top_p))
+    for _ in range(200):
+        p = _random_dist(rng, 8)
+        got, _ = acc.adjust(np.log(p), temperature, top_k, top_p)
+        want = _brute_adjust(p, temperature, top_k, top_p)
+        assert np.abs(got - want).max() < 1e-14, (p, got, want)
+
+
+def test_adjust_special_cases():
+    z = np.array([0.3, 2.0, -1.0, 2.0, 0.5])
+    # top-k = 1 and a tiny nucleus are the greedy one-hot; equal logits go to the lower id
+    for p, _ in (acc.adjust(z, 1.0, top_k=1), acc.adjust(z, 1.0, top_p=1e-6)):
+        assert np.array_equal(p, np.eye(5)[1])
+    # switched off: plain softmax
+    p, m = acc.adjust(z, 0.8, top_k=0, top_p=1.0)
+    e = np.exp(z / 0.8 - (z / 0.8).max())
+    assert np.abs(p - e / e.sum()).max() < 1e-15 and m == np.inf
+    p, _ = acc.adjust(z, 1.0, top_k=5)
+    assert np.abs(p - acc.softmax(z, 1.0)).max() < 1e-15
+    # top-k = 2 keeps the two tied maxima; top-k = 3 adds logit 0.5 (id 4)
+    assert np.array_equal(acc.adjust(z, 1.0, top_k=2)[0] > 0, [False, True, False, True, False])
+    assert np.array_equal(acc.adjust(z, 1.0, top_k=3)[0] > 0, [False, True, False, True, True])
+    # a nucleus that must split the tie keeps the lower id
+    y = np.log(np.array([0.1, 0.3, 0.3, 0.3]))
+    assert np.array_equal(acc.adjust(y, 1.0, top_p=0.5)[0] > 0, [False, True, True, False])
+    # the margin is the distance of the cumulative mass to top_p at the cut
+    p4 = np.array([0.4, 0.3, 0.2, 0.1])
+    _, m = acc.adjust(np.log(p4), 1.0, top_p=0.65)
+    assert abs(m - 0.05) < 1e-12
+
+
+@pytest.mark.parametrize("temperature,top_k,top_p,adjust_q", [
+    (1.0, 3, 1.0, True), (1.0, 0, 0.75, True), (0.7, 5, 0.8, True), (1.0, 4, 0.9, False)])
+def test_chain_enumeration_adjusted_output(temperature, top_k, top_p, adjust_q):
+    """With the adjustments the round's output is exactly the adjusted target,
+    whether the draft was adjusted the same way or not (section 7.3: the rule
+    holds for any q, an unadjusted draft is only accepted less often)."""
+    gamma = 2
+    raw = _Tables(V=8, depth=gamma, seed=40 + top_k)
+    tab = _Tables(V=8, depth=0, seed=0)
+    tab.p = {k: _brute_adjust(v, temperature, top_k, top_p) for k, v in raw.p.items()}
+    tab.q = {k: (_brute_adjust(v, temperature, top_k, top_p) if adjust_q else v) for k, v in raw.q.items()}
+    got = _enumerate_chain(tab, gamma, ztab=raw, temperature=temperature,
+                           adj=dict(top_k=top_k, top_p=top_p))
+    want = _target_joint(tab, gamma)
+    assert abs(got.sum() - 1.0) < 1e-12
+    assert np.abs(got - want).max() < 1e-12
+    # and it is not the unadjusted target
+    assert 0.5 * np.abs(got - _target_joint(raw, gamma)).sum() > 1e-2
+
+
+def test_tree_sampled_adjusted_output():
+    """Sampled tree walk with top-k and top-p on both sides: the first two
+    emitted tokens follow the adjusted target (chi-square)."""
+    V, branching, N = 5, [2, 2], 40000
+    raw = _Tables(V=V, depth=3, seed=24)
+    adj = dict(top_k=4, top_p=0.8)
+    tab = _Tables(V=V, depth=0, seed=0)
+    tab.p = {k: _brute_adjust(v, 1.0, **adj) for k, v in raw.p.items()}
+    tab.q = {k: _brute_adjust(v, 1.0, **adj) for k, v in raw.q.items()}
+    rng = np.random.default_rng(25)
+    counts = np.zeros((V, V))
+    for _ in range(N):
+        counts[_tree_round_sample(rng, tab, branching, False, ztab=raw, adj=adj)] += 1
+    want = np.array([[tab.p[()][a] * tab.p[(a,)][b] for b in range(V)] for a in range(V)])
+    chi2, dof = _chi2(counts, want * N)
+    assert chi2 < 50 + 2.5 * (dof - 15), (chi2, dof)
