@@ -88,12 +88,23 @@ typedef struct spec_config {
  *   (slot, sequence, round, 0); u = (word0 >> 40) * 2^-24.
  *   tree_replacement: 0 if each node's children were drawn from its draft
  *   distribution without replacement (the rejected token is removed from q'
- *   and q' renormalised), 1 if drawn with replacement (q' unchanged). */
+ *   and q' renormalised), 1 if drawn with replacement (q' unchanged).
+ *   top_k, top_p: the target is sampled from the adjusted distribution of
+ *   CS349E Lecture 6, section 7.3: softmax(z / temperature) restricted to
+ *   the top_k most likely tokens and renormalised, then restricted to the
+ *   nucleus (the shortest run of most likely tokens whose renormalised mass
+ *   reaches top_p) and renormalised.  Most likely = larger logit first,
+ *   equal logits by lower token id.  top_k = 0 (or >= vocab) and top_p = 1
+ *   switch them off; greedy ignores both.  The output then follows the
+ *   adjusted target for any q; q should be the draft's distribution after
+ *   the same adjustment, or acceptance drops (same section). */
 typedef struct spec_sampling {
   float temperature;
   uint32_t tree_replacement;
   uint64_t seed;
   uint64_t round;
+  int32_t top_k;
+  float top_p;
 } spec_sampling;
 
 typedef struct spec_handle spec_handle;
@@ -169,8 +180,9 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
  *     kv_len + n + 1 (may alias d_kv_len).  With a tree, the accepted path's
  *     K/V are also copied to slots kv_len + 0 .. n.  Pass d_kv_len_out = NULL
  *     to skip the commit.
- *   Errors: INVALID_ARG (null where required, temperature < 0 or not finite),
- *   CAPACITY, DEVICE.  Flags: TOKEN_RANGE (a draft token outside [0, V)),
+ *   Errors: INVALID_ARG (null where required, temperature < 0 or not finite,
+ *   top_k < 0, top_p outside [0, 1]), CAPACITY, DEVICE.
+ *   Flags: TOKEN_RANGE (a draft token outside [0, V)),
  *   TREE. */
 spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_logits,
                         const float* d_q, const int32_t* d_tokens, const int32_t* d_tree_parent,

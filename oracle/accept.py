@@ -46,7 +46,10 @@ Readings where the pages say nothing:
 Each function also returns a trace of the margins of the decisions it took, so
 a test can tell a genuine mismatch from a near-tie: accept tests record
 |u - min(1, p/q)|, draws record the distance of u * R to the nearest CDF
-boundary divided by R, argmax decisions the top-2 gap over max |z|.
+boundary divided by R, argmax decisions the top-2 gap over max |z|.  The
+nucleus cuts' margins (distance of the cumulative mass to top_p) are kept
+apart, in `adjust_margins`: they are masses, compared against a different
+band.
 """
 from __future__ import annotations
 
@@ -120,11 +123,13 @@ def inverse_cdf(r: np.ndarray, u: float):
     return x, float(margin)
 
 
-def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0, top_p=1.0):
+def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0, top_p=1.0,
+                     adjust_margins=None):
     """One sequence.  z [gamma+1, V] target logits for the window rows;
     q [gamma, V] draft probabilities (row j: distribution draft j+1 came from);
     tokens [gamma+1] = [pending, x_1 .. x_gamma]; u(slot) -> uniform;
-    top_k / top_p adjust the target (see `adjust`).
+    top_k / top_p adjust the target (see `adjust`); the nucleus cuts'
+    margins are appended to `adjust_margins` when given.
     Returns (n_accepted, emitted tokens [n+1], margins).
 
     _variant plants one of the two wrong implementations of section 7.5 for
@@ -132,6 +137,7 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
     after a rejection; "deterministic" rejects whenever q > p."""
     gamma = len(tokens) - 1
     margins = []
+    adjust_margins = [] if adjust_margins is None else adjust_margins
     if temperature == 0.0:
         n = 0
         while n < gamma:
@@ -147,7 +153,7 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
     n = 0
     for i in range(gamma):
         p, am = adjust(z[i], temperature, top_k, top_p)
-        margins.append(am)
+        adjust_margins.append(am)
         x = int(tokens[i + 1])
         ui = u(i)
         margins.append(abs(ui - min(1.0, p[x] / q[i][x])) if q[i][x] > 0 else np.inf)
@@ -157,7 +163,7 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
         else:
             break
     p, am = adjust(z[n], temperature, top_k, top_p)
-    margins.append(am)
+    adjust_margins.append(am)
     if n < gamma and _variant != "resample_from_p":
         r = np.maximum(0.0, p - np.asarray(q[n], dtype=np.float64))
         if not (r.sum() > 0.0):
@@ -170,7 +176,7 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
 
 
 def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _variant="residual",
-                    top_k=0, top_p=1.0):
+                    top_k=0, top_p=1.0, adjust_margins=None):
     """One sequence with a token tree.  z [T, V] logits per node; q [T, V] the
     draft distribution each node's children were drawn from; tokens [T] node
     tokens (node 0 = pending token); parent [T] (root -1).  u(slot) -> uniform.
@@ -180,6 +186,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
     for c in range(1, T):
         children[int(parent[c])].append(c)
     margins = []
+    adjust_margins = [] if adjust_margins is None else adjust_margins
     v = 0
     path = [0]
 
@@ -195,7 +202,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
 
     while True:
         r, am = adjust(z[v], temperature, top_k, top_p)
-        margins.append(am)
+        adjust_margins.append(am)
         if not children[v]:
             extra, m = inverse_cdf(r, u(T - 1))
             margins.append(m)
@@ -232,25 +239,28 @@ def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replaceme
     """Batch driver.  logits [B, T, V]; q [B, T-1, V] (chain) or [B, T, V] (tree);
     tokens [B, T]; uniforms(b, slot) -> float; top_k / top_p as in `adjust`.
     Returns dict with n_accepted [B], out_tokens [B, T] (-1 padded), paths,
-    margins (list per sequence)."""
+    margins and adjust_margins (lists per sequence)."""
     logits = np.asarray(logits)
     B, T = np.asarray(tokens).shape
     n_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, T), -1, dtype=np.int64)
-    paths, margins = [], []
+    paths, margins, adj_margins = [], [], []
     for b in range(B):
         ub = (lambda s, b=b: uniforms(b, s))
+        am = []
         if tree_parent is None:
             n, toks, m = accept_chain_one(logits[b], None if q is None else q[b], tokens[b],
-                                          temperature, ub, _variant, top_k, top_p)
+                                          temperature, ub, _variant, top_k, top_p, am)
             path = list(range(n + 1))
         else:
             path, toks, m = accept_tree_one(logits[b], None if q is None else q[b], tokens[b],
                                             tree_parent[b], temperature, ub, replacement, _variant,
-                                            top_k, top_p)
+                                            top_k, top_p, am)
             n = len(path) - 1
         n_acc[b] = n
         out[b, : len(toks)] = toks
         paths.append(path)
         margins.append(m)
-    return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins}
+        adj_margins.append(am)
+    return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins,
+            "adjust_margins": adj_margins}

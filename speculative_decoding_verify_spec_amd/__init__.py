@@ -48,7 +48,7 @@ class spec_config(C.Structure):
 
 class spec_sampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("tree_replacement", C.c_uint32),
-                ("seed", C.c_uint64), ("round", C.c_uint64)]
+                ("seed", C.c_uint64), ("round", C.c_uint64), ("top_k", C.c_int32), ("top_p", C.c_float)]
 
 
 class spec_kernel_stat(C.Structure):

@@ -124,6 +124,276 @@ DEVI int clamp_token(const AcceptParams& p, int x, bool& bad) {
   return x < 0 ? 0 : (x >= p.V ? p.V - 1 : x);
 }
 
+// ---------------------------------------------------------------- top-k / top-p
+// CS349E Lecture 6, section 7.3: the target is the adjusted distribution
+// softmax(z / T), cut to the top-k tokens, renormalised, cut to the top-p
+// nucleus, renormalised.  A row's kept set is a prefix of its tokens in
+// likelihood order (larger logit first, equal logits by lower id), found by
+// a radix selection over keys that order the logits, one 8-bit digit per
+// pass from the top: every chunk workgroup counts the candidates of each
+// digit value (tokens, and their mass exp(z/T - M) in fp64), the next pass
+// merges the chunk counts and fixes the digit.  Top-k selects by count; the
+// nucleus then selects by mass among the top-k tokens.  After the last digit
+// the threshold key tau is exact; of the tokens whose key equals tau the
+// first j by id are kept, j being what the count or the mass still needs.
+
+// a larger float gets a larger key
+DEVI uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+DEVI float key_float(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+DEVI bool sel_keep(uint32_t tau, int cut, uint32_t key, int y) { return key > tau || (key == tau && y <= cut); }
+
+// Keep rule of a row for the sampling kernels: everything when no
+// adjustment applies.
+struct RowRule {
+  uint32_t tau;
+  int cut;
+};
+DEVI RowRule row_rule(const AcceptParams& p, int row) {
+  if (!p.fres) return RowRule{0u, 0x7fffffff};
+  return RowRule{p.fres[row].tau, p.fres[row].cut};
+}
+// adjusted target probability of token y of a row with statistics (M, S)
+DEVI float pval(const AcceptParams& p, const RowRule& r, float zy, int y, float M, float S) {
+  const float v = expf(zy / p.temperature - M) / S;
+  return sel_keep(r.tau, r.cut, order_key(zy), y) ? v : 0.f;
+}
+
+struct SelArgs {
+  int row0;   // first row of this batch
+  int phase;  // 0 top-k (by count), 1 top-p (by mass)
+  int digit;  // 0..3: digit this pass counts; 4: finish
+};
+
+// Merge the previous digit's chunk counts of batch row rb and fix that digit.
+// blockDim.x == 256: thread t sums bin t over the chunks.  Leaves the state
+// after the digit in *st, the digit in *bin, and the merged bins in s_cnt /
+// s_mass; ends synchronised.
+DEVI void sel_merge(const AcceptParams& p, const SelArgs& a, int rb, SelState* st, int* bin, uint32_t* s_cnt,
+                    double* s_mass) {
+  const int t = threadIdx.x;
+  const int pd = (a.digit - 1) & 1;
+  const size_t hb = ((size_t)pd * SEL_ROWS + rb) * p.nch * 256;
+  uint32_t cn = 0;
+  double ms = 0.0;
+  for (int c = 0; c < p.nch; ++c) {
+    cn += p.fcnt[hb + (size_t)c * 256 + t];
+    ms += p.fmass[hb + (size_t)c * 256 + t];
+  }
+  s_cnt[t] = cn;
+  s_mass[t] = ms;
+  __syncthreads();
+  if (t == 0) {
+    SelState s = p.fstate[pd * SEL_ROWS + rb];
+    const int shift = 24 - 8 * (a.digit - 1);
+    int b;
+    if (a.phase == 0) {
+      // the bin holding the need-th token from the top
+      uint32_t cum = 0;
+      double above = 0.0;
+      for (b = 255; b > 0; --b) {
+        if (cum + s_cnt[b] >= s.need) break;
+        cum += s_cnt[b];
+        above += s_mass[b];
+      }
+      s.need -= cum;
+      s.above += above;
+    } else {
+      if (s.rem < 0.0) {
+        double tot = 0.0;
+        for (int i = 0; i < 256; ++i) tot += s_mass[i];
+        s.rem = (double)p.top_p * tot;
+      }
+      // the bin where the mass from the top reaches rem; if rounding leaves
+      // it short, the lowest occupied bin, taken whole
+      double cum = 0.0;
+      int last = 0;
+      b = -1;
+      for (int i = 255; i >= 0; --i) {
+        if (!s_cnt[i]) continue;
+        last = i;
+        if (cum + s_mass[i] >= s.rem) { b = i; break; }
+        cum += s_mass[i];
+      }
+      if (b < 0) {
+        b = last;
+        cum -= s_mass[last];
+        s.rem = INFINITY;
+      } else {
+        s.rem -= cum;
+      }
+      s.above += cum;
+    }
+    s.prefix |= (uint32_t)b << shift;
+    *st = s;
+    *bin = b;
+  }
+  __syncthreads();
+}
+
+// One digit of the selection over one chunk of one row.  Grid (nch, rows).
+__global__ __launch_bounds__(256) void accept_select_kernel(AcceptParams p, SelArgs a) {
+  __shared__ uint32_t s_cnt[256];
+  __shared__ double s_mass[256];
+  __shared__ SelState st;
+  __shared__ int s_bin;
+  const int c = blockIdx.x, rb = blockIdx.y, row = a.row0 + rb, t = threadIdx.x;
+  if (a.digit == 0) {
+    if (t == 0) st = SelState{0u, (uint32_t)p.top_k, -1.0, 0.0};
+  } else {
+    sel_merge(p, a, rb, &st, &s_bin, s_cnt, s_mass);
+  }
+  s_cnt[t] = 0;
+  s_mass[t] = 0.0;
+  __syncthreads();
+  const SelState s = st;
+  // phase 1 selects among the top-k set
+  const uint32_t tk = a.phase == 1 ? p.fres[row].tau_k : 0u;
+  const int ck = a.phase == 1 ? p.fres[row].cut_k : 0x7fffffff;
+  float M, S;
+  row_ms(p, row, M, S);
+  const float Tt = p.temperature;
+  const int shift = 24 - 8 * a.digit;
+  const float* z = p.logits + (size_t)row * p.V;
+  const int y1 = min(p.V, (c + 1) * CH);
+  for (int y = c * CH + t; y < y1; y += 256) {
+    const float zy = z[y];
+    const uint32_t key = order_key(zy);
+    if (a.digit > 0 && (key >> (shift + 8)) != (s.prefix >> (shift + 8))) continue;
+    if (!sel_keep(tk, ck, key, y)) continue;
+    const int bn = (key >> shift) & 255;
+    atomicAdd(&s_cnt[bn], 1u);
+    atomicAdd(&s_mass[bn], (double)expf(zy / Tt - M));
+  }
+  __syncthreads();
+  const size_t hb = (((size_t)(a.digit & 1) * SEL_ROWS + rb) * p.nch + c) * 256;
+  p.fcnt[hb + t] = s_cnt[t];
+  p.fmass[hb + t] = s_mass[t];
+  if (c == 0 && t == 0) p.fstate[(a.digit & 1) * SEL_ROWS + rb] = s;
+}
+
+// Fix the last digit, then find the j-th token (by id) whose key equals the
+// threshold and write the row's rule.  Grid (rows), 256 threads.
+__global__ __launch_bounds__(256) void accept_select_finish_kernel(AcceptParams p, SelArgs a) {
+  constexpr int PER = CH / 256;
+  __shared__ uint32_t s_cnt[256];
+  __shared__ double s_mass[256];
+  __shared__ SelState st;
+  __shared__ int s_bin, s_chunk, s_rank, s_cut;
+  __shared__ uint32_t scan[256];
+  const int rb = blockIdx.x, row = a.row0 + rb, t = threadIdx.x;
+  sel_merge(p, a, rb, &st, &s_bin, s_cnt, s_mass);
+  const uint32_t tau = st.prefix;
+  float M, S;
+  row_ms(p, row, M, S);
+  const float Tt = p.temperature;
+  const uint32_t ties = s_cnt[s_bin];
+  if (t == 0) {
+    uint32_t j;
+    if (a.phase == 0) {
+      j = st.need;
+    } else {
+      const double e = (double)expf(key_float(tau) / Tt - M);
+      const double need = st.rem / e;
+      j = (need >= (double)ties) ? ties : (uint32_t)ceil(need);
+    }
+    j = j < 1 ? 1 : (j > ties ? ties : j);
+    // chunk and rank of the j-th tie, from the last digit's chunk counts
+    const size_t hb = ((size_t)1 * SEL_ROWS + rb) * p.nch * 256 + s_bin;
+    uint32_t cum = 0;
+    int ch = p.nch - 1;
+    for (int c = 0; c < p.nch; ++c) {
+      const uint32_t k = p.fcnt[hb + (size_t)c * 256];
+      if (cum + k >= j) { ch = c; break; }
+      cum += k;
+    }
+    s_chunk = ch;
+    s_rank = (int)(j - cum);
+    s_cut = ch * CH + CH - 1;
+    const double mass = st.above + (double)j * (double)expf(key_float(tau) / Tt - M);
+    if (a.phase == 0) p.fres[row].mass_k = mass;
+  }
+  __syncthreads();
+  // in-chunk scan: thread t owns ids chunk*CH + PER*t .. + PER - 1
+  const uint32_t tk = a.phase == 1 ? p.fres[row].tau_k : 0u;
+  const int ck = a.phase == 1 ? p.fres[row].cut_k : 0x7fffffff;
+  const float* z = p.logits + (size_t)row * p.V;
+  const int y0 = s_chunk * CH + PER * t;
+  uint32_t mine = 0;
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + e;
+    if (y < p.V) {
+      const uint32_t key = order_key(z[y]);
+      mine += (key == tau && sel_keep(tk, ck, key, y)) ? 1u : 0u;
+    }
+  }
+  scan[t] = mine;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t add = t >= o ? scan[t - o] : 0u;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  const int excl = (int)(scan[t] - mine);
+  if (excl < s_rank && s_rank <= excl + (int)mine) {
+    int r = s_rank - excl;
+    for (int e = 0; e < PER; ++e) {
+      const int y = y0 + e;
+      if (y >= p.V) break;
+      const uint32_t key = order_key(z[y]);
+      if (key == tau && sel_keep(tk, ck, key, y) && --r == 0) {
+        s_cut = y;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    p.fres[row].tau = tau;
+    p.fres[row].cut = s_cut;
+    if (a.phase == 0) {
+      p.fres[row].tau_k = tau;
+      p.fres[row].cut_k = s_cut;
+    }
+  }
+}
+
+// Rows whose adjustment has no top-k step keep everything before top-p.
+__global__ void accept_select_init_kernel(AcceptParams p, int row0, int nrows) {
+  const int rb = blockIdx.x * blockDim.x + threadIdx.x;
+  if (rb >= nrows) return;
+  p.fres[row0 + rb] = SelRule{0u, 0x7fffffff, 0u, 0x7fffffff, 0.0};
+}
+
+// Replace each chunk's statistics by those of the kept tokens, relative to
+// the row max (kept always: it is the first token in likelihood order), so
+// that row_ms and the chunk sums describe the adjusted target.  Grid (nch,
+// rows).  Other chunks' entries may be rewritten meanwhile: their maximum is
+// M either way.
+__global__ __launch_bounds__(256) void accept_select_apply_kernel(AcceptParams p, int row0) {
+  __shared__ float shf[16];
+  const int c = blockIdx.x, row = row0 + blockIdx.y;
+  float M, S;
+  row_ms(p, row, M, S);
+  const RowRule r = row_rule(p, row);
+  const float Tt = p.temperature;
+  const float* z = p.logits + (size_t)row * p.V;
+  const int y1 = min(p.V, (c + 1) * CH);
+  float acc = 0.f;
+  for (int y = c * CH + threadIdx.x; y < y1; y += 256) {
+    const float zy = z[y];
+    if (sel_keep(r.tau, r.cut, order_key(zy), y)) acc += expf(zy / Tt - M);
+  }
+  acc = block_sum(acc, shf);
+  if (threadIdx.x == 0) {
+    p.rowstat[((size_t)row * p.nch + c) * 2] = M;
+    p.rowstat[((size_t)row * p.nch + c) * 2 + 1] = acc;
+  }
+}
+
 // ---------------------------------------------------------------- chain, pass 2
 __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams p) {
   __shared__ float sM[128], sS[128];
@@ -146,7 +416,7 @@ __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams
       bool bad;
       const int x = clamp_token(p, p.tokens[b * T + i + 1], bad);
       if (bad) break;
-      const float pz = expf(p.logits[((size_t)(b * T + i)) * p.V + x] / Tt - sM[i]) / sS[i];
+      const float pz = pval(p, row_rule(p, b * T + i), p.logits[((size_t)(b * T + i)) * p.V + x], x, sM[i], sS[i]);
       const float qx = p.q[((size_t)(b * gamma + i)) * p.V + x];
       const float u = philox_uniform(p.seed, p.round, b, i);
       if (u * qx < pz) ++n;
@@ -160,10 +430,11 @@ __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams
   const float* z = p.logits + ((size_t)(b * T + n)) * p.V;
   const float* q = (n < gamma) ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
   const float M = sM[n], S = sS[n];
+  const RowRule rr = row_rule(p, b * T + n);
   const int y0 = c * CH, y1 = min(p.V, y0 + CH);
   float acc = 0.f;
   for (int y = y0 + threadIdx.x; y < y1; y += 256) {
-    const float pv = expf(z[y] / Tt - M) / S;
+    const float pv = pval(p, rr, z[y], y, M, S);
     acc += q ? fmaxf(0.f, pv - q[y]) : pv;
   }
   acc = block_sum(acc, shf);
@@ -226,6 +497,7 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
   const float* z = p.logits + (size_t)row * p.V;
   const float* q = use_res ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
   const int y0 = c * CH + threadIdx.x * PER;
+  const RowRule rr = row_rule(p, row);
   float r[PER];
   float loc = 0.f;
 #pragma unroll
@@ -233,7 +505,7 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
     const int y = y0 + e;
     float v = 0.f;
     if (y < p.V) {
-      const float pv = expf(z[y] / Tt - M) / S;
+      const float pv = pval(p, rr, z[y], y, M, S);
       v = q ? fmaxf(0.f, pv - q[y]) : pv;
     }
     r[e] = v;
@@ -416,7 +688,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
         bool bad;
         const int x = clamp_token(p, p.tokens[b * T + c], bad);
         const float u = philox_uniform(p.seed, p.round, b, c - 1);
-        const float rx = (s_cur < 0) ? expf(z[x] / Tt - s_M) / s_S : (s_cur == 0 ? rb0 : rb1)[x] / s_Zr;
+        const float rx = (s_cur < 0) ? pval(p, row_rule(p, row), z[x], x, s_M, s_S) : (s_cur == 0 ? rb0 : rb1)[x] / s_Zr;
         float qx = qv[x];
         if (!p.replacement && s_nrem > 0) {
           bool gone = false;
@@ -435,9 +707,10 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
       const float M = s_M, S = s_S, Zr = s_Zr;
       const int nrem = s_nrem;
       const float qscale = (!p.replacement && nrem > 0) ? 1.0f / (s_qtot - s_qmass) : 1.0f;
+      const RowRule rr = row_rule(p, row);
       double zs = 0.0, qs = 0.0;
       for (int y = threadIdx.x; y < V; y += blockDim.x) {
-        const float ry = cur < 0 ? expf(z[y] / Tt - M) / S : src[y] / Zr;
+        const float ry = cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y] / Zr;
         float qy = qv[y];
         qs += (double)qy;
         if (!p.replacement) {
@@ -484,10 +757,11 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
     const int cur = s_cur;
     const float* src = cur == 1 ? rb1 : rb0;
     const float M = s_M, S = s_S;
+    const RowRule rr = row_rule(p, row);
     const int per = (V + blockDim.x - 1) / blockDim.x;
     const int y0 = threadIdx.x * per, y1 = min(V, y0 + per);
     double loc = 0.0;
-    for (int y = y0; y < y1; ++y) loc += (double)(cur < 0 ? expf(z[y] / Tt - M) / S : src[y]);
+    for (int y = y0; y < y1; ++y) loc += (double)(cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]);
     __shared__ double scan[1024];
     scan[threadIdx.x] = loc;
     if (threadIdx.x == 0) s_tok = 0x7fffffff;
@@ -505,7 +779,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
     double run = scan[threadIdx.x] - loc;
     if (run <= t && run + loc > t) {
       for (int y = y0; y < y1; ++y) {
-        run += (double)(cur < 0 ? expf(z[y] / Tt - M) / S : src[y]);
+        run += (double)(cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]);
         if (run > t) { atomicMin(&s_tok, y); break; }
       }
     }
@@ -514,7 +788,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
       // rounding: take the last token with positive mass
       int last = -1;
       for (int y = y0; y < y1; ++y)
-        if ((cur < 0 ? expf(z[y] / Tt - M) / S : src[y]) > 0.f) last = y;
+        if ((cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]) > 0.f) last = y;
       __shared__ int s_last;
       if (threadIdx.x == 0) s_last = -1;
       __syncthreads();
@@ -528,8 +802,30 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
   tree_commit(p, b, path, plen);
 }
 
-hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
-  const bool greedy = p.temperature == 0.f;
+// Top-k / top-p selection for all rows, in batches of SEL_ROWS rows, then the
+// chunk statistics of the kept tokens.
+static hipError_t launch_select(const AcceptParams& p, hipStream_t s) {
+  const int rows = p.B * p.T;
+  const bool topk = p.top_k > 0 && p.top_k < p.V, topp = p.top_p < 1.f;
+  for (int row0 = 0; row0 < rows; row0 += SEL_ROWS) {
+    const int nr = min(SEL_ROWS, rows - row0);
+    accept_select_init_kernel<<<(nr + 63) / 64, 64, 0, s>>>(p, row0, nr);
+    for (int phase = 0; phase < 2; ++phase) {
+      if ((phase == 0 && !topk) || (phase == 1 && !topp)) continue;
+      for (int d = 0; d < 4; ++d) accept_select_kernel<<<dim3(p.nch, nr), 256, 0, s>>>(p, SelArgs{row0, phase, d});
+      accept_select_finish_kernel<<<nr, 256, 0, s>>>(p, SelArgs{row0, phase, 4});
+    }
+    accept_select_apply_kernel<<<dim3(p.nch, nr), 256, 0, s>>>(p, row0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const AcceptParams& pin, hipStream_t s) {
+  const bool greedy = pin.temperature == 0.f;
+  const bool adjust = !greedy && ((pin.top_k > 0 && pin.top_k < pin.V) || pin.top_p < 1.f);
+  AcceptParams p = pin;
+  if (!adjust) p.fres = nullptr;
+  if (adjust && (!p.fcnt || !p.fmass || !p.fstate || !p.fres)) return hipErrorInvalidValue;
   dim3 g1(p.nch, p.B * p.T);
   if (greedy)
     accept_rowstats_kernel<true><<<g1, 256, 0, s>>>(p);
@@ -537,6 +833,7 @@ hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
     accept_rowstats_kernel<false><<<g1, 256, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (adjust && (e = launch_select(p, s)) != hipSuccess) return e;
   if (p.parent) {
     if (greedy) accept_tree_greedy_kernel<<<p.B, 128, 0, s>>>(p);
     else accept_tree_sampled_kernel<<<p.B, 1024, 0, s>>>(p);

@@ -120,7 +120,38 @@ struct AcceptParams {
   uint16_t* kv_cache;
   int L, maxB, Hkv, D, max_ctx;
   int B, T, V, nch;
+  // top-k / top-p adjustment of the target (0 and 1 switch them off) and the
+  // selection scratch: chunk histograms [2][SEL_ROWS][nch][256], running
+  // state [2][SEL_ROWS], and one keep rule per row [B*T] (null in the
+  // sampling kernels when no adjustment applies)
+  int top_k;
+  float top_p;
+  uint32_t* fcnt;
+  double* fmass;
+  struct SelState* fstate;
+  struct SelRule* fres;
 };
+// Running state of one row's radix selection: the key bits chosen so far,
+// the tokens still to take (top-k) or the mass still to reach (top-p; -1
+// until the first digit has been counted), and the mass of the tokens
+// already known to be above the threshold.
+struct SelState {
+  uint32_t prefix;
+  uint32_t need;
+  double rem;
+  double above;
+};
+// A row's kept set: tokens with key > tau, and those with key == tau and id
+// <= cut (keys order logits; equal logits go by id).  tau_k / cut_k /
+// mass_k: the top-k set and its unnormalised mass.
+struct SelRule {
+  uint32_t tau;
+  int32_t cut;
+  uint32_t tau_k;
+  int32_t cut_k;
+  double mass_k;
+};
+constexpr int SEL_ROWS = 128;  // rows per selection batch
 int accept_chunks(int V);
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 

@@ -65,7 +65,8 @@ size_t gemm_xs_elems(const spec_config& c) {
 
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, flags, total;
+  size_t tok, pos, slot, anc, kvw, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
+      flags, total;
 };
 
 Layout plan(const spec_config& c) {
@@ -108,6 +109,12 @@ Layout plan(const spec_config& c) {
   L.rsum = take((size_t)c.max_batch * nch * 4);
   L.nacc = take((size_t)c.max_batch * 4);
   L.rbuf = take(2 * (size_t)c.max_batch * c.vocab * 4);
+  // top-k / top-p selection: histograms and state are indexed by a batch
+  // row below SEL_ROWS in each of two alternating buffers
+  L.fcnt = take((size_t)2 * SEL_ROWS * nch * 256 * 4);
+  L.fmass = take((size_t)2 * SEL_ROWS * nch * 256 * 8);
+  L.fstate = take((size_t)2 * SEL_ROWS * sizeof(SelState));
+  L.fres = take(Mmax * sizeof(SelRule));
   L.flags = take(256);
   L.total = off;
   return L;
@@ -472,6 +479,7 @@ spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_log
     return SPEC_ERR_INVALID_ARG;
   const float temp = sampling->temperature;
   if (!(temp >= 0.f) || !std::isfinite(temp)) return SPEC_ERR_INVALID_ARG;
+  if (sampling->top_k < 0 || !(sampling->top_p >= 0.f && sampling->top_p <= 1.f)) return SPEC_ERR_INVALID_ARG;
   if (temp > 0.f && !d_q && (d_tree_parent || T > 1)) return SPEC_ERR_INVALID_ARG;
   if (d_kv_len_out && !d_kv_len) return SPEC_ERR_INVALID_ARG;
   const spec_config& c = h->cfg;
@@ -487,6 +495,9 @@ spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_log
   ap.nacc = h->at<int32_t>(L.nacc); ap.rbuf = h->at<float>(L.rbuf); ap.flags = h->at<uint32_t>(L.flags);
   ap.kv_cache = h->kv; ap.L = c.n_layers; ap.maxB = c.max_batch; ap.Hkv = c.n_kv_heads; ap.D = c.head_dim;
   ap.max_ctx = c.max_ctx; ap.B = B; ap.T = T; ap.V = c.vocab; ap.nch = accept_chunks(c.vocab);
+  ap.top_k = sampling->top_k; ap.top_p = sampling->top_p;
+  ap.fcnt = h->at<uint32_t>(L.fcnt); ap.fmass = h->at<double>(L.fmass);
+  ap.fstate = h->at<SelState>(L.fstate); ap.fres = h->at<SelRule>(L.fres);
   hipStream_t s = (hipStream_t)stream;
   const int nq_rows = d_tree_parent ? T : T - 1;
   const double bytes = (double)B * T * c.vocab * 4 + (temp > 0 ? (double)B * nq_rows * c.vocab * 4 : 0.0);

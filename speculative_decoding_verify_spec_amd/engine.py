@@ -33,9 +33,10 @@ class VerifyEngine:
         return spec_verify_step(self.handle, B, T, tokens, kv_len, tree_parent, logits, self.stream)
 
     def accept(self, logits, q, tokens, out_tokens, num_accepted, kv_len, kv_len_out=None,
-               tree_parent=None, temperature=1.0, seed=0, round_=0, replacement=False):
+               tree_parent=None, temperature=1.0, seed=0, round_=0, replacement=False, top_k=0, top_p=1.0):
         B, T = tokens.shape
-        smp = spec_sampling(float(temperature), 1 if replacement else 0, int(seed), int(round_))
+        smp = spec_sampling(float(temperature), 1 if replacement else 0, int(seed), int(round_), int(top_k),
+                            float(top_p))
         return spec_accept(self.handle, B, T, logits, q, tokens, tree_parent, smp, out_tokens,
                            num_accepted, kv_len, kv_len_out, self.stream)
 

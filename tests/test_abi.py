@@ -87,7 +87,7 @@ def test_init_argument_errors_without_device():
 
 
 def test_calls_on_null_handle_are_rejected():
-    smp = S.spec_sampling(1.0, 0, 1, 0)
+    smp = S.spec_sampling(1.0, 0, 1, 0, 0, 1.0)
     assert S.spec_verify_step(None, 1, 1, 16, 16, None, 16, None, check=False) == S.SPEC_ERR_INVALID_ARG
     assert S.spec_accept(None, 1, 2, 16, 16, 16, None, smp, 16, 16, 16, 16, None,
                          check=False) == S.SPEC_ERR_INVALID_ARG
