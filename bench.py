@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--gamma", type=int, default=3)
     ap.add_argument("--sigma", type=float, default=1.0)
     ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--top-k", type=int, default=0, help="top-k adjustment of the target (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="top-p adjustment of the target (1: off); the synthetic drafts stay unadjusted")
     ap.add_argument("--rounds", type=int, default=8, help="distinct pre-drafted rounds cycled")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
     ap.add_argument("--profile-steps", type=int, default=10)
@@ -174,7 +177,7 @@ def main():
         tokens, qt = rounds[k % len(rounds)]
         eng.step(tokens, kv_len, logits)
         eng.accept(logits, qt if gamma else None, tokens, out, nacc_hist[k], kv_len, kv_out,
-                   temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
+                   temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k, top_k=a.top_k, top_p=a.top_p)
 
     for k in range(a.warmup):
         one_step(k)
@@ -246,9 +249,11 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32 (bf16 weights, fp32 activations/accum)",
         "data": "synthetic (random-init weights, random bf16 KV context, noisy-target drafts)",
         "config": {"workload": f"llama3-8b-shape chain verify B={B} ctx={ctx} gamma={gamma} "
-                               f"sigma={a.sigma} T={a.temperature}",
+                               f"sigma={a.sigma} T={a.temperature}"
+                               + (f" top_k={a.top_k}" if a.top_k else "")
+                               + (f" top_p={a.top_p}" if a.top_p < 1.0 else ""),
                    "B": B, "ctx": ctx, "gamma": gamma, "sigma": a.sigma, "temperature": a.temperature,
-                   "parallelism": "single GPU"},
+                   "top_k": a.top_k, "top_p": a.top_p, "parallelism": "single GPU"},
         "c_verify": round(c_v, 4), "t_verify_ms": round(t_verify, 4), "t_decode_ms": round(t_decode, 4),
         "mean_accepted": round(float(n_timed.mean()), 4), "alpha_hat": round(alpha_hat, 4),
         "tokens_per_round": round(float((n_timed + 1).mean()), 4),
@@ -317,7 +322,8 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
     while nrounds < 3 and (nrounds == 0 or dt < a.cpu_seconds):
         t0 = time.perf_counter()
         z, _, _ = OM.forward(sh, Wn, tok, np.full(B, ctx), kc, vc)
-        res = OA.accept(z, qn, tok, a.temperature, philox.Uniforms(synth.SEED_ACCEPT, nrounds))
+        res = OA.accept(z, qn, tok, a.temperature, philox.Uniforms(synth.SEED_ACCEPT, nrounds),
+                        top_k=a.top_k, top_p=a.top_p)
         dt += time.perf_counter() - t0
         toks += int((res["n_accepted"] + 1).sum())
         nrounds += 1

@@ -99,12 +99,25 @@ __global__ __launch_bounds__(256) void accept_rowstats_kernel(AcceptParams p) {
 }
 
 // Combine the chunk statistics of one row: M = max, S = sum exp(z/T - M).
+// The chunk loads are issued 16 at a time (one thread reads them all).
 DEVI void row_ms(const AcceptParams& p, int row, float& M, float& S) {
-  const float* st = p.rowstat + (size_t)row * p.nch * 2;
+  const float2* st = (const float2*)(p.rowstat + (size_t)row * p.nch * 2);
   M = -INFINITY;
-  for (int c = 0; c < p.nch; ++c) M = fmaxf(M, st[2 * c]);
   S = 0.f;
-  for (int c = 0; c < p.nch; ++c) S += st[2 * c + 1] * expf(st[2 * c] - M);
+  for (int c0 = 0; c0 < p.nch; c0 += 16) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < p.nch ? st[c0 + i] : make_float2(-INFINITY, 0.f);
+    float m = M;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, v[i].x);
+    // rescale the running sum to the new maximum, then add this batch
+    S = (M == -INFINITY) ? 0.f : S * expf(M - m);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (v[i].y != 0.f) S += v[i].y * expf(v[i].x - m);
+    M = m;
+  }
 }
 DEVI void row_argmax(const AcceptParams& p, int row, int& idx) {
   const float* st = p.rowstat + (size_t)row * p.nch * 2;
@@ -168,62 +181,68 @@ struct SelArgs {
 };
 
 // Merge the previous digit's chunk counts of batch row rb and fix that digit.
-// blockDim.x == 256: thread t sums bin t over the chunks.  Leaves the state
-// after the digit in *st, the digit in *bin, and the merged bins in s_cnt /
-// s_mass; ends synchronised.
+// blockDim.x == 256: thread t sums bin t over the chunks, then suffix sums
+// over the bins (from the top) locate the bin where the count or the mass
+// from the top reaches what is still needed.  Leaves the state after the
+// digit in *st, the digit in *bin, and the merged bins in s_cnt / s_mass;
+// ends synchronised.
 DEVI void sel_merge(const AcceptParams& p, const SelArgs& a, int rb, SelState* st, int* bin, uint32_t* s_cnt,
                     double* s_mass) {
+  __shared__ uint32_t sc[256];
+  __shared__ double sm[256];
+  __shared__ int s_pick, s_low;
   const int t = threadIdx.x;
   const int pd = (a.digit - 1) & 1;
   const size_t hb = ((size_t)pd * SEL_ROWS + rb) * p.nch * 256;
   uint32_t cn = 0;
   double ms = 0.0;
+#pragma unroll 8
   for (int c = 0; c < p.nch; ++c) {
     cn += p.fcnt[hb + (size_t)c * 256 + t];
     ms += p.fmass[hb + (size_t)c * 256 + t];
   }
   s_cnt[t] = cn;
   s_mass[t] = ms;
+  sc[t] = cn;
+  sm[t] = ms;
+  if (t == 0) {
+    s_pick = -1;
+    s_low = 256;
+  }
+  __syncthreads();
+  // inclusive suffix sums: sc[t] = sum of bins >= t
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t ac = t + o < 256 ? sc[t + o] : 0u;
+    const double am = t + o < 256 ? sm[t + o] : 0.0;
+    __syncthreads();
+    sc[t] += ac;
+    sm[t] += am;
+    __syncthreads();
+  }
+  SelState s = p.fstate[pd * SEL_ROWS + rb];
+  if (a.phase == 1 && s.rem < 0.0) s.rem = (double)p.top_p * sm[0];
+  // the highest bin whose suffix reaches the target
+  const bool hit = a.phase == 0 ? (sc[t] >= s.need) : (cn > 0 && sm[t] >= s.rem);
+  if (hit) atomicMax(&s_pick, t);
+  if (cn > 0) atomicMin(&s_low, t);
   __syncthreads();
   if (t == 0) {
-    SelState s = p.fstate[pd * SEL_ROWS + rb];
     const int shift = 24 - 8 * (a.digit - 1);
-    int b;
+    int b = s_pick;
     if (a.phase == 0) {
-      // the bin holding the need-th token from the top
-      uint32_t cum = 0;
-      double above = 0.0;
-      for (b = 255; b > 0; --b) {
-        if (cum + s_cnt[b] >= s.need) break;
-        cum += s_cnt[b];
-        above += s_mass[b];
-      }
+      if (b < 0) b = 0;
+      const uint32_t cum = b < 255 ? sc[b + 1] : 0u;
       s.need -= cum;
-      s.above += above;
+      s.above += b < 255 ? sm[b + 1] : 0.0;
+    } else if (b < 0) {
+      // rounding left the total short of the target: the lowest occupied
+      // bin, taken whole
+      b = s_low < 256 ? s_low : 0;
+      s.above += b < 255 ? sm[b + 1] : 0.0;
+      s.rem = INFINITY;
     } else {
-      if (s.rem < 0.0) {
-        double tot = 0.0;
-        for (int i = 0; i < 256; ++i) tot += s_mass[i];
-        s.rem = (double)p.top_p * tot;
-      }
-      // the bin where the mass from the top reaches rem; if rounding leaves
-      // it short, the lowest occupied bin, taken whole
-      double cum = 0.0;
-      int last = 0;
-      b = -1;
-      for (int i = 255; i >= 0; --i) {
-        if (!s_cnt[i]) continue;
-        last = i;
-        if (cum + s_mass[i] >= s.rem) { b = i; break; }
-        cum += s_mass[i];
-      }
-      if (b < 0) {
-        b = last;
-        cum -= s_mass[last];
-        s.rem = INFINITY;
-      } else {
-        s.rem -= cum;
-      }
+      const double cum = b < 255 ? sm[b + 1] : 0.0;
+      s.rem -= cum;
       s.above += cum;
     }
     s.prefix |= (uint32_t)b << shift;
@@ -301,11 +320,21 @@ __global__ __launch_bounds__(256) void accept_select_finish_kernel(AcceptParams 
     }
     j = j < 1 ? 1 : (j > ties ? ties : j);
     // chunk and rank of the j-th tie, from the last digit's chunk counts
+    // (staged in scan[] by all threads below)
+    s_rank = (int)j;
+  }
+  __syncthreads();
+  {
     const size_t hb = ((size_t)1 * SEL_ROWS + rb) * p.nch * 256 + s_bin;
+    for (int c = t; c < p.nch; c += 256) scan[c] = p.fcnt[hb + (size_t)c * 256];
+  }
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t j = (uint32_t)s_rank;
     uint32_t cum = 0;
     int ch = p.nch - 1;
     for (int c = 0; c < p.nch; ++c) {
-      const uint32_t k = p.fcnt[hb + (size_t)c * 256];
+      const uint32_t k = scan[c];
       if (cum + k >= j) { ch = c; break; }
       cum += k;
     }
@@ -825,7 +854,8 @@ hipError_t launch_accept(const AcceptParams& pin, hipStream_t s) {
   const bool adjust = !greedy && ((pin.top_k > 0 && pin.top_k < pin.V) || pin.top_p < 1.f);
   AcceptParams p = pin;
   if (!adjust) p.fres = nullptr;
-  if (adjust && (!p.fcnt || !p.fmass || !p.fstate || !p.fres)) return hipErrorInvalidValue;
+  // the selection stages one count per chunk in a 256-entry LDS array
+  if (adjust && (!p.fcnt || !p.fmass || !p.fstate || !p.fres || p.nch > 256)) return hipErrorInvalidValue;
   dim3 g1(p.nch, p.B * p.T);
   if (greedy)
     accept_rowstats_kernel<true><<<g1, 256, 0, s>>>(p);
