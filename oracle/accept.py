@@ -264,3 +264,34 @@ def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replaceme
         adj_margins.append(am)
     return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins,
             "adjust_margins": adj_margins}
+
+
+def accept_ragged(logits_rows, q_rows, tokens_rows, row_start, lens, q_start, temperature, uniforms,
+                  max_len=None, top_k=0, top_p=1.0):
+    """Ragged chains (the DeepSeek-V4 analysis page, section 4): sequence b is
+    a chain of gamma_b = lens[b] - 1 drafts whose window rows start at
+    row_start[b] of logits_rows / tokens_rows and whose draft distributions
+    start at q_start[b] of q_rows.  Each sequence is accepted exactly as a
+    chain of its own length (same uniforms' slots 0 .. gamma_b).  Compact
+    mode packs the rows; cap-accept keeps a fixed width T and caps the
+    length.  Returns the same dict as `accept`, out_tokens [B, max_len]."""
+    B = len(lens)
+    max_len = int(max(lens)) if max_len is None else int(max_len)
+    n_acc = np.zeros(B, dtype=np.int64)
+    out = np.full((B, max_len), -1, dtype=np.int64)
+    margins, adj_margins, paths = [], [], []
+    for b in range(B):
+        r0, n_b = int(row_start[b]), int(lens[b])
+        z = np.asarray(logits_rows)[r0:r0 + n_b]
+        q = None if q_rows is None else np.asarray(q_rows)[int(q_start[b]):int(q_start[b]) + n_b - 1]
+        toks = np.asarray(tokens_rows)[r0:r0 + n_b]
+        am = []
+        n, em, m = accept_chain_one(z, q, toks, temperature, (lambda s, b=b: uniforms(b, s)),
+                                    top_k=top_k, top_p=top_p, adjust_margins=am)
+        n_acc[b] = n
+        out[b, :len(em)] = em
+        margins.append(m)
+        adj_margins.append(am)
+        paths.append(list(range(n + 1)))
+    return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins,
+            "adjust_margins": adj_margins}

@@ -190,6 +190,26 @@ def forward(shape, W: Weights, tokens, kv_len, k_cache, v_cache, tree_parent=Non
     return logits, k_new, v_new
 
 
+def forward_ragged(shape, W: Weights, tokens_rows, cu, kv_len, k_cache, v_cache):
+    """Compact ("ragged") verify, the DeepSeek-V4 analysis page, section 4:
+    sequence b verifies its own chain of len_b = cu[b+1] - cu[b] rows, packed
+    back to back in tokens_rows.  No row attends across sequences, so each
+    sequence's rows are exactly the chain forward of that sequence alone with
+    T = len_b.  Returns logits [cu[B], V] and per-sequence lists of the
+    suffix keys / values [L, len_b, Hkv, D]."""
+    tokens_rows = np.asarray(tokens_rows)
+    cu = [int(c) for c in cu]
+    logits, k_new, v_new = [], [], []
+    for b in range(len(cu) - 1):
+        toks = tokens_rows[cu[b]:cu[b + 1]][None, :]
+        lg, kn, vn = forward(shape, W, toks, np.asarray(kv_len)[b:b + 1], k_cache[:, b:b + 1],
+                             v_cache[:, b:b + 1])
+        logits.append(lg[0])
+        k_new.append(kn[:, 0])
+        v_new.append(vn[:, 0])
+    return np.concatenate(logits, axis=0), k_new, v_new
+
+
 def write_suffix(k_cache, v_cache, k_new, v_new, kv_len, rows=None):
     """Store the window's K/V (rounded to bf16) at slots kv_len[b] + i, as the
     verify step does for every row before acceptance is known.  Caches are

@@ -250,3 +250,53 @@ def test_bad_tree_rejected():
         M.check_tree([-1, 0, 2])
     with pytest.raises(ValueError):
         M.check_tree([0, 0])
+
+
+def test_window_prefix_rows_do_not_depend_on_later_rows():
+    """The property cap-accept rests on (DeepSeek-V4 analysis page, section 4):
+    in a chain window the first L rows' logits do not depend on the rows after
+    them, so a fixed-width forward capped at L rows gives the logits of an
+    L-row (compact) forward."""
+    sh = _shape()
+    W = M.Weights(*_weights(sh, seed=3))
+    rng = np.random.default_rng(8)
+    B, T, ctx = 2, 6, 12
+    kc = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, ctx + T, sh.head_dim))
+    vc = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, sh.head_dim, ctx + T))
+    kv_len = np.array([4, 11])
+    toks = rng.integers(0, sh.vocab, size=(B, T))
+    full, _, _ = M.forward(sh, W, toks, kv_len, kc, vc)
+    for L in range(1, T):
+        part, _, _ = M.forward(sh, W, toks[:, :L], kv_len, kc, vc)
+        assert np.allclose(part, full[:, :L], atol=1e-12)
+        # and the later rows do depend on a changed earlier token
+    toks2 = toks.copy()
+    toks2[:, 2] = (toks2[:, 2] + 1) % sh.vocab
+    z2, _, _ = M.forward(sh, W, toks2, kv_len, kc, vc)
+    assert np.allclose(z2[:, :2], full[:, :2], atol=1e-12)
+    assert not np.allclose(z2[:, 3:], full[:, 3:], atol=1e-6)
+
+
+def test_forward_ragged_packs_the_batched_forward():
+    """Compact verify with equal lengths packs the batched chain forward row
+    for row; with unequal lengths every sequence's rows are its own forward."""
+    sh = _shape()
+    W = M.Weights(*_weights(sh, seed=4))
+    rng = np.random.default_rng(9)
+    B, T, ctx = 3, 4, 10
+    kc = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, ctx + T, sh.head_dim))
+    vc = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, sh.head_dim, ctx + T))
+    kv_len = np.array([2, 9, 5])
+    toks = rng.integers(0, sh.vocab, size=(B, T))
+    full, kn, vn = M.forward(sh, W, toks, kv_len, kc, vc)
+    cu = [0, 4, 8, 12]
+    zr, knr, vnr = M.forward_ragged(sh, W, toks.reshape(-1), cu, kv_len, kc, vc)
+    assert np.allclose(zr, full.reshape(B * T, -1), atol=1e-12)
+    for b in range(B):
+        assert np.allclose(knr[b], kn[:, b], atol=1e-12) and np.allclose(vnr[b], vn[:, b], atol=1e-12)
+    lens = [3, 1, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    rows = np.concatenate([toks[b, :lens[b]] for b in range(B)])
+    zr, _, _ = M.forward_ragged(sh, W, rows, cu, kv_len, kc, vc)
+    for b in range(B):
+        assert np.allclose(zr[cu[b]:cu[b + 1]], full[b, :lens[b]], atol=1e-12)

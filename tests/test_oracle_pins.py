@@ -602,3 +602,48 @@ def test_tree_sampled_adjusted_output():
     want = np.array([[tab.p[()][a] * tab.p[(a,)][b] for b in range(V)] for a in range(V)])
     chi2, dof = _chi2(counts, want * N)
     assert chi2 < 50 + 2.5 * (dof - 15), (chi2, dof)
+
+
+# ----------------------------------------------------------------------------
+# ragged chains (DeepSeek-V4 analysis page, section 4)
+# ----------------------------------------------------------------------------
+
+def test_accept_ragged_equal_lengths_is_the_chain_accept():
+    rng = np.random.default_rng(31)
+    B, T, V = 3, 4, 16
+    z = rng.normal(size=(B, T, V)) * 2
+    q = np.stack([[_random_dist(rng, V) for _ in range(T - 1)] for _ in range(B)])
+    toks = rng.integers(0, V, size=(B, T))
+    U = philox.Uniforms(5, 2)
+    want = acc.accept(z, q, toks, 1.0, U)
+    got = acc.accept_ragged(z.reshape(B * T, V), q.reshape(B * (T - 1), V), toks.reshape(-1),
+                            [b * T for b in range(B)], [T] * B, [b * (T - 1) for b in range(B)], 1.0, U)
+    assert np.array_equal(got["n_accepted"], want["n_accepted"])
+    assert np.array_equal(got["out_tokens"], want["out_tokens"])
+
+
+def test_accept_ragged_caps_and_packing_agree():
+    """Cap-accept on a fixed-width window and compact accept on the packed
+    rows decide the same: sequence b's first len_b rows are the same rows, and
+    it is accepted as a chain of len_b - 1 drafts either way; at most len_b - 1
+    drafts are accepted."""
+    rng = np.random.default_rng(32)
+    B, T, V = 4, 5, 12
+    z = rng.normal(size=(B, T, V)) * 2
+    q = np.stack([[_random_dist(rng, V) for _ in range(T - 1)] for _ in range(B)])
+    toks = rng.integers(0, V, size=(B, T))
+    lens = [5, 1, 3, 2]
+    U = philox.Uniforms(9, 4)
+    cap = acc.accept_ragged(z.reshape(B * T, V), q.reshape(B * (T - 1), V), toks.reshape(-1),
+                            [b * T for b in range(B)], lens, [b * (T - 1) for b in range(B)], 1.0, U, max_len=T)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    zp = np.concatenate([z[b, :lens[b]] for b in range(B)])
+    qp = np.concatenate([q[b, :lens[b] - 1] for b in range(B)])
+    tp = np.concatenate([toks[b, :lens[b]] for b in range(B)])
+    cmp_ = acc.accept_ragged(zp, qp, tp, cu[:-1], lens, cu[:-1] - np.arange(B), 1.0, U, max_len=T)
+    assert np.array_equal(cap["out_tokens"], cmp_["out_tokens"])
+    assert np.all(cap["n_accepted"] <= np.array(lens) - 1)
+    # a length-1 sequence has no draft: its one token is a draw from p of its row
+    p1 = acc.softmax(z[1, 0], 1.0)
+    x, _ = acc.inverse_cdf(p1, U(1, 0))
+    assert cap["n_accepted"][1] == 0 and cap["out_tokens"][1, 0] == x
