@@ -63,6 +63,9 @@ typedef int32_t spec_status;
 #define SPEC_FLAG_TOKEN_RANGE 1u  /* a token id outside [0, vocab)              */
 #define SPEC_FLAG_TREE 2u         /* parent[0] != -1 or parent[i] not in [0,i)   */
 #define SPEC_FLAG_KV_OVERFLOW 4u  /* kv_len < 0 or kv_len + T > max_ctx          */
+#define SPEC_FLAG_LAYOUT 8u       /* ragged row offsets not increasing from 0,
+                                     a length outside [1, max_len], or rows
+                                     past the padded row count              */
 
 /* Model shape and capacities, fixed at init.
  *   Llama-style decoder: RMSNorm, rotary embedding (rotate-half, theta),
@@ -164,6 +167,29 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
                              const int32_t* d_kv_len, const int32_t* d_tree_parent,
                              float* d_logits, void* stream);
 
+/* Ragged (compact) verify forward: the DeepSeek-V4 analysis page, section 4
+ * (static, cap-accept and compact modes; the RaggedVerifyLayout of
+ * per-request verify lengths, their sum, and the graph tier it is padded to).
+ * Sequence b verifies its own chain of len_b = cu[b+1] - cu[b] rows,
+ * 1 <= len_b <= max_len, packed back to back: rows cu[b] .. cu[b+1] - 1 of
+ * d_tokens / d_logits, row i at position and cache slot kv_len[b] + i.  Rows
+ * cu[B] .. rows - 1 are padding up to the caller's execution tier: they are
+ * computed (their logits are meaningless) but write no cache slot.  Only the
+ * packed rows are read from the weights' point of view: the GEMMs run on
+ * `rows` rows instead of B * max_len.
+ *   d_cu_rows [B+1] int32 device, cu[0] = 0, increasing, cu[B] <= rows.
+ *   d_tokens [rows] int32 (row cu[b] is sequence b's pending token).
+ *   d_kv_len [B]; d_logits [rows, vocab] fp32 output.
+ *   rows <= max_batch * max_rows_per_seq; max_len <= max_rows_per_seq.
+ *   Recorded launch sequences are kept per (B, max_len, rows), so a caller
+ *   that pads `rows` to a few tiers reuses them.
+ *   Errors: INVALID_ARG, CAPACITY, DEVICE.  Flags: TOKEN_RANGE, KV_OVERFLOW,
+ *   LAYOUT (offsets not increasing from 0, a length outside [1, max_len] or
+ *   rows past `rows`; values are clamped, nothing faults). */
+spec_status spec_verify_step_ragged(spec_handle* h, int32_t B, int32_t max_len, int32_t rows,
+                                    const int32_t* d_cu_rows, const int32_t* d_tokens,
+                                    const int32_t* d_kv_len, float* d_logits, void* stream);
+
 /* Speculative-sampling accept and cache commit.
  *   d_logits [B, T, vocab] fp32 from spec_verify_step.
  *   d_q: draft probabilities, fp32, rows summing to 1.  Chain: [B, T-1, vocab],
@@ -189,6 +215,29 @@ spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_log
                         const spec_sampling* sampling, int32_t* d_out_tokens,
                         int32_t* d_num_accepted, const int32_t* d_kv_len, int32_t* d_kv_len_out,
                         void* stream);
+
+/* Accept of ragged chains (same section): sequence b has len_b rows starting
+ * at logits / token row row_start[b] (its pending token and len_b - 1
+ * drafts), and its drafts' distributions at q rows q_start[b] .. q_start[b] +
+ * len_b - 2.  At most len_b - 1 drafts are accepted, the extra token comes
+ * from row n, the commit is kv_len + n + 1; the uniforms use slots 0 ..
+ * len_b - 1 as a chain of gamma = len_b - 1 does.
+ *   Compact mode: row_start = cu[b], q_start = cu[b] - b for q packed without
+ *   each sequence's last row, logits from spec_verify_step_ragged.
+ *   Cap-accept mode: logits from spec_verify_step at T = max_len, row_start =
+ *   b * T, q_start = b * (T - 1), len_b the cap.
+ *   rows / q_rows: rows in d_logits and d_tokens / in d_q.
+ *   d_out_tokens [B, max_len] (n accepted drafts, the extra token, -1
+ *   padding); d_num_accepted [B]; kv_len / kv_len_out as for spec_accept.
+ *   d_q and d_q_start may be NULL when temperature == 0 or max_len == 1.
+ *   sampling as for spec_accept (tree_replacement unused).
+ *   Errors: INVALID_ARG, CAPACITY, DEVICE.  Flags: TOKEN_RANGE, LAYOUT. */
+spec_status spec_accept_ragged(spec_handle* h, int32_t B, int32_t max_len, int32_t rows, int32_t q_rows,
+                               const int32_t* d_row_start, const int32_t* d_len, const int32_t* d_q_start,
+                               const float* d_logits, const float* d_q, const int32_t* d_tokens,
+                               const spec_sampling* sampling, int32_t* d_out_tokens,
+                               int32_t* d_num_accepted, const int32_t* d_kv_len, int32_t* d_kv_len_out,
+                               void* stream);
 
 /* Synchronise `stream`, return the sticky device flag word (SPEC_FLAG_*) in
  * *flags and clear it.  Returns SPEC_OK, or DEVICE if a HIP call failed. */

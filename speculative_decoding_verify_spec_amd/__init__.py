@@ -30,10 +30,11 @@ SPEC_DTYPE_BF16 = 1
 SPEC_FLAG_TOKEN_RANGE = 1
 SPEC_FLAG_TREE = 2
 SPEC_FLAG_KV_OVERFLOW = 4
+SPEC_FLAG_LAYOUT = 8
 
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
-    "spec_accept", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
+    "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
     "spec_profile_gemm", "spec_graph_enable", "spec_verify_destroy", "spec_status_str",
 ]
 
@@ -85,8 +86,13 @@ def lib():
     L.spec_verify_init.restype = i32
     L.spec_verify_step.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
     L.spec_verify_step.restype = i32
+    L.spec_verify_step_ragged.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.spec_verify_step_ragged.restype = i32
     L.spec_accept.argtypes = [vp, i32, i32, vp, vp, vp, vp, C.POINTER(spec_sampling), vp, vp, vp, vp, vp]
     L.spec_accept.restype = i32
+    L.spec_accept_ragged.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(spec_sampling),
+                                     vp, vp, vp, vp, vp]
+    L.spec_accept_ragged.restype = i32
     L.spec_device_errors.argtypes = [vp, C.POINTER(C.c_uint32), vp]
     L.spec_device_errors.restype = i32
     L.spec_profile_enable.argtypes = [vp, i32]
@@ -165,6 +171,26 @@ def spec_verify_step(h, B, T, tokens, kv_len, tree_parent, logits, stream=None, 
                                 _ptr(logits), _stream(stream))
     if check:
         _check("spec_verify_step", st)
+    return st
+
+
+def spec_verify_step_ragged(h, B, max_len, rows, cu_rows, tokens, kv_len, logits, stream=None, check=True):
+    st = lib().spec_verify_step_ragged(h, int(B), int(max_len), int(rows), _ptr(cu_rows), _ptr(tokens),
+                                       _ptr(kv_len), _ptr(logits), _stream(stream))
+    if check:
+        _check("spec_verify_step_ragged", st)
+    return st
+
+
+def spec_accept_ragged(h, B, max_len, rows, q_rows, row_start, lens, q_start, logits, q, tokens,
+                       sampling: spec_sampling, out_tokens, num_accepted, kv_len, kv_len_out, stream=None,
+                       check=True):
+    st = lib().spec_accept_ragged(h, int(B), int(max_len), int(rows), int(q_rows), _ptr(row_start), _ptr(lens),
+                                  _ptr(q_start), _ptr(logits), _ptr(q), _ptr(tokens), C.byref(sampling),
+                                  _ptr(out_tokens), _ptr(num_accepted), _ptr(kv_len), _ptr(kv_len_out),
+                                  _stream(stream))
+    if check:
+        _check("spec_accept_ragged", st)
     return st
 
 

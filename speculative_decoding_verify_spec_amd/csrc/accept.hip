@@ -423,30 +423,60 @@ __global__ __launch_bounds__(256) void accept_select_apply_kernel(AcceptParams p
   }
 }
 
+// ---------------------------------------------------------------- chain layout
+// Sequence b of a chain has T rows from row b*T, and its drafts' q rows from
+// b*(T-1); a ragged layout (DeepSeek-V4 analysis page, section 4) gives each
+// sequence its own first row, length and first q row.  Lengths are clamped
+// to [1, T] and rows to the buffers (FLAG_LAYOUT marks a clamp).
+DEVI int chain_len(const AcceptParams& p, int b) {
+  if (!p.rlen) return p.T;
+  const int l = p.rlen[b];
+  return l < 1 ? 1 : (l > p.T ? p.T : l);
+}
+DEVI int chain_row(const AcceptParams& p, int b, int i) {
+  if (!p.rstart) return b * p.T + i;
+  const int r = p.rstart[b] + i;
+  return r < 0 ? 0 : (r >= p.rows ? p.rows - 1 : r);
+}
+DEVI int chain_qrow(const AcceptParams& p, int b, int i) {
+  if (!p.qstart) return b * (p.T - 1) + i;
+  const int r = p.qstart[b] + i;
+  return r < 0 ? 0 : (r >= p.qrows ? p.qrows - 1 : r);
+}
+// FLAG_LAYOUT when sequence b's rows or q rows leave their buffers
+DEVI void check_layout(const AcceptParams& p, int b) {
+  if (!p.rstart) return;
+  const int l = p.rlen[b], r = p.rstart[b], qr = p.qstart ? p.qstart[b] : 0;
+  if (l < 1 || l > p.T || r < 0 || r + l > p.rows || (p.qstart && (qr < 0 || qr + l - 1 > p.qrows)))
+    atomicOr(p.flags, FLAG_LAYOUT);
+}
+
 // ---------------------------------------------------------------- chain, pass 2
 __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams p) {
   __shared__ float sM[128], sS[128];
   __shared__ int sn;
   __shared__ float shf[16];
   const int c = blockIdx.x, b = blockIdx.y;
-  const int T = p.T, gamma = T - 1;
+  const int T = chain_len(p, b), gamma = T - 1;
   for (int i = threadIdx.x; i < T; i += blockDim.x) {
     float M, S;
-    row_ms(p, b * T + i, M, S);
+    const int row = chain_row(p, b, i);
+    row_ms(p, row, M, S);
     sM[i] = M;
     sS[i] = S;
-    if (c == 0) { p.rowms[2 * (b * T + i)] = M; p.rowms[2 * (b * T + i) + 1] = S; }
+    if (c == 0) { p.rowms[2 * row] = M; p.rowms[2 * row + 1] = S; }
   }
   __syncthreads();
-  const float Tt = p.temperature;
   if (threadIdx.x == 0) {
+    if (c == 0) check_layout(p, b);
     int n = 0;
     for (int i = 0; i < gamma; ++i) {
       bool bad;
-      const int x = clamp_token(p, p.tokens[b * T + i + 1], bad);
+      const int x = clamp_token(p, p.tokens[chain_row(p, b, i + 1)], bad);
       if (bad) break;
-      const float pz = pval(p, row_rule(p, b * T + i), p.logits[((size_t)(b * T + i)) * p.V + x], x, sM[i], sS[i]);
-      const float qx = p.q[((size_t)(b * gamma + i)) * p.V + x];
+      const int row = chain_row(p, b, i);
+      const float pz = pval(p, row_rule(p, row), p.logits[(size_t)row * p.V + x], x, sM[i], sS[i]);
+      const float qx = p.q[(size_t)chain_qrow(p, b, i) * p.V + x];
       const float u = philox_uniform(p.seed, p.round, b, i);
       if (u * qx < pz) ++n;
       else break;
@@ -456,10 +486,10 @@ __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams
   }
   __syncthreads();
   const int n = sn;
-  const float* z = p.logits + ((size_t)(b * T + n)) * p.V;
-  const float* q = (n < gamma) ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
+  const float* z = p.logits + (size_t)chain_row(p, b, n) * p.V;
+  const float* q = (n < gamma) ? p.q + (size_t)chain_qrow(p, b, n) * p.V : nullptr;
   const float M = sM[n], S = sS[n];
-  const RowRule rr = row_rule(p, b * T + n);
+  const RowRule rr = row_rule(p, chain_row(p, b, n));
   const int y0 = c * CH, y1 = min(p.V, y0 + CH);
   float acc = 0.f;
   for (int y = y0 + threadIdx.x; y < y1; y += 256) {
@@ -476,7 +506,7 @@ DEVI void write_chain_outputs(const AcceptParams& p, int b, int n, int extra) {
   const int T = p.T;
   for (int i = threadIdx.x; i < T; i += blockDim.x) {
     int v = -1;
-    if (i < n) v = p.tokens[b * T + i + 1];
+    if (i < n) v = p.tokens[chain_row(p, b, i + 1)];
     else if (i == n) v = extra;
     p.out_tokens[b * T + i] = v;
   }
@@ -493,11 +523,10 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
   __shared__ int s_c, s_deg, s_tok;
   __shared__ double s_base, s_t;
   const int b = blockIdx.x;
-  const int T = p.T, gamma = T - 1;
+  const int T = chain_len(p, b), gamma = T - 1;
   const int n = p.nacc[b];
-  const int row = b * T + n;
+  const int row = chain_row(p, b, n);
   const float M = p.rowms[2 * row], S = p.rowms[2 * row + 1];
-  const float Tt = p.temperature;
   if (threadIdx.x == 0) {
     double R = 0.0;
     for (int c = 0; c < p.nch; ++c) R += (double)p.rsum[(size_t)b * p.nch + c];
@@ -524,7 +553,7 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
   const int c = s_c;
   const bool use_res = (n < gamma) && !s_deg;
   const float* z = p.logits + (size_t)row * p.V;
-  const float* q = use_res ? p.q + ((size_t)(b * gamma + n)) * p.V : nullptr;
+  const float* q = use_res ? p.q + (size_t)chain_qrow(p, b, n) * p.V : nullptr;
   const int y0 = c * CH + threadIdx.x * PER;
   const RowRule rr = row_rule(p, row);
   float r[PER];
@@ -585,14 +614,15 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
 __global__ __launch_bounds__(128) void accept_chain_greedy_kernel(AcceptParams p) {
   __shared__ int am[128];
   __shared__ int s_n;
-  const int b = blockIdx.x, T = p.T, gamma = T - 1;
-  for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, b * T + i, am[i]);
+  const int b = blockIdx.x, T = chain_len(p, b), gamma = T - 1;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, chain_row(p, b, i), am[i]);
   __syncthreads();
   if (threadIdx.x == 0) {
+    check_layout(p, b);
     int n = 0;
     while (n < gamma) {
       bool bad;
-      const int x = clamp_token(p, p.tokens[b * T + n + 1], bad);
+      const int x = clamp_token(p, p.tokens[chain_row(p, b, n + 1)], bad);
       if (bad || x != am[n]) break;
       ++n;
     }
@@ -834,7 +864,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
 // Top-k / top-p selection for all rows, in batches of SEL_ROWS rows, then the
 // chunk statistics of the kept tokens.
 static hipError_t launch_select(const AcceptParams& p, hipStream_t s) {
-  const int rows = p.B * p.T;
+  const int rows = p.rows;
   const bool topk = p.top_k > 0 && p.top_k < p.V, topp = p.top_p < 1.f;
   for (int row0 = 0; row0 < rows; row0 += SEL_ROWS) {
     const int nr = min(SEL_ROWS, rows - row0);
@@ -856,7 +886,7 @@ hipError_t launch_accept(const AcceptParams& pin, hipStream_t s) {
   if (!adjust) p.fres = nullptr;
   // the selection stages one count per chunk in a 256-entry LDS array
   if (adjust && (!p.fcnt || !p.fmass || !p.fstate || !p.fres || p.nch > 256)) return hipErrorInvalidValue;
-  dim3 g1(p.nch, p.B * p.T);
+  dim3 g1(p.nch, p.rows);
   if (greedy)
     accept_rowstats_kernel<true><<<g1, 256, 0, s>>>(p);
   else

@@ -54,9 +54,11 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
   float* s_v = s_k + KC * KS;  // [KC][KS]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
-  const int nq = G * p.T;
+  const int Tb = p.rlen ? p.rlen[b] : p.T;  // this sequence's rows (ragged: its own length)
+  const int rs = p.rstart ? p.rstart[b] : b * p.T;
+  const int nq = G * p.T;                   // query slots per (sequence, kv head)
   const int qi = qg * QN + 4 * sw + w;
-  const bool qok = qi < nq;  // wave-uniform
+  const bool qok = qi < G * Tb;             // wave-uniform
   const int i = qok ? qi / G : 0;
   // staging loads are issued before the LDS stores (float4 granules, loops
   // fully unrolled), so each stage costs one memory latency
@@ -64,13 +66,13 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
   static_assert(KV * 256 * 4 == KC * D && D / 4 <= 64, "staging granules");
   if (lane < D / 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (qok) v = *(const float4*)(p.q + ((size_t)(b * p.T + i) * p.Hq + kvh * G + qi % G) * D + 4 * lane);
+    if (qok) v = *(const float4*)(p.q + ((size_t)(rs + i) * p.Hq + kvh * G + qi % G) * D + 4 * lane);
     *(float4*)(s_q + w * D + 4 * lane) = make_float4(v.x * p.scale, v.y * p.scale, v.z * p.scale, v.w * p.scale);
   }
   float mq = -INFINITY, lq = 0.f, oq[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) oq[e] = 0.f;
-  for (int c0 = 0; c0 < p.T; c0 += KC) {
+  for (int c0 = 0; c0 < Tb; c0 += KC) {
     {
       float4 kv[KV], vv[KV];
 #pragma unroll
@@ -79,8 +81,8 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
         const int t = e4 / (D / 4), d4 = e4 % (D / 4);
         const int jj = c0 + t;
         kv[r] = vv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (jj < p.T) {
-          const size_t src = ((size_t)(b * p.T + jj) * p.Hkv + kvh) * D + 4 * d4;
+        if (jj < Tb) {
+          const size_t src = ((size_t)(rs + jj) * p.Hkv + kvh) * D + 4 * d4;
           kv[r] = *(const float4*)(p.k_suf + src);
           vv[r] = *(const float4*)(p.v_suf + src);
         }
@@ -97,8 +99,8 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
     }
     if (!qok) continue;  // wave-uniform; the barriers above are shared by all
     const int jj = c0 + lane;
-    bool vis = lane < KC && jj < p.T;
-    if (vis) vis = p.anc ? (((p.anc[2 * (b * p.T + i) + (jj >> 6)] >> (jj & 63)) & 1ull) != 0) : (jj <= i);
+    bool vis = lane < KC && jj < Tb;
+    if (vis) vis = p.anc ? (((p.anc[2 * (rs + i) + (jj >> 6)] >> (jj & 63)) & 1ull) != 0) : (jj <= i);
     float sc = -INFINITY;
     if (vis) {
       const float* qr = s_q + w * D;
@@ -175,6 +177,8 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
     attn_suffix<D, QT>(p, kvh, qg, b, s - p.splits, &s_o[0][0]);
     return;
   }
+  const int rs = p.rstart ? p.rstart[b] : b * p.T;
+  const int nqb = G * (p.rlen ? p.rlen[b] : p.T);  // this sequence's queries
   int L = p.kv_len[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   int chunk = (L + p.splits - 1) / p.splits;
@@ -215,9 +219,9 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   for (int qt = 0; qt < QT; ++qt) {
     const int qi = (qg * QT + qt) * 16 + j;
     float qv[DG];
-    if (qi < nq) {
+    if (qi < nqb) {
       const int i = qi / G, gg = qi % G;
-      const float* src = p.q + (((size_t)(b * p.T + i)) * p.Hq + kvh * G + gg) * D + g * DG;
+      const float* src = p.q + (((size_t)(rs + i)) * p.Hq + kvh * G + gg) * D + g * DG;
 #pragma unroll
       for (int e = 0; e < DG; e += 4) {
         float4 v = *(const float4*)(src + e);
@@ -366,14 +370,14 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   for (int e = threadIdx.x; e < QN * D; e += 256) {
     const int qq = e / D, dd = e % D;
     const int qi = (qg * QT) * 16 + qq;
-    if (qi >= nq) continue;
+    if (qi >= nqb) continue;
     const int o2 = qq * OS + dd;
     p.part_o[(pbase + qi) * D + dd] = s_o[0][o2] + s_o[1][o2] + s_o[2][o2] + s_o[3][o2];
   }
   if (threadIdx.x < QN) {
     const int qq = threadIdx.x;
     const int qi = (qg * QT) * 16 + qq;
-    if (qi < nq) {
+    if (qi < nqb) {
       const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
       p.part_ml[2 * (pbase + qi)] = mall;
       p.part_ml[2 * (pbase + qi) + 1] = s_l[0][qq] + s_l[1][qq] + s_l[2][qq] + s_l[3][qq];
@@ -412,8 +416,9 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   const int lane = threadIdx.x & 63, gg = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
   const int nq = G * p.T;
+  if (p.rlen && i >= p.rlen[b]) return;  // ragged: past this sequence's rows
   const int qi = i * G + gg;
-  const int m = b * p.T + i;
+  const int m = (p.rstart ? p.rstart[b] : b * p.T) + i;
   const int ns = p.nsplit;
   const size_t stride = (size_t)p.B * p.Hkv * nq;  // between splits, in queries
   const size_t q0 = ((size_t)b * p.Hkv + kvh) * nq + qi;

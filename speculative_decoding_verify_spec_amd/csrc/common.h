@@ -95,3 +95,4 @@ DEVI float philox_uniform(uint64_t seed, uint64_t round, int b, int slot) {
 #define FLAG_TOKEN_RANGE 1u
 #define FLAG_TREE 2u
 #define FLAG_KV_OVERFLOW 4u
+#define FLAG_LAYOUT 8u

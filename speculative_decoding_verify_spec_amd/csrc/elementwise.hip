@@ -81,7 +81,85 @@ __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
   }
 }
 
+// Ragged (packed) chain rows, DeepSeek-V4 analysis page, section 4 (compact
+// verify): sequence b owns rows cu[b] .. cu[b+1]-1 of the caller's token
+// array, at positions and cache slots kv_len[b] + i; rows cu[B] .. rows-1 pad
+// the launch up to its recorded size (token 0, no cache slot, sequence 0).
+// Workgroup b < B prepares sequence b, workgroup B the padding rows.  An
+// offset array that is not increasing, lengths outside [1, T] or offsets
+// past `rows` set FLAG_LAYOUT; the values are clamped so every later access
+// stays in bounds.
+template <typename WT>
+__global__ __launch_bounds__(256) void prep_ragged_kernel(PrepParams p) {
+  const int b = blockIdx.x;
+  __shared__ int s_start, s_len, s_kv;
+  if (threadIdx.x == 0) {
+    int start, len, kv = 0;
+    if (b < p.B) {
+      const int c0 = p.cu[b], c1 = p.cu[b + 1];
+      start = c0 < 0 ? 0 : (c0 > p.rows ? p.rows : c0);
+      len = c1 - c0;
+      bool bad = c0 < 0 || c1 > p.rows || len < 1 || len > p.T || (b == 0 && c0 != 0);
+      len = len < 0 ? 0 : (len > p.T ? p.T : len);
+      if (start + len > p.rows) len = p.rows - start;
+      if (bad) atomicOr(p.flags, FLAG_LAYOUT);
+      kv = p.kv_len[b];
+      p.kv_copy[b] = kv;
+      p.rstart[b] = start;
+      p.rlen[b] = len;
+      if (kv < 0 || kv > p.max_ctx - len) atomicOr(p.flags, FLAG_KV_OVERFLOW);
+    } else {
+      const int c = p.cu[p.B];
+      start = c < 0 ? 0 : (c > p.rows ? p.rows : c);
+      len = p.rows - start;
+    }
+    s_start = start;
+    s_len = len;
+    s_kv = kv;
+  }
+  __syncthreads();
+  const int start = s_start, len = s_len, kv = s_kv;
+  const bool pad = b == p.B;
+  const int kvc = kv < 0 ? 0 : kv;
+  for (int i = threadIdx.x; i < len; i += blockDim.x) {
+    const int m = start + i;
+    int t = pad ? 0 : p.tokens[m];
+    if (t < 0 || t >= p.vocab) {
+      atomicOr(p.flags, FLAG_TOKEN_RANGE);
+      t = t < 0 ? 0 : p.vocab - 1;
+    }
+    p.tok[m] = t;
+    const int ps = kvc + i;
+    p.pos[m] = pad ? 0 : (ps < p.max_ctx ? ps : p.max_ctx - 1);
+    p.slot[m] = (!pad && kv >= 0 && ps < p.max_ctx) ? ps : -1;
+    p.seq[m] = pad ? 0 : b;
+  }
+  __syncthreads();
+  const WT* E = (const WT*)p.embed;
+  const int per_row = p.d / 8;
+  for (int e = threadIdx.x; e < len * per_row; e += blockDim.x) {
+    const int i = e / per_row, c = (e % per_row) * 8;
+    const WT* src = E + (size_t)p.tok[start + i] * p.d + c;
+    float* dst = p.x + ((size_t)(start + i)) * p.d + c;
+    if constexpr (sizeof(WT) == 2) {
+      const uint4 v = *(const uint4*)src;
+      *(float4*)dst = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+      *(float4*)(dst + 4) = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+    } else {
+      *(float4*)dst = *(const float4*)src;
+      *(float4*)(dst + 4) = *(const float4*)(src + 4);
+    }
+  }
+}
+
 hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
+  if (p.cu) {
+    if (p.wdtype == 1)
+      prep_ragged_kernel<uint16_t><<<p.B + 1, 256, 0, s>>>(p);
+    else
+      prep_ragged_kernel<float><<<p.B + 1, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
   if (p.wdtype == 1)
     prep_embed_kernel<uint16_t><<<p.B, 256, 0, s>>>(p);
   else

@@ -243,7 +243,7 @@ DEVI void epilogue(const GemmParams& p, int rg, const float* tot, const QkvStage
       const int D = p.D, half = D / 2;
       const int hh = r0 / D, i = r0 % D;  // i < D/2
       const int mg = p.m0 + m;            // global row
-      const int bseq = mg / p.T;
+      const int bseq = p.seq ? p.seq[mg] : mg / p.T;
       const int sl = st ? st->slot[m] : p.slot[mg];
       if (hh < p.Hq + p.Hkv) {
         float c, s;

@@ -87,7 +87,7 @@ DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
     const int D = p.D, half = D / 2;
     const int hh = ra / D, i = ra % D;
     const int mg = p.m0 + m;
-    const int bseq = mg / p.T;
+    const int bseq = p.seq ? p.seq[mg] : mg / p.T;
     const int sl = p.slot[mg];
     if (hh < p.Hq + p.Hkv) {
       const int ps = p.pos[mg];

@@ -21,6 +21,15 @@ struct PrepParams {
   float* x;               // [M][d] residual stream, written with the rows' embeddings
   int32_t* kv_copy;       // [B] copy of kv_len for the later kernels of the step
   int B, T, vocab, max_ctx, d;
+  // ragged (packed) rows: cu [B+1] row offsets of the sequences in the
+  // caller's token array (null: B x T rows); rows = padded row count; the
+  // kernel writes each sequence's first row and length and each row's
+  // sequence for the later kernels
+  const int32_t* cu;
+  int rows;
+  int32_t* rstart;        // [B]
+  int32_t* rlen;          // [B]
+  int32_t* seq;           // [rows]
 };
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
 
@@ -59,6 +68,8 @@ struct GemmParams {
   uint16_t* xs;
   size_t xs_elems;
   float* xs_ssq;
+  // QKV epilogue, ragged rows: sequence of each global row (null: row / T)
+  const int32_t* seq;
 };
 constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
@@ -80,6 +91,10 @@ struct AttnParams {
   int B, T, Hq, Hkv, D, max_ctx;
   int splits;              // context workgroups per (sequence, kv head, query group)
   float scale;
+  // ragged rows: first row and length of each sequence (null: b * T, T;
+  // T is then the longest length)
+  const int32_t* rstart;
+  const int32_t* rlen;
 };
 // number of partial slots per query the attention kernel writes: the context
 // splits plus one for the step's own (suffix) keys
@@ -93,6 +108,8 @@ struct CombineParams {
   int nsplit;
   float* out;              // [M][Hq][D]
   int B, T, Hq, Hkv, D;
+  const int32_t* rstart;   // ragged rows, as in AttnParams
+  const int32_t* rlen;
 };
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
 
@@ -130,6 +147,13 @@ struct AcceptParams {
   double* fmass;
   struct SelState* fstate;
   struct SelRule* fres;
+  // ragged layout (null: sequence b has T rows from row b*T, its drafts' q
+  // rows from b*(T-1)): first logits / token row, length, first q row
+  const int32_t* rstart;
+  const int32_t* rlen;
+  const int32_t* qstart;
+  int rows;                // logits (and token) rows: B*T when not ragged
+  int qrows;               // rows of q
 };
 // Running state of one row's radix selection: the key bits chosen so far,
 // the tokens still to take (top-k) or the mass still to reach (top-p; -1

@@ -63,9 +63,19 @@ size_t gemm_xs_elems(const spec_config& c) {
   return Mmax >= 5 ? 2 * Mmax * K : 0;
 }
 
+// Shape of one forward: B sequences, T rows each (ragged: at most T, M rows
+// in all, padding included), a token tree or a chain.
+struct StepShape {
+  int B, T, M;
+  bool tree, ragged;
+  bool operator==(const StepShape& o) const {
+    return B == o.B && T == o.T && M == o.M && tree == o.tree && ragged == o.ragged;
+  }
+};
+
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
+  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
       flags, total;
 };
 
@@ -101,6 +111,9 @@ Layout plan(const spec_config& c) {
   L.slot = take(Mmax * 4);
   L.anc = take(Mmax * 2 * 8);
   L.kvw = take((size_t)c.max_batch * 4);
+  L.rstart = take((size_t)c.max_batch * 4);
+  L.rlen = take((size_t)c.max_batch * 4);
+  L.rseq = take(Mmax * 4);
   L.gpart = take(gemm_part_floats(c) * 4);
   L.gxs = take(gemm_xs_elems(c) * 2);
   L.gssq = take(Mmax * 4);
@@ -144,10 +157,9 @@ struct spec_handle {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
-  // recorded layer sequences, one per (B, T, tree) shape, replayed as HIP graphs
+  // recorded layer sequences, one per step shape, replayed as HIP graphs
   struct Graph {
-    int B, T;
-    bool tree;
+    StepShape sh;
     hipGraphExec_t exec;
     uint64_t used;
   };
@@ -234,10 +246,14 @@ namespace {
 // The per-layer kernels of a step.  They read only the weights, the cache and
 // the workspace (kv_len through its copy made by the prep kernel), so for a
 // given (B, T, chain/tree) the launch sequence is fixed and can be recorded.
-hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s) {
+hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   const spec_config& c = h->cfg;
   const Layout& L = h->lay;
-  const int M = B * T, d = c.d_model, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn;
+  const int B = sh.B, T = sh.T;
+  const bool tree = sh.tree;
+  const int32_t* rstart = sh.ragged ? h->at<int32_t>(L.rstart) : nullptr;
+  const int32_t* rlen = sh.ragged ? h->at<int32_t>(L.rlen) : nullptr;
+  const int M = sh.M, d = c.d_model, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, F = c.d_ffn;
   float* x = h->at<float>(L.x);
   float* q = h->at<float>(L.q);
   float* ks = h->at<float>(L.ksuf);
@@ -271,13 +287,14 @@ hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s)
     gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
     gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
     gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
+    gq.seq = sh.ragged ? h->at<int32_t>(L.rseq) : nullptr;
     if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return e;
 
     AttnParams ap{q, kreg, vreg, kvw, ks, vs, tree ? anc : nullptr, h->at<float>(L.part_o),
-                  h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale};
+                  h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale, rstart, rlen};
     e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
     if (e != hipSuccess) return e;
-    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D};
+    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D, rstart, rlen};
     e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
     if (e != hipSuccess) return e;
 
@@ -303,9 +320,9 @@ hipError_t launch_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s)
 // Replay of the recorded layer sequence for this shape, recorded on first use
 // on the handle's private stream (recording runs nothing).  Returns null when
 // recording or instantiation fails.
-hipGraphExec_t layer_graph(spec_handle* h, int B, int T, bool tree) {
+hipGraphExec_t layer_graph(spec_handle* h, const StepShape& sh) {
   for (auto& g : h->gcache)
-    if (g.B == B && g.T == T && g.tree == tree) {
+    if (g.sh == sh) {
       g.used = ++h->gclock;
       return g.exec;
     }
@@ -314,7 +331,7 @@ hipGraphExec_t layer_graph(spec_handle* h, int B, int T, bool tree) {
     return nullptr;
   }
   if (hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
-  const hipError_t le = launch_layers(h, B, T, tree, h->cap);
+  const hipError_t le = launch_layers(h, sh, h->cap);
   hipGraph_t graph = nullptr;
   const hipError_t ce = hipStreamEndCapture(h->cap, &graph);
   if (le != hipSuccess || ce != hipSuccess || !graph) {
@@ -337,22 +354,22 @@ hipGraphExec_t layer_graph(spec_handle* h, int B, int T, bool tree) {
     hipGraphExecDestroy(h->gcache[old].exec);
     h->gcache.erase(h->gcache.begin() + old);
   }
-  h->gcache.push_back({B, T, tree, ex, ++h->gclock});
+  h->gcache.push_back({sh, ex, ++h->gclock});
   return ex;
 }
 
-spec_status run_layers(spec_handle* h, int B, int T, bool tree, hipStream_t s) {
+spec_status run_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   if (h->graphs && !h->prof) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SPEC_ERR_DEVICE;
     if (cs == hipStreamCaptureStatusNone) {
       // the caller is not recording: replay our own recording
-      hipGraphExec_t ex = layer_graph(h, B, T, tree);
+      hipGraphExec_t ex = layer_graph(h, sh);
       if (!ex) return SPEC_ERR_DEVICE;
       return dev(hipGraphLaunch(ex, s));
     }
   }
-  return dev(launch_layers(h, B, T, tree, s));
+  return dev(launch_layers(h, sh, s));
 }
 
 }  // namespace
@@ -435,31 +452,27 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
   return SPEC_OK;
 }
 
-spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
-                             const int32_t* d_kv_len, const int32_t* d_tree_parent, float* d_logits,
-                             void* stream) {
-  if (!h || !d_tokens || !d_kv_len || !d_logits) return SPEC_ERR_INVALID_ARG;
+namespace {
+
+// The forward of one step: prep + embedding, the recorded layers, the LM head.
+spec_status verify_forward(spec_handle* h, const StepShape& sh, const int32_t* d_tokens, const int32_t* d_kv_len,
+                           const int32_t* d_tree_parent, const int32_t* d_cu, float* d_logits, hipStream_t s) {
   const spec_config& c = h->cfg;
-  if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
-  hipStream_t s = (hipStream_t)stream;
   const Layout& L = h->lay;
-  const int M = B * T, d = c.d_model;
+  const int M = sh.M, d = c.d_model;
   const int V = c.vocab;
   const size_t wb = c.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   float* x = h->at<float>(L.x);
-  int32_t* tok = h->at<int32_t>(L.tok);
-  int32_t* pos = h->at<int32_t>(L.pos);
-  int32_t* slot = h->at<int32_t>(L.slot);
-  uint64_t* anc = h->at<uint64_t>(L.anc);
-  uint32_t* flags = h->at<uint32_t>(L.flags);
   hipError_t e;
 
-  PrepParams pp{d_tokens, d_kv_len, d_tree_parent, tok, pos, slot, anc, flags, h->W(0), c.weight_dtype, x,
-                h->at<int32_t>(L.kvw), B, T, V, c.max_ctx, d};
+  PrepParams pp{d_tokens, d_kv_len, d_tree_parent, h->at<int32_t>(L.tok), h->at<int32_t>(L.pos),
+                h->at<int32_t>(L.slot), h->at<uint64_t>(L.anc), h->at<uint32_t>(L.flags), h->W(0),
+                c.weight_dtype, x, h->at<int32_t>(L.kvw), sh.B, sh.T, V, c.max_ctx, d,
+                d_cu, M, h->at<int32_t>(L.rstart), h->at<int32_t>(L.rlen), h->at<int32_t>(L.rseq)};
   e = timed(h, K_PREP, (double)M * d * (wb + 4), s, [&] { return launch_prep(pp, s); });
   if (e != hipSuccess) return SPEC_ERR_DEVICE;
 
-  spec_status st = run_layers(h, B, T, d_tree_parent != nullptr, s);
+  spec_status st = run_layers(h, sh, s);
   if (st != SPEC_OK) return st;
 
   const float* gf = (const float*)h->W(1 + 6 * (size_t)c.n_layers);
@@ -471,37 +484,93 @@ spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t
   return SPEC_OK;
 }
 
+}  // namespace
+
+spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
+                             const int32_t* d_kv_len, const int32_t* d_tree_parent, float* d_logits,
+                             void* stream) {
+  if (!h || !d_tokens || !d_kv_len || !d_logits) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  return verify_forward(h, StepShape{B, T, B * T, d_tree_parent != nullptr, false}, d_tokens, d_kv_len,
+                        d_tree_parent, nullptr, d_logits, (hipStream_t)stream);
+}
+
+spec_status spec_verify_step_ragged(spec_handle* h, int32_t B, int32_t max_len, int32_t rows,
+                                    const int32_t* d_cu_rows, const int32_t* d_tokens, const int32_t* d_kv_len,
+                                    float* d_logits, void* stream) {
+  if (!h || !d_cu_rows || !d_tokens || !d_kv_len || !d_logits) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (B < 1 || max_len < 1 || B > c.max_batch || max_len > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  if (rows < 1 || rows > c.max_batch * c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  return verify_forward(h, StepShape{B, max_len, rows, false, true}, d_tokens, d_kv_len, nullptr, d_cu_rows,
+                        d_logits, (hipStream_t)stream);
+}
+
+namespace {
+
+// Shared by the chain / tree accept and the ragged chain accept: validate the
+// sampling settings and launch.
+spec_status accept_impl(spec_handle* h, AcceptParams ap, const spec_sampling* sampling, bool need_q,
+                        hipStream_t s) {
+  if (!sampling) return SPEC_ERR_INVALID_ARG;
+  const float temp = sampling->temperature;
+  if (!(temp >= 0.f) || !std::isfinite(temp)) return SPEC_ERR_INVALID_ARG;
+  if (sampling->top_k < 0 || !(sampling->top_p >= 0.f && sampling->top_p <= 1.f)) return SPEC_ERR_INVALID_ARG;
+  if (temp > 0.f && need_q && !ap.q) return SPEC_ERR_INVALID_ARG;
+  if (ap.kv_len_out && !ap.kv_len) return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  const Layout& L = h->lay;
+  ap.temperature = temp; ap.replacement = sampling->tree_replacement ? 1 : 0;
+  ap.seed = sampling->seed; ap.round = sampling->round;
+  ap.rowstat = h->at<float>(L.rowstat); ap.rowms = h->at<float>(L.rowms); ap.rsum = h->at<float>(L.rsum);
+  ap.nacc = h->at<int32_t>(L.nacc); ap.rbuf = h->at<float>(L.rbuf); ap.flags = h->at<uint32_t>(L.flags);
+  ap.kv_cache = h->kv; ap.L = c.n_layers; ap.maxB = c.max_batch; ap.Hkv = c.n_kv_heads; ap.D = c.head_dim;
+  ap.max_ctx = c.max_ctx; ap.V = c.vocab; ap.nch = accept_chunks(c.vocab);
+  ap.top_k = sampling->top_k; ap.top_p = sampling->top_p;
+  ap.fcnt = h->at<uint32_t>(L.fcnt); ap.fmass = h->at<double>(L.fmass);
+  ap.fstate = h->at<SelState>(L.fstate); ap.fres = h->at<SelRule>(L.fres);
+  const double bytes = (double)ap.rows * c.vocab * 4 + (temp > 0 ? (double)ap.qrows * c.vocab * 4 : 0.0);
+  return dev(timed(h, K_ACC, bytes, s, [&] { return launch_accept(ap, s); }));
+}
+
+}  // namespace
+
 spec_status spec_accept(spec_handle* h, int32_t B, int32_t T, const float* d_logits, const float* d_q,
                         const int32_t* d_tokens, const int32_t* d_tree_parent,
                         const spec_sampling* sampling, int32_t* d_out_tokens, int32_t* d_num_accepted,
                         const int32_t* d_kv_len, int32_t* d_kv_len_out, void* stream) {
   if (!h || !d_logits || !d_tokens || !sampling || !d_out_tokens || !d_num_accepted)
     return SPEC_ERR_INVALID_ARG;
-  const float temp = sampling->temperature;
-  if (!(temp >= 0.f) || !std::isfinite(temp)) return SPEC_ERR_INVALID_ARG;
-  if (sampling->top_k < 0 || !(sampling->top_p >= 0.f && sampling->top_p <= 1.f)) return SPEC_ERR_INVALID_ARG;
-  if (temp > 0.f && !d_q && (d_tree_parent || T > 1)) return SPEC_ERR_INVALID_ARG;
-  if (d_kv_len_out && !d_kv_len) return SPEC_ERR_INVALID_ARG;
   const spec_config& c = h->cfg;
   if (B < 1 || T < 1 || B > c.max_batch || T > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
-  const Layout& L = h->lay;
   AcceptParams ap{};
   ap.logits = d_logits; ap.q = d_q; ap.tokens = d_tokens; ap.parent = d_tree_parent;
-  ap.temperature = temp; ap.replacement = sampling->tree_replacement ? 1 : 0;
-  ap.seed = sampling->seed; ap.round = sampling->round;
   ap.out_tokens = d_out_tokens; ap.num_accepted = d_num_accepted; ap.kv_len = d_kv_len;
   ap.kv_len_out = d_kv_len_out;
-  ap.rowstat = h->at<float>(L.rowstat); ap.rowms = h->at<float>(L.rowms); ap.rsum = h->at<float>(L.rsum);
-  ap.nacc = h->at<int32_t>(L.nacc); ap.rbuf = h->at<float>(L.rbuf); ap.flags = h->at<uint32_t>(L.flags);
-  ap.kv_cache = h->kv; ap.L = c.n_layers; ap.maxB = c.max_batch; ap.Hkv = c.n_kv_heads; ap.D = c.head_dim;
-  ap.max_ctx = c.max_ctx; ap.B = B; ap.T = T; ap.V = c.vocab; ap.nch = accept_chunks(c.vocab);
-  ap.top_k = sampling->top_k; ap.top_p = sampling->top_p;
-  ap.fcnt = h->at<uint32_t>(L.fcnt); ap.fmass = h->at<double>(L.fmass);
-  ap.fstate = h->at<SelState>(L.fstate); ap.fres = h->at<SelRule>(L.fres);
-  hipStream_t s = (hipStream_t)stream;
-  const int nq_rows = d_tree_parent ? T : T - 1;
-  const double bytes = (double)B * T * c.vocab * 4 + (temp > 0 ? (double)B * nq_rows * c.vocab * 4 : 0.0);
-  return dev(timed(h, K_ACC, bytes, s, [&] { return launch_accept(ap, s); }));
+  ap.B = B; ap.T = T; ap.rows = B * T; ap.qrows = d_tree_parent ? B * T : B * (T - 1);
+  return accept_impl(h, ap, sampling, d_tree_parent || T > 1, (hipStream_t)stream);
+}
+
+spec_status spec_accept_ragged(spec_handle* h, int32_t B, int32_t max_len, int32_t rows, int32_t q_rows,
+                               const int32_t* d_row_start, const int32_t* d_len, const int32_t* d_q_start,
+                               const float* d_logits, const float* d_q, const int32_t* d_tokens,
+                               const spec_sampling* sampling, int32_t* d_out_tokens, int32_t* d_num_accepted,
+                               const int32_t* d_kv_len, int32_t* d_kv_len_out, void* stream) {
+  if (!h || !d_row_start || !d_len || !d_logits || !d_tokens || !sampling || !d_out_tokens || !d_num_accepted)
+    return SPEC_ERR_INVALID_ARG;
+  const spec_config& c = h->cfg;
+  if (B < 1 || max_len < 1 || B > c.max_batch || max_len > c.max_rows_per_seq) return SPEC_ERR_CAPACITY;
+  if (rows < 1 || rows > c.max_batch * c.max_rows_per_seq || q_rows < 0) return SPEC_ERR_CAPACITY;
+  const bool drafts = max_len > 1;
+  if (sampling->temperature > 0.f && drafts && (!d_q || !d_q_start || q_rows < 1)) return SPEC_ERR_INVALID_ARG;
+  AcceptParams ap{};
+  ap.logits = d_logits; ap.q = d_q; ap.tokens = d_tokens; ap.parent = nullptr;
+  ap.out_tokens = d_out_tokens; ap.num_accepted = d_num_accepted; ap.kv_len = d_kv_len;
+  ap.kv_len_out = d_kv_len_out;
+  ap.B = B; ap.T = max_len; ap.rows = rows; ap.qrows = q_rows;
+  ap.rstart = d_row_start; ap.rlen = d_len; ap.qstart = d_q_start;
+  return accept_impl(h, ap, sampling, drafts, (hipStream_t)stream);
 }
 
 spec_status spec_device_errors(spec_handle* h, uint32_t* flags, void* stream) {

@@ -5,9 +5,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (make_config, spec_accept, spec_device_errors, spec_graph_enable, spec_kv_cache_bytes,
-               spec_profile_gemm, spec_sampling, spec_verify_destroy, spec_verify_init,
-               spec_verify_step, spec_workspace_bytes)
+from . import (make_config, spec_accept, spec_accept_ragged, spec_device_errors, spec_graph_enable,
+               spec_kv_cache_bytes, spec_profile_gemm, spec_sampling, spec_verify_destroy, spec_verify_init,
+               spec_verify_step, spec_verify_step_ragged, spec_workspace_bytes)
 
 
 class VerifyEngine:
@@ -31,6 +31,24 @@ class VerifyEngine:
     def step(self, tokens, kv_len, logits, tree_parent=None):
         B, T = tokens.shape
         return spec_verify_step(self.handle, B, T, tokens, kv_len, tree_parent, logits, self.stream)
+
+    def step_ragged(self, cu_rows, max_len, tokens, kv_len, logits):
+        """Compact verify: cu_rows [B+1] int32 row offsets; tokens [rows]; logits
+        [rows, V] with rows >= cu_rows[B] (the padded execution tier)."""
+        B = cu_rows.shape[0] - 1
+        return spec_verify_step_ragged(self.handle, B, max_len, tokens.shape[0], cu_rows, tokens, kv_len, logits,
+                                       self.stream)
+
+    def accept_ragged(self, row_start, lens, q_start, max_len, logits, q, tokens, out_tokens, num_accepted,
+                      kv_len, kv_len_out=None, temperature=1.0, seed=0, round_=0, top_k=0, top_p=1.0):
+        """Ragged chain accept: sequence b has lens[b] rows from logits / token
+        row row_start[b], its drafts' q rows from q_start[b]."""
+        B = row_start.shape[0]
+        smp = spec_sampling(float(temperature), 0, int(seed), int(round_), int(top_k), float(top_p))
+        q_rows = 0 if q is None else q.reshape(-1, q.shape[-1]).shape[0]
+        return spec_accept_ragged(self.handle, B, max_len, logits.reshape(-1, logits.shape[-1]).shape[0], q_rows,
+                                  row_start, lens, q_start, logits, q, tokens, smp, out_tokens, num_accepted,
+                                  kv_len, kv_len_out, self.stream)
 
     def accept(self, logits, q, tokens, out_tokens, num_accepted, kv_len, kv_len_out=None,
                tree_parent=None, temperature=1.0, seed=0, round_=0, replacement=False, top_k=0, top_p=1.0):
