@@ -91,6 +91,10 @@ def parse():
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p adjustment of the target (1: off); the synthetic drafts stay unadjusted")
     ap.add_argument("--rounds", type=int, default=8, help="distinct pre-drafted rounds cycled")
+    ap.add_argument("--ragged-lens", type=str, default="",
+                    help="comma-separated per-sequence verify lengths (one per sequence of --batch): also time "
+                         "the compact ragged forward against the fixed-width one")
+    ap.add_argument("--ragged-tier", type=int, default=8, help="packed rows are padded to a multiple of this")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -221,6 +225,34 @@ def main():
     c_v = t_verify / t_decode
     log(f"T_verify({T}) {t_verify:.3f} ms, T_decode(1) {t_decode:.3f} ms, c = {c_v:.3f}")
 
+    # ---- ragged verify: compact forward of the packed lengths (padded to the
+    # execution tier) against the fixed-width forward at T = max length
+    ragged = None
+    if a.ragged_lens:
+        lens = [int(x) for x in a.ragged_lens.split(",")]
+        assert len(lens) == B and all(1 <= n <= T for n in lens), "one length in [1, gamma+1] per sequence"
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        rows = int(-(-int(cu[-1]) // a.ragged_tier) * a.ragged_tier)
+        cu_d = torch.from_numpy(cu).to(dev)
+        tok_r = torch.cat([rounds[0][0][b, :lens[b]] for b in range(B)]
+                          + [rounds[0][0][0, :1].expand(rows - int(cu[-1]))]).contiguous()
+        lg_r = torch.empty((rows, sh.vocab), device=dev)
+        for _ in range(3):
+            eng.step_ragged(cu_d, max(lens), tok_r, kv_len, lg_r)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            eng.step_ragged(cu_d, max(lens), tok_r, kv_len, lg_r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_compact = e0.elapsed_time(e1) / iters
+        ragged = {"lens": lens, "total_verify_tokens": int(cu[-1]), "graph_num_tokens": rows,
+                  "t_compact_ms": round(t_compact, 4), "t_fixed_width_ms": round(t_verify, 4),
+                  "fixed_width_rows": B * T}
+        log(f"ragged lens {lens}: compact {t_compact:.3f} ms ({rows} rows) vs fixed width {t_verify:.3f} ms "
+            f"({B * T} rows)")
+
     # ---- roofline of the dominant kernel (the gate/up GEMM, the largest weight
     # stream): its launches for all 32 layers back to back at the verify's
     # B*T rows, bracketed by one pair of HIP events on the launch stream
@@ -259,6 +291,8 @@ def main():
         "tokens_per_round": round(float((n_timed + 1).mean()), 4),
         "kernels": kernels, "roofline": roofline,
     }
+    if ragged is not None:
+        result["ragged"] = ragged
 
     if a.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a, kv_len)
