@@ -418,15 +418,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
 // a row group.  Against the vector-ALU kernel this removes the widening of
 // the weights and three quarters of the multiply-add issue, which is what
 // makes the cost of a group grow with M there.
-template <int MT, int EPI, bool NORM, int CPW, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
+template <int MT, int EPI, bool NORM, int CPW, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_mfma_kernel(GemmParams p) {
   constexpr int MG = (MT + 3) / 4;  // sets of 4 activation rows
   constexpr int RG = YT / 4;        // sets of 4 weight rows per group
   constexpr int NV = YT * MT;
   static_assert(!SPLIT || (!NORM && EPI == EPI_RESID), "K is split only for residual GEMMs");
-  __shared__ float red[KSTAT_WAVES][YT][4 * MG];
+  __shared__ float red[NW][YT][4 * MG];
   __shared__ float tot[64];
-  __shared__ float ssq[KSTAT_WAVES][4 * MG];
+  __shared__ float ssq[NW][4 * MG];
   __shared__ QkvStage<(EPI == EPI_QKV) ? MT : 1> qst;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 3, blk = lane >> 2;
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
   bool cok[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    const int c = w + KSTAT_WAVES * i;
+    const int c = w + NW * i;
     cok[i] = c < nch;
     kofs[i] = kbase + (cok[i] ? c : 0) * 128 + 8 * blk;
   }
@@ -563,9 +563,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmParams p) {
     lds_barrier();
     if (threadIdx.x < NV) {
       const int y = threadIdx.x / MT, m = threadIdx.x % MT;
-      float t = red[0][y][m] + red[1][y][m] + red[2][y][m] + red[3][y][m];
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) t += red[i][y][m];
       if constexpr (NORM) {
-        const float q = ssq[0][m] + ssq[1][m] + ssq[2][m] + ssq[3][m];
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) q += ssq[i][m];
         t *= 1.0f / sqrtf(q / (float)p.K + p.eps);
       }
       tot[threadIdx.x] = t;
@@ -669,10 +673,10 @@ bool gemm_use_mfma(const GemmParams& p, int rows) {
   return rows >= 5 || (rows >= 3 && elems >= 64.0 * 1024 * 1024);
 }
 
-template <int MT, int EPI, int CPW>
+template <int MT, int EPI, int CPW, int NW>
 static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
-  if (p.norm_g) gemm_mfma_kernel<MT, EPI, true, CPW, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else gemm_mfma_kernel<MT, EPI, false, CPW, false><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  if (p.norm_g) gemm_mfma_kernel<MT, EPI, true, CPW, false, NW><<<grid, 64 * NW, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI, false, CPW, false, NW><<<grid, 64 * NW, 0, s>>>(p);
 }
 
 // A residual GEMM over a long K (the down projection) at M >= 3: the
@@ -694,9 +698,9 @@ static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
   const int rounds = (groups + slots - 1) / slots;
   const dim3 grid((groups + rounds - 1) / rounds, GEMM_KSPLIT);
   const int cpw = ((p.K / GEMM_KSPLIT >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
-  if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
   gemm_split_reduce_kernel<<<(p.M * p.N + 255) / 256, 256, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -715,10 +719,21 @@ static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
     if (gemm_use_split(p)) return launch_split<MT>(p, s);
   }
   if (gemm_use_mfma(p, p.M)) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE) {
+      // the two largest weight streams take 8 waves of 4 chunks: gate/up
+      // with one workgroup per CU (39.6 -> 38.2 us at 4 rows), the LM head
+      // with three (171.6 -> 166 us)
+      if (p.K <= 8 * 4 * 128) {
+        const int slots8 = (EPI == EPI_SWIGLU ? 1 : 3) * device_cus();
+        const int rounds8 = (groups + slots8 - 1) / slots8;
+        launch_mfma_cpw<MT, EPI, 4, 8>(p, (groups + rounds8 - 1) / rounds8, s);
+        return hipGetLastError();
+      }
+    }
     const int cpw = ((p.K >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
-    if (cpw <= 2) launch_mfma_cpw<MT, EPI, 2>(p, grid, s);
-    else if (cpw <= 4) launch_mfma_cpw<MT, EPI, 4>(p, grid, s);
-    else launch_mfma_cpw<MT, EPI, 8>(p, grid, s);
+    if (cpw <= 2) launch_mfma_cpw<MT, EPI, 2, KSTAT_WAVES>(p, grid, s);
+    else if (cpw <= 4) launch_mfma_cpw<MT, EPI, 4, KSTAT_WAVES>(p, grid, s);
+    else launch_mfma_cpw<MT, EPI, 8, KSTAT_WAVES>(p, grid, s);
   } else if (gemm_is_kstat(p.K)) {
     if constexpr (EPI == EPI_QKV || EPI == EPI_RESID) {
       // the smaller projections (QKV, O) ramp up faster with 8 waves of one K
