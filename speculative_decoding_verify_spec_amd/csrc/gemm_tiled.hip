@@ -124,15 +124,18 @@ DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
 
 // Activations for the tiled kernel: X (fp32, times the RMSNorm gain when
 // NORM) split into bf16 hi and lo planes [2][M][K], and each row's sum of
-// squares.  One workgroup per row.
+// squares in SSQ_BLK partial sums (one per 1024 k, added in a fixed order by
+// row_factor).  One workgroup per (1024 k, row), one float4 per thread, so
+// the whole pass costs one memory latency.
 template <bool NORM>
 __global__ __launch_bounds__(256) void gemm_split_x_kernel(GemmParams p) {
-  const int m = blockIdx.x;
+  const int blk = blockIdx.x, m = blockIdx.y;
   const float* x = p.X + (size_t)m * p.ldx;
   uint16_t* hi = p.xs + (size_t)m * p.K;
   uint16_t* lo = hi + (size_t)p.M * p.K;
   float ss = 0.f;
-  for (int k = 4 * threadIdx.x; k < p.K; k += 1024) {
+  const int k = blk * 1024 + 4 * threadIdx.x;
+  if (k < p.K) {
     const float4 v = *(const float4*)(x + k);
     float xv[4] = {v.x, v.y, v.z, v.w};
     if (NORM) {
@@ -160,8 +163,16 @@ __global__ __launch_bounds__(256) void gemm_split_x_kernel(GemmParams p) {
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    if (threadIdx.x == 0) p.xs_ssq[m] = red[0] + red[1] + red[2] + red[3];
+    if (threadIdx.x == 0) p.xs_ssq[m * SSQ_BLK + blk] = red[0] + red[1] + red[2] + red[3];
   }
+}
+
+// RMSNorm factor of activation row m from its partial sums of squares
+DEVI float row_factor(const GemmParams& p, int m) {
+  const int nblk = (p.K + 1023) / 1024;
+  float q = 0.f;
+  for (int b = 0; b < nblk; ++b) q += p.xs_ssq[m * SSQ_BLK + b];
+  return 1.0f / sqrtf(q / (float)p.K + p.eps);
 }
 
 // LDS tile rows are 128 bytes (64 bf16 of k) in eight 16-byte chunks; chunk
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
           dst[1] = b;
         } else {
           if constexpr (NORM) {
-            const float f = 1.0f / sqrtf(p.xs_ssq[m] / (float)p.K + p.eps);
+            const float f = row_factor(p, m);
             a *= f;
             b *= f;
           }
@@ -385,11 +396,44 @@ __global__ __launch_bounds__(256) void gemm_tiled_finish_kernel(GemmParams p, in
     b += src[1];
   }
   if (NORM) {
-    const float f = 1.0f / sqrtf(p.xs_ssq[m] / (float)p.K + p.eps);
+    const float f = row_factor(p, m);
     a *= f;
     b *= f;
   }
   epilogue_pair<EPI>(p, m, j, a, b);
+}
+
+// Finish of a library GEMM over the stacked planes: d [2M][ldd] holds the
+// products of the hi rows (0 .. M-1) and of the lo rows (M .. 2M-1) with
+// every weight row.  Adds the two, applies the RMSNorm row factor and the
+// epilogue.  One thread per (row, pair).
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256) void gemm_blas_finish_kernel(GemmParams p, const float* d, int ldd) {
+  const int npairs = pair_count<EPI>(p);
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (size_t)p.M * npairs) return;
+  const int m = (int)(e / npairs), j = (int)(e % npairs);
+  int rb;
+  const int ra = pair_rows<EPI>(p, j, rb);
+  const float* hi = d + (size_t)m * ldd;
+  const float* lo = d + (size_t)(p.M + m) * ldd;
+  float a = ra < ldd ? hi[ra] + lo[ra] : 0.f;
+  float b = rb < ldd ? hi[rb] + lo[rb] : 0.f;
+  if (NORM) {
+    const float f = row_factor(p, m);
+    a *= f;
+    b *= f;
+  }
+  epilogue_pair<EPI>(p, m, j, a, b);
+}
+
+template <int EPI>
+static hipError_t launch_blas_finish_epi(const GemmParams& p, const float* d, int ldd, hipStream_t s) {
+  const size_t n = (size_t)p.M * pair_count<EPI>(p);
+  const int blocks = (int)((n + 255) / 256);
+  if (p.norm_g) gemm_blas_finish_kernel<EPI, true><<<blocks, 256, 0, s>>>(p, d, ldd);
+  else gemm_blas_finish_kernel<EPI, false><<<blocks, 256, 0, s>>>(p, d, ldd);
+  return hipGetLastError();
 }
 
 template <int MB, int KW, int EPI>
@@ -404,8 +448,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
          (size_t)2 * nsplit * p.M * pair_count<EPI>(p) * 2 <= p.part_floats)
     nsplit *= 2;
   const bool norm = p.norm_g != nullptr;
-  if (norm) gemm_split_x_kernel<true><<<p.M, 256, 0, s>>>(p);
-  else gemm_split_x_kernel<false><<<p.M, 256, 0, s>>>(p);
+  launch_split_x(p, s);
   const dim3 grid(tiles_n, tiles_m, nsplit);
   if (nsplit == 1) {
     if (norm) gemm_tiled_kernel<MB, KW, R, EPI, true, false><<<grid, 256, 0, s>>>(p);
@@ -436,8 +479,24 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t s) {
 // tiled kernel beats the skinny matrix-core kernel on the QKV, gate/up and LM
 // head GEMMs (gate/up 48 vs 58 us at 5..8 rows); the residual GEMMs (O, down)
 // gain only beyond 8 rows.
+hipError_t launch_split_x(const GemmParams& p, hipStream_t s) {
+  const dim3 grid((p.K + 1023) / 1024, p.M);
+  if (p.norm_g) gemm_split_x_kernel<true><<<grid, 256, 0, s>>>(p);
+  else gemm_split_x_kernel<false><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_blas_finish(const GemmParams& p, const float* d, int ldd, hipStream_t s) {
+  switch (p.epi) {
+    case EPI_STORE: return launch_blas_finish_epi<EPI_STORE>(p, d, ldd, s);
+    case EPI_RESID: return launch_blas_finish_epi<EPI_RESID>(p, d, ldd, s);
+    case EPI_SWIGLU: return launch_blas_finish_epi<EPI_SWIGLU>(p, d, ldd, s);
+    default: return launch_blas_finish_epi<EPI_QKV>(p, d, ldd, s);
+  }
+}
+
 bool gemm_tiled_ok(const GemmParams& p) {
-  if (p.wdtype != 1 || p.K % TK || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;
+  if (p.wdtype != 1 || p.K % TK || p.K > SSQ_BLK * 1024 || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;
   return p.M > 8 || (p.M >= 5 && p.epi != EPI_RESID);
 }
 

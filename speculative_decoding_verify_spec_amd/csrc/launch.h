@@ -67,15 +67,33 @@ struct GemmParams {
   // elements available) and their rows' sums of squares [M]
   uint16_t* xs;
   size_t xs_elems;
-  float* xs_ssq;
+  float* xs_ssq;          // [M][SSQ_BLK] partial sums of squares per 1024 k
   // QKV epilogue, ragged rows: sequence of each global row (null: row / T)
   const int32_t* seq;
+  // many rows: the library GEMM path (null: not available)
+  struct BlasCtx* blas;
 };
 constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
+constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
 bool gemm_tiled_ok(const GemmParams& p);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);
+// the activation planes of the tiled kernel ([2][M][K] in p.xs, row sums of
+// squares in p.xs_ssq), and the finish of a library GEMM over them
+hipError_t launch_split_x(const GemmParams& p, hipStream_t s);
+hipError_t launch_blas_finish(const GemmParams& p, const float* d, int ldd, hipStream_t s);
+// Many-row GEMMs through hipBLASLt (gemm_blas.hip): one plain bf16 GEMM of
+// the stacked hi / lo activation planes against the weights into fp32
+// scratch, then the finish kernel.  blas_create borrows the library's
+// workspace and the fp32 scratch; algorithms are chosen per shape on first
+// use, by timing when `tune` is set (never while the stream is recording).
+struct BlasCtx;
+BlasCtx* blas_create(void* ws, size_t ws_bytes, float* d, size_t d_floats);
+void blas_destroy(BlasCtx* ctx);
+bool gemm_blas_ok(const GemmParams& p);
+bool blas_ready(const BlasCtx* c);  // the library handle exists (created by a tuning call)
+hipError_t launch_gemm_blas(const GemmParams& p, hipStream_t s, bool tune);
 
 // ---------------------------------------------------------------- attention
 struct AttnParams {

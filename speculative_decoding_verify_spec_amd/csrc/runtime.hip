@@ -63,6 +63,20 @@ size_t gemm_xs_elems(const spec_config& c) {
   return Mmax >= 5 ? 2 * Mmax * K : 0;
 }
 
+// The library GEMM path for 64 or more rows: its workspace and the fp32
+// product scratch [2 rows][weight rows] for up to 256 rows per launch.
+size_t blas_ws_bytes(const spec_config& c) {
+  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
+  return (Mmax >= 64 && c.weight_dtype == SPEC_DTYPE_BF16) ? ((size_t)64 << 20) : 0;
+}
+size_t blas_d_floats(const spec_config& c) {
+  if (!blas_ws_bytes(c)) return 0;
+  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
+  const size_t nw = std::max<size_t>(std::max<size_t>(2 * (size_t)c.d_ffn, (size_t)c.vocab),
+                                     (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim);
+  return 2 * std::min<size_t>(Mmax, 256) * nw;
+}
+
 // Shape of one forward: B sequences, T rows each (ragged: at most T, M rows
 // in all, padding included), a token tree or a chain.
 struct StepShape {
@@ -75,7 +89,7 @@ struct StepShape {
 
 struct Layout {
   size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
+  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, gbws, gbd, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
       flags, total;
 };
 
@@ -116,7 +130,9 @@ Layout plan(const spec_config& c) {
   L.rseq = take(Mmax * 4);
   L.gpart = take(gemm_part_floats(c) * 4);
   L.gxs = take(gemm_xs_elems(c) * 2);
-  L.gssq = take(Mmax * 4);
+  L.gssq = take(Mmax * SSQ_BLK * 4);
+  L.gbws = take(blas_ws_bytes(c));
+  L.gbd = take(blas_d_floats(c) * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
@@ -164,6 +180,8 @@ struct spec_handle {
     uint64_t used;
   };
   bool graphs = true;
+  bool recording = false;     // launches are being recorded: no library tuning
+  BlasCtx* blas = nullptr;    // library GEMMs for 64 or more rows
   hipStream_t cap = nullptr;  // private stream used only to record
   std::vector<Graph> gcache;
   uint64_t gclock = 0;
@@ -215,9 +233,18 @@ hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s
   p.xs = h->at<uint16_t>(h->lay.gxs);
   p.xs_elems = gemm_xs_elems(h->cfg);
   p.xs_ssq = h->at<float>(h->lay.gssq);
+  p.blas = h->blas;
   {
     GemmParams q = p;
     q.M = M;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool tune = !h->recording && hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+    if (gemm_blas_ok(q) && (tune || blas_ready(h->blas))) {
+      // many rows: one library GEMM of the stacked activation planes
+      const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
+                           (double)M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
+      return timed(h, cls, bytes, s, [&] { return launch_gemm_blas(q, s, tune); });
+    }
     if (gemm_tiled_ok(q)) {
       // many rows: one tiled launch reads the weights once per 128 rows
       const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
@@ -351,7 +378,7 @@ hipGraphExec_t layer_graph(spec_handle* h, const StepShape& sh) {
       hipGraphExecDestroy(ex);
       return nullptr;
     }
-    hipGraphExecDestroy(h->gcache[old].exec);
+    if (h->gcache[old].exec) hipGraphExecDestroy(h->gcache[old].exec);
     h->gcache.erase(h->gcache.begin() + old);
   }
   h->gcache.push_back({sh, ex, ++h->gclock});
@@ -363,10 +390,26 @@ spec_status run_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SPEC_ERR_DEVICE;
     if (cs == hipStreamCaptureStatusNone) {
-      // the caller is not recording: replay our own recording
-      hipGraphExec_t ex = layer_graph(h, sh);
-      if (!ex) return SPEC_ERR_DEVICE;
-      return dev(hipGraphLaunch(ex, s));
+      // the caller is not recording: replay our own recording of this shape
+      for (auto& g : h->gcache)
+        if (g.sh == sh) {
+          g.used = ++h->gclock;
+          // a shape whose recording failed stays on direct launches
+          return g.exec ? dev(hipGraphLaunch(g.exec, s)) : dev(launch_layers(h, sh, s));
+        }
+      // first step of this shape: launch directly (the library GEMMs of
+      // many-row shapes choose their algorithms here), then record the same
+      // sequence for the next steps; recording runs nothing
+      spec_status st = dev(launch_layers(h, sh, s));
+      if (st != SPEC_OK) return st;
+      h->recording = true;
+      const hipGraphExec_t ex = layer_graph(h, sh);
+      h->recording = false;
+      if (!ex) {
+        hipGetLastError();  // clear a capture error; this shape keeps direct launches
+        h->gcache.push_back({sh, nullptr, ++h->gclock});
+      }
+      return SPEC_OK;
     }
   }
   return dev(launch_layers(h, sh, s));
@@ -427,6 +470,8 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
   h->kv = (uint16_t*)d_kv_cache;
   h->ws = (char*)d_workspace;
   h->lay = L;
+  if (blas_ws_bytes(*cfg))
+    h->blas = blas_create(h->at<void>(L.gbws), blas_ws_bytes(*cfg), h->at<float>(L.gbd), blas_d_floats(*cfg));
 
   // rotary tables: angle = pos * theta^(-2i/D), evaluated in double
   const int D = cfg->head_dim, half = D / 2;
@@ -445,6 +490,7 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
   if (e == hipSuccess) e = hipMemsetAsync(h->at<uint32_t>(L.flags), 0, 256, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
+    blas_destroy(h->blas);
     delete h;
     return SPEC_ERR_DEVICE;
   }
@@ -690,8 +736,10 @@ void spec_verify_destroy(spec_handle* h) {
   }
   for (auto e : h->pool) hipEventDestroy(e);
   if (!h->gcache.empty()) hipDeviceSynchronize();  // a replay may still be running
-  for (auto& g : h->gcache) hipGraphExecDestroy(g.exec);
+  for (auto& g : h->gcache)
+    if (g.exec) hipGraphExecDestroy(g.exec);
   if (h->cap) hipStreamDestroy(h->cap);
+  blas_destroy(h->blas);
   delete h;
 }
 
