@@ -24,7 +24,7 @@ def _step(eng, tokens, kv, parent=None):
 
 def _written(cache, sh, tokens, kv, max_ctx):
     """The cache slots a step over `tokens` writes: [kv_len, kv_len + T) per sequence."""
-    k, v = synth.kv_views(cache, sh, 3, max_ctx)
+    k, v = synth.kv_views(cache, sh, 4, max_ctx)
     T = tokens.shape[1]
     out = []
     for b, L in enumerate(kv.tolist()):
@@ -36,7 +36,7 @@ def _written(cache, sh, tokens, kv, max_ctx):
 def test_graph_replay_matches_direct_launches():
     sh = synth.MINI8B
     max_ctx = 512
-    eng, names, w, cache = build_engine(sh, 3, max_ctx, 16, ctx_len=[200, 31, 0])
+    eng, names, w, cache = build_engine(sh, 4, max_ctx, 16, ctx_len=[200, 31, 0, 77])
     shapes = [
         (synth.make_tokens(2, 4, sh.vocab, seed=11, device=dev()),
          torch.tensor([200, 31], dtype=torch.int32, device=dev()), None),
@@ -45,6 +45,9 @@ def test_graph_replay_matches_direct_launches():
         (synth.make_tokens(3, 7, sh.vocab, seed=13, device=dev()),
          torch.tensor([200, 31, 0], dtype=torch.int32, device=dev()),
          synth.random_tree([2, 2], 3).to(dev())),
+        # 64 rows: the library GEMM path inside the recording
+        (synth.make_tokens(4, 16, sh.vocab, seed=14, device=dev()),
+         torch.tensor([200, 31, 0, 77], dtype=torch.int32, device=dev()), None),
     ]
     # direct launches first: the reference logits and cache bytes per shape
     eng.graphs(False)
