@@ -13,7 +13,8 @@
 // same way; accumulation is fp32.  V is stored transposed in the cache so the
 // key index (the contraction of P V) is contiguous.  A wave's first key block
 // is requested before the queries are prepared, so the cache reads and the
-// query reads overlap.
+// query reads overlap, and each next block is requested as soon as the
+// current one is converted into matrix operands.
 //
 // Suffix part: 4*QT more workgroups per (sequence, KV head, query group), one
 // wave per query, attend to the step's own keys in fp32 (chain: rows 0..i;
@@ -29,7 +30,9 @@
 
 namespace sv {
 
-int attn_query_tiles_per_wave(int nq) { return 1; }
+// Query groups (16 query vectors) per context workgroup: two when there are
+// at least two, so that both groups' waves read each key block on one CU.
+int attn_groups_per_wg(int nq) { return nq > 16 ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
@@ -140,8 +143,8 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
   }
 }
 
-template <int D, int QT>
-__global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
+template <int D, int QT, int QGW>
+__global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
   constexpr int DG = D / 4;   // dims per lane group
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 16;  // output dim tiles
@@ -149,20 +152,27 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   const int j = lane & 15, g = lane >> 4;
   const int G = p.Hq / p.Hkv;
   const int nq = G * p.T;
-  // Workgroup placement.  Workgroups are dispatched round-robin over the 8
-  // XCDs (each with its own L2), in launch order.  The query groups of one
-  // (sequence, KV head, split) read the same keys and values, so they are
-  // given ids that land on the same XCD one after another: unit u = (split,
-  // kv head, sequence) goes to XCD u % 8, and its query groups take
-  // consecutive places in that XCD's sequence.
-  const int ncol = p.splits + 4 * QT;            // context splits + suffix workgroups
+  // Query groups of 16 query vectors.  A context workgroup serves QGW of
+  // them: its waves form QGW sets of WPG waves, set q holding group
+  // QGW * qgw + q, and the sets walk the same key blocks, so each block is
+  // fetched from HBM once per workgroup (the second set's reads hit the CU's
+  // cache).
+  constexpr int WPG = 4 / QGW;  // waves per query group
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
+  const int nqw = (nqg + QGW - 1) / QGW;           // query-group sets
+  // Workgroup placement.  Workgroups are dispatched round-robin over the 8
+  // XCDs (each with its own L2), in launch order.  The query-group sets of
+  // one (sequence, KV head, split) read the same keys and values, so they
+  // are given ids that land on the same XCD one after another: unit u =
+  // (split, kv head, sequence) goes to XCD u % 8, and its sets take
+  // consecutive places in that XCD's sequence.
+  const int ncol = p.splits + 4 * QT * QGW;        // context splits + suffix workgroups
   const int units = ncol * p.Hkv * p.B;
   const int id = blockIdx.x;
   const int n = id / 8;
-  const int u = (n / nqg) * 8 + id % 8;
+  const int u = (n / nqw) * 8 + id % 8;
   if (u >= units) return;  // padding of the last XCD round
-  const int qg = n % nqg;
+  const int qgw = n % nqw;
   const int s = u % ncol;
   const int kvh = (u / ncol) % p.Hkv;
   const int b = u / (ncol * p.Hkv);
@@ -174,9 +184,14 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   __shared__ float s_o[4][QN * OS];
   static_assert(4 * D + 2 * 16 * (D + 4) <= 4 * QN * OS, "suffix staging must fit the output stage");
   if (s >= p.splits) {  // the step's own keys; the output stage is its scratch
-    attn_suffix<D, QT>(p, kvh, qg, b, s - p.splits, &s_o[0][0]);
+    const int sw = s - p.splits;
+    const int grp = qgw * QGW + sw / (4 * QT);
+    if (grp >= nqg) return;
+    attn_suffix<D, QT>(p, kvh, grp, b, sw % (4 * QT), &s_o[0][0]);
     return;
   }
+  const int qsub = w / WPG, kw = w % WPG;
+  const int qg = qgw * QGW + qsub;  // this wave's query group
   const int rs = p.rstart ? p.rstart[b] : b * p.T;
   const int nqb = G * (p.rlen ? p.rlen[b] : p.T);  // this sequence's queries
   int L = p.kv_len[b];
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
       vraw[dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
     }
   };
-  int kb = kbeg + 32 * w;
+  int kb = kbeg + 32 * kw;
   if (kb < kend) load_block(kb);
 
   // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (; kb < kend; kb += 128) {
+  for (; kb < kend; kb += 32 * WPG) {
     // ---- K operand (A of S^T): lane row j of tile kt is key blk_key(kb, kt, j)
     shortx4 ka[2][KSTEPS];
 #pragma unroll
@@ -285,6 +300,11 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
         }
       }
     }
+    // the wave's next block (long contexts) is requested as soon as this
+    // one's raw registers are converted, so its latency overlaps this block's
+    // products; two workgroups per CU still fit (238 VGPRs, no spills),
+    // measured at 32K context: 440 -> 409 us at T = 1, 682 -> 599 us at T = 8
+    if (kb + 32 * WPG < kend) load_block(kb + 32 * WPG);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       floatx4 st[2];
@@ -336,13 +356,10 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
         }
       }
     }
-    // the wave's next block (long contexts) is requested once this one's
-    // operands are consumed, which keeps the raw and converted copies from
-    // being live together
-    if (kb + 128 < kend) load_block(kb + 128);
   }
 
-  // ---- merge the four waves' states in LDS and write one partial per query
+  // ---- merge the waves of each query group in LDS and write one partial
+  // per query
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     float l = lrun[qt];
@@ -352,10 +369,13 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
     if (g == 0) s_m[w][qt * 16 + j] = mrun[qt];
   }
   __syncthreads();
+  const int w0 = qsub * WPG;  // first wave of this wave's group
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qq = qt * 16 + j;
-    const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+    float mall = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < WPG; ++i) mall = fmaxf(mall, s_m[w0 + i][qq]);
     // a wave that saw no key has m = -inf and contributes nothing
     const float f = (mrun[qt] == -INFINITY) ? 0.f : __expf(mrun[qt] - mall);
     if (g == 0) s_l[w][qq] = lrun[qt] * f;
@@ -367,39 +387,50 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(AttnParams p) {
   }
   __syncthreads();
   const size_t pbase = (((size_t)s * p.B + b) * p.Hkv + kvh) * nq;
-  for (int e = threadIdx.x; e < QN * D; e += 256) {
-    const int qq = e / D, dd = e % D;
-    const int qi = (qg * QT) * 16 + qq;
+  for (int e = threadIdx.x; e < QGW * QN * D; e += 256) {
+    const int grp = e / (QN * D), r = e % (QN * D);
+    const int qq = r / D, dd = r % D;
+    const int qi = ((qgw * QGW + grp) * QT) * 16 + qq;
     if (qi >= nqb) continue;
     const int o2 = qq * OS + dd;
-    p.part_o[(pbase + qi) * D + dd] = s_o[0][o2] + s_o[1][o2] + s_o[2][o2] + s_o[3][o2];
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPG; ++i) t += s_o[grp * WPG + i][o2];
+    p.part_o[(pbase + qi) * D + dd] = t;
   }
-  if (threadIdx.x < QN) {
-    const int qq = threadIdx.x;
-    const int qi = (qg * QT) * 16 + qq;
+  if (threadIdx.x < QGW * QN) {
+    const int grp = threadIdx.x / QN, qq = threadIdx.x % QN;
+    const int qi = ((qgw * QGW + grp) * QT) * 16 + qq;
     if (qi < nqb) {
-      const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+      float mall = -INFINITY, lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPG; ++i) {
+        mall = fmaxf(mall, s_m[grp * WPG + i][qq]);
+        lsum += s_l[grp * WPG + i][qq];
+      }
       p.part_ml[2 * (pbase + qi)] = mall;
-      p.part_ml[2 * (pbase + qi) + 1] = s_l[0][qq] + s_l[1][qq] + s_l[2][qq] + s_l[3][qq];
+      p.part_ml[2 * (pbase + qi) + 1] = lsum;
     }
   }
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nq = (p.Hq / p.Hkv) * p.T;
-  const int QT = attn_query_tiles_per_wave(nq);
-  const int nqg = (nq + 16 * QT - 1) / (16 * QT);
+  const int nqg = (nq + 15) / 16;
+  const int QGW = attn_groups_per_wg(nq);
+  const int nqw = (nqg + QGW - 1) / QGW;
   if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
-  // (context splits + QT*4 suffix workgroups) per (kv head, sequence), each
-  // repeated per query group, laid out XCD by XCD (see the kernel)
-  const int units = (p.splits + 4 * QT) * p.Hkv * p.B;
-  const dim3 grid(((units + 7) / 8) * 8 * nqg);
+  // (context splits + 4 suffix workgroups per query group) per (kv head,
+  // sequence), each repeated per set of QGW query groups, laid out XCD by
+  // XCD (see the kernel)
+  const int units = (p.splits + 4 * QGW) * p.Hkv * p.B;
+  const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
-    if (QT == 1) attn_ctx_kernel<128, 1><<<grid, 256, 0, s>>>(p);
-    else attn_ctx_kernel<128, 2><<<grid, 256, 0, s>>>(p);
+    if (QGW == 1) attn_ctx_kernel<128, 1, 1><<<grid, 256, 0, s>>>(p);
+    else attn_ctx_kernel<128, 1, 2><<<grid, 256, 0, s>>>(p);
   } else {
-    if (QT == 1) attn_ctx_kernel<64, 1><<<grid, 256, 0, s>>>(p);
-    else attn_ctx_kernel<64, 2><<<grid, 256, 0, s>>>(p);
+    if (QGW == 1) attn_ctx_kernel<64, 1, 1><<<grid, 256, 0, s>>>(p);
+    else attn_ctx_kernel<64, 1, 2><<<grid, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }

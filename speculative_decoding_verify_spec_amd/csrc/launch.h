@@ -117,7 +117,7 @@ struct AttnParams {
 // number of partial slots per query the attention kernel writes: the context
 // splits plus one for the step's own (suffix) keys
 int attn_nsplit(int splits);
-int attn_query_tiles_per_wave(int nq);
+int attn_groups_per_wg(int nq);  // query groups of 16 served by one context workgroup
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 struct CombineParams {
