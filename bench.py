@@ -95,6 +95,12 @@ def parse():
                     help="comma-separated per-sequence verify lengths (one per sequence of --batch): also time "
                          "the compact ragged forward against the fixed-width one")
     ap.add_argument("--ragged-tier", type=int, default=8, help="packed rows are padded to a multiple of this")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="1: a paged KV cache (64-slot pages, a random block table) instead of the dense one; "
+                         "the CPU baseline is then skipped")
+    ap.add_argument("--tree", type=str, default="",
+                    help="comma-separated branching per depth (e.g. 4,4,2,2): measure token-tree verify instead "
+                         "of the chain")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -122,13 +128,25 @@ def main():
     dev = torch.device("cuda:0")
     sh = synth.LLAMA8B
     B, ctx, gamma, T = a.batch, a.ctx, a.gamma, a.gamma + 1
+    if a.tree:
+        branching = [int(x) for x in a.tree.split(",")]
+        T = int(synth.random_tree(branching, 1).shape[1])
     max_ctx = ((ctx + T + 63) // 64) * 64
     log(f"workload: {sh.n_layers}L d={sh.d_model} V={sh.vocab} B={B} ctx={ctx} gamma={gamma}")
 
     t0 = time.time()
     names, w = synth.make_weights(sh, device=dev)
-    cache = synth.make_kv_cache(sh, B, max_ctx, ctx, device=dev, poison_tail=False)
-    eng = VerifyEngine(sh, w, cache, B, max_ctx, max(T, 1))
+    if a.paged:
+        # a pool of 64-slot pages; each sequence's pages in a seeded random order
+        pps = max_ctx // 64
+        kv_pages = B * pps + 8
+        cache = synth.make_kv_pool(sh, kv_pages, device=dev)
+        eng = VerifyEngine(sh, w, cache, B, max_ctx, max(T, 1), kv_pages=kv_pages)
+        eng.set_block_table(synth.random_block_table(B, pps, kv_pages).to(dev))
+        a.cpu_baseline = 0
+    else:
+        cache = synth.make_kv_cache(sh, B, max_ctx, ctx, device=dev, poison_tail=False)
+        eng = VerifyEngine(sh, w, cache, B, max_ctx, max(T, 1))
     torch.cuda.synchronize()
     log(f"weights + cache ready in {time.time() - t0:.1f}s")
 
@@ -147,6 +165,8 @@ def main():
     kv_len = torch.full((B,), ctx, dtype=torch.int32, device=dev)
     kv_out = torch.empty_like(kv_len)
     pending = synth.make_tokens(B, 1, sh.vocab, seed=synth.SEED_PROMPT, device=dev)
+    if a.tree:
+        return run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev)
 
     # ---- pre-draft R rounds from the same state: gamma sequential T=1 decodes
     # give the target logits z_i of each drafted prefix; q_i = softmax(z_i + eps)
@@ -283,7 +303,8 @@ def main():
         "config": {"workload": f"llama3-8b-shape chain verify B={B} ctx={ctx} gamma={gamma} "
                                f"sigma={a.sigma} T={a.temperature}"
                                + (f" top_k={a.top_k}" if a.top_k else "")
-                               + (f" top_p={a.top_p}" if a.top_p < 1.0 else ""),
+                               + (f" top_p={a.top_p}" if a.top_p < 1.0 else "")
+                               + (" paged-kv(64)" if a.paged else ""),
                    "B": B, "ctx": ctx, "gamma": gamma, "sigma": a.sigma, "temperature": a.temperature,
                    "top_k": a.top_k, "top_p": a.top_p, "parallelism": "single GPU"},
         "c_verify": round(c_v, 4), "t_verify_ms": round(t_verify, 4), "t_decode_ms": round(t_decode, 4),
@@ -296,6 +317,109 @@ def main():
 
     if a.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a, kv_len)
+    print(json.dumps(result), flush=True)
+
+
+def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
+    """Token-tree verify (CS349E Lecture 6, section 10.3): B sequences, each a
+    full tree with the given branching per depth.  Drafting (untimed): level
+    by level, the verify forward gives every node's target logits, the draft
+    distribution of a node is q = softmax(z + noise) and its children are drawn
+    from q without replacement.  Timed: verify + tree accept (+ path commit to
+    a separate length buffer, so the context stays fixed)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    branching = [int(x) for x in a.tree.split(",")]
+    B, V = a.batch, sh.vocab
+    parent = synth.random_tree(branching, B).to(dev)
+    T = int(parent.shape[1])
+    ch = synth.tree_children(parent[0].cpu().tolist())
+    depth = [0] * T
+    for v in range(1, T):
+        depth[v] = depth[int(parent[0, v])] + 1
+    log(f"tree {branching}: {T} nodes per sequence, {B * T} rows")
+    logits = torch.empty((B, T, V), device=dev)
+    rounds = []
+    g = torch.Generator(device="cpu")
+    for r in range(a.rounds):
+        tokens = torch.zeros((B, T), dtype=torch.int32, device=dev)
+        tokens[:, 0] = pending[:, 0]
+        q = None
+        for lvl in range(len(branching)):
+            eng.step(tokens, kv_len, logits, tree_parent=parent)
+            q, _ = synth.noisy_draft_dist(logits, a.sigma, synth.SEED_NOISE * 1000 + r * 16 + lvl,
+                                          a.temperature if a.temperature > 0 else 1.0)
+            g.manual_seed(synth.SEED_DRAFT * 1000 + r * 16 + lvl)
+            qc = q.double().cpu()
+            tk = tokens.cpu()
+            for b in range(B):
+                for v in range(T):
+                    if depth[v] == lvl and ch[v]:
+                        picks = torch.multinomial(qc[b, v], len(ch[v]), replacement=False, generator=g)
+                        for c, x in zip(ch[v], picks.tolist()):
+                            tk[b, c] = x
+            tokens = tk.to(dev)
+        rounds.append((tokens.contiguous(), q.contiguous()))
+    torch.cuda.synchronize()
+    log(f"{a.rounds} tree rounds drafted")
+    out = torch.empty((B, T), dtype=torch.int32, device=dev)
+    nacc_hist = torch.zeros((a.steps + a.warmup, B), dtype=torch.int32, device=dev)
+    kv_out = torch.empty_like(kv_len)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(k):
+        tokens, q = rounds[k % len(rounds)]
+        eng.step(tokens, kv_len, logits, tree_parent=parent)
+        eng.accept(logits, q, tokens, out, nacc_hist[k], kv_len, kv_out, tree_parent=parent,
+                   temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
+
+    for k in range(a.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.warmup, a.warmup + a.steps):
+        one_step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_timed = nacc_hist[a.warmup:].cpu().numpy()
+    tokens_out = int((n_timed + 1).sum())
+    ms_per_step = wall * 1000.0 / a.steps
+
+    def time_forward(tok, par, iters=10):
+        lg = torch.empty((B, tok.shape[1], V), device=dev)
+        for _ in range(3):
+            eng.step(tok, kv_len, lg, tree_parent=par)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            eng.step(tok, kv_len, lg, tree_parent=par)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    t_verify = time_forward(rounds[0][0], parent)
+    t_decode = time_forward(rounds[0][0][:, :1].contiguous(), None)
+    assert eng.device_errors() == 0
+    result = {
+        "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
+        "value": round(tokens_out / wall, 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 (bf16 weights, fp32 activations/accum)",
+        "data": "synthetic (random-init weights, random bf16 KV context, noisy-target tree drafts)",
+        "config": {"workload": f"llama3-8b-shape tree verify B={B} ctx={a.ctx} tree={branching} ({T} nodes) "
+                               f"sigma={a.sigma} T={a.temperature}",
+                   "B": B, "ctx": a.ctx, "tree": branching, "nodes": T, "sigma": a.sigma,
+                   "temperature": a.temperature, "parallelism": "single GPU"},
+        "c_verify": round(t_verify / t_decode, 4), "t_verify_ms": round(t_verify, 4),
+        "t_decode_ms": round(t_decode, 4), "mean_accepted": round(float(n_timed.mean()), 4),
+        "tokens_per_round": round(float((n_timed + 1).mean()), 4),
+    }
+    log(f"tree: {ms_per_step:.3f} ms/step, {result['value']} tok/s, T_verify {t_verify:.3f} ms, "
+        f"T_decode {t_decode:.3f} ms")
     print(json.dumps(result), flush=True)
 
 

@@ -82,6 +82,14 @@ typedef struct spec_config {
   float rms_eps, rope_theta;
   int32_t weight_dtype;
   int32_t max_batch, max_ctx, max_rows_per_seq;
+  /* KV cache layout.  kv_page_size 0: dense, per layer K [max_batch][Hkv]
+   * [max_ctx][D] and V [max_batch][Hkv][D][max_ctx].  kv_page_size 64: paged
+   * (PagedAttention, CS349E Lecture 6's reading list; the page size of the
+   * ninfer sweep page), a pool of kv_pages pages shared by all sequences,
+   * per layer K [kv_pages][Hkv][64][D] and V [kv_pages][Hkv][D][64]; each
+   * sequence's slots are mapped to pages by the block table given to
+   * spec_set_block_table. */
+  int32_t kv_page_size, kv_pages;
 } spec_config;
 
 /* Sampling for one accept call.
@@ -155,17 +163,36 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
  *   they are (a position-indexed cache abandons a rejected tail for free).
  *   Launches: a prep kernel, the per-layer kernels, the LM head.  The
  *   per-layer kernels read only weights, cache and workspace, so for each
- *   (B, T, chain or tree) their launch sequence is recorded once as a HIP
- *   graph on a private stream of the handle and replayed on `stream` (at most
- *   32 shapes are kept; the least recently used is dropped).  When `stream`
- *   is itself being captured by the caller, or graphs are switched off with
- *   spec_graph_enable, the kernels are launched directly instead.  The HIP
- *   runtime may allocate internal memory when a shape is first recorded.
+ *   (B, T, chain or tree) their launch sequence is recorded as a HIP graph on
+ *   a private stream of the handle and replayed on `stream`: the first step
+ *   of a shape launches them directly (choosing library GEMM algorithms for
+ *   64+ rows) and then records them, later steps replay (at most 32 shapes
+ *   are kept; the least recently used is dropped).  When `stream` is itself
+ *   being captured by the caller, or graphs are switched off with
+ *   spec_graph_enable, the kernels are launched directly.  The HIP runtime
+ *   and the GEMM library may allocate internal memory on a shape's first step.
  *   Errors: INVALID_ARG, CAPACITY (B > max_batch, T > max_rows_per_seq,
- *   T < 1), DEVICE.  Flags: TOKEN_RANGE, TREE, KV_OVERFLOW. */
+ *   T < 1), STATE (a paged cache without a block table), DEVICE.
+ *   Flags: TOKEN_RANGE, TREE, KV_OVERFLOW, LAYOUT (a paged table entry
+ *   outside the pool). */
 spec_status spec_verify_step(spec_handle* h, int32_t B, int32_t T, const int32_t* d_tokens,
                              const int32_t* d_kv_len, const int32_t* d_tree_parent,
                              float* d_logits, void* stream);
+
+/* Block table of a paged cache (kv_page_size 64): d_table [max_batch]
+ * [pages_per_seq] int32 device, row b listing the pool pages of sequence b's
+ * slots 0..63, 64..127, ...  The library keeps the pointer and reads the
+ * entries on the device at every later step and accept, so the caller edits
+ * them in place between steps (stream-ordered): appending a page as a
+ * sequence grows, and on rollback shrinking kv_len and returning the pages
+ * past the new length to its pool (CS349E Lecture 6, section 6.2 and its
+ * list of serving concerns: a paged rollback edits the table's length and
+ * frees the surplus blocks).  A sequence's capacity is min(max_ctx,
+ * 64 * pages_per_seq).  Entries outside [0, kv_pages) for slots in use set
+ * SPEC_FLAG_LAYOUT and are clamped.
+ *   Errors: INVALID_ARG (null handle or table, pages_per_seq < 1),
+ *   STATE (the cache is dense). */
+spec_status spec_set_block_table(spec_handle* h, const int32_t* d_table, int32_t pages_per_seq);
 
 /* Ragged (compact) verify forward: the DeepSeek-V4 analysis page, section 4
  * (static, cap-accept and compact modes; the RaggedVerifyLayout of

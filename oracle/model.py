@@ -210,6 +210,39 @@ def forward_ragged(shape, W: Weights, tokens_rows, cu, kv_len, k_cache, v_cache)
     return np.concatenate(logits, axis=0), k_new, v_new
 
 
+def page_slots(table_row, n_slots: int, page: int = 64):
+    """Paged KV (PagedAttention, the CS349E lecture's reading list; 64-slot
+    pages as on the ninfer sweep page): a block table maps a sequence's
+    logically contiguous slots to scattered physical pages; slot s is offset
+    s % page of page table_row[s // page].  Returns (page, offset) per slot."""
+    s = np.arange(n_slots)
+    return np.asarray(table_row)[s // page], s % page
+
+
+def gather_pages(k_pool, v_pool, table, n_slots: int, page: int = 64):
+    """Dense views of the sequences' first n_slots slots from a page pool:
+    k_pool [L, pages, Hkv, page, D], v_pool [L, pages, Hkv, D, page], table
+    [B, pages_per_seq] -> K [L, B, Hkv, n_slots, D], V [L, B, Hkv, D, n_slots]."""
+    B = len(table)
+    L, _, H, _, D = k_pool.shape
+    k = np.zeros((L, B, H, n_slots, D), dtype=k_pool.dtype)
+    v = np.zeros((L, B, H, D, n_slots), dtype=v_pool.dtype)
+    for b in range(B):
+        pg, off = page_slots(table[b], n_slots, page)
+        k[:, b] = k_pool[:, pg, :, off, :].transpose(1, 2, 0, 3)
+        v[:, b] = v_pool[:, pg, :, :, off].transpose(1, 2, 3, 0)
+    return k, v
+
+
+def scatter_pages(k_dense, v_dense, table, k_pool, v_pool, page: int = 64):
+    """Inverse of gather_pages: write the dense slots into their pages."""
+    B, n_slots = k_dense.shape[1], k_dense.shape[3]
+    for b in range(B):
+        pg, off = page_slots(table[b], n_slots, page)
+        k_pool[:, pg, :, off, :] = k_dense[:, b].transpose(2, 0, 1, 3)
+        v_pool[:, pg, :, :, off] = v_dense[:, b].transpose(3, 0, 1, 2)
+
+
 def write_suffix(k_cache, v_cache, k_new, v_new, kv_len, rows=None):
     """Store the window's K/V (rounded to bf16) at slots kv_len[b] + i, as the
     verify step does for every row before acceptance is known.  Caches are

@@ -35,7 +35,7 @@ SPEC_FLAG_LAYOUT = 8
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_profile_gemm", "spec_graph_enable", "spec_verify_destroy", "spec_status_str",
+    "spec_profile_gemm", "spec_graph_enable", "spec_set_block_table", "spec_verify_destroy", "spec_status_str",
 ]
 
 
@@ -44,7 +44,7 @@ class spec_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32),
                 ("vocab", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
                 ("weight_dtype", C.c_int32), ("max_batch", C.c_int32), ("max_ctx", C.c_int32),
-                ("max_rows_per_seq", C.c_int32)]
+                ("max_rows_per_seq", C.c_int32), ("kv_page_size", C.c_int32), ("kv_pages", C.c_int32)]
 
 
 class spec_sampling(C.Structure):
@@ -104,6 +104,8 @@ def lib():
     L.spec_profile_gemm.restype = i32
     L.spec_graph_enable.argtypes = [vp, i32]
     L.spec_graph_enable.restype = i32
+    L.spec_set_block_table.argtypes = [vp, vp, i32]
+    L.spec_set_block_table.restype = i32
     L.spec_verify_destroy.argtypes = [vp]
     L.spec_verify_destroy.restype = None
     L.spec_status_str.argtypes = [i32]
@@ -133,12 +135,17 @@ def _check(fn, st):
         raise SpecError(fn, st)
 
 
-def make_config(shape, max_batch, max_ctx, max_rows_per_seq) -> spec_config:
-    """spec_config from any object with the model-shape attributes."""
+KV_PAGE = 64  # slots per page of a paged cache
+
+
+def make_config(shape, max_batch, max_ctx, max_rows_per_seq, kv_pages: int = 0) -> spec_config:
+    """spec_config from any object with the model-shape attributes; kv_pages > 0
+    selects a paged cache of that many 64-slot pages."""
     return spec_config(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                        shape.d_ffn, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
                        SPEC_DTYPE_BF16 if shape.weight_dtype == "bf16" else SPEC_DTYPE_F32,
-                       int(max_batch), int(max_ctx), int(max_rows_per_seq))
+                       int(max_batch), int(max_ctx), int(max_rows_per_seq),
+                       KV_PAGE if kv_pages else 0, int(kv_pages))
 
 
 def spec_status_str(status: int) -> str:
@@ -230,6 +237,10 @@ def spec_profile_gemm(h, cls: str, rows: int, iters: int, stream=None):
     _check("spec_profile_gemm", lib().spec_profile_gemm(h, cls.encode(), int(rows), int(iters),
                                                         _stream(stream), C.byref(ms), C.byref(nbytes)))
     return ms.value, nbytes.value
+
+
+def spec_set_block_table(h, table, pages_per_seq: int):
+    _check("spec_set_block_table", lib().spec_set_block_table(h, _ptr(table), int(pages_per_seq)))
 
 
 def spec_graph_enable(h, enable: bool):

@@ -654,18 +654,21 @@ DEVI void tree_commit(const AcceptParams& p, int b, const int* path, int plen) {
   if (!p.kv_len_out) return;
   const int base = p.kv_len[b];
   if (threadIdx.x == 0) p.kv_len_out[b] = base + plen;
-  if (base < 0 || base + p.T > p.max_ctx) return;
-  const size_t per = (size_t)p.maxB * p.Hkv * p.max_ctx * p.D;  // one K or V region
+  const int cap = p.kvm.table ? min(p.max_ctx, p.kvm.ppseq * KV_PAGE) : p.max_ctx;
+  if (base < 0 || base + p.T > cap) return;
+  // one K or V region: [maxB][Hkv][max_ctx][D] dense, [npages][Hkv][page][D] paged
+  const size_t per = p.kvm.table ? (size_t)p.kvm.npages * p.Hkv * KV_PAGE * p.D
+                                 : (size_t)p.maxB * p.Hkv * p.max_ctx * p.D;
   const int nel = p.L * p.Hkv * p.D;
   for (int e = threadIdx.x; e < nel; e += blockDim.x) {
     const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
-    uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per + ((size_t)b * p.Hkv + hk) * p.max_ctx * p.D + d;
-    uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per + (((size_t)b * p.Hkv + hk) * p.D + d) * p.max_ctx;
+    uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per + d;
+    uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
     for (int j = 1; j < plen; ++j) {
       const int src = path[j];
       if (src == j) continue;
-      kreg[(size_t)(base + j) * p.D] = kreg[(size_t)(base + src) * p.D];
-      vreg[base + j] = vreg[base + src];
+      kreg[kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + j)] = kreg[kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + src)];
+      vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + j)] = vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + src)];
     }
   }
 }

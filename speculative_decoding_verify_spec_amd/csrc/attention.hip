@@ -195,7 +195,8 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
   const int rs = p.rstart ? p.rstart[b] : b * p.T;
   const int nqb = G * (p.rlen ? p.rlen[b] : p.T);  // this sequence's queries
   int L = p.kv_len[b];
-  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int cap = p.kvm.table ? min(p.max_ctx, p.kvm.ppseq * KV_PAGE) : p.max_ctx;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
   int chunk = (L + p.splits - 1) / p.splits;
   chunk = (chunk + 127) & ~127;
   const int kbeg = s * chunk;
@@ -203,24 +204,26 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
 
   // ---- raw cache loads of one 32-key block, issued before they are needed:
   // K rows of the block's two key tiles and the V^T columns of its keys;
-  // keys at or past kend read as zeros
-  const uint16_t* kbase = p.kc + ((size_t)b * p.Hkv + kvh) * (size_t)p.max_ctx * D;
-  const uint16_t* vbase = p.vc + ((size_t)b * p.Hkv + kvh) * (size_t)D * p.max_ctx;
+  // keys at or past kend read as zeros.  A block's 32 slots are contiguous
+  // (one page holds two blocks), so one lookup places the whole block.
+  const int vstride = kv_v_stride(p.kvm);
   uint4 kraw[2][DG / 8];
   uint4 vraw[DT];
   auto load_block = [&](int kb) {
+    const uint16_t* kblk = p.kc + kv_k_off(p.kvm, p.Hkv, D, b, kvh, kb);
+    const uint16_t* vblk = p.vc + kv_v_off(p.kvm, p.Hkv, D, b, kvh, 0, kb);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int key = blk_key(kb, kt, j);
       const bool ok = key < kend;
-      const uint16_t* src = kbase + (size_t)(ok ? key : 0) * D + g * DG;
+      const uint16_t* src = kblk + (size_t)(ok ? key - kb : 0) * D + g * DG;
 #pragma unroll
       for (int e = 0; e < DG / 8; ++e) kraw[kt][e] = ok ? *(const uint4*)(src + 8 * e) : make_uint4(0, 0, 0, 0);
     }
     const int k8 = kb + 8 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* src = vbase + (size_t)(dt * 16 + j) * p.max_ctx + (k8 < kend ? k8 : 0);
+      const uint16_t* src = vblk + (size_t)(dt * 16 + j) * vstride + (k8 < kend ? 8 * g : 0);
       vraw[dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
     }
   };

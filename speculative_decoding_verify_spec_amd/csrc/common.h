@@ -96,3 +96,40 @@ DEVI float philox_uniform(uint64_t seed, uint64_t round, int b, int slot) {
 #define FLAG_TREE 2u
 #define FLAG_KV_OVERFLOW 4u
 #define FLAG_LAYOUT 8u
+
+// ---------------------------------------------------------------- KV addressing
+// A layer's cache, dense or paged.  Dense: K region [maxB][Hkv][max_ctx][D],
+// V region [maxB][Hkv][D][max_ctx] (V transposed so the key index, the
+// contraction index of P V, is contiguous).  Paged (PagedAttention, pages of
+// KV_PAGE slots): K region [npages][Hkv][KV_PAGE][D], V region
+// [npages][Hkv][D][KV_PAGE]; slot s of sequence b lives in page
+// table[b * ppseq + s / KV_PAGE] at offset s % KV_PAGE.  Page ids outside the
+// pool are clamped (the prep kernel flags them), so no access leaves it.
+constexpr int KV_PAGE = 64;
+struct KvMap {
+  const int32_t* table;  // [B][ppseq] page ids, or null: dense
+  int ppseq;             // pages per sequence (table row length)
+  int npages;            // pages in the pool
+  int max_ctx;           // dense slot stride
+};
+// first slot of slot s's run of contiguous slots (a page, or the whole
+// sequence when dense), as an element offset of K row s and of V (dim 0, s)
+DEVI size_t kv_k_off(const KvMap& m, int Hkv, int D, int b, int h, int s) {
+  if (!m.table) return (((size_t)b * Hkv + h) * m.max_ctx + s) * D;
+  int pi = s / KV_PAGE;
+  pi = pi < 0 ? 0 : (pi >= m.ppseq ? m.ppseq - 1 : pi);
+  int pg = m.table[(size_t)b * m.ppseq + pi];
+  pg = pg < 0 ? 0 : (pg >= m.npages ? m.npages - 1 : pg);
+  return (((size_t)pg * Hkv + h) * KV_PAGE + (s % KV_PAGE)) * D;
+}
+// element offset of V (dim, slot s); slots of one page (or all slots, dense)
+// are contiguous for a fixed dim, with this stride between dims
+DEVI int kv_v_stride(const KvMap& m) { return m.table ? KV_PAGE : m.max_ctx; }
+DEVI size_t kv_v_off(const KvMap& m, int Hkv, int D, int b, int h, int dim, int s) {
+  if (!m.table) return (((size_t)b * Hkv + h) * D + dim) * (size_t)m.max_ctx + s;
+  int pi = s / KV_PAGE;
+  pi = pi < 0 ? 0 : (pi >= m.ppseq ? m.ppseq - 1 : pi);
+  int pg = m.table[(size_t)b * m.ppseq + pi];
+  pg = pg < 0 ? 0 : (pg >= m.npages ? m.npages - 1 : pg);
+  return (((size_t)pg * Hkv + h) * D + dim) * KV_PAGE + (s % KV_PAGE);
+}

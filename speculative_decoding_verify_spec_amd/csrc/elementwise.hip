@@ -4,6 +4,24 @@
 
 namespace sv {
 
+// Slots a sequence may use: max_ctx, and with a paged cache also its table
+// row's pages.  Paged: table entries for the pages of slots [0, n) must name
+// pool pages (FLAG_LAYOUT otherwise; the addressing clamps them).
+DEVI int seq_capacity(const PrepParams& p) {
+  return p.kvm.table ? min(p.max_ctx, p.kvm.ppseq * KV_PAGE) : p.max_ctx;
+}
+DEVI void check_pages(const PrepParams& p, int b, int n) {
+  if (!p.kvm.table) return;
+  const int np = min(p.kvm.ppseq, (n + KV_PAGE - 1) / KV_PAGE);
+  for (int i = 0; i < np; ++i) {
+    const int pg = p.kvm.table[(size_t)b * p.kvm.ppseq + i];
+    if (pg < 0 || pg >= p.kvm.npages) {
+      atomicOr(p.flags, FLAG_LAYOUT);
+      break;
+    }
+  }
+}
+
 // One workgroup per sequence.  Copies kv_len into the workspace (the later
 // kernels of the step read only the workspace, weights and cache, so their
 // launch sequence can be recorded once and replayed); validates tokens, cache
@@ -20,9 +38,11 @@ __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
   __shared__ uint64_t anc_lo[128], anc_hi[128];
   __shared__ int stok[128];
   const int kv = p.kv_len[b];
+  const int cap = seq_capacity(p);
   if (threadIdx.x == 0) {
     p.kv_copy[b] = kv;
-    if (kv < 0 || kv > p.max_ctx - T) atomicOr(p.flags, FLAG_KV_OVERFLOW);
+    if (kv < 0 || kv > cap - T) atomicOr(p.flags, FLAG_KV_OVERFLOW);
+    check_pages(p, b, min(cap, (kv < 0 ? 0 : kv) + T));
     if (p.parent) {
       const int32_t* par = p.parent + (size_t)b * T;
       bool bad = par[0] != -1;
@@ -56,7 +76,7 @@ __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
     const int ps = kvc + (p.parent ? depth[i] : i);
     p.pos[m] = ps < p.max_ctx ? ps : p.max_ctx - 1;
     const int sl = kvc + i;
-    p.slot[m] = (kv >= 0 && sl < p.max_ctx) ? sl : -1;
+    p.slot[m] = (kv >= 0 && sl < cap) ? sl : -1;
     if (p.parent) {
       p.anc[2 * m] = anc_lo[i];
       p.anc[2 * m + 1] = anc_hi[i];
@@ -107,7 +127,8 @@ __global__ __launch_bounds__(256) void prep_ragged_kernel(PrepParams p) {
       p.kv_copy[b] = kv;
       p.rstart[b] = start;
       p.rlen[b] = len;
-      if (kv < 0 || kv > p.max_ctx - len) atomicOr(p.flags, FLAG_KV_OVERFLOW);
+      if (kv < 0 || kv > seq_capacity(p) - len) atomicOr(p.flags, FLAG_KV_OVERFLOW);
+      check_pages(p, b, min(seq_capacity(p), (kv < 0 ? 0 : kv) + len));
     } else {
       const int c = p.cu[p.B];
       start = c < 0 ? 0 : (c > p.rows ? p.rows : c);
@@ -131,7 +152,7 @@ __global__ __launch_bounds__(256) void prep_ragged_kernel(PrepParams p) {
     p.tok[m] = t;
     const int ps = kvc + i;
     p.pos[m] = pad ? 0 : (ps < p.max_ctx ? ps : p.max_ctx - 1);
-    p.slot[m] = (!pad && kv >= 0 && ps < p.max_ctx) ? ps : -1;
+    p.slot[m] = (!pad && kv >= 0 && ps < seq_capacity(p)) ? ps : -1;
     p.seq[m] = pad ? 0 : b;
   }
   __syncthreads();

@@ -103,7 +103,7 @@ DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
         k[i] = x0;
         k[i + half] = x1;
         if (sl >= 0) {
-          uint16_t* kc = p.kcache + (((size_t)bseq * p.Hkv + hk) * p.max_ctx + sl) * D;
+          uint16_t* kc = p.kcache + kv_k_off(p.kvm, p.Hkv, D, bseq, hk, sl);
           kc[i] = (uint16_t)f32_to_bf16_rne(x0);
           kc[i + half] = (uint16_t)f32_to_bf16_rne(x1);
         }
@@ -114,9 +114,8 @@ DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
       v[i] = a;
       v[i + half] = b;
       if (sl >= 0) {
-        uint16_t* vc = p.vcache + ((size_t)bseq * p.Hkv + hv) * D * (size_t)p.max_ctx;
-        vc[(size_t)i * p.max_ctx + sl] = (uint16_t)f32_to_bf16_rne(a);
-        vc[(size_t)(i + half) * p.max_ctx + sl] = (uint16_t)f32_to_bf16_rne(b);
+        p.vcache[kv_v_off(p.kvm, p.Hkv, D, bseq, hv, i, sl)] = (uint16_t)f32_to_bf16_rne(a);
+        p.vcache[kv_v_off(p.kvm, p.Hkv, D, bseq, hv, i + half, sl)] = (uint16_t)f32_to_bf16_rne(b);
       }
     }
   }

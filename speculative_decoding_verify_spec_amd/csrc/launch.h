@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace sv {
 
 // ---------------------------------------------------------------- prep + embedding
@@ -30,6 +32,7 @@ struct PrepParams {
   int32_t* rstart;        // [B]
   int32_t* rlen;          // [B]
   int32_t* seq;           // [rows]
+  KvMap kvm;              // cache addressing; paged: the table is checked here
 };
 hipError_t launch_prep(const PrepParams& p, hipStream_t s);
 
@@ -72,6 +75,7 @@ struct GemmParams {
   const int32_t* seq;
   // many rows: the library GEMM path (null: not available)
   struct BlasCtx* blas;
+  KvMap kvm;                // cache addressing of the QKV epilogue's writes
 };
 constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
@@ -113,6 +117,7 @@ struct AttnParams {
   // T is then the longest length)
   const int32_t* rstart;
   const int32_t* rlen;
+  KvMap kvm;               // cache addressing
 };
 // number of partial slots per query the attention kernel writes: the context
 // splits plus one for the step's own (suffix) keys
@@ -172,6 +177,7 @@ struct AcceptParams {
   const int32_t* qstart;
   int rows;                // logits (and token) rows: B*T when not ragged
   int qrows;               // rows of q
+  KvMap kvm;               // cache addressing of the tree commit
 };
 // Running state of one row's radix selection: the key bits chosen so far,
 // the tokens still to take (top-k) or the mass still to reach (top-p; -1

@@ -30,7 +30,15 @@ bool valid_config(const spec_config* c) {
   if (c->max_batch < 1 || c->max_rows_per_seq < 1 || c->max_rows_per_seq > 128) return false;
   if (c->max_ctx < 64 || c->max_ctx % 64 || c->max_ctx < c->max_rows_per_seq) return false;
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return false;
+  if (c->kv_page_size != 0 && c->kv_page_size != KV_PAGE) return false;
+  if (c->kv_page_size && c->kv_pages < 1) return false;
   return true;
+}
+
+// elements of one layer's K (or V) region
+size_t kv_region_elems(const spec_config& c) {
+  if (c.kv_page_size) return (size_t)c.kv_pages * c.n_kv_heads * KV_PAGE * c.head_dim;
+  return (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
 }
 
 // Attention workgroups per (sequence, KV head, query group): about 128 keys
@@ -181,6 +189,8 @@ struct spec_handle {
   };
   bool graphs = true;
   bool recording = false;     // launches are being recorded: no library tuning
+  const int32_t* kv_table = nullptr;  // paged cache: [max_batch][kv_ppseq] page ids
+  int kv_ppseq = 0;
   BlasCtx* blas = nullptr;    // library GEMMs for 64 or more rows
   hipStream_t cap = nullptr;  // private stream used only to record
   std::vector<Graph> gcache;
@@ -224,6 +234,13 @@ hipError_t timed(spec_handle* h, int cls, double bytes, hipStream_t s, F&& launc
 spec_status dev(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_DEVICE; }
 
 // GEMM over M rows in launches of at most 8 activation rows.
+// the cache addressing of the kernels: dense, or paged through the table
+KvMap kv_map(const spec_handle* h) {
+  const spec_config& c = h->cfg;
+  if (!c.kv_page_size) return KvMap{nullptr, 0, 0, c.max_ctx};
+  return KvMap{h->kv_table, h->kv_ppseq, c.kv_pages, c.max_ctx};
+}
+
 hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
   const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   const size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
@@ -292,7 +309,7 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   uint64_t* anc = h->at<uint64_t>(L.anc);
   const int32_t* kvw = h->at<int32_t>(L.kvw);
   hipError_t e;
-  const size_t per_region = (size_t)c.max_batch * Hkv * c.max_ctx * D;  // elements of one K or V region
+  const size_t per_region = kv_region_elems(c);  // elements of one K or V region
   const int splits = attn_splits(c, B, T);
   const int nsplit = attn_nsplit(splits);
   const float scale = 1.0f / std::sqrt((float)D);
@@ -315,10 +332,11 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
     gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
     gq.T = T; gq.Hq = Hq; gq.Hkv = Hkv; gq.D = D; gq.max_ctx = c.max_ctx;
     gq.seq = sh.ragged ? h->at<int32_t>(L.rseq) : nullptr;
+    gq.kvm = kv_map(h);
     if ((e = gemm_rows(h, K_QKV, gq, M, s)) != hipSuccess) return e;
 
     AttnParams ap{q, kreg, vreg, kvw, ks, vs, tree ? anc : nullptr, h->at<float>(L.part_o),
-                  h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale, rstart, rlen};
+                  h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale, rstart, rlen, kv_map(h)};
     e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
     if (e != hipSuccess) return e;
     CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D, rstart, rlen};
@@ -440,7 +458,7 @@ size_t spec_workspace_bytes(const spec_config* cfg) {
 
 size_t spec_kv_cache_bytes(const spec_config* c) {
   if (!valid_config(c)) return 0;
-  return (size_t)c->n_layers * 2 * c->max_batch * c->n_kv_heads * (size_t)c->max_ctx * c->head_dim * 2;
+  return (size_t)c->n_layers * 2 * kv_region_elems(*c) * 2;
 }
 
 spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weights, size_t n_weights,
@@ -504,6 +522,7 @@ namespace {
 spec_status verify_forward(spec_handle* h, const StepShape& sh, const int32_t* d_tokens, const int32_t* d_kv_len,
                            const int32_t* d_tree_parent, const int32_t* d_cu, float* d_logits, hipStream_t s) {
   const spec_config& c = h->cfg;
+  if (c.kv_page_size && !h->kv_table) return SPEC_ERR_STATE;
   const Layout& L = h->lay;
   const int M = sh.M, d = c.d_model;
   const int V = c.vocab;
@@ -514,7 +533,7 @@ spec_status verify_forward(spec_handle* h, const StepShape& sh, const int32_t* d
   PrepParams pp{d_tokens, d_kv_len, d_tree_parent, h->at<int32_t>(L.tok), h->at<int32_t>(L.pos),
                 h->at<int32_t>(L.slot), h->at<uint64_t>(L.anc), h->at<uint32_t>(L.flags), h->W(0),
                 c.weight_dtype, x, h->at<int32_t>(L.kvw), sh.B, sh.T, V, c.max_ctx, d,
-                d_cu, M, h->at<int32_t>(L.rstart), h->at<int32_t>(L.rlen), h->at<int32_t>(L.rseq)};
+                d_cu, M, h->at<int32_t>(L.rstart), h->at<int32_t>(L.rlen), h->at<int32_t>(L.rseq), kv_map(h)};
   e = timed(h, K_PREP, (double)M * d * (wb + 4), s, [&] { return launch_prep(pp, s); });
   if (e != hipSuccess) return SPEC_ERR_DEVICE;
 
@@ -566,6 +585,7 @@ spec_status accept_impl(spec_handle* h, AcceptParams ap, const spec_sampling* sa
   if (temp > 0.f && need_q && !ap.q) return SPEC_ERR_INVALID_ARG;
   if (ap.kv_len_out && !ap.kv_len) return SPEC_ERR_INVALID_ARG;
   const spec_config& c = h->cfg;
+  if (c.kv_page_size && !h->kv_table && ap.parent && ap.kv_len_out) return SPEC_ERR_STATE;
   const Layout& L = h->lay;
   ap.temperature = temp; ap.replacement = sampling->tree_replacement ? 1 : 0;
   ap.seed = sampling->seed; ap.round = sampling->round;
@@ -576,6 +596,7 @@ spec_status accept_impl(spec_handle* h, AcceptParams ap, const spec_sampling* sa
   ap.top_k = sampling->top_k; ap.top_p = sampling->top_p;
   ap.fcnt = h->at<uint32_t>(L.fcnt); ap.fmass = h->at<double>(L.fmass);
   ap.fstate = h->at<SelState>(L.fstate); ap.fres = h->at<SelRule>(L.fres);
+  ap.kvm = kv_map(h);
   const double bytes = (double)ap.rows * c.vocab * 4 + (temp > 0 ? (double)ap.qrows * c.vocab * 4 : 0.0);
   return dev(timed(h, K_ACC, bytes, s, [&] { return launch_accept(ap, s); }));
 }
@@ -741,6 +762,21 @@ void spec_verify_destroy(spec_handle* h) {
   if (h->cap) hipStreamDestroy(h->cap);
   blas_destroy(h->blas);
   delete h;
+}
+
+spec_status spec_set_block_table(spec_handle* h, const int32_t* d_table, int32_t pages_per_seq) {
+  if (!h || !d_table || pages_per_seq < 1) return SPEC_ERR_INVALID_ARG;
+  if (!h->cfg.kv_page_size) return SPEC_ERR_STATE;
+  if (h->kv_table != d_table || h->kv_ppseq != pages_per_seq) {
+    // the recorded launch sequences hold the old table: drop them
+    if (!h->gcache.empty()) hipDeviceSynchronize();
+    for (auto& g : h->gcache)
+      if (g.exec) hipGraphExecDestroy(g.exec);
+    h->gcache.clear();
+  }
+  h->kv_table = d_table;
+  h->kv_ppseq = pages_per_seq;
+  return SPEC_OK;
 }
 
 spec_status spec_graph_enable(spec_handle* h, int32_t enable) {

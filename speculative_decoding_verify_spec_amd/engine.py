@@ -6,15 +6,15 @@ from __future__ import annotations
 import torch
 
 from . import (make_config, spec_accept, spec_accept_ragged, spec_device_errors, spec_graph_enable,
-               spec_kv_cache_bytes, spec_profile_gemm, spec_sampling, spec_verify_destroy, spec_verify_init,
-               spec_verify_step, spec_verify_step_ragged, spec_workspace_bytes)
+               spec_kv_cache_bytes, spec_profile_gemm, spec_sampling, spec_set_block_table, spec_verify_destroy,
+               spec_verify_init, spec_verify_step, spec_verify_step_ragged, spec_workspace_bytes)
 
 
 class VerifyEngine:
     def __init__(self, shape, weights, kv_cache: torch.Tensor, max_batch: int, max_ctx: int,
-                 max_rows_per_seq: int, stream=None):
+                 max_rows_per_seq: int, stream=None, kv_pages: int = 0):
         self.shape = shape
-        self.cfg = make_config(shape, max_batch, max_ctx, max_rows_per_seq)
+        self.cfg = make_config(shape, max_batch, max_ctx, max_rows_per_seq, kv_pages)
         self.weights = list(weights)
         self.kv_cache = kv_cache
         need = spec_kv_cache_bytes(self.cfg)
@@ -27,6 +27,12 @@ class VerifyEngine:
         self.stream = stream if stream is not None else torch.cuda.current_stream(dev)
         self.handle = spec_verify_init(self.cfg, self.weights, self.kv_cache, self.workspace,
                                        self.ws_bytes, self.stream)
+
+    def set_block_table(self, table):
+        """Paged cache: table [max_batch, pages_per_seq] int32 on the device,
+        read at every later step (edit it in place to grow or roll back)."""
+        self.block_table = table
+        spec_set_block_table(self.handle, table, table.shape[1])
 
     def step(self, tokens, kv_len, logits, tree_parent=None):
         B, T = tokens.shape

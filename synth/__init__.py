@@ -196,6 +196,32 @@ def make_kv_cache(shape: ModelShape, max_batch: int, max_ctx: int, ctx_len, seed
     return cache
 
 
+def paged_kv_views(pool: torch.Tensor, shape: ModelShape, kv_pages: int, page: int = 64):
+    """K view [L, pages, Hkv, page, D] and V view [L, pages, Hkv, D, page] of a
+    flat bf16 page pool."""
+    L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    c = pool.view(L, 2, kv_pages, H, page * D)
+    return c[:, 0].view(L, kv_pages, H, page, D), c[:, 1].view(L, kv_pages, H, D, page)
+
+
+def make_kv_pool(shape: ModelShape, kv_pages: int, seed: int = SEED_KV, device="cpu", page: int = 64):
+    """A page pool filled with i.i.d. N(0, KV_STD^2) bf16 (the synthetic
+    context's distribution), for timing a paged cache."""
+    L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    g = _gen(seed, device)
+    n = L * 2 * kv_pages * H * page * D
+    return (torch.randn((n,), generator=g, device=device) * KV_STD).to(torch.bfloat16)
+
+
+def random_block_table(max_batch: int, pages_per_seq: int, kv_pages: int, seed: int = SEED_KV):
+    """A block table [max_batch, pages_per_seq] int32 naming distinct pool pages
+    in a seeded random order (kv_pages >= max_batch * pages_per_seq)."""
+    assert kv_pages >= max_batch * pages_per_seq
+    g = torch.Generator(device="cpu").manual_seed(seed + 77)
+    perm = torch.randperm(kv_pages, generator=g)[: max_batch * pages_per_seq]
+    return perm.view(max_batch, pages_per_seq).to(torch.int32)
+
+
 # ----------------------------------------------------------------------------
 # tokens, logits and synthetic drafts
 # ----------------------------------------------------------------------------

@@ -300,3 +300,46 @@ def test_forward_ragged_packs_the_batched_forward():
     zr, _, _ = M.forward_ragged(sh, W, rows, cu, kv_len, kc, vc)
     for b in range(B):
         assert np.allclose(zr[cu[b]:cu[b + 1]], full[b, :lens[b]], atol=1e-12)
+
+
+def test_paged_gather_follows_the_block_table():
+    """Paged KV: every slot s of sequence b is read from page table[b][s // 64]
+    at offset s % 64 (pool values encode their own page and offset)."""
+    L, H, D, page, npages = 2, 2, 3, 64, 10
+    rng = np.random.default_rng(12)
+    table = rng.permutation(npages)[:6].reshape(2, 3)
+    code = np.arange(npages)[None, :, None, None, None] * 1000 + np.arange(page)[None, None, None, :, None]
+    kp = np.broadcast_to(code, (L, npages, H, page, D)).astype(np.float64)
+    vp = np.broadcast_to(code.transpose(0, 1, 2, 4, 3), (L, npages, H, D, page)).astype(np.float64)
+    k, v = M.gather_pages(kp, vp, table, 3 * page)
+    for b in range(2):
+        for s in range(3 * page):
+            want = table[b][s // page] * 1000 + s % page
+            assert np.all(k[:, b, :, s, :] == want) and np.all(v[:, b, :, :, s] == want)
+    # scatter is its inverse on the mapped slots
+    kq, vq = np.zeros_like(kp), np.zeros_like(vp)
+    M.scatter_pages(k, v, table, kq, vq)
+    assert np.array_equal(M.gather_pages(kq, vq, table, 3 * page)[0], k)
+
+
+def test_paged_placement_does_not_change_the_forward():
+    """Two pools holding the same sequences on different physical pages give
+    the same logits (the table only names where slots live)."""
+    sh = _shape()
+    W = M.Weights(*_weights(sh, seed=5))
+    rng = np.random.default_rng(13)
+    B, T, page, pps, npages = 2, 3, 64, 2, 7
+    kd = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, pps * page, sh.head_dim))
+    vd = rng.normal(size=(sh.n_layers, B, sh.n_kv_heads, sh.head_dim, pps * page))
+    kv_len = np.array([70, 33])
+    toks = rng.integers(0, sh.vocab, size=(B, T))
+    outs = []
+    for seed in (1, 2):
+        table = np.random.default_rng(seed).permutation(npages)[:B * pps].reshape(B, pps)
+        kp = np.zeros((sh.n_layers, npages, sh.n_kv_heads, page, sh.head_dim))
+        vp = np.zeros((sh.n_layers, npages, sh.n_kv_heads, sh.head_dim, page))
+        M.scatter_pages(kd, vd, table, kp, vp)
+        kg, vg = M.gather_pages(kp, vp, table, pps * page)
+        outs.append(M.forward(sh, W, toks, kv_len, kg, vg)[0])
+    assert np.array_equal(outs[0], outs[1])
+    assert np.allclose(outs[0], M.forward(sh, W, toks, kv_len, kd, vd)[0], atol=0)
