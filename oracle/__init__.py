@@ -11,7 +11,10 @@ path computes, written from the pages:
   * philox.py  -- Philox4x64-10 (Salmon et al., SC'11), the uniforms' source;
   * metrics.py -- the closed forms the pages give (beta, tokens per round,
                   speedup, compute increase, accept-rate metrics);
-  * numerics.py -- bf16 decoding and round-to-nearest-even.
+  * numerics.py -- bf16 decoding and round-to-nearest-even;
+  * recurrent.py -- verify on a recurrent (gated delta-rule) layer: the state
+                  advanced through the window, its snapshots and the
+                  post-verify survivor scatter.
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package.  It shares no code with the HIP path and imports nothing from it.
@@ -22,4 +25,4 @@ in tests/test_oracle_model.py (closed forms, library special cases, causal and
 prefill/decode consistency).  The sibling order of a token tree has no printed
 example; enumeration and sampling pin only losslessness.
 """
-from . import philox, numerics, model, accept, metrics  # noqa: F401
+from . import philox, numerics, model, accept, metrics, recurrent  # noqa: F401

@@ -288,6 +288,54 @@ def tree_children(parent_row):
 
 
 # ----------------------------------------------------------------------------
+# recurrent (linear-attention) layer inputs
+# ----------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class RecurrentShape:
+    n_heads: int     # H
+    head_dim: int    # D, key and value width per head
+    conv_width: int  # W, taps of the causal convolution
+
+    @property
+    def channels(self):
+        return 3 * self.n_heads * self.head_dim
+
+
+# 32 heads of width 128 with a 4-tap convolution: the mixer of a hybrid
+# model's recurrent layers at the 8B width (d_model = 32 * 128)
+RECURRENT_8B = RecurrentShape(n_heads=32, head_dim=128, conv_width=4)
+SEED_RECURRENT = 4242
+
+
+def make_recurrent_inputs(rs: RecurrentShape, B: int, T: int, n_slots: int, seed: int = SEED_RECURRENT,
+                          device="cpu"):
+    """Random inputs of one verify window of a recurrent layer, fp32:
+      x          [B][T][3HD]     raw q|k|v channels, N(0, 1)
+      gate       [B][T][H][D]    log decay, uniform in [-0.5, 0]
+      beta       [B][T][H]       write strength, uniform in [0, 1]
+      conv_w     [3HD][W]        taps, N(0, 1/W)
+      conv_state [n_slots][W-1][3HD]  raw inputs before the window, N(0, 1)
+      state      [n_slots][H][D][D]   recurrent states, N(0, 0.25)
+    Each tensor has its own stream (seed * 1000003 + index)."""
+    H, D, W, C = rs.n_heads, rs.head_dim, rs.conv_width, rs.channels
+
+    def g(i):
+        return _gen(seed * 1000003 + i, "cpu")
+
+    out = {
+        "x": torch.randn((B, T, C), generator=g(0)),
+        "gate": -0.5 * torch.rand((B, T, H, D), generator=g(1)),
+        "beta": torch.rand((B, T, H), generator=g(2)),
+        "conv_w": torch.randn((C, W), generator=g(3)) / math.sqrt(W),
+        "conv_state": torch.randn((n_slots, W - 1, C), generator=g(4)),
+        "state": 0.5 * torch.randn((n_slots, H, D, D), generator=g(5)),
+    }
+    return {k: v.to(device) for k, v in out.items()}
+
+
+# ----------------------------------------------------------------------------
 # bf16 helpers for moving tensors to the oracle (bit reinterpretation only)
 # ----------------------------------------------------------------------------
 
