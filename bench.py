@@ -101,6 +101,9 @@ def parse():
     ap.add_argument("--tree", type=str, default="",
                     help="comma-separated branching per depth (e.g. 4,4,2,2): measure token-tree verify instead "
                          "of the chain")
+    ap.add_argument("--recurrent", type=int, default=0,
+                    help="N > 0: time verify + commit of a recurrent (gated delta-rule) layer for N sequences "
+                         "instead of the 8B model (32 heads of 128, 4-tap conv, T = gamma + 1)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -126,6 +129,8 @@ def main():
 
     S.lib()  # fail loudly when the HIP library is missing
     dev = torch.device("cuda:0")
+    if a.recurrent:
+        return run_recurrent(a, dev)
     sh = synth.LLAMA8B
     B, ctx, gamma, T = a.batch, a.ctx, a.gamma, a.gamma + 1
     if a.tree:
@@ -420,6 +425,130 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
     }
     log(f"tree: {ms_per_step:.3f} ms/step, {result['value']} tok/s, T_verify {t_verify:.3f} ms, "
         f"T_decode {t_decode:.3f} ms")
+    print(json.dumps(result), flush=True)
+
+
+def run_recurrent(a, dev):
+    """Verify on a recurrent layer (Kimi-K3 tuning page, "Verification on a
+    recurrent layer is not a cache write"): N sequences, a window of
+    T = gamma + 1 positions, 32 heads of width 128, a 4-tap conv.  One step =
+    spec_recurrent_verify over the window + spec_recurrent_commit of the
+    survivor after a synthetic accept count per sequence, with the pool
+    resident in HBM.  Both ways of recovering the survivor are timed: keeping
+    the T candidate states (snapshots, the pages' engines) and replaying the
+    committed positions at commit time; `value` is the replay step, the
+    snapshot step is reported beside it.  A step commits to a copy of the
+    pool, so every step starts from the same state."""
+    import numpy as np
+    import torch
+
+    import synth
+    import speculative_decoding_verify_spec_amd as S
+
+    rs = synth.RECURRENT_8B
+    B, T = a.recurrent, a.gamma + 1
+    H, D, W = rs.n_heads, rs.head_dim, rs.conv_width
+    log(f"recurrent workload: B={B} T={T} H={H} D={D} W={W}")
+    inp = synth.make_recurrent_inputs(rs, B, T, B)
+    d = {k: v.to(dev).contiguous() for k, v in inp.items()}
+    dims = S.spec_recurrent_dims(H, D, W, B)
+    out = torch.empty((B, T, H, D), device=dev)
+    snaps = torch.empty((B, T, H, D, D), device=dev)
+    cs, st = d["conv_state"].clone(), d["state"].clone()
+    g = torch.Generator().manual_seed(synth.SEED_ACCEPT)
+    naccs = [torch.randint(0, T, (B,), generator=g, dtype=torch.int32).to(dev) for _ in range(8)]
+    stream = torch.cuda.current_stream(dev)
+
+    def verify(keep):
+        S.spec_recurrent_verify(dims, B, T, d["x"], d["gate"], d["beta"], d["conv_w"], None, d["conv_state"],
+                                d["state"], out, snaps if keep else None, stream)
+
+    def commit(keep, k):
+        S.spec_recurrent_commit(dims, B, T, d["x"], d["gate"], d["beta"], d["conv_w"], None, naccs[k % 8],
+                                snaps if keep else None, cs, st, stream)
+
+    def timed(fn, iters):
+        for k in range(3):
+            fn(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(iters):
+            fn(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    def step(keep):
+        def f(k):
+            verify(keep)
+            commit(keep, k)
+        return f
+
+    for _ in range(a.warmup):
+        step(True)(0)
+        step(False)(0)
+    torch.cuda.synchronize()
+    ms_snap = timed(step(True), a.steps)
+    ms_replay = timed(step(False), a.steps)
+    # per-kernel averages, launches back to back between one pair of events
+    iters = max(a.steps, 20)
+    us = {"verify_snapshots": timed(lambda k: verify(True), iters) * 1e3,
+          "verify": timed(lambda k: verify(False), iters) * 1e3,
+          "commit_scatter": timed(lambda k: commit(True, k), iters) * 1e3,
+          "commit_replay": timed(lambda k: commit(False, k), iters) * 1e3}
+    # algorithmic bytes (fp32): the state D x D per (sequence, head), the
+    # window's raw channels, gates and betas, the outputs
+    st_b = B * H * D * D * 4
+    win_b = B * T * (3 * H * D + H * D + H) * 4
+    conv_b = B * (W - 1) * 3 * H * D * 4
+    out_b = B * T * H * D * 4
+    nbar = float(torch.stack(naccs).float().mean()) + 1.0  # committed positions per sequence
+    algo = {"verify_snapshots": st_b + T * st_b + win_b + conv_b + out_b,
+            "verify": st_b + win_b + conv_b + out_b,
+            "commit_scatter": 2 * st_b + 2 * conv_b,
+            "commit_replay": 2 * st_b + win_b * nbar / T + 2 * conv_b}
+    kern = {k: {"avg_us": round(us[k], 3), "algo_bytes": int(algo[k]),
+                "GBps": round(algo[k] / (us[k] * 1e-6) / 1e9, 1)} for k in us}
+    for k, v in kern.items():
+        log(f"{k}: {v['avg_us']} us, {v['GBps']} GB/s")
+    # the step that value reports: verify without snapshots + replay commit
+    # (the same committed state as the snapshot scatter, bit for bit); its
+    # longer kernel is the replay commit
+    dom = "commit_replay"
+    roofline = {"bound": "hbm", "kernel": "rec_replay_kernel (survivor state re-advanced, written back)",
+                "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "algo_bytes_per_launch": algo[dom], "avg_launch_us": kern[dom]["avg_us"]}
+    value = B * T / (ms_replay * 1e-3)
+    result = {
+        "metric": "recurrent-state verify: window positions verified per second (verify + survivor commit)",
+        "value": round(value, 1), "unit": "window positions/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_replay, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (random window inputs and states)",
+        "config": {"workload": f"recurrent gated delta-rule verify B={B} T={T} H={H} D={D} conv={W}",
+                   "B": B, "T": T, "heads": H, "head_dim": D, "conv_width": W, "parallelism": "single GPU"},
+        "commit": "replay",
+        "ms_per_step_snapshots": round(ms_snap, 4),
+        "value_snapshots": round(B * T / (ms_snap * 1e-3), 1),
+        "kernels": kern, "roofline": roofline,
+    }
+    if a.cpu_baseline:
+        from oracle import recurrent as OR
+        n = min(B, 4)
+        h = {k: v[:n].double().numpy() if k not in ("conv_w",) else v.double().numpy() for k, v in inp.items()}
+        nacc = naccs[0][:n].cpu().numpy()
+        t0, reps = time.perf_counter(), 0
+        while reps == 0 or time.perf_counter() - t0 < a.cpu_seconds:
+            o, sn = OR.verify(h["x"], h["gate"], h["beta"], h["conv_w"], h["conv_state"], h["state"])
+            OR.commit(h["x"], nacc, h["conv_state"], h["state"], sn)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n * T * reps / dt, 2), "unit": "window positions/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{reps} windows of {n} sequences (the first {n} of the workload), "
+                                            f"verify + snapshot commit; {dt:.1f} s"}
+    log(f"recurrent: {ms_replay:.4f} ms/step (replay), {ms_snap:.4f} ms/step (snapshots)")
     print(json.dumps(result), flush=True)
 
 

@@ -1,5 +1,5 @@
 """Python binding of the MI355X speculative verify step (C ABI in
-include/spec_verify.h).
+include/spec_verify.h and include/spec_recurrent.h).
 
 Argument marshalling only: every function below forwards to the symbol of the
 same name in libspec_verify.so.  Device buffers may be passed as torch tensors
@@ -36,6 +36,7 @@ EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
     "spec_profile_gemm", "spec_graph_enable", "spec_set_block_table", "spec_verify_destroy", "spec_status_str",
+    "spec_recurrent_verify", "spec_recurrent_commit",
 ]
 
 
@@ -55,6 +56,11 @@ class spec_sampling(C.Structure):
 class spec_kernel_stat(C.Structure):
     _fields_ = [("name", C.c_char * 24), ("launches", C.c_int64), ("total_ms", C.c_double),
                 ("algo_bytes", C.c_double)]
+
+
+class spec_recurrent_dims(C.Structure):
+    _fields_ = [("n_heads", C.c_int32), ("head_dim", C.c_int32), ("conv_width", C.c_int32),
+                ("n_slots", C.c_int32)]
 
 
 class SpecError(RuntimeError):
@@ -110,6 +116,12 @@ def lib():
     L.spec_verify_destroy.restype = None
     L.spec_status_str.argtypes = [i32]
     L.spec_status_str.restype = C.c_char_p
+    L.spec_recurrent_verify.argtypes = [C.POINTER(spec_recurrent_dims), i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]
+    L.spec_recurrent_verify.restype = i32
+    L.spec_recurrent_commit.argtypes = [C.POINTER(spec_recurrent_dims), i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]
+    L.spec_recurrent_commit.restype = i32
     _lib = L
     return L
 
@@ -250,3 +262,23 @@ def spec_graph_enable(h, enable: bool):
 def spec_verify_destroy(h):
     if h:
         lib().spec_verify_destroy(h)
+
+
+def spec_recurrent_verify(dims: spec_recurrent_dims, B, T, x, gate, beta, conv_w, slot, conv_state, state, out,
+                          snapshots=None, stream=None, check=True):
+    st = lib().spec_recurrent_verify(C.byref(dims), int(B), int(T), _ptr(x), _ptr(gate), _ptr(beta),
+                                     _ptr(conv_w), _ptr(slot), _ptr(conv_state), _ptr(state), _ptr(out),
+                                     _ptr(snapshots), _stream(stream))
+    if check:
+        _check("spec_recurrent_verify", st)
+    return st
+
+
+def spec_recurrent_commit(dims: spec_recurrent_dims, B, T, x, gate, beta, conv_w, slot, num_accepted, snapshots,
+                          conv_state, state, stream=None, check=True):
+    st = lib().spec_recurrent_commit(C.byref(dims), int(B), int(T), _ptr(x), _ptr(gate), _ptr(beta),
+                                     _ptr(conv_w), _ptr(slot), _ptr(num_accepted), _ptr(snapshots),
+                                     _ptr(conv_state), _ptr(state), _stream(stream))
+    if check:
+        _check("spec_recurrent_commit", st)
+    return st

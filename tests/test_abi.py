@@ -2,6 +2,7 @@
 header declares, sizes buffers as documented and rejects bad arguments before
 touching the device (all without a GPU)."""
 import ctypes as C
+import glob
 import os
 import re
 
@@ -10,11 +11,12 @@ import pytest
 import speculative_decoding_verify_spec_amd as S
 import synth
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "spec_verify.h")
+HEADERS = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                                        "*.h")))
 
 
 def _declared():
-    txt = open(HEADER).read()
+    txt = "".join(open(h).read() for h in HEADERS)
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", txt)))
 
@@ -94,3 +96,39 @@ def test_calls_on_null_handle_are_rejected():
     assert S.lib().spec_profile_enable(None, 1) == S.SPEC_ERR_INVALID_ARG
     assert S.lib().spec_profile_read(None, None, 0, 0) == -1
     S.spec_verify_destroy(None)
+
+
+def test_recurrent_calls_reject_bad_arguments_without_device():
+    dims = S.spec_recurrent_dims(4, 128, 4, 8)
+    P = 256  # a fake, aligned address: nothing is launched on these paths
+    ok = dict(x=P, gate=P, beta=P, conv_w=P, slot=None, conv_state=P, state=P, out=P)
+
+    def ver(d=dims, B=2, T=4, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return S.spec_recurrent_verify(d, B, T, a["x"], a["gate"], a["beta"], a["conv_w"], a["slot"],
+                                       a["conv_state"], a["state"], a["out"], None, None, check=False)
+
+    def com(d=dims, B=2, T=4, snaps=None, **kw):
+        a = dict(ok, nacc=P)
+        a.update(kw)
+        return S.spec_recurrent_commit(d, B, T, a["x"], a["gate"], a["beta"], a["conv_w"], a["slot"], a["nacc"],
+                                       snaps, a["conv_state"], a["state"], None, check=False)
+
+    assert ver(B=0) == S.SPEC_OK and com(B=0) == S.SPEC_OK  # empty batch: nothing to do
+    for bad in (S.spec_recurrent_dims(0, 128, 4, 8), S.spec_recurrent_dims(4, 96, 4, 8),
+                S.spec_recurrent_dims(4, 128, 0, 8), S.spec_recurrent_dims(4, 128, 9, 8),
+                S.spec_recurrent_dims(4, 128, 4, 0)):
+        assert ver(d=bad) == S.SPEC_ERR_SHAPE and com(d=bad) == S.SPEC_ERR_SHAPE
+    assert ver(T=0) == S.SPEC_ERR_INVALID_ARG and ver(T=17) == S.SPEC_ERR_INVALID_ARG
+    assert ver(B=-1) == S.SPEC_ERR_INVALID_ARG
+    assert ver(B=9) == S.SPEC_ERR_INVALID_ARG  # more sequences than pool rows, no slot map
+    assert ver(x=None) == S.SPEC_ERR_INVALID_ARG and ver(out=None) == S.SPEC_ERR_INVALID_ARG
+    assert ver(conv_state=None) == S.SPEC_ERR_INVALID_ARG
+    assert ver(state=P + 4) == S.SPEC_ERR_INVALID_ARG  # misaligned
+    assert com(nacc=None) == S.SPEC_ERR_INVALID_ARG
+    assert com(gate=None) == S.SPEC_ERR_INVALID_ARG  # replay needs the window inputs
+    assert com(B=0, gate=None, snaps=P) == S.SPEC_OK  # the scatter does not
+    assert com(x=None, snaps=P) == S.SPEC_ERR_INVALID_ARG  # conv state needs x when W > 1
+    assert S.lib().spec_recurrent_verify(None, 1, 1, P, P, P, P, None, P, P, P, None, None) == \
+        S.SPEC_ERR_INVALID_ARG
