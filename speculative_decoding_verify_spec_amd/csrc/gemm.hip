@@ -336,9 +336,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const bool ok = kok[i] && (m < p.M);
-      const float* xs = p.X + (size_t)(m < p.M ? m : 0) * p.ldx + kofs[i];
-      const float4 a = *(const float4*)xs;
-      const float4 b = *(const float4*)(xs + 4);
+      const int mm = m < p.M ? m : 0;
+      const float* xs = p.X + (size_t)mm * p.ldx + kofs[i];
+      float4 a = *(const float4*)xs;
+      float4 b = *(const float4*)(xs + 4);
+      if (p.xpart) {
+        // the deferred reduce of the previous residual GEMM, in its order
+        float4 ta = make_float4(0.f, 0.f, 0.f, 0.f), tb = ta;
+#pragma unroll
+        for (int sl = 0; sl < GEMM_KSPLIT; ++sl) {
+          const float* ps = p.xpart + ((size_t)(sl * 8 + mm)) * p.ldx + kofs[i];
+          const float4 pa = *(const float4*)ps;
+          const float4 pb = *(const float4*)(ps + 4);
+          ta.x += pa.x; ta.y += pa.y; ta.z += pa.z; ta.w += pa.w;
+          tb.x += pb.x; tb.y += pb.y; tb.z += pb.z; tb.w += pb.w;
+        }
+        a.x += ta.x; a.y += ta.y; a.z += ta.z; a.w += ta.w;
+        b.x += tb.x; b.y += tb.y; b.z += tb.z; b.w += tb.w;
+        if (blockIdx.x == 0 && ok) {
+          float* xo = p.xout + (size_t)m * p.ldx + kofs[i];
+          *(float4*)xo = a;
+          *(float4*)(xo + 4) = b;
+        }
+      }
       xr[i][m][0] = ok ? a.x : 0.f; xr[i][m][1] = ok ? a.y : 0.f;
       xr[i][m][2] = ok ? a.z : 0.f; xr[i][m][3] = ok ? a.w : 0.f;
       xr[i][m][4] = ok ? b.x : 0.f; xr[i][m][5] = ok ? b.y : 0.f;
@@ -690,6 +710,12 @@ bool gemm_use_split(const GemmParams& p) {
   return p.K / GEMM_KSPLIT <= KSTAT_WAVES * 8 * 128;
 }
 
+bool gemm_takes_xpart(const GemmParams& p) {
+  // the k-stationary kernel with a fused norm, one launch of at most 4 rows
+  return p.epi == EPI_QKV && p.norm_g && p.M >= 1 && p.M <= 4 && !gemm_tiled_ok(p) && !gemm_blas_ok(p) &&
+         !gemm_use_mfma(p, p.M) && gemm_is_kstat(p.K) && p.K % 512 == 0;
+}
+
 template <int MT>
 static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
   const int groups = gemm_groups<EPI_RESID>(p);
@@ -700,7 +726,7 @@ static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
   if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
   else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
   else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  gemm_split_reduce_kernel<<<(p.M * p.N + 255) / 256, 256, 0, s>>>(p);
+  if (!p.defer_reduce) gemm_split_reduce_kernel<<<(p.M * p.N + 255) / 256, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -777,6 +803,7 @@ static hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  if (p.xpart && !gemm_takes_xpart(p)) return hipErrorInvalidValue;
   if (gemm_tiled_ok(p)) return launch_gemm_tiled(p, s);
   if (p.M <= 1) return launch_mt<1>(p, s);
   if (p.M <= 2) return launch_mt<2>(p, s);

@@ -76,10 +76,26 @@ struct GemmParams {
   // many rows: the library GEMM path (null: not available)
   struct BlasCtx* blas;
   KvMap kvm;                // cache addressing of the QKV epilogue's writes
+  // Activation rows still owed the K-slice partial sums of a split residual
+  // GEMM whose reduce was deferred: with xpart set, row m is taken as
+  // X[m][k] + (xpart[(0*8+m)*ldx+k] + ... + xpart[(3*8+m)*ldx+k]), the slices
+  // summed in order and the sum added to X as the reduce kernel does, and
+  // the launch's first workgroup stores the completed rows to xout ([M][ldx],
+  // not X).  Only the k-stationary kernel takes it (gemm_takes_xpart).
+  const float* xpart;
+  float* xout;
+  // split residual GEMM: leave the partial sums in `part` for the next
+  // GEMM's prologue instead of launching the reduce
+  bool defer_reduce;
 };
 constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// the residual GEMM of these parameters runs as K slices + reduce
+bool gemm_use_split(const GemmParams& p);
+// the launch of these parameters can complete its activation rows from
+// deferred partial sums (xpart / xout)
+bool gemm_takes_xpart(const GemmParams& p);
 // the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
 bool gemm_tiled_ok(const GemmParams& p);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);

@@ -96,7 +96,7 @@ struct StepShape {
 };
 
 struct Layout {
-  size_t x, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
+  size_t x, x2, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
   size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, gbws, gbd, rowstat, rowms, rsum, nacc, rbuf, fcnt, fmass, fstate, fres,
       flags, total;
 };
@@ -119,6 +119,7 @@ Layout plan(const spec_config& c) {
     return o;
   };
   L.x = take(Mmax * c.d_model * 4);
+  L.x2 = take(Mmax * c.d_model * 4);  // residual rows, second buffer (deferred reduce)
   L.q = take(Mmax * Hq * D * 4);
   L.ksuf = take(Mmax * Hkv * D * 4);
   L.vsuf = take(Mmax * Hkv * D * 4);
@@ -241,16 +242,22 @@ KvMap kv_map(const spec_handle* h) {
   return KvMap{h->kv_table, h->kv_ppseq, c.kv_pages, c.max_ctx};
 }
 
-hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
-  const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
-  const size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
-  const size_t out_cols = (p.epi == EPI_SWIGLU) ? p.F : p.N;
+// the library's scratch buffers in a GEMM's parameters
+void gemm_scratch(const spec_handle* h, GemmParams& p) {
   p.part = h->at<float>(h->lay.gpart);
   p.part_floats = gemm_part_floats(h->cfg);
   p.xs = h->at<uint16_t>(h->lay.gxs);
   p.xs_elems = gemm_xs_elems(h->cfg);
   p.xs_ssq = h->at<float>(h->lay.gssq);
   p.blas = h->blas;
+}
+
+hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
+  const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
+  const size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
+  const size_t out_cols = (p.epi == EPI_SWIGLU) ? p.F : p.N;
+  gemm_scratch(h, p);
+  if (p.xpart && M > 8) return hipErrorInvalidValue;  // the partial sums are one launch's rows
   {
     GemmParams q = p;
     q.M = M;
@@ -287,6 +294,31 @@ hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s
 
 namespace {
 
+// At M rows the down projection runs as K slices and the next layer's QKV
+// launch can finish their reduce in its prologue: then the reduce kernel of
+// every layer but the last is left out.  The residual rows alternate between
+// two buffers, because the QKV launch reads the old rows in every workgroup
+// while its first workgroup writes the completed ones.
+bool defer_down_reduce(const spec_handle* h, int M) {
+  const spec_config& c = h->cfg;
+  GemmParams gd{};
+  gd.wdtype = c.weight_dtype; gd.ldx = c.d_ffn; gd.N = c.d_model; gd.K = c.d_ffn; gd.M = M;
+  gd.epi = EPI_RESID; gd.ldo = c.d_model;
+  gemm_scratch(h, gd);
+  GemmParams gq{};
+  gq.wdtype = c.weight_dtype; gq.ldx = c.d_model; gq.N = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  gq.K = c.d_model; gq.M = M; gq.epi = EPI_QKV;
+  gq.norm_g = (const float*)h->W(h->layer_w(0, 0));
+  gemm_scratch(h, gq);
+  return c.n_layers > 1 && gemm_use_split(gd) && gemm_takes_xpart(gq);
+}
+
+// residual rows the LM head reads after the layers
+float* final_residual(const spec_handle* h, int M) {
+  const bool odd = defer_down_reduce(h, M) && (h->cfg.n_layers - 1) % 2 == 1;
+  return h->at<float>(odd ? h->lay.x2 : h->lay.x);
+}
+
 // The per-layer kernels of a step.  They read only the weights, the cache and
 // the workspace (kv_len through its copy made by the prep kernel), so for a
 // given (B, T, chain/tree) the launch sequence is fixed and can be recorded.
@@ -313,6 +345,9 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   const int splits = attn_splits(c, B, T);
   const int nsplit = attn_nsplit(splits);
   const float scale = 1.0f / std::sqrt((float)D);
+  const bool defer = defer_down_reduce(h, M);
+  float* x2 = h->at<float>(L.x2);
+  float* cur = x;  // residual rows entering the layer
 
   for (int l = 0; l < c.n_layers; ++l) {
     const float* g1 = (const float*)h->W(h->layer_w(l, 0));
@@ -324,8 +359,15 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
     uint16_t* kreg = h->kv + (size_t)(2 * l) * per_region;
     uint16_t* vreg = h->kv + (size_t)(2 * l + 1) * per_region;
 
+    // with the previous layer's down reduce deferred, the QKV launch
+    // completes the rows into the other buffer, which the layer then updates
+    float* nxt = (defer && l > 0) ? (cur == x ? x2 : x) : cur;
     GemmParams gq{};
-    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = x; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    gq.W = wqkv; gq.wdtype = c.weight_dtype; gq.X = cur; gq.ldx = d; gq.N = (Hq + 2 * Hkv) * D; gq.K = d;
+    if (nxt != cur) {
+      gq.xpart = h->at<float>(L.gpart);
+      gq.xout = nxt;
+    }
     gq.norm_g = g1; gq.eps = c.rms_eps;
     gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
     gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
@@ -345,19 +387,21 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
 
     GemmParams go{};
     go.W = wo; go.wdtype = c.weight_dtype; go.X = at; go.ldx = Hq * D; go.N = d; go.K = Hq * D;
-    go.epi = EPI_RESID; go.out = x; go.ldo = d;
+    go.epi = EPI_RESID; go.out = nxt; go.ldo = d;
     if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return e;
 
     GemmParams gg{};
-    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = x; gg.ldx = d; gg.N = 2 * F; gg.K = d;
+    gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = nxt; gg.ldx = d; gg.N = 2 * F; gg.K = d;
     gg.norm_g = g2; gg.eps = c.rms_eps;
     gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
     if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return e;
 
     GemmParams gd{};
     gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
-    gd.epi = EPI_RESID; gd.out = x; gd.ldo = d;
+    gd.epi = EPI_RESID; gd.out = nxt; gd.ldo = d;
+    gd.defer_reduce = defer && l + 1 < c.n_layers;
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
+    cur = nxt;
   }
   return hipSuccess;
 }
@@ -542,7 +586,8 @@ spec_status verify_forward(spec_handle* h, const StepShape& sh, const int32_t* d
 
   const float* gf = (const float*)h->W(1 + 6 * (size_t)c.n_layers);
   GemmParams gl{};
-  gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = x; gl.ldx = d; gl.N = V;
+  gl.W = h->W(2 + 6 * (size_t)c.n_layers); gl.wdtype = c.weight_dtype; gl.X = final_residual(h, M); gl.ldx = d;
+  gl.N = V;
   gl.K = d; gl.epi = EPI_STORE; gl.out = d_logits; gl.ldo = V;
   gl.norm_g = gf; gl.eps = c.rms_eps;
   if ((e = gemm_rows(h, K_LM, gl, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
