@@ -39,6 +39,7 @@ constexpr int YT = 8;            // weight rows per row group
 constexpr int KSTAT_WAVES = 4;   // waves per workgroup, k-stationary kernel
 constexpr int KSTAT_SPW = 2;     // K steps per wave, k-stationary kernel
 constexpr int STREAM_WAVES = 8;  // waves per workgroup, streaming kernel
+constexpr int SPLIT_WAVES = 8;   // waves per workgroup, K-split matrix-core kernel
 
 template <int MT>
 struct MaxPow2 {
@@ -707,7 +708,7 @@ static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
 bool gemm_use_split(const GemmParams& p) {
   if (!p.part || p.part_floats < (size_t)GEMM_KSPLIT * 8 * p.ldo || p.epi != EPI_RESID || p.norm_g || p.wdtype != 1 || p.M < 3) return false;
   if (p.K <= KSTAT_WAVES * 8 * 128 || p.K % (GEMM_KSPLIT * 128)) return false;
-  return p.K / GEMM_KSPLIT <= KSTAT_WAVES * 8 * 128;
+  return p.K / GEMM_KSPLIT <= SPLIT_WAVES * 8 * 128;
 }
 
 bool gemm_takes_xpart(const GemmParams& p) {
@@ -719,13 +720,13 @@ bool gemm_takes_xpart(const GemmParams& p) {
 template <int MT>
 static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
   const int groups = gemm_groups<EPI_RESID>(p);
-  const int slots = 2 * device_cus() / GEMM_KSPLIT;
+  const int slots = device_cus() / GEMM_KSPLIT;  // one 8-wave workgroup per CU
   const int rounds = (groups + slots - 1) / slots;
   const dim3 grid((groups + rounds - 1) / rounds, GEMM_KSPLIT);
-  const int cpw = ((p.K / GEMM_KSPLIT >> 7) + KSTAT_WAVES - 1) / KSTAT_WAVES;
-  if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
-  else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true, KSTAT_WAVES><<<grid, 64 * KSTAT_WAVES, 0, s>>>(p);
+  const int cpw = ((p.K / GEMM_KSPLIT >> 7) + SPLIT_WAVES - 1) / SPLIT_WAVES;
+  if (cpw <= 4) gemm_mfma_kernel<MT, EPI_RESID, false, 4, true, SPLIT_WAVES><<<grid, 64 * SPLIT_WAVES, 0, s>>>(p);
+  else if (cpw <= 7) gemm_mfma_kernel<MT, EPI_RESID, false, 7, true, SPLIT_WAVES><<<grid, 64 * SPLIT_WAVES, 0, s>>>(p);
+  else gemm_mfma_kernel<MT, EPI_RESID, false, 8, true, SPLIT_WAVES><<<grid, 64 * SPLIT_WAVES, 0, s>>>(p);
   if (!p.defer_reduce) gemm_split_reduce_kernel<<<(p.M * p.N + 255) / 256, 256, 0, s>>>(p);
   return hipGetLastError();
 }

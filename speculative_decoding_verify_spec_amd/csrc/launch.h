@@ -88,7 +88,7 @@ struct GemmParams {
   // GEMM's prologue instead of launching the reduce
   bool defer_reduce;
 };
-constexpr int GEMM_KSPLIT = 4;  // K slices of the skinny residual GEMM
+constexpr int GEMM_KSPLIT = 2;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // the residual GEMM of these parameters runs as K slices + reduce
