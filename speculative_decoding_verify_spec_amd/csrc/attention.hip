@@ -30,9 +30,20 @@
 
 namespace sv {
 
-// Query groups (16 query vectors) per context workgroup: two when there are
-// at least two, so that both groups' waves read each key block on one CU.
-int attn_groups_per_wg(int nq) { return nq > 16 ? 2 : 1; }
+// Shapes of the context workgroups, by the queries nq of a (sequence, KV
+// head):
+//   nq <= 16: one 16-query tile per wave, two workgroups per CU;
+//   16 < nq <= 64 (chain windows of 5..16 rows): two 16-query tiles per
+//     wave, so every wave's key block serves 32 queries, and two key blocks
+//     in flight per wave (PFB = 2), which needs more than 256 registers per
+//     lane: one workgroup per CU.  At B = 16, 32K context, T = 8: 496 us
+//     against 609 us for the form below;
+//   nq > 64 (token trees): two 16-query groups per workgroup that walk the
+//     same key blocks, two workgroups per CU.  The one-per-CU form would also
+//     run the many suffix workgroups of a tree one per CU (32.1 against
+//     29.9 ms per step at B = 4, tree [4,4,2,2]).
+int attn_query_tiles(int nq) { return (nq > 16 && nq <= 64) ? 2 : 1; }
+int attn_groups_per_wg(int nq) { return nq > 64 ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
@@ -143,8 +154,10 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
   }
 }
 
-template <int D, int QT, int QGW>
-__global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
+// PFB: key blocks each wave has in flight.  With PFB = 1 two workgroups fit
+// on a CU; with more, one.
+template <int D, int QT, int QGW, int PFB>
+__global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnParams p) {
   constexpr int DG = D / 4;   // dims per lane group
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 16;  // output dim tiles
@@ -152,8 +165,8 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
   const int j = lane & 15, g = lane >> 4;
   const int G = p.Hq / p.Hkv;
   const int nq = G * p.T;
-  // Query groups of 16 query vectors.  A context workgroup serves QGW of
-  // them: its waves form QGW sets of WPG waves, set q holding group
+  // Query groups of 16 * QT query vectors.  A context workgroup serves QGW
+  // of them: its waves form QGW sets of WPG waves, set q holding group
   // QGW * qgw + q, and the sets walk the same key blocks, so each block is
   // fetched from HBM once per workgroup (the second set's reads hit the CU's
   // cache).
@@ -207,9 +220,9 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
   // keys at or past kend read as zeros.  A block's 32 slots are contiguous
   // (one page holds two blocks), so one lookup places the whole block.
   const int vstride = kv_v_stride(p.kvm);
-  uint4 kraw[2][DG / 8];
-  uint4 vraw[DT];
-  auto load_block = [&](int kb) {
+  uint4 kraw[PFB][2][DG / 8];
+  uint4 vraw[PFB][DT];
+  auto load_block = [&](int kb, int sl) {
     const uint16_t* kblk = p.kc + kv_k_off(p.kvm, p.Hkv, D, b, kvh, kb);
     const uint16_t* vblk = p.vc + kv_v_off(p.kvm, p.Hkv, D, b, kvh, 0, kb);
 #pragma unroll
@@ -218,17 +231,20 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
       const bool ok = key < kend;
       const uint16_t* src = kblk + (size_t)(ok ? key - kb : 0) * D + g * DG;
 #pragma unroll
-      for (int e = 0; e < DG / 8; ++e) kraw[kt][e] = ok ? *(const uint4*)(src + 8 * e) : make_uint4(0, 0, 0, 0);
+      for (int e = 0; e < DG / 8; ++e) kraw[sl][kt][e] = ok ? *(const uint4*)(src + 8 * e) : make_uint4(0, 0, 0, 0);
     }
     const int k8 = kb + 8 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint16_t* src = vblk + (size_t)(dt * 16 + j) * vstride + (k8 < kend ? 8 * g : 0);
-      vraw[dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
+      vraw[sl][dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
     }
   };
-  int kb = kbeg + 32 * kw;
-  if (kb < kend) load_block(kb);
+#pragma unroll
+  for (int sl = 0; sl < PFB; ++sl) {
+    const int kb0 = kbeg + 32 * kw + sl * 32 * WPG;
+    if (kb0 < kend) load_block(kb0, sl);
+  }
 
   // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
   // g*DG + 4*ks + e for k-step ks.
@@ -272,14 +288,18 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (; kb < kend; kb += 32 * WPG) {
+  for (int kbase = kbeg + 32 * kw; kbase < kend; kbase += 32 * WPG * PFB) {
+#pragma unroll
+  for (int sl = 0; sl < PFB; ++sl) {
+    const int kb = kbase + sl * 32 * WPG;
+    if (kb >= kend) break;
     // ---- K operand (A of S^T): lane row j of tile kt is key blk_key(kb, kt, j)
     shortx4 ka[2][KSTEPS];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < DG / 8; ++e) {
-        const uint4 v = kraw[kt][e];
+        const uint4 v = kraw[sl][kt][e];
         const int ks = 2 * e;
         ka[kt][ks][0] = (short)(v.x & 0xffff); ka[kt][ks][1] = (short)(v.x >> 16);
         ka[kt][ks][2] = (short)(v.y & 0xffff); ka[kt][ks][3] = (short)(v.y >> 16);
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
       const int k8 = kb + 8 * g;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint4 v = vraw[dt];
+        const uint4 v = vraw[sl][dt];
         uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -303,11 +323,11 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
         }
       }
     }
-    // the wave's next block (long contexts) is requested as soon as this
-    // one's raw registers are converted, so its latency overlaps this block's
-    // products; two workgroups per CU still fit (238 VGPRs, no spills),
-    // measured at 32K context: 440 -> 409 us at T = 1, 682 -> 599 us at T = 8
-    if (kb + 32 * WPG < kend) load_block(kb + 32 * WPG);
+    // the block PFB further on takes this one's raw registers as soon as they
+    // are converted, so its latency overlaps the products of the blocks in
+    // between; with PFB = 1 two workgroups per CU still fit (240 VGPRs, no
+    // spills), measured at 32K context: 440 -> 409 us at T = 1
+    if (kb + 32 * WPG * PFB < kend) load_block(kb + 32 * WPG * PFB, sl);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       floatx4 st[2];
@@ -361,6 +381,7 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
     }
   }
 
+  }
   // ---- merge the waves of each query group in LDS and write one partial
   // per query
 #pragma unroll
@@ -419,21 +440,23 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_kernel(AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nq = (p.Hq / p.Hkv) * p.T;
-  const int nqg = (nq + 15) / 16;
-  const int QGW = attn_groups_per_wg(nq);
+  const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
+  const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int nqw = (nqg + QGW - 1) / QGW;
   if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
-  // (context splits + 4 suffix workgroups per query group) per (kv head,
+  // (context splits + 4 * QT * QGW suffix workgroups) per (kv head,
   // sequence), each repeated per set of QGW query groups, laid out XCD by
   // XCD (see the kernel)
-  const int units = (p.splits + 4 * QGW) * p.Hkv * p.B;
+  const int units = (p.splits + 4 * QT * QGW) * p.Hkv * p.B;
   const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
-    if (QGW == 1) attn_ctx_kernel<128, 1, 1><<<grid, 256, 0, s>>>(p);
-    else attn_ctx_kernel<128, 1, 2><<<grid, 256, 0, s>>>(p);
+    if (QT == 2) attn_ctx_kernel<128, 2, 1, 2><<<grid, 256, 0, s>>>(p);
+    else if (QGW == 2) attn_ctx_kernel<128, 1, 2, 1><<<grid, 256, 0, s>>>(p);
+    else attn_ctx_kernel<128, 1, 1, 1><<<grid, 256, 0, s>>>(p);
   } else {
-    if (QGW == 1) attn_ctx_kernel<64, 1, 1><<<grid, 256, 0, s>>>(p);
-    else attn_ctx_kernel<64, 1, 2><<<grid, 256, 0, s>>>(p);
+    if (QT == 2) attn_ctx_kernel<64, 2, 1, 2><<<grid, 256, 0, s>>>(p);
+    else if (QGW == 2) attn_ctx_kernel<64, 1, 2, 1><<<grid, 256, 0, s>>>(p);
+    else attn_ctx_kernel<64, 1, 1, 1><<<grid, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }

@@ -46,11 +46,13 @@ size_t kv_region_elems(const spec_config& c) {
 // workgroups and the combine merges at most 128 partials (with the suffix's).
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
-  const int nqg = (nq + 15) / 16;
-  const int QGW = attn_groups_per_wg(nq);
+  const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
+  const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int units = B * c.n_kv_heads * ((nqg + QGW - 1) / QGW);
   int s = (c.max_ctx + 127) / 128;
-  const int cap = std::max(1, (4096 + units - 1) / units);
+  // about 4096 context workgroups at two per CU (16-query tiles), 2048 at
+  // one per CU (32-query tiles); measured at 32K context
+  const int cap = std::max(1, ((QT == 1 ? 4096 : 2048) + units - 1) / units);
   s = std::min(s, cap);
   return std::max(1, std::min(s, 127));
 }
