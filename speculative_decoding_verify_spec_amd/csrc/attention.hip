@@ -51,12 +51,13 @@ int attn_nsplit(int splits) { return splits + 1; }
 // load of V^T feeds both tiles.
 DEVI int blk_key(int kb, int kt, int r) { return kb + 8 * (r >> 2) + 4 * kt + (r & 3); }
 
-// The step's own keys, in fp32, for four queries of one (sequence, KV head,
-// query group): suffix workgroup sw takes queries 4*sw .. 4*sw+3 of the
-// group, one per wave.  The queries are staged in LDS, the keys and values
-// come through LDS in chunks of KC rows shared by the four waves; scores are
-// lane-parallel over the chunk's keys, the value sum lane-parallel over
-// dimensions.  `smem` must hold 4*D + 2*KC*(D+4) floats.
+// The step's own keys of a chain, in fp32, for four queries of one
+// (sequence, KV head, query group): suffix workgroup sw takes queries
+// 4*sw .. 4*sw+3 of the group, one per wave; row i sees rows 0..i.  The
+// queries are staged in LDS, the keys and values come through LDS in chunks
+// of KC rows shared by the four waves; scores are lane-parallel over the
+// chunk's keys, the value sum lane-parallel over dimensions.  `smem` must
+// hold 4*D + 2*KC*(D+4) floats.
 template <int D, int QT>
 DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float* smem) {
   constexpr int PL = D / 64;
@@ -114,7 +115,7 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
     if (!qok) continue;  // wave-uniform; the barriers above are shared by all
     const int jj = c0 + lane;
     bool vis = lane < KC && jj < Tb;
-    if (vis) vis = p.anc ? (((p.anc[2 * (rs + i) + (jj >> 6)] >> (jj & 63)) & 1ull) != 0) : (jj <= i);
+    if (vis) vis = jj <= i;
     float sc = -INFINITY;
     if (vis) {
       const float* qr = s_q + w * D;
@@ -154,6 +155,100 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float
   }
 }
 
+// One query of the tree suffix (attn_suffix_tree below).
+template <int D>
+DEVI void attn_suffix_tree_query(const AttnParams& p, int kvh, int b, int qi) {
+  constexpr int PL = D / 64;
+  constexpr int SB = 8;  // visible rows whose loads are in flight at once
+  const int lane = threadIdx.x & 63;
+  const int G = p.Hq / p.Hkv;
+  const int Tb = p.rlen ? p.rlen[b] : p.T;
+  const int rs = p.rstart ? p.rstart[b] : b * p.T;
+  const int nq = G * p.T;
+  const int i = qi / G;
+  float qv[PL];
+  const float* qsrc = p.q + ((size_t)(rs + i) * p.Hq + kvh * G + qi % G) * D;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) qv[e] = qsrc[lane + 64 * e] * p.scale;
+  // visible rows: the ancestor-or-self bits of row i, below the sequence's
+  // row count
+  uint64_t lo = p.anc[2 * (rs + i)], hi = p.anc[2 * (rs + i) + 1];
+  if (Tb < 64) lo &= (1ull << Tb) - 1ull;
+  if (Tb <= 64) hi = 0;
+  else if (Tb < 128) hi &= (1ull << (Tb - 64)) - 1ull;
+  float m = -INFINITY, l = 0.f, o[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) o[e] = 0.f;
+  while (lo | hi) {
+    int js[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      int j = -1;
+      if (lo) {
+        j = __builtin_ctzll(lo);
+        lo &= lo - 1ull;
+      } else if (hi) {
+        j = 64 + __builtin_ctzll(hi);
+        hi &= hi - 1ull;
+      }
+      js[k] = j;
+    }
+    float kk[SB][PL], vv[SB][PL];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      const size_t src = ((size_t)(rs + (js[k] < 0 ? 0 : js[k])) * p.Hkv + kvh) * D;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) {
+        kk[k][e] = js[k] >= 0 ? p.k_suf[src + lane + 64 * e] : 0.f;
+        vv[k][e] = js[k] >= 0 ? p.v_suf[src + lane + 64 * e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (js[k] < 0) break;  // wave-uniform
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) t += qv[e] * kk[k][e];
+      const float sc = wave_sum(t);
+      const float mn = fmaxf(m, sc);
+      const float f = (m == -INFINITY) ? 0.f : __expf(m - mn);
+      const float pe = __expf(sc - mn);
+      l = l * f + pe;
+      m = mn;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) o[e] = o[e] * f + pe * vv[k][e];
+    }
+  }
+  const size_t slot = (((size_t)p.splits * p.B + b) * p.Hkv + kvh) * nq;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) p.part_o[(slot + qi) * D + lane + 64 * e] = o[e];
+  if (lane == 0) {
+    p.part_ml[2 * (slot + qi)] = m;
+    p.part_ml[2 * (slot + qi) + 1] = l;
+  }
+}
+
+// The step's own keys of a token tree: a node sees itself and its ancestors
+// only (CS349E Lecture 6, section 10.3), a handful of the tree's nodes, so
+// each wave walks the set bits of its query's ancestor mask instead of every
+// suffix row: the keys and values of up to SB visible rows are requested at
+// once, straight from the fp32 suffix buffers, then folded into an online
+// softmax one key at a time (scores reduced over the wave).  No LDS, no
+// barrier: waves of one workgroup are independent here.  Workgroup `sub` of a
+// query group takes its queries 16*sub .. 16*sub+15, four per wave.
+template <int D, int QT>
+DEVI void attn_suffix_tree(const AttnParams& p, int kvh, int qg, int b, int sub) {
+  constexpr int QN = QT * 16;
+  const int w = threadIdx.x >> 6;
+  const int G = p.Hq / p.Hkv;
+  const int Tb = p.rlen ? p.rlen[b] : p.T;
+  for (int k = 0; k < 4; ++k) {
+    const int qi = qg * QN + 16 * sub + 4 * w + k;
+    if (qi >= G * Tb) break;  // wave-uniform
+    attn_suffix_tree_query<D>(p, kvh, b, qi);
+  }
+}
+
 // PFB: key blocks each wave has in flight.  With PFB = 1 two workgroups fit
 // on a CU; with more, one.
 template <int D, int QT, int QGW, int PFB>
@@ -179,7 +274,9 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   // are given ids that land on the same XCD one after another: unit u =
   // (split, kv head, sequence) goes to XCD u % 8, and its sets take
   // consecutive places in that XCD's sequence.
-  const int ncol = p.splits + 4 * QT * QGW;        // context splits + suffix workgroups
+  // context splits + suffix workgroups (four queries each for a chain,
+  // sixteen for a tree)
+  const int ncol = p.splits + (p.anc ? QT * QGW : 4 * QT * QGW);
   const int units = ncol * p.Hkv * p.B;
   const int id = blockIdx.x;
   const int n = id / 8;
@@ -198,9 +295,11 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   static_assert(4 * D + 2 * 16 * (D + 4) <= 4 * QN * OS, "suffix staging must fit the output stage");
   if (s >= p.splits) {  // the step's own keys; the output stage is its scratch
     const int sw = s - p.splits;
-    const int grp = qgw * QGW + sw / (4 * QT);
+    const int per = p.anc ? QT : 4 * QT;  // suffix workgroups per query group
+    const int grp = qgw * QGW + sw / per;
     if (grp >= nqg) return;
-    attn_suffix<D, QT>(p, kvh, grp, b, sw % (4 * QT), &s_o[0][0]);
+    if (p.anc) attn_suffix_tree<D, QT>(p, kvh, grp, b, sw % per);
+    else attn_suffix<D, QT>(p, kvh, grp, b, sw % per, &s_o[0][0]);
     return;
   }
   const int qsub = w / WPG, kw = w % WPG;
@@ -444,10 +543,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int nqw = (nqg + QGW - 1) / QGW;
   if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
-  // (context splits + 4 * QT * QGW suffix workgroups) per (kv head,
-  // sequence), each repeated per set of QGW query groups, laid out XCD by
-  // XCD (see the kernel)
-  const int units = (p.splits + 4 * QT * QGW) * p.Hkv * p.B;
+  // (context splits + suffix workgroups) per (kv head, sequence), each
+  // repeated per set of QGW query groups, laid out XCD by XCD (see the
+  // kernel)
+  const int units = (p.splits + (p.anc ? QT * QGW : 4 * QT * QGW)) * p.Hkv * p.B;
   const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
     if (QT == 2) attn_ctx_kernel<128, 2, 1, 2><<<grid, 256, 0, s>>>(p);

@@ -50,9 +50,10 @@ int attn_splits(const spec_config& c, int B, int T) {
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int units = B * c.n_kv_heads * ((nqg + QGW - 1) / QGW);
   int s = (c.max_ctx + 127) / 128;
-  // about 4096 context workgroups at two per CU (16-query tiles), 2048 at
-  // one per CU (32-query tiles); measured at 32K context
-  const int cap = std::max(1, ((QT == 1 ? 4096 : 2048) + units - 1) / units);
+  // about 4096 context workgroups with one 16-query group per workgroup,
+  // at most 2048 for the other two shapes (measured at 32K context, T = 8,
+  // and on the [4,4,2,2] tree at 4K context)
+  const int cap = (QT == 1 && QGW == 1) ? std::max(1, (4096 + units - 1) / units) : std::max(1, 2048 / units);
   s = std::min(s, cap);
   return std::max(1, std::min(s, 127));
 }
