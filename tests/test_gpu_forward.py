@@ -93,6 +93,9 @@ GQA_CASES = [
     (2, 8, [1000, 64], None),
     (2, 15, [129, 500], [2, 2, 2]),
     (1, 7, [0], None),
+    # a deep tree (a 71-node chain, then a fork): nodes with more than 64
+    # ancestors, several batches of visible suffix rows per query
+    (1, 74, [200], [1] * 71 + [2]),
 ]
 
 
@@ -104,7 +107,7 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
     sh = synth.MINI8B
     print(f"[gqa] B={B} T={T} ctx={ctx} tree={branching}", flush=True)
     max_ctx = 1088
-    eng, names, w, cache = build_engine(sh, 4, max_ctx, 16, ctx_len=ctx + [0] * (4 - B))
+    eng, names, w, cache = build_engine(sh, 4, max_ctx, max(16, T), ctx_len=ctx + [0] * (4 - B))
     W = oracle_weights(names, w)
     kc, vc = oracle_cache(cache, sh, 4, max_ctx)
     tokens = synth.make_tokens(B, T, sh.vocab, seed=77 + T, device=dev())
