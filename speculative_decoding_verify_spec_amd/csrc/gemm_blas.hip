@@ -66,7 +66,7 @@ void blas_destroy(BlasCtx* c) {
 
 namespace {
 
-constexpr int kCandidates = 8;
+constexpr int kCandidates = 32;
 
 int weight_rows(const GemmParams& p) { return p.epi == EPI_SWIGLU ? 2 * p.F : p.N; }
 
