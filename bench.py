@@ -544,8 +544,14 @@ def run_recurrent(a, dev):
             OR.commit(h["x"], nacc, h["conv_state"], h["state"], sn)
             reps += 1
         dt = time.perf_counter() - t0
+        threads = None
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((q.get("num_threads") or 0) for q in threadpool_info()) or None
+        except Exception:
+            pass
         result["cpu_baseline"] = {"value": round(n * T * reps / dt, 2), "unit": "window positions/s",
-                                  "cores": 1, "kind": "oracle",
+                                  "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
                                   "sample": f"{reps} windows of {n} sequences (the first {n} of the workload), "
                                             f"verify + snapshot commit; {dt:.1f} s"}
     log(f"recurrent: {ms_replay:.4f} ms/step (replay), {ms_snap:.4f} ms/step (snapshots)")
