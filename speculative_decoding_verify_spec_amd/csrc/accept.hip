@@ -454,10 +454,15 @@ DEVI void check_layout(const AcceptParams& p, int b) {
 // ---------------------------------------------------------------- chain, pass 2
 __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams p) {
   __shared__ float sM[128], sS[128];
+  __shared__ float s_pz[128], s_qx[128], s_u[128];
+  __shared__ int s_bad[128];
   __shared__ int sn;
   __shared__ float shf[16];
   const int c = blockIdx.x, b = blockIdx.y;
   const int T = chain_len(p, b), gamma = T - 1;
+  // thread i: row i's statistics, then the inputs of draft i's accept test
+  // (token, target and draft probability, uniform), all rows in parallel so
+  // that the sequential decisions below read LDS only
   for (int i = threadIdx.x; i < T; i += blockDim.x) {
     float M, S;
     const int row = chain_row(p, b, i);
@@ -465,20 +470,26 @@ __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams
     sM[i] = M;
     sS[i] = S;
     if (c == 0) { p.rowms[2 * row] = M; p.rowms[2 * row + 1] = S; }
+    if (i < gamma) {
+      const int xr = p.tokens[chain_row(p, b, i + 1)];
+      const bool bad = xr < 0 || xr >= p.V;
+      const int x = bad ? 0 : xr;
+      s_pz[i] = pval(p, row_rule(p, row), p.logits[(size_t)row * p.V + x], x, M, S);
+      s_qx[i] = p.q[(size_t)chain_qrow(p, b, i) * p.V + x];
+      s_u[i] = philox_uniform(p.seed, p.round, b, i);
+      s_bad[i] = bad;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     if (c == 0) check_layout(p, b);
     int n = 0;
     for (int i = 0; i < gamma; ++i) {
-      bool bad;
-      const int x = clamp_token(p, p.tokens[chain_row(p, b, i + 1)], bad);
-      if (bad) break;
-      const int row = chain_row(p, b, i);
-      const float pz = pval(p, row_rule(p, row), p.logits[(size_t)row * p.V + x], x, sM[i], sS[i]);
-      const float qx = p.q[(size_t)chain_qrow(p, b, i) * p.V + x];
-      const float u = philox_uniform(p.seed, p.round, b, i);
-      if (u * qx < pz) ++n;
+      if (s_bad[i]) {  // a token outside the vocabulary ends the chain
+        atomicOr(p.flags, FLAG_TOKEN_RANGE);
+        break;
+      }
+      if (s_u[i] * s_qx[i] < s_pz[i]) ++n;
       else break;
     }
     sn = n;
@@ -612,18 +623,26 @@ __global__ __launch_bounds__(256) void accept_chain_sample_kernel(AcceptParams p
 
 // ---------------------------------------------------------------- chain, greedy
 __global__ __launch_bounds__(128) void accept_chain_greedy_kernel(AcceptParams p) {
-  __shared__ int am[128];
+  __shared__ int am[128], s_tok[128];
   __shared__ int s_n;
   const int b = blockIdx.x, T = chain_len(p, b), gamma = T - 1;
-  for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, chain_row(p, b, i), am[i]);
+  // every row's argmax and every draft token in parallel; the sequential
+  // comparisons below read LDS only
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    row_argmax(p, chain_row(p, b, i), am[i]);
+    if (i < gamma) s_tok[i] = p.tokens[chain_row(p, b, i + 1)];
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     check_layout(p, b);
     int n = 0;
     while (n < gamma) {
-      bool bad;
-      const int x = clamp_token(p, p.tokens[chain_row(p, b, n + 1)], bad);
-      if (bad || x != am[n]) break;
+      const int x = s_tok[n];
+      if (x < 0 || x >= p.V) {  // a token outside the vocabulary ends the chain
+        atomicOr(p.flags, FLAG_TOKEN_RANGE);
+        break;
+      }
+      if (x != am[n]) break;
       ++n;
     }
     s_n = n;
