@@ -135,8 +135,10 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
 
 
 FFN_CASES = [
-    # B, T, ctx lengths: M = 1, 4 (split-K down, matrix-core gate/up), 8 (all matrix cores), 12
+    # B, T, ctx lengths: M = 1, 3 and 4 (split-K down whose sum the next QKV
+    # launch adds, matrix-core gate/up), 8 (split-K down + reduce, tiled QKV), 12
     (1, 1, [700]),
+    (1, 3, [700]),
     (1, 4, [700]),
     (2, 4, [700, 33]),
     (3, 4, [5, 700, 129]),
