@@ -43,14 +43,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama8b_m4_hbm_traff
 
 
 def gemm_sources_sha256():
-    """Hash of the GEMM kernel's sources; the committed counter summary is
-    valid only while it matches."""
+    """Hash of the GEMM kernel's sources with comments and blank space
+    removed (an edited explanation does not change the kernel); the committed
+    counter summary is valid only while it matches."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(PKG_CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(PKG_CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -20,8 +20,10 @@
 //     together hold entire activation rows, an RMSNorm in front of the GEMM is
 //     fused here: the prologue sums x^2 over the rows, and scales each
 //     register by g[k] / sqrt(mean + eps).
-//   * streaming (longer K, the down projection): activations are re-read
-//     through the caches with every step.
+//   * streaming (longer K, the down projection at 1-2 rows): activations are
+//     re-read through the caches with every step.
+// (At 3-8 rows the down projection runs on the matrix-core kernel below, in
+// K slices.)
 //
 // Epilogues:
 //   STORE  out[m][n] = y                      (LM head -> logits)
@@ -702,9 +704,11 @@ static void launch_mfma_cpw(const GemmParams& p, int grid, hipStream_t s) {
 // A residual GEMM over a long K (the down projection) at M >= 3: the
 // streaming kernel re-reads the activation rows for every row group, and at
 // 4 rows that traffic equals the weight traffic.  Instead GEMM_KSPLIT slices
-// of K, each held in registers by the matrix-core kernel (7 chunks of 128 per
-// wave for K = 14336), write partial sums, and a small kernel adds them to
-// the residual in a fixed order.
+// of K, each held in registers by the matrix-core kernel (8 waves of 7
+// chunks of 128 for K = 14336), write partial sums, and their sum is added
+// to the residual in slice order: by the small reduce kernel, or, with
+// defer_reduce, by the prologue of the next GEMM that reads the residual
+// rows (xpart).
 bool gemm_use_split(const GemmParams& p) {
   if (!p.part || p.part_floats < (size_t)GEMM_KSPLIT * 8 * p.ldo || p.epi != EPI_RESID || p.norm_g || p.wdtype != 1 || p.M < 3) return false;
   if (p.K <= KSTAT_WAVES * 8 * 128 || p.K % (GEMM_KSPLIT * 128)) return false;
