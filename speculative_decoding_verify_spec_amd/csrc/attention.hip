@@ -11,16 +11,18 @@
 // 16x16x16: S^T = K Q^T with K exact in bf16 and the fp32 queries split into
 // bf16 hi + lo, then O^T += V^T P^T with the fp32 probabilities split the
 // same way; accumulation is fp32.  V is stored transposed in the cache so the
-// key index (the contraction of P V) is contiguous.  A wave's first key block
-// is requested before the queries are prepared, so the cache reads and the
-// query reads overlap, and each next block is requested as soon as the
-// current one is converted into matrix operands.
+// key index (the contraction of P V) is contiguous.  A wave's first key
+// blocks (PFB of them) are requested before the queries are prepared, so the
+// cache reads and the query reads overlap, and the block PFB further on is
+// requested as soon as a block is converted into matrix operands.
 //
-// Suffix part: 4*QT more workgroups per (sequence, KV head, query group), one
-// wave per query, attend to the step's own keys in fp32 (chain: rows 0..i;
-// tree: the node and its ancestors) and write their partials in the slot
-// after the context splits, so the suffix runs beside the context instead of
-// after it.
+// Suffix part: more workgroups per (sequence, KV head, query group) attend
+// to the step's own keys in fp32 and write their partials in the slot after
+// the context splits, so the suffix runs beside the context instead of after
+// it.  Chain (row i sees rows 0..i): 4*QT workgroups, one wave per query,
+// keys staged through LDS.  Tree (a node sees itself and its ancestors): QT
+// workgroups of 16 queries, each wave walking only the set bits of its
+// queries' ancestor masks.
 //
 // Combine part (attn_combine_kernel), one wave per (row, query head): merges
 // the nsplit partials of a query and normalises.  Keys at or beyond kv_len
