@@ -41,19 +41,28 @@ size_t kv_region_elems(const spec_config& c) {
   return (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
 }
 
-// Attention workgroups per (sequence, KV head, query group): about 128 keys
-// each (one 32-key block per wave), capped so the grid stays near 4096
-// workgroups and the combine merges at most 128 partials (with the suffix's).
+// Context splits per (sequence, KV head, query group).  The larger of
+//   * enough workgroups to fill the GPU: ~512 with the 16-query form (two
+//     per CU), ~256 with the one-per-CU forms;
+//   * splits of ~512 keys (1024 for 32-query tiles, whose waves do twice the
+//     work per block), so a workgroup's fixed cost is spread over enough
+//     blocks;
+// bounded by splits of at least 128 keys, ~4096 context workgroups (16-query
+// form) or ~2048 (the others), and a combine of at most 128 partials.
+// Measured on the 8B shape: B=1, 2K context: 17 (the 128-key bound); B=16,
+// 32K: 32 at T=1, 16 at T=8; B=128, 1K: 2 at T=4 (150 against 212 us for 4),
+// 1 at T=8 (265 against 299 us for 2); tree [4,4,2,2] at B=4, 4K: 4.
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
   const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int units = B * c.n_kv_heads * ((nqg + QGW - 1) / QGW);
-  int s = (c.max_ctx + 127) / 128;
-  // about 4096 context workgroups with one 16-query group per workgroup,
-  // at most 2048 for the other two shapes (measured at 32K context, T = 8,
-  // and on the [4,4,2,2] tree at 4K context)
-  const int cap = (QT == 1 && QGW == 1) ? std::max(1, (4096 + units - 1) / units) : std::max(1, 2048 / units);
+  const bool two_per_cu = QT == 1 && QGW == 1;
+  const int fill = ((two_per_cu ? 512 : 256) + units - 1) / units;
+  const int keys = std::max(1, c.max_ctx / (QT == 2 ? 1024 : 512));
+  int s = std::max(fill, keys);
+  s = std::min(s, (c.max_ctx + 127) / 128);
+  const int cap = two_per_cu ? std::max(1, (4096 + units - 1) / units) : std::max(1, 2048 / units);
   s = std::min(s, cap);
   return std::max(1, std::min(s, 127));
 }
