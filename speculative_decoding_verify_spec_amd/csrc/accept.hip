@@ -63,12 +63,22 @@ __global__ __launch_bounds__(256) void accept_rowstats_kernel(AcceptParams p) {
   const float* z = p.logits + (size_t)row * p.V;
   const int y0 = c * CH, y1 = min(p.V, y0 + CH);
   float* out = p.rowstat + ((size_t)row * p.nch + c) * 2;
+  // the thread's CH/256 entries are loaded at once (one memory latency), then
+  // reduced from registers in ascending token order
+  constexpr int PER = CH / 256;
+  float zv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + threadIdx.x + 256 * e;
+    zv[e] = y < y1 ? z[y] : 0.f;
+  }
   if (GREEDY) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int y = y0 + threadIdx.x; y < y1; y += 256) {
-      const float v = z[y];
-      if (better(v, y, bv, bi)) { bv = v; bi = y; }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int y = y0 + threadIdx.x + 256 * e;
+      if (y < y1 && better(zv[e], y, bv, bi)) { bv = zv[e]; bi = y; }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -90,10 +100,14 @@ __global__ __launch_bounds__(256) void accept_rowstats_kernel(AcceptParams p) {
   }
   const float Tt = p.temperature;
   float mx = -INFINITY;
-  for (int y = y0 + threadIdx.x; y < y1; y += 256) mx = fmaxf(mx, z[y] / Tt);
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (y0 + (int)threadIdx.x + 256 * e < y1) mx = fmaxf(mx, zv[e] / Tt);
   mx = block_max(mx, shf);
   float s = 0.f;
-  for (int y = y0 + threadIdx.x; y < y1; y += 256) s += expf(z[y] / Tt - mx);
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (y0 + (int)threadIdx.x + 256 * e < y1) s += expf(zv[e] / Tt - mx);
   s = block_sum(s, shf);
   if (threadIdx.x == 0) { out[0] = mx; out[1] = s; }
 }
@@ -502,10 +516,24 @@ __global__ __launch_bounds__(256) void accept_chain_residual_kernel(AcceptParams
   const float M = sM[n], S = sS[n];
   const RowRule rr = row_rule(p, chain_row(p, b, n));
   const int y0 = c * CH, y1 = min(p.V, y0 + CH);
+  // the chunk's logits (and draft probabilities) of this thread, loaded at
+  // once, then summed in ascending token order
+  constexpr int PER = CH / 256;
+  float zv[PER], qv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + threadIdx.x + 256 * e;
+    zv[e] = y < y1 ? z[y] : 0.f;
+    qv[e] = (q && y < y1) ? q[y] : 0.f;
+  }
   float acc = 0.f;
-  for (int y = y0 + threadIdx.x; y < y1; y += 256) {
-    const float pv = pval(p, rr, z[y], y, M, S);
-    acc += q ? fmaxf(0.f, pv - q[y]) : pv;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + threadIdx.x + 256 * e;
+    if (y < y1) {
+      const float pv = pval(p, rr, zv[e], y, M, S);
+      acc += q ? fmaxf(0.f, pv - qv[e]) : pv;
+    }
   }
   acc = block_sum(acc, shf);
   if (threadIdx.x == 0) p.rsum[(size_t)b * p.nch + c] = acc;
