@@ -133,14 +133,21 @@ DEVI void row_ms(const AcceptParams& p, int row, float& M, float& S) {
     M = m;
   }
 }
+// Combine the chunk argmaxes of one row (loads issued 16 at a time).
 DEVI void row_argmax(const AcceptParams& p, int row, int& idx) {
-  const float* st = p.rowstat + (size_t)row * p.nch * 2;
+  const float2* st = (const float2*)(p.rowstat + (size_t)row * p.nch * 2);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int c = 0; c < p.nch; ++c) {
-    const float v = st[2 * c];
-    const int i = __float_as_int(st[2 * c + 1]);
-    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  for (int c0 = 0; c0 < p.nch; c0 += 16) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < p.nch ? st[c0 + i] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (c0 + i >= p.nch) break;
+      const int k = __float_as_int(v[i].y);
+      if (better(v[i].x, k, bv, bi)) { bv = v[i].x; bi = k; }
+    }
   }
   idx = bi;
 }
@@ -291,8 +298,18 @@ __global__ __launch_bounds__(256) void accept_select_kernel(AcceptParams p, SelA
   const int shift = 24 - 8 * a.digit;
   const float* z = p.logits + (size_t)row * p.V;
   const int y1 = min(p.V, (c + 1) * CH);
-  for (int y = c * CH + t; y < y1; y += 256) {
-    const float zy = z[y];
+  constexpr int PER = CH / 256;
+  float zv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = c * CH + t + 256 * e;
+    zv[e] = y < y1 ? z[y] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = c * CH + t + 256 * e;
+    if (y >= y1) break;
+    const float zy = zv[e];
     const uint32_t key = order_key(zy);
     if (a.digit > 0 && (key >> (shift + 8)) != (s.prefix >> (shift + 8))) continue;
     if (!sel_keep(tk, ck, key, y)) continue;
@@ -425,10 +442,19 @@ __global__ __launch_bounds__(256) void accept_select_apply_kernel(AcceptParams p
   const float Tt = p.temperature;
   const float* z = p.logits + (size_t)row * p.V;
   const int y1 = min(p.V, (c + 1) * CH);
+  constexpr int PER = CH / 256;
+  float zv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = c * CH + threadIdx.x + 256 * e;
+    zv[e] = y < y1 ? z[y] : 0.f;
+  }
   float acc = 0.f;
-  for (int y = c * CH + threadIdx.x; y < y1; y += 256) {
-    const float zy = z[y];
-    if (sel_keep(r.tau, r.cut, order_key(zy), y)) acc += expf(zy / Tt - M);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = c * CH + threadIdx.x + 256 * e;
+    if (y >= y1) break;
+    if (sel_keep(r.tau, r.cut, order_key(zv[e]), y)) acc += expf(zv[e] / Tt - M);
   }
   acc = block_sum(acc, shf);
   if (threadIdx.x == 0) {
