@@ -19,10 +19,9 @@
 // Suffix part: more workgroups per (sequence, KV head, query group) attend
 // to the step's own keys in fp32 and write their partials in the slot after
 // the context splits, so the suffix runs beside the context instead of after
-// it.  Chain (row i sees rows 0..i): 4*QT workgroups, one wave per query,
-// keys staged through LDS.  Tree (a node sees itself and its ancestors): QT
-// workgroups of 16 queries, each wave walking only the set bits of its
-// queries' ancestor masks.
+// it.  Each wave walks only the rows its query sees (chain: rows 0..i; tree:
+// the node and its ancestors), one query per wave for a small chain batch,
+// four otherwise.
 //
 // Combine part (attn_combine_kernel), one wave per (row, query head): merges
 // the nsplit partials of a query and normalises.  Keys at or beyond kv_len
@@ -47,119 +46,19 @@ namespace sv {
 int attn_query_tiles(int nq) { return (nq > 16 && nq <= 64) ? 2 : 1; }
 int attn_groups_per_wg(int nq) { return nq > 64 ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
+// Suffix queries per wave: four for trees and for chains of many
+// (sequence, KV head) pairs, one otherwise (a small batch's suffix must not
+// outlast its context workgroups).
+__host__ __device__ inline int attn_suffix_qpw(bool tree, int pairs) { return (tree || pairs >= 256) ? 4 : 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
 // 4g..4g+3 of both tiles cover keys kb + 8g .. kb + 8g + 7, so one 16-byte
 // load of V^T feeds both tiles.
 DEVI int blk_key(int kb, int kt, int r) { return kb + 8 * (r >> 2) + 4 * kt + (r & 3); }
 
-// The step's own keys of a chain, in fp32, for four queries of one
-// (sequence, KV head, query group): suffix workgroup sw takes queries
-// 4*sw .. 4*sw+3 of the group, one per wave; row i sees rows 0..i.  The
-// queries are staged in LDS, the keys and values come through LDS in chunks
-// of KC rows shared by the four waves; scores are lane-parallel over the
-// chunk's keys, the value sum lane-parallel over dimensions.  `smem` must
-// hold 4*D + 2*KC*(D+4) floats.
-template <int D, int QT>
-DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sw, float* smem) {
-  constexpr int PL = D / 64;
-  constexpr int QN = QT * 16;
-  constexpr int KC = 16;       // keys per chunk
-  constexpr int KS = D + 4;    // padded key-row stride
-  float* s_q = smem;           // [4][D]
-  float* s_k = s_q + 4 * D;    // [KC][KS]
-  float* s_v = s_k + KC * KS;  // [KC][KS]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int G = p.Hq / p.Hkv;
-  const int Tb = p.rlen ? p.rlen[b] : p.T;  // this sequence's rows (ragged: its own length)
-  const int rs = p.rstart ? p.rstart[b] : b * p.T;
-  const int nq = G * p.T;                   // query slots per (sequence, kv head)
-  const int qi = qg * QN + 4 * sw + w;
-  const bool qok = qi < G * Tb;             // wave-uniform
-  const int i = qok ? qi / G : 0;
-  // staging loads are issued before the LDS stores (float4 granules, loops
-  // fully unrolled), so each stage costs one memory latency
-  constexpr int KV = KC * D / 4 / 256;  // key (and value) float4s per thread
-  static_assert(KV * 256 * 4 == KC * D && D / 4 <= 64, "staging granules");
-  if (lane < D / 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (qok) v = *(const float4*)(p.q + ((size_t)(rs + i) * p.Hq + kvh * G + qi % G) * D + 4 * lane);
-    *(float4*)(s_q + w * D + 4 * lane) = make_float4(v.x * p.scale, v.y * p.scale, v.z * p.scale, v.w * p.scale);
-  }
-  float mq = -INFINITY, lq = 0.f, oq[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) oq[e] = 0.f;
-  for (int c0 = 0; c0 < Tb; c0 += KC) {
-    {
-      float4 kv[KV], vv[KV];
-#pragma unroll
-      for (int r = 0; r < KV; ++r) {
-        const int e4 = threadIdx.x + 256 * r;
-        const int t = e4 / (D / 4), d4 = e4 % (D / 4);
-        const int jj = c0 + t;
-        kv[r] = vv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (jj < Tb) {
-          const size_t src = ((size_t)(rs + jj) * p.Hkv + kvh) * D + 4 * d4;
-          kv[r] = *(const float4*)(p.k_suf + src);
-          vv[r] = *(const float4*)(p.v_suf + src);
-        }
-      }
-      __syncthreads();  // the previous chunk is consumed
-#pragma unroll
-      for (int r = 0; r < KV; ++r) {
-        const int e4 = threadIdx.x + 256 * r;
-        const int t = e4 / (D / 4), d4 = e4 % (D / 4);
-        *(float4*)(s_k + t * KS + 4 * d4) = kv[r];
-        *(float4*)(s_v + t * KS + 4 * d4) = vv[r];
-      }
-      __syncthreads();
-    }
-    if (!qok) continue;  // wave-uniform; the barriers above are shared by all
-    const int jj = c0 + lane;
-    bool vis = lane < KC && jj < Tb;
-    if (vis) vis = jj <= i;
-    float sc = -INFINITY;
-    if (vis) {
-      const float* qr = s_q + w * D;
-      const float* kr = s_k + lane * KS;
-      float t = 0.f;
-#pragma unroll 8
-      for (int d4 = 0; d4 < D; d4 += 4) {
-        const float4 a = *(const float4*)(qr + d4);
-        const float4 k = *(const float4*)(kr + d4);
-        t += a.x * k.x + a.y * k.y + a.z * k.z + a.w * k.w;
-      }
-      sc = t;
-    }
-    const float cm = wave_max(sc);
-    if (cm == -INFINITY) continue;  // no visible key in this chunk
-    const float mn = fmaxf(mq, cm);
-    const float f = (mq == -INFINITY) ? 0.f : __expf(mq - mn);
-    const float pe = vis ? __expf(sc - mn) : 0.f;
-    lq = lq * f + wave_sum(pe);
-    mq = mn;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) oq[e] *= f;
-#pragma unroll
-    for (int t = 0; t < KC; ++t) {
-      const float pt = __shfl(pe, t, 64);
-#pragma unroll
-      for (int e = 0; e < PL; ++e) oq[e] += pt * s_v[t * KS + lane + 64 * e];
-    }
-  }
-  if (!qok) return;
-  const size_t slot = (((size_t)p.splits * p.B + b) * p.Hkv + kvh) * nq;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) p.part_o[(slot + qi) * D + lane + 64 * e] = oq[e];
-  if (lane == 0) {
-    p.part_ml[2 * (slot + qi)] = mq;
-    p.part_ml[2 * (slot + qi) + 1] = lq;
-  }
-}
-
-// One query of the tree suffix (attn_suffix_tree below).
+// One query of the suffix part (attn_suffix below).
 template <int D>
-DEVI void attn_suffix_tree_query(const AttnParams& p, int kvh, int b, int qi) {
+DEVI void attn_suffix_query(const AttnParams& p, int kvh, int b, int qi) {
   constexpr int PL = D / 64;
   constexpr int SB = 8;  // visible rows whose loads are in flight at once
   const int lane = threadIdx.x & 63;
@@ -172,9 +71,16 @@ DEVI void attn_suffix_tree_query(const AttnParams& p, int kvh, int b, int qi) {
   const float* qsrc = p.q + ((size_t)(rs + i) * p.Hq + kvh * G + qi % G) * D;
 #pragma unroll
   for (int e = 0; e < PL; ++e) qv[e] = qsrc[lane + 64 * e] * p.scale;
-  // visible rows: the ancestor-or-self bits of row i, below the sequence's
-  // row count
-  uint64_t lo = p.anc[2 * (rs + i)], hi = p.anc[2 * (rs + i) + 1];
+  // visible rows: a tree row's ancestor-or-self bits, a chain row's rows
+  // 0..i, below the sequence's row count
+  uint64_t lo, hi;
+  if (p.anc) {
+    lo = p.anc[2 * (rs + i)];
+    hi = p.anc[2 * (rs + i) + 1];
+  } else {  // chain: rows 0..i
+    lo = i >= 63 ? ~0ull : (2ull << i) - 1ull;
+    hi = i < 64 ? 0ull : (i >= 127 ? ~0ull : (2ull << (i - 64)) - 1ull);
+  }
   if (Tb < 64) lo &= (1ull << Tb) - 1ull;
   if (Tb <= 64) hi = 0;
   else if (Tb < 128) hi &= (1ull << (Tb - 64)) - 1ull;
@@ -230,24 +136,25 @@ DEVI void attn_suffix_tree_query(const AttnParams& p, int kvh, int b, int qi) {
   }
 }
 
-// The step's own keys of a token tree: a node sees itself and its ancestors
-// only (CS349E Lecture 6, section 10.3), a handful of the tree's nodes, so
-// each wave walks the set bits of its query's ancestor mask instead of every
-// suffix row: the keys and values of up to SB visible rows are requested at
-// once, straight from the fp32 suffix buffers, then folded into an online
-// softmax one key at a time (scores reduced over the wave).  No LDS, no
-// barrier: waves of one workgroup are independent here.  Workgroup `sub` of a
-// query group takes its queries 16*sub .. 16*sub+15, four per wave.
+// The step's own keys, in fp32: a chain row i sees rows 0..i; a token-tree
+// node sees itself and its ancestors only (CS349E Lecture 6, section 10.3),
+// a handful of the tree's nodes.  Each wave walks the set bits of its
+// query's visibility mask instead of every suffix row: the keys and values
+// of up to SB visible rows are requested at once, straight from the fp32
+// suffix buffers, then folded into an online softmax one key at a time
+// (scores reduced over the wave).  No LDS, no barrier: waves of one
+// workgroup are independent here.  Workgroup `sub` of a query group takes
+// 4*qpw queries, qpw per wave.
 template <int D, int QT>
-DEVI void attn_suffix_tree(const AttnParams& p, int kvh, int qg, int b, int sub) {
+DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sub, int qpw) {
   constexpr int QN = QT * 16;
   const int w = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
   const int Tb = p.rlen ? p.rlen[b] : p.T;
-  for (int k = 0; k < 4; ++k) {
-    const int qi = qg * QN + 16 * sub + 4 * w + k;
+  for (int k = 0; k < qpw; ++k) {
+    const int qi = qg * QN + 4 * qpw * sub + qpw * w + k;
     if (qi >= G * Tb) break;  // wave-uniform
-    attn_suffix_tree_query<D>(p, kvh, b, qi);
+    attn_suffix_query<D>(p, kvh, b, qi);
   }
 }
 
@@ -278,7 +185,8 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   // consecutive places in that XCD's sequence.
   // context splits + suffix workgroups (four queries each for a chain,
   // sixteen for a tree)
-  const int ncol = p.splits + (p.anc ? QT * QGW : 4 * QT * QGW);
+  const int qpw = attn_suffix_qpw(p.anc != nullptr, p.B * p.Hkv * nqw);
+  const int ncol = p.splits + 4 * QT * QGW / qpw;
   const int units = ncol * p.Hkv * p.B;
   const int id = blockIdx.x;
   const int n = id / 8;
@@ -294,14 +202,12 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   __shared__ float s_m[4][QN];
   __shared__ float s_l[4][QN];
   __shared__ float s_o[4][QN * OS];
-  static_assert(4 * D + 2 * 16 * (D + 4) <= 4 * QN * OS, "suffix staging must fit the output stage");
-  if (s >= p.splits) {  // the step's own keys; the output stage is its scratch
+  if (s >= p.splits) {  // the step's own keys
     const int sw = s - p.splits;
-    const int per = p.anc ? QT : 4 * QT;  // suffix workgroups per query group
+    const int per = 4 * QT / qpw;  // suffix workgroups per query group
     const int grp = qgw * QGW + sw / per;
     if (grp >= nqg) return;
-    if (p.anc) attn_suffix_tree<D, QT>(p, kvh, grp, b, sw % per);
-    else attn_suffix<D, QT>(p, kvh, grp, b, sw % per, &s_o[0][0]);
+    attn_suffix<D, QT>(p, kvh, grp, b, sw % per, qpw);
     return;
   }
   const int qsub = w / WPG, kw = w % WPG;
@@ -548,7 +454,8 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   // (context splits + suffix workgroups) per (kv head, sequence), each
   // repeated per set of QGW query groups, laid out XCD by XCD (see the
   // kernel)
-  const int units = (p.splits + (p.anc ? QT * QGW : 4 * QT * QGW)) * p.Hkv * p.B;
+  const int qpw = attn_suffix_qpw(p.anc != nullptr, p.B * p.Hkv * nqw);
+  const int units = (p.splits + 4 * QT * QGW / qpw) * p.Hkv * p.B;
   const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
     if (QT == 2) attn_ctx_kernel<128, 2, 1, 2><<<grid, 256, 0, s>>>(p);
