@@ -100,6 +100,24 @@ spec_status spec_recurrent_commit(const spec_recurrent_dims* dims, int32_t B, in
                                   const int32_t* d_slot, const int32_t* d_num_accepted,
                                   const float* d_snapshots, float* d_conv_state, float* d_state, void* stream);
 
+/* The two calls of consecutive rounds in one: the replay commit of the
+ * previous window (T_prev positions, d_prev_* its inputs, d_prev_accepted its
+ * accept counts; T_prev == 0: nothing to commit, the d_prev_* may be NULL),
+ * then the verify of the new window (T positions, no snapshots) from the
+ * committed state still on chip.  The pool ends committed through the
+ * previous window; the new window is committed by the next call (or by
+ * spec_recurrent_commit in replay mode).  The results equal
+ * spec_recurrent_commit(previous window, replay) followed by
+ * spec_recurrent_verify(new window), bit for bit, with one read and one
+ * write of each state instead of two reads and a write.
+ * Errors: as spec_recurrent_verify; T_prev outside [0, 16] is INVALID_ARG. */
+spec_status spec_recurrent_commit_verify(const spec_recurrent_dims* dims, int32_t B, int32_t T_prev,
+                                         const float* d_prev_x, const float* d_prev_gate, const float* d_prev_beta,
+                                         const int32_t* d_prev_accepted, int32_t T, const float* d_x,
+                                         const float* d_gate, const float* d_beta, const float* d_conv_w,
+                                         const int32_t* d_slot, float* d_conv_state, float* d_state, float* d_out,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
     "spec_profile_gemm", "spec_graph_enable", "spec_set_block_table", "spec_verify_destroy", "spec_status_str",
-    "spec_recurrent_verify", "spec_recurrent_commit",
+    "spec_recurrent_verify", "spec_recurrent_commit", "spec_recurrent_commit_verify",
 ]
 
 
@@ -122,6 +122,9 @@ def lib():
     L.spec_recurrent_commit.argtypes = [C.POINTER(spec_recurrent_dims), i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp]
     L.spec_recurrent_commit.restype = i32
+    L.spec_recurrent_commit_verify.argtypes = [C.POINTER(spec_recurrent_dims), i32, i32, vp, vp, vp, vp, i32, vp,
+                                               vp, vp, vp, vp, vp, vp, vp, vp]
+    L.spec_recurrent_commit_verify.restype = i32
     _lib = L
     return L
 
@@ -281,4 +284,15 @@ def spec_recurrent_commit(dims: spec_recurrent_dims, B, T, x, gate, beta, conv_w
                                      _ptr(conv_state), _ptr(state), _stream(stream))
     if check:
         _check("spec_recurrent_commit", st)
+    return st
+
+
+def spec_recurrent_commit_verify(dims: spec_recurrent_dims, B, T_prev, prev_x, prev_gate, prev_beta, prev_accepted,
+                                 T, x, gate, beta, conv_w, slot, conv_state, state, out, stream=None, check=True):
+    st = lib().spec_recurrent_commit_verify(C.byref(dims), int(B), int(T_prev), _ptr(prev_x), _ptr(prev_gate),
+                                            _ptr(prev_beta), _ptr(prev_accepted), int(T), _ptr(x), _ptr(gate),
+                                            _ptr(beta), _ptr(conv_w), _ptr(slot), _ptr(conv_state), _ptr(state),
+                                            _ptr(out), _stream(stream))
+    if check:
+        _check("spec_recurrent_commit_verify", st)
     return st

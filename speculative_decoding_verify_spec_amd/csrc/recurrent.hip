@@ -291,6 +291,46 @@ __global__ __launch_bounds__(REC_THREADS) void rec_replay_kernel(RecParams p) {
   if (p.W > 1) rec_commit_conv<D>(p, b, h, s, n);
 }
 
+// grid (H, B): the previous window's replay commit, then the verify of the
+// new window from the committed state still in registers (one read and one
+// write of the state per round instead of two reads and a write).  `pp`
+// describes the previous window (pp.T == 0: nothing to commit), `p` the new
+// one.  The same per-position code as the two separate kernels, so the
+// results are identical to a replay commit followed by a verify.
+template <int D>
+__global__ __launch_bounds__(REC_THREADS) void rec_commit_verify_kernel(RecParams p, RecParams pp) {
+  __shared__ RecLds<D> L;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int s = rec_slot(p, b);
+  if (s < 0) return;
+  const RecGeom<D> g;
+  float* sp = p.state + ((size_t)s * p.H + h) * D * D;
+  float st[RecGeom<D>::RPT];
+  if (pp.T > 0) {
+    const int n = rec_committed(pp, b);
+    RecIn<D> in;
+    rec_issue<D>(pp, b, h, s, n + 1, in);
+    rec_load_state<D>(st, g, sp);
+    rec_prologue<D>(pp, n + 1, in, L);
+    for (int t = 0; t <= n; ++t) rec_step<D, false>(st, g, L, t);
+#pragma unroll
+    for (int r = 0; r < RecGeom<D>::RPT; ++r) sp[(size_t)g.row(r) * D + g.j] = st[r];
+    if (p.W > 1) rec_commit_conv<D>(pp, b, h, s, n);
+    // the new conv state is read back below by this workgroup, and the
+    // window's LDS arrays are refilled
+    __syncthreads();
+  } else {
+    rec_load_state<D>(st, g, sp);
+  }
+  RecIn<D> in;
+  rec_issue<D>(p, b, h, s, p.T, in);
+  rec_prologue<D>(p, p.T, in, L);
+  for (int t = 0; t < p.T; ++t) {
+    const float o = rec_step<D, true>(st, g, L, t);
+    if (g.band == 0) p.out[(((size_t)b * p.T + t) * p.H + h) * D + g.j] = o;
+  }
+}
+
 // grid (H, B): scatter commit, the survivor snapshot copied to the pool
 template <int D>
 __global__ __launch_bounds__(REC_THREADS) void rec_scatter_kernel(RecParams p) {
@@ -382,6 +422,42 @@ spec_status spec_recurrent_commit(const spec_recurrent_dims* dims, int32_t B, in
   p.x = d_x, p.gate = d_gate, p.beta = d_beta, p.conv_w = d_conv_w, p.slot = d_slot;
   p.nacc = d_num_accepted, p.snap_in = d_snapshots, p.conv_state = d_conv_state, p.state = d_state;
   return rec_run(d_snapshots ? 2 : 1, dims->head_dim, p, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+spec_status spec_recurrent_commit_verify(const spec_recurrent_dims* dims, int32_t B, int32_t T_prev,
+                                         const float* d_prev_x, const float* d_prev_gate, const float* d_prev_beta,
+                                         const int32_t* d_prev_accepted, int32_t T, const float* d_x,
+                                         const float* d_gate, const float* d_beta, const float* d_conv_w,
+                                         const int32_t* d_slot, float* d_conv_state, float* d_state, float* d_out,
+                                         void* stream) {
+  const spec_status st = rec_check(dims, B, T);
+  if (st != SPEC_OK) return st;
+  if (T_prev < 0 || T_prev > REC_MAX_T) return SPEC_ERR_INVALID_ARG;
+  if (!d_x || !d_gate || !d_beta || !d_conv_w || !d_state || !d_out) return SPEC_ERR_INVALID_ARG;
+  if (dims->conv_width > 1 && !d_conv_state) return SPEC_ERR_INVALID_ARG;
+  if (T_prev > 0 && (!d_prev_x || !d_prev_gate || !d_prev_beta || !d_prev_accepted)) return SPEC_ERR_INVALID_ARG;
+  if (!d_slot && dims->n_slots < B) return SPEC_ERR_INVALID_ARG;
+  const void* ptrs[] = {d_prev_x, d_prev_gate, d_prev_beta, d_prev_accepted, d_x, d_gate, d_beta, d_conv_w,
+                        d_slot, d_conv_state, d_state, d_out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return SPEC_ERR_INVALID_ARG;
+  RecParams p{};
+  p.B = B, p.T = T, p.H = dims->n_heads, p.W = dims->conv_width, p.n_slots = dims->n_slots;
+  p.x = d_x, p.gate = d_gate, p.beta = d_beta, p.conv_w = d_conv_w, p.slot = d_slot;
+  p.conv_state = d_conv_state, p.state = d_state, p.out = d_out;
+  RecParams pp = p;
+  pp.T = T_prev;
+  pp.x = d_prev_x, pp.gate = d_prev_gate, pp.beta = d_prev_beta, pp.nacc = d_prev_accepted;
+  if (B == 0) return SPEC_OK;
+  const dim3 grid(p.H, p.B);
+  hipStream_t s = (hipStream_t)stream;
+  if (dims->head_dim == 64) rec_commit_verify_kernel<64><<<grid, REC_THREADS, 0, s>>>(p, pp);
+  else rec_commit_verify_kernel<128><<<grid, REC_THREADS, 0, s>>>(p, pp);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_DEVICE;
 }
 
 }  // extern "C"

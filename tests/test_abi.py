@@ -132,3 +132,17 @@ def test_recurrent_calls_reject_bad_arguments_without_device():
     assert com(x=None, snaps=P) == S.SPEC_ERR_INVALID_ARG  # conv state needs x when W > 1
     assert S.lib().spec_recurrent_verify(None, 1, 1, P, P, P, P, None, P, P, P, None, None) == \
         S.SPEC_ERR_INVALID_ARG
+
+    def cv(d=dims, B=2, Tp=4, T=4, prev=P, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return S.spec_recurrent_commit_verify(d, B, Tp, prev, prev, prev, prev, T, a["x"], a["gate"], a["beta"],
+                                              a["conv_w"], a["slot"], a["conv_state"], a["state"], a["out"],
+                                              None, check=False)
+
+    assert cv(B=0) == S.SPEC_OK and cv(B=0, Tp=0, prev=None) == S.SPEC_OK
+    assert cv(Tp=-1) == S.SPEC_ERR_INVALID_ARG and cv(Tp=17) == S.SPEC_ERR_INVALID_ARG
+    assert cv(prev=None) == S.SPEC_ERR_INVALID_ARG  # a previous window needs its inputs
+    assert cv(T=0) == S.SPEC_ERR_INVALID_ARG and cv(out=None) == S.SPEC_ERR_INVALID_ARG
+    assert cv(d=S.spec_recurrent_dims(4, 96, 4, 8)) == S.SPEC_ERR_SHAPE
+    assert cv(prev=P + 8) == S.SPEC_ERR_INVALID_ARG  # misaligned

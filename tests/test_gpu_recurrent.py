@@ -170,3 +170,47 @@ def test_empty_batch_is_a_no_op():
     z = torch.zeros(16, device=dev())
     assert S.spec_recurrent_verify(dims, 0, 4, z, z, z, z, None, z, z, z, None, check=False) == S.SPEC_OK
     assert S.spec_recurrent_commit(dims, 0, 4, z, z, z, z, None, z, None, z, z, check=False) == S.SPEC_OK
+
+
+def test_commit_verify_equals_separate_calls():
+    """Three rounds as fused calls (commit of the previous window + verify of
+    the new one) against the same rounds as verify + replay commit: the
+    outputs of every round and the final pool are bit-identical, and follow
+    the oracle."""
+    rs = synth.RecurrentShape(4, 128, 4)
+    B, T = 3, 4
+    dims = S.spec_recurrent_dims(4, 128, 4, B)
+    base = synth.make_recurrent_inputs(rs, B, T, B, seed=11)
+    conv_w = base["conv_w"].to(dev())
+    cs_a, st_a = base["conv_state"].to(dev()), base["state"].to(dev())
+    cs_b, st_b = cs_a.clone(), st_a.clone()
+    cs_o, st_o = base["conv_state"].double().numpy(), base["state"].double().numpy()
+    prev = None
+    for rnd in range(3):
+        print(f"recurrent fused round {rnd}", flush=True)
+        w = synth.make_recurrent_inputs(rs, B, T, B, seed=2000 + rnd)
+        wd = {k: w[k].to(dev()) for k in ("x", "gate", "beta")}
+        nacc = torch.tensor([(rnd * 2 + b) % (T + 1) - (b == 2) for b in range(B)], dtype=torch.int32, device=dev())
+        out_a = torch.empty((B, T, 4, 128), device=dev())
+        S.spec_recurrent_verify(dims, B, T, wd["x"], wd["gate"], wd["beta"], conv_w, None, cs_a, st_a, out_a, None)
+        S.spec_recurrent_commit(dims, B, T, wd["x"], wd["gate"], wd["beta"], conv_w, None, nacc, None, cs_a, st_a)
+        out_b = torch.empty_like(out_a)
+        if prev is None:
+            S.spec_recurrent_commit_verify(dims, B, 0, None, None, None, None, T, wd["x"], wd["gate"], wd["beta"],
+                                           conv_w, None, cs_b, st_b, out_b)
+        else:
+            S.spec_recurrent_commit_verify(dims, B, T, prev[0]["x"], prev[0]["gate"], prev[0]["beta"], prev[1], T,
+                                           wd["x"], wd["gate"], wd["beta"], conv_w, None, cs_b, st_b, out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), f"round {rnd}: fused outputs differ"
+        h = {k: w[k].double().numpy() for k in ("x", "gate", "beta")}
+        o_out, o_snaps = OR.verify(h["x"], h["gate"], h["beta"], base["conv_w"].double().numpy(), cs_o, st_o)
+        cs_o, st_o = OR.commit(h["x"], nacc.cpu().numpy(), cs_o, st_o, o_snaps)
+        _close(out_b.cpu().numpy(), o_out, f"round {rnd} outputs", 1)
+        prev = (wd, nacc)
+    # the fused pool is one window behind: commit the last window
+    S.spec_recurrent_commit(dims, B, T, prev[0]["x"], prev[0]["gate"], prev[0]["beta"], conv_w, None, prev[1], None,
+                            cs_b, st_b)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b) and torch.equal(cs_a, cs_b)
+    _close(st_b.cpu().numpy(), st_o, "final state", 2)
