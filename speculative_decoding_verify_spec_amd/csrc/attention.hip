@@ -35,10 +35,10 @@ namespace sv {
 // head):
 //   nq <= 16: one 16-query tile per wave, two workgroups per CU;
 //   16 < nq <= 64 (chain windows of 5..16 rows): two 16-query tiles per
-//     wave, so every wave's key block serves 32 queries, and two key blocks
-//     in flight per wave (PFB = 2), which needs more than 256 registers per
-//     lane: one workgroup per CU.  At B = 16, 32K context, T = 8: 496 us
-//     against 609 us for the form below;
+//     wave, so every wave's key block serves 32 queries.  At D = 128 the
+//     blocks are staged in LDS (attn_ctx_lds_kernel below, two workgroups
+//     per CU); at D = 64 two blocks are in flight per wave in registers
+//     (PFB = 2), more than 256 registers per lane: one workgroup per CU;
 //   nq > 64 (token trees): two 16-query groups per workgroup that walk the
 //     same key blocks, two workgroups per CU.  The one-per-CU form would also
 //     run the many suffix workgroups of a tree one per CU (32.1 against
@@ -445,6 +445,291 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   }
 }
 
+// Context attention with the key blocks staged in LDS (D = 128, chain
+// windows of 5..16 rows: two 16-query tiles per wave).  The register form
+// above holds two raw key blocks per wave in flight, which with the two
+// query tiles' operands and accumulators exceeds the 256 registers of a
+// lane: one wave per SIMD, values moving between the register files, and the
+// loop bound by issue rather than HBM.  Here each wave streams its 32-key
+// block (K rows and V^T columns, 16 KiB) straight from the cache into its
+// own LDS buffer with direct global-to-LDS loads and takes the matrix
+// operands from there, so no register holds raw cache data: two workgroups
+// fit per CU (two waves per SIMD), and one wave's products cover the other's
+// waits.  The next block is requested as soon as the current one has been
+// read out of LDS.
+//
+// LDS layout of a wave's buffer (16-byte chunks; XOR swizzles keep the 16
+// lanes of a read on distinct banks):
+//   K: row R = 16*kt + j holds key blk_key(kb, kt, j); its chunk c (dims
+//      8c..8c+7) sits at R*16 + (c ^ j);
+//   V^T: row r = 16*dt + j holds dim r for the block's 32 keys; its chunk g
+//      (keys 8g..8g+7) sits at 512 + r*4 + (g ^ (j >> 2)).
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+template <int QT>
+__global__ __launch_bounds__(256, 2) void attn_ctx_lds_kernel(AttnParams p) {
+  constexpr int D = 128, DG = D / 4, KSTEPS = D / 32, DT = D / 16;
+  constexpr int QN = QT * 16, OS = D + 4;
+  __shared__ __attribute__((aligned(16))) uint4 s_kv[4][1024];
+  __shared__ float s_m[4][QN];
+  __shared__ float s_l[4][QN];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+  const int nq = G * p.T;
+  // grid decode of attn_ctx_kernel with one query group per workgroup
+  const int nqw = (nq + QN - 1) / QN;
+  const int qpw = attn_suffix_qpw(p.anc != nullptr, p.B * p.Hkv * nqw);
+  const int ncol = p.splits + 4 * QT / qpw;
+  const int units = ncol * p.Hkv * p.B;
+  const int id = blockIdx.x;
+  const int n = id / 8;
+  const int u = (n / nqw) * 8 + id % 8;
+  if (u >= units) return;
+  const int qg = n % nqw;
+  const int s = u % ncol;
+  const int kvh = (u / ncol) % p.Hkv;
+  const int b = u / (ncol * p.Hkv);
+  if (s >= p.splits) {
+    const int sw = s - p.splits;
+    const int per = 4 * QT / qpw;
+    if (sw / per > 0) return;
+    attn_suffix<D, QT>(p, kvh, qg, b, sw % per, qpw);
+    return;
+  }
+  const int rs = p.rstart ? p.rstart[b] : b * p.T;
+  const int nqb = G * (p.rlen ? p.rlen[b] : p.T);
+  int L = p.kv_len[b];
+  const int cap = p.kvm.table ? min(p.max_ctx, p.kvm.ppseq * KV_PAGE) : p.max_ctx;
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int chunk = (L + p.splits - 1) / p.splits;
+  chunk = (chunk + 127) & ~127;
+  const int kbeg = s * chunk;
+  const int kend = min(L, kbeg + chunk);
+
+  // ---- a block's K rows and V^T columns into this wave's buffer.  All 32
+  // slots of a block are inside the cache (blocks start at multiples of 32
+  // below kend; a page holds two blocks); slots at or past kend may hold
+  // anything and are masked after the read.
+  const int vstride = kv_v_stride(p.kvm);
+  uint4* kbuf = &s_kv[w][0];
+  uint4* vbuf = &s_kv[w][512];
+  auto issue_k = [&](int kb, int pg) {
+    const uint16_t* kblk = p.kc + kv_k_off_pg(p.kvm, p.Hkv, D, b, kvh, kb, pg);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int R = 4 * i + (lane >> 4), jj = R & 15;
+      const int key = 8 * (jj >> 2) + 4 * (R >> 4) + (jj & 3);
+      const int c = (lane & 15) ^ jj;
+      __builtin_amdgcn_global_load_lds((gptr_t)(kblk + (size_t)key * D + 8 * c), (lptr_t)(kbuf + 64 * i), 16, 0, 0);
+    }
+  };
+  auto issue_v = [&](int kb, int pg) {
+    const uint16_t* vblk = p.vc + kv_v_off_pg(p.kvm, p.Hkv, D, b, kvh, 0, kb, pg);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      const int gl = (lane & 3) ^ ((r & 15) >> 2);
+      __builtin_amdgcn_global_load_lds((gptr_t)(vblk + (size_t)r * vstride + 8 * gl), (lptr_t)(vbuf + 64 * i), 16, 0,
+                                       0);
+    }
+  };
+  // page of a block (paged cache), looked up a block ahead so that no wait
+  // for it sits between a block's loads
+  auto page_of = [&](int kb) { return p.kvm.table ? kv_page(p.kvm, b, kb) : 0; };
+  int kb = kbeg + 32 * w;
+  if (kb < kend) {
+    const int pg = page_of(kb);
+    issue_k(kb, pg);
+    issue_v(kb, pg);
+  }
+
+  // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's
+  // dims g*DG + 8*ks + e for k-step ks (32 dims per step)
+  shortx8 qhi[QT][KSTEPS], qlo[QT][KSTEPS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qi = (qg * QT + qt) * 16 + j;
+    float qv[DG];
+    if (qi < nqb) {
+      const int i = qi / G, gg = qi % G;
+      const float* src = p.q + (((size_t)(rs + i)) * p.Hq + kvh * G + gg) * D + g * DG;
+#pragma unroll
+      for (int e = 0; e < DG; e += 4) {
+        float4 v = *(const float4*)(src + e);
+        qv[e] = v.x * p.scale; qv[e + 1] = v.y * p.scale;
+        qv[e + 2] = v.z * p.scale; qv[e + 3] = v.w * p.scale;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DG; ++e) qv[e] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        short hi, lo;
+        split_bf16(qv[8 * ks + e], hi, lo);
+        qhi[qt][ks][e] = hi;
+        qlo[qt][ks][e] = lo;
+      }
+    }
+  }
+
+  floatx4 o[QT][DT];
+  float mrun[QT], lrun[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mrun[qt] = -INFINITY;
+    lrun[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const shortx8* kb8 = (const shortx8*)kbuf;
+  const shortx8* vb8 = (const shortx8*)vbuf;
+  for (; kb < kend; kb += 128) {
+    const bool more = kb + 128 < kend;
+    const int pgn = more ? page_of(kb + 128) : 0;
+    // this block has landed in LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool tail = kb + 32 > kend;  // wave-uniform
+    // ---- the block's operands out of LDS, then the buffer takes the next
+    // block, whose load overlaps this block's products and softmax
+    // lane row j of key tile kt, dims g*DG + 8*ks + e: chunk 4g + ks
+    shortx8 ka[2][KSTEPS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) ka[kt][ks] = kb8[(16 * kt + j) * 16 + ((4 * g + ks) ^ j)];
+    // lane row j of dim tile dt, keys kb + 8g + e: chunk g of V^T row 16dt + j
+    shortx8 va[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) va[dt] = vb8[(16 * dt + j) * 4 + (g ^ (j >> 2))];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (more) {
+      issue_k(kb + 128, pgn);
+      issue_v(kb + 128, pgn);
+    }
+    if (tail) {
+      // never multiply a probability by data past the range
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kb + 8 * g + e >= kend) va[dt][e] = 0;
+    }
+    // ---- S^T = K Q^T for both query tiles
+    floatx4 st[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          acc = mfma16x16x32(ka[kt][ks], qhi[qt][ks], acc);
+          acc = mfma16x16x32(ka[kt][ks], qlo[qt][ks], acc);
+        }
+        st[qt][kt] = acc;
+      }
+    // ---- online softmax; st[qt][kt][e] is query j, key kb + 8g + 4kt + e
+    // B operand of O^T += V^T P^T: lane (j, g) holds query j's probabilities
+    // of keys kb + 8g + e, which is where S^T left them (kt = e / 4)
+    shortx8 phi[QT], plo[QT];
+    float factor[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      if (tail) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kb + 8 * g + 4 * kt + e >= kend) st[qt][kt][e] = -INFINITY;
+      }
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bmax = fmaxf(bmax, st[qt][kt][e]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      const float mnew = fmaxf(mrun[qt], bmax);
+      factor[qt] = __expf(mrun[qt] - mnew);
+      mrun[qt] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = __expf(st[qt][kt][e] - mnew);
+          psum += pe;
+          short hi, lo;
+          split_bf16(pe, hi, lo);
+          phi[qt][4 * kt + e] = hi;
+          plo[qt][4 * kt + e] = lo;
+        }
+      lrun[qt] = lrun[qt] * factor[qt] + psum;
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[qt][dt] *= factor[qt];
+        o[qt][dt] = mfma16x16x32(va[dt], phi[qt], o[qt][dt]);
+        o[qt][dt] = mfma16x16x32(va[dt], plo[qt], o[qt][dt]);
+      }
+  }
+
+  // ---- merge the four waves' states and write one partial per query; the
+  // key buffers (no load is outstanding after the last block) hold the
+  // staged outputs, one query tile at a time
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float l = lrun[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    lrun[qt] = l;
+    if (g == 0) s_m[w][qt * 16 + j] = mrun[qt];
+  }
+  __syncthreads();
+  float* s_o = (float*)&s_kv[0][0];
+  const size_t pbase = (((size_t)s * p.B + b) * p.Hkv + kvh) * nq;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qq = qt * 16 + j;
+    const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+    // a wave that saw no key has m = -inf and contributes nothing
+    const float f = (mrun[qt] == -INFINITY) ? 0.f : __expf(mrun[qt] - mall);
+    if (g == 0) s_l[w][qq] = lrun[qt] * f;
+    if (qt > 0) __syncthreads();  // the previous tile's sums have been read
+    float* dst = s_o + (w * 16 + j) * OS;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *(float4*)(dst + dt * 16 + 4 * g) =
+          make_float4(o[qt][dt][0] * f, o[qt][dt][1] * f, o[qt][dt][2] * f, o[qt][dt][3] * f);
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * D; e += 256) {
+      const int q16 = e / D, dd = e % D;
+      const int qi = (qg * QT + qt) * 16 + q16;
+      if (qi >= nqb) continue;
+      const int o2 = q16 * OS + dd;
+      p.part_o[(pbase + qi) * D + dd] = s_o[o2] + s_o[16 * OS + o2] + s_o[32 * OS + o2] + s_o[48 * OS + o2];
+    }
+  }
+  if (threadIdx.x < QN) {
+    const int qq = threadIdx.x;
+    const int qi = qg * QN + qq;
+    if (qi < nqb) {
+      const float mall = fmaxf(fmaxf(s_m[0][qq], s_m[1][qq]), fmaxf(s_m[2][qq], s_m[3][qq]));
+      p.part_ml[2 * (pbase + qi)] = mall;
+      p.part_ml[2 * (pbase + qi) + 1] = s_l[0][qq] + s_l[1][qq] + s_l[2][qq] + s_l[3][qq];
+    }
+  }
+}
+
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nq = (p.Hq / p.Hkv) * p.T;
   const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
@@ -458,7 +743,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int units = (p.splits + 4 * QT * QGW / qpw) * p.Hkv * p.B;
   const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
-    if (QT == 2) attn_ctx_kernel<128, 2, 1, 2><<<grid, 256, 0, s>>>(p);
+    if (QT == 2) attn_ctx_lds_kernel<2><<<grid, 256, 0, s>>>(p);
     else if (QGW == 2) attn_ctx_kernel<128, 1, 2, 1><<<grid, 256, 0, s>>>(p);
     else attn_ctx_kernel<128, 1, 1, 1><<<grid, 256, 0, s>>>(p);
   } else {

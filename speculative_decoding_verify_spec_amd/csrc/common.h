@@ -40,6 +40,15 @@ DEVI void split_bf16(float x, short& hi, short& lo) {
 DEVI floatx4 mfma16x16x16(shortx4 a, shortx4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16), the gfx950 form with
+// twice the contraction per instruction: lane l holds A[l%16][8(l/16) + e],
+// B[8(l/16) + e][l%16] (e = 0..7) and D as above.
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+DEVI floatx4 mfma16x16x32(shortx8 a, shortx8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
 
 // --- wave reductions ------------------------------------------------------
 DEVI float wave_sum(float v) {
@@ -112,24 +121,30 @@ struct KvMap {
   int npages;            // pages in the pool
   int max_ctx;           // dense slot stride
 };
-// first slot of slot s's run of contiguous slots (a page, or the whole
-// sequence when dense), as an element offset of K row s and of V (dim 0, s)
-DEVI size_t kv_k_off(const KvMap& m, int Hkv, int D, int b, int h, int s) {
-  if (!m.table) return (((size_t)b * Hkv + h) * m.max_ctx + s) * D;
+// page holding slot s of sequence b (paged cache only), clamped into the pool
+DEVI int kv_page(const KvMap& m, int b, int s) {
   int pi = s / KV_PAGE;
   pi = pi < 0 ? 0 : (pi >= m.ppseq ? m.ppseq - 1 : pi);
-  int pg = m.table[(size_t)b * m.ppseq + pi];
-  pg = pg < 0 ? 0 : (pg >= m.npages ? m.npages - 1 : pg);
+  const int pg = m.table[(size_t)b * m.ppseq + pi];
+  return pg < 0 ? 0 : (pg >= m.npages ? m.npages - 1 : pg);
+}
+// first slot of slot s's run of contiguous slots (a page, or the whole
+// sequence when dense), as an element offset of K row s and of V (dim 0, s);
+// the _pg forms take the page of slot s already looked up (ignored when dense)
+DEVI size_t kv_k_off_pg(const KvMap& m, int Hkv, int D, int b, int h, int s, int pg) {
+  if (!m.table) return (((size_t)b * Hkv + h) * m.max_ctx + s) * D;
   return (((size_t)pg * Hkv + h) * KV_PAGE + (s % KV_PAGE)) * D;
+}
+DEVI size_t kv_k_off(const KvMap& m, int Hkv, int D, int b, int h, int s) {
+  return kv_k_off_pg(m, Hkv, D, b, h, s, m.table ? kv_page(m, b, s) : 0);
 }
 // element offset of V (dim, slot s); slots of one page (or all slots, dense)
 // are contiguous for a fixed dim, with this stride between dims
 DEVI int kv_v_stride(const KvMap& m) { return m.table ? KV_PAGE : m.max_ctx; }
-DEVI size_t kv_v_off(const KvMap& m, int Hkv, int D, int b, int h, int dim, int s) {
+DEVI size_t kv_v_off_pg(const KvMap& m, int Hkv, int D, int b, int h, int dim, int s, int pg) {
   if (!m.table) return (((size_t)b * Hkv + h) * D + dim) * (size_t)m.max_ctx + s;
-  int pi = s / KV_PAGE;
-  pi = pi < 0 ? 0 : (pi >= m.ppseq ? m.ppseq - 1 : pi);
-  int pg = m.table[(size_t)b * m.ppseq + pi];
-  pg = pg < 0 ? 0 : (pg >= m.npages ? m.npages - 1 : pg);
   return (((size_t)pg * Hkv + h) * D + dim) * KV_PAGE + (s % KV_PAGE);
+}
+DEVI size_t kv_v_off(const KvMap& m, int Hkv, int D, int b, int h, int dim, int s) {
+  return kv_v_off_pg(m, Hkv, D, b, h, dim, s, m.table ? kv_page(m, b, s) : 0);
 }

@@ -50,7 +50,8 @@ def _gather(pool, sh, table, npages, max_ctx):
     return OM.gather_pages(kp, vp, table.cpu().numpy(), max_ctx), (kp, vp)
 
 
-@pytest.mark.parametrize("B,T,ctx,branching", [(3, 4, [300, 17, 700], None), (2, 15, [129, 500], [2, 2, 2])])
+@pytest.mark.parametrize("B,T,ctx,branching", [(3, 4, [300, 17, 700], None), (2, 8, [1000, 37], None),
+                                               (2, 15, [129, 500], [2, 2, 2])])
 def test_paged_step_matches_oracle(B, T, ctx, branching):
     sh = synth.MINI8B
     print(f"[paged] B={B} T={T} ctx={ctx} tree={branching}", flush=True)
