@@ -43,8 +43,8 @@ namespace sv {
 //     same key blocks, two workgroups per CU.  The one-per-CU form would also
 //     run the many suffix workgroups of a tree one per CU (32.1 against
 //     29.9 ms per step at B = 4, tree [4,4,2,2]).
-int attn_query_tiles(int nq) { return (nq > 16 && nq <= 64) ? 2 : 1; }
-int attn_groups_per_wg(int nq) { return nq > 64 ? 2 : 1; }
+int attn_query_tiles(int nq, int D) { return (nq > 16 && (D == 128 || nq <= 64)) ? 2 : 1; }
+int attn_groups_per_wg(int nq, int D) { return (D != 128 && nq > 64) ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
 // Suffix queries per wave: four for trees and for chains of many
 // (sequence, KV head) pairs, one otherwise (a small batch's suffix must not
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_lds_kernel(AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int nq = (p.Hq / p.Hkv) * p.T;
-  const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
+  const int QT = attn_query_tiles(nq, p.D), QGW = attn_groups_per_wg(nq, p.D);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int nqw = (nqg + QGW - 1) / QGW;
   if (p.T > 128) return hipErrorInvalidValue;  // the suffix workgroup holds up to 128 keys
@@ -744,7 +744,6 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const dim3 grid(((units + 7) / 8) * 8 * nqw);
   if (p.D == 128) {
     if (QT == 2) attn_ctx_lds_kernel<2><<<grid, 256, 0, s>>>(p);
-    else if (QGW == 2) attn_ctx_kernel<128, 1, 2, 1><<<grid, 256, 0, s>>>(p);
     else attn_ctx_kernel<128, 1, 1, 1><<<grid, 256, 0, s>>>(p);
   } else {
     if (QT == 2) attn_ctx_kernel<64, 2, 1, 2><<<grid, 256, 0, s>>>(p);

@@ -138,8 +138,8 @@ struct AttnParams {
 // number of partial slots per query the attention kernel writes: the context
 // splits plus one for the step's own (suffix) keys
 int attn_nsplit(int splits);
-int attn_query_tiles(int nq);    // 16-query tiles per wave of the context attention (1 or 2)
-int attn_groups_per_wg(int nq);  // query groups sharing a context workgroup's key blocks (1 or 2)
+int attn_query_tiles(int nq, int D);    // 16-query tiles per wave of the context attention (1 or 2)
+int attn_groups_per_wg(int nq, int D);  // query groups sharing a context workgroup's key blocks (1 or 2)
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 struct CombineParams {

@@ -54,7 +54,7 @@ size_t kv_region_elems(const spec_config& c) {
 // 1 at T=8 (265 against 299 us for 2); tree [4,4,2,2] at B=4, 4K: 4.
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
-  const int QT = attn_query_tiles(nq), QGW = attn_groups_per_wg(nq);
+  const int QT = attn_query_tiles(nq, c.head_dim), QGW = attn_groups_per_wg(nq, c.head_dim);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
   const int units = B * c.n_kv_heads * ((nqg + QGW - 1) / QGW);
   const bool two_per_cu = QT == 1 && QGW == 1;
