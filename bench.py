@@ -301,7 +301,8 @@ def main():
     # ---- per-kernel-class event timing (a separate profiled pass)
     kernels = {}
     if a.profile_steps > 0:
-        kernels, agg = profile_pass(S, eng, one_step, a.profile_steps)
+        # the pass reuses the accept-count rows of the timed steps
+        kernels, agg = profile_pass(S, eng, lambda k: one_step(k % (a.steps + a.warmup)), a.profile_steps)
         roofline.update(agg)
 
     result = {

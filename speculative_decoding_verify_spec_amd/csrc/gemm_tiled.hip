@@ -1,7 +1,7 @@
 // Tiled GEMM for many activation rows (5 or more for the QKV, gate/up and LM
 // head projections, more than 8 for the residual ones):
 // Y[m][n] = sum_k X[m][k] W[n][k]
-// on the 16x16x16 bf16 matrix instruction, with the fp32 activations split
+// on the 16x16x32 bf16 matrix instruction, with the fp32 activations split
 // into bf16 hi + lo (two products per tile) so they keep ~2^-16 relative
 // accuracy, fp32 accumulation.  This is the regime where the skinny kernels
 // run out of vector or matrix throughput, or stream the weights once per 8
@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
   constexpr int NPB = NPAIR / 16;
   constexpr int PBW = MB * NPB * KW / 4;
   static_assert(PBW >= 1 && MB * (NPB / PBW) * KW == 4, "four waves");
+  static_assert(KW == 1 || KW == 2, "a 64-k stage holds two 32-k steps");
   constexpr int BM = 32 * MB;
   constexpr int ROWS = WROWS + 2 * BM;  // tile rows per stage: W, X hi, X lo
   constexpr int CH = ROWS * 8 / 256;    // 16-byte chunks per thread per stage
@@ -260,28 +261,29 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
     const uint16_t* tw = s_t[B];
     const uint16_t* th = tw + WROWS * 64;
     const uint16_t* tl = th + BM * 64;
+    // k-steps of 32 (the 16x16x32 instruction): lane group lg takes the
+    // stage's 16-byte chunk 4 * step + lg of every row it reads
 #pragma unroll
-    for (int ss = 0; ss < 4 / KW; ++ss) {
-      const int kk = 16 * (kw + KW * ss) + 4 * lg;  // k within the stage
-      const int c = kk >> 3, o = kk & 7;
-      shortx4 ah[2], al[2];
+    for (int ss = 0; ss < 2 / KW; ++ss) {
+      const int c = 4 * (kw + KW * ss) + lg;
+      shortx8 ah[2], al[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int r = 32 * mb + 16 * mt + l16;
-        ah[mt] = *(const shortx4*)(th + r * 64 + 8 * swz(r, c) + o);
-        al[mt] = *(const shortx4*)(tl + r * 64 + 8 * swz(r, c) + o);
+        ah[mt] = *(const shortx8*)(th + r * 64 + 8 * swz(r, c));
+        al[mt] = *(const shortx8*)(tl + r * 64 + 8 * swz(r, c));
       }
 #pragma unroll
       for (int q = 0; q < PBW; ++q) {
         const int ra = 16 * (pbw * PBW + q) + l16, rb = NPAIR + ra;
-        const shortx4 ba = *(const shortx4*)(tw + ra * 64 + 8 * swz(ra, c) + o);
-        const shortx4 bb = *(const shortx4*)(tw + rb * 64 + 8 * swz(rb, c) + o);
+        const shortx8 ba = *(const shortx8*)(tw + ra * 64 + 8 * swz(ra, c));
+        const shortx8 bb = *(const shortx8*)(tw + rb * 64 + 8 * swz(rb, c));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          acc[mt][q][0] = mfma16x16x16(ah[mt], ba, acc[mt][q][0]);
-          acc[mt][q][0] = mfma16x16x16(al[mt], ba, acc[mt][q][0]);
-          acc[mt][q][1] = mfma16x16x16(ah[mt], bb, acc[mt][q][1]);
-          acc[mt][q][1] = mfma16x16x16(al[mt], bb, acc[mt][q][1]);
+          acc[mt][q][0] = mfma16x16x32(ah[mt], ba, acc[mt][q][0]);
+          acc[mt][q][0] = mfma16x16x32(al[mt], ba, acc[mt][q][0]);
+          acc[mt][q][1] = mfma16x16x32(ah[mt], bb, acc[mt][q][1]);
+          acc[mt][q][1] = mfma16x16x32(al[mt], bb, acc[mt][q][1]);
         }
       }
     }
@@ -493,6 +495,12 @@ hipError_t launch_blas_finish(const GemmParams& p, const float* d, int ldd, hipS
     default: return launch_blas_finish_epi<EPI_QKV>(p, d, ldd, s);
   }
 }
+
+// Between 64 and 128 rows the library GEMM wins on the 4096-deep
+// projections, but the tiled kernel wins on the 14336-deep down projection
+// (128 rows: 69 against 80 us per layer), where the library's product
+// scratch and finish pass cost the most.
+bool gemm_tiled_preferred(const GemmParams& p) { return p.K > 8192 && p.M <= 128 && gemm_tiled_ok(p); }
 
 bool gemm_tiled_ok(const GemmParams& p) {
   if (p.wdtype != 1 || p.K % TK || p.K > SSQ_BLK * 1024 || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;

@@ -98,6 +98,8 @@ bool gemm_use_split(const GemmParams& p);
 bool gemm_takes_xpart(const GemmParams& p);
 // the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
 bool gemm_tiled_ok(const GemmParams& p);
+// the tiled kernel beats the library GEMM on this launch (deep K, few rows)
+bool gemm_tiled_preferred(const GemmParams& p);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);
 // the activation planes of the tiled kernel ([2][M][K] in p.xs, row sums of
 // squares in p.xs_ssq), and the finish of a library GEMM over them

@@ -275,7 +275,7 @@ hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s
     q.M = M;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     const bool tune = !h->recording && hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
-    if (gemm_blas_ok(q) && (tune || blas_ready(h->blas))) {
+    if (gemm_blas_ok(q) && !gemm_tiled_preferred(q) && (tune || blas_ready(h->blas))) {
       // many rows: one library GEMM of the stacked activation planes
       const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
                            (double)M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
