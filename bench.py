@@ -414,6 +414,10 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
 
     t_verify = time_forward(rounds[0][0], parent)
     t_decode = time_forward(rounds[0][0][:, :1].contiguous(), None)
+    kernels = {}
+    if a.profile_steps > 0:
+        import speculative_decoding_verify_spec_amd as S
+        kernels, _ = profile_pass(S, eng, lambda k: one_step(k % (a.steps + a.warmup)), a.profile_steps)
     assert eng.device_errors() == 0
     result = {
         "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
@@ -427,7 +431,7 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
                    "temperature": a.temperature, "parallelism": "single GPU"},
         "c_verify": round(t_verify / t_decode, 4), "t_verify_ms": round(t_verify, 4),
         "t_decode_ms": round(t_decode, 4), "mean_accepted": round(float(n_timed.mean()), 4),
-        "tokens_per_round": round(float((n_timed + 1).mean()), 4),
+        "tokens_per_round": round(float((n_timed + 1).mean()), 4), "kernels": kernels,
     }
     log(f"tree: {ms_per_step:.3f} ms/step, {result['value']} tok/s, T_verify {t_verify:.3f} ms, "
         f"T_decode {t_decode:.3f} ms")

@@ -163,7 +163,7 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sub, int 
 template <int D, int QT, int QGW, int PFB>
 __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnParams p) {
   constexpr int DG = D / 4;   // dims per lane group
-  constexpr int KSTEPS = D / 16;
+  constexpr int KSTEPS = D / 32;  // 32-dim k-steps of the 16x16x32 products
   constexpr int DT = D / 16;  // output dim tiles
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   }
 
   // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
-  // g*DG + 4*ks + e for k-step ks.
-  shortx4 qhi[QT][KSTEPS], qlo[QT][KSTEPS];
+  // g*DG + 8*ks + e for k-step ks.
+  shortx8 qhi[QT][KSTEPS], qlo[QT][KSTEPS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qi = (qg * QT + qt) * 16 + j;
@@ -276,9 +276,9 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 8; ++e) {
         short hi, lo;
-        split_bf16(qv[4 * ks + e], hi, lo);
+        split_bf16(qv[8 * ks + e], hi, lo);
         qhi[qt][ks][e] = hi;
         qlo[qt][ks][e] = lo;
       }
@@ -300,35 +300,24 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   for (int sl = 0; sl < PFB; ++sl) {
     const int kb = kbase + sl * 32 * WPG;
     if (kb >= kend) break;
-    // ---- K operand (A of S^T): lane row j of tile kt is key blk_key(kb, kt, j)
-    shortx4 ka[2][KSTEPS];
+    // ---- K operand (A of S^T): lane row j of tile kt is key blk_key(kb, kt, j);
+    // the raw 16 bytes of k-step ks are its dims g*DG + 8*ks .. + 7
+    shortx8 ka[2][KSTEPS];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < DG / 8; ++e) {
-        const uint4 v = kraw[sl][kt][e];
-        const int ks = 2 * e;
-        ka[kt][ks][0] = (short)(v.x & 0xffff); ka[kt][ks][1] = (short)(v.x >> 16);
-        ka[kt][ks][2] = (short)(v.y & 0xffff); ka[kt][ks][3] = (short)(v.y >> 16);
-        ka[kt][ks + 1][0] = (short)(v.z & 0xffff); ka[kt][ks + 1][1] = (short)(v.z >> 16);
-        ka[kt][ks + 1][2] = (short)(v.w & 0xffff); ka[kt][ks + 1][3] = (short)(v.w >> 16);
-      }
+      for (int ks = 0; ks < KSTEPS; ++ks) ka[kt][ks] = __builtin_bit_cast(shortx8, kraw[sl][kt][ks]);
     // ---- V^T operand (A of O^T += V^T P^T): lane row j of dim tile dt is
-    // dim dt*16 + j; its k index 4g + e in key tile kt is key kb + 8g + 4kt + e.
-    shortx4 va[DT][2];
-    {
-      const int k8 = kb + 8 * g;
+    // dim dt*16 + j; its k index 8g + e is key kb + 8g + e (the raw 16 bytes)
+    shortx8 va[DT];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint4 v = vraw[sl][dt];
-        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int dt = 0; dt < DT; ++dt) va[dt] = __builtin_bit_cast(shortx8, vraw[sl][dt]);
+    if (kb + 32 > kend) {  // wave-uniform: the block that holds kend
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffff);
-          if (k8 + e >= kend) h = 0;  // never multiply a probability by data past the range
-          va[dt][e >> 2][e & 3] = (short)h;
-        }
-      }
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kb + 8 * g + e >= kend) va[dt][e] = 0;  // never multiply a probability by data past the range
     }
     // the block PFB further on takes this one's raw registers as soon as they
     // are converted, so its latency overlaps the products of the blocks in
@@ -343,8 +332,8 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          acc = mfma16x16x16(ka[kt][ks], qhi[qt][ks], acc);
-          acc = mfma16x16x16(ka[kt][ks], qlo[qt][ks], acc);
+          acc = mfma16x16x32(ka[kt][ks], qhi[qt][ks], acc);
+          acc = mfma16x16x32(ka[kt][ks], qlo[qt][ks], acc);
         }
         st[kt] = acc;
       }
@@ -363,7 +352,9 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
       const float factor = __expf(mrun[qt] - mnew);
       mrun[qt] = mnew;
       float psum = 0.f;
-      shortx4 phi[2], plo[2];
+      // B operand of the PV product: query j's probabilities of keys
+      // kb + 8g + e, where S^T left them (kt = e / 4)
+      shortx8 phi, plo;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -372,18 +363,15 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
           psum += pe;
           short hi, lo;
           split_bf16(pe, hi, lo);
-          phi[kt][e] = hi;
-          plo[kt][e] = lo;
+          phi[4 * kt + e] = hi;
+          plo[4 * kt + e] = lo;
         }
       lrun[qt] = lrun[qt] * factor + psum;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         o[qt][dt] *= factor;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          o[qt][dt] = mfma16x16x16(va[dt][kt], phi[kt], o[qt][dt]);
-          o[qt][dt] = mfma16x16x16(va[dt][kt], plo[kt], o[qt][dt]);
-        }
+        o[qt][dt] = mfma16x16x32(va[dt], phi, o[qt][dt]);
+        o[qt][dt] = mfma16x16x32(va[dt], plo, o[qt][dt]);
       }
     }
   }
