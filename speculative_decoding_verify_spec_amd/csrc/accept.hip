@@ -707,18 +707,28 @@ __global__ __launch_bounds__(128) void accept_chain_greedy_kernel(AcceptParams p
 
 // ---------------------------------------------------------------- tree
 // Validate the parent array and build child lists (children in ascending id).
-DEVI void build_tree(const AcceptParams& p, int b, int* first_child, int* next_sib) {
+// Called by every thread of the workgroup: the parent array is staged in LDS
+// by all threads, then one thread links the children in ascending order.
+DEVI void build_tree(const AcceptParams& p, int b, int* first_child, int* next_sib, int* spar) {
   const int T = p.T;
   const int32_t* par = p.parent + (size_t)b * T;
-  for (int v = 0; v < T; ++v) { first_child[v] = -1; next_sib[v] = -1; }
-  bool bad = par[0] != -1;
-  for (int c = T - 1; c >= 1; --c) {
-    int pc = par[c];
-    if (pc < 0 || pc >= c) { bad = true; pc = c - 1; }
-    next_sib[c] = first_child[pc];
-    first_child[pc] = c;
+  for (int v = threadIdx.x; v < T; v += blockDim.x) {
+    spar[v] = par[v];
+    first_child[v] = -1;
+    next_sib[v] = -1;
   }
-  if (bad) atomicOr(p.flags, FLAG_TREE);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool bad = spar[0] != -1;
+    for (int c = T - 1; c >= 1; --c) {
+      int pc = spar[c];
+      if (pc < 0 || pc >= c) { bad = true; pc = c - 1; }
+      next_sib[c] = first_child[pc];
+      first_child[pc] = c;
+    }
+    if (bad) atomicOr(p.flags, FLAG_TREE);
+  }
+  __syncthreads();
 }
 
 // Copy the accepted path's K/V (path[j] -> slot kv_len + j) in ascending j;
@@ -732,16 +742,56 @@ DEVI void tree_commit(const AcceptParams& p, int b, const int* path, int plen) {
   // one K or V region: [maxB][Hkv][max_ctx][D] dense, [npages][Hkv][page][D] paged
   const size_t per = p.kvm.table ? (size_t)p.kvm.npages * p.Hkv * KV_PAGE * p.D
                                  : (size_t)p.maxB * p.Hkv * p.max_ctx * p.D;
-  const int nel = p.L * p.Hkv * p.D;
-  for (int e = threadIdx.x; e < nel; e += blockDim.x) {
-    const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
-    uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per + d;
-    uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
-    for (int j = 1; j < plen; ++j) {
-      const int src = path[j];
-      if (src == j) continue;
-      kreg[kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + j)] = kreg[kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + src)];
-      vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + j)] = vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + src)];
+  // Node path[j] moves to slot base + j, for j in order.  A source slot is
+  // never a slot written earlier (path[j] >= j), and each thread keeps the
+  // same elements for every j, so no barrier is needed.  K rows move in
+  // 16-byte chunks; V^T entries (one slot of a dim row) one by one.  A batch
+  // of CB loads is issued before its stores, since the compiler cannot tell
+  // that sources and destinations differ.
+  constexpr int CB = 16;
+  const int kch = p.D / 8;
+  const int nk = p.L * p.Hkv * kch;   // K chunks per slot
+  const int nv = p.L * p.Hkv * p.D;   // V^T entries per slot
+  for (int j = 1; j < plen; ++j) {
+    const int src = path[j];
+    if (src == j) continue;  // uniform: path is shared
+    for (int e0 = threadIdx.x; e0 < nk; e0 += CB * blockDim.x) {
+      uint4 v[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int e = min(e0 + u * (int)blockDim.x, nk - 1);
+        const int c = e % kch, hk = (e / kch) % p.Hkv, l = e / (kch * p.Hkv);
+        const uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per;
+        v[u] = *(const uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + src) + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int e = e0 + u * blockDim.x;
+        if (e < nk) {
+          const int c = e % kch, hk = (e / kch) % p.Hkv, l = e / (kch * p.Hkv);
+          uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per;
+          *(uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + j) + 8 * c) = v[u];
+        }
+      }
+    }
+    for (int e0 = threadIdx.x; e0 < nv; e0 += CB * blockDim.x) {
+      uint16_t v[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int e = min(e0 + u * (int)blockDim.x, nv - 1);
+        const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
+        const uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
+        v[u] = vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + src)];
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int e = e0 + u * blockDim.x;
+        if (e < nv) {
+          const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
+          uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
+          vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + j)] = v[u];
+        }
+      }
     }
   }
 }
@@ -758,12 +808,11 @@ DEVI void write_tree_outputs(const AcceptParams& p, int b, const int* path, int 
 }
 
 __global__ __launch_bounds__(128) void accept_tree_greedy_kernel(AcceptParams p) {
-  __shared__ int first_child[128], next_sib[128], path[128], am[128];
+  __shared__ int first_child[128], next_sib[128], path[128], am[128], spar[128];
   __shared__ int s_plen, s_extra;
   const int b = blockIdx.x, T = p.T;
   for (int i = threadIdx.x; i < T; i += blockDim.x) row_argmax(p, b * T + i, am[i]);
-  if (threadIdx.x == 0) build_tree(p, b, first_child, next_sib);
-  __syncthreads();
+  build_tree(p, b, first_child, next_sib, spar);
   if (threadIdx.x == 0) {
     int v = 0, plen = 1;
     path[0] = 0;
@@ -793,7 +842,7 @@ __global__ __launch_bounds__(128) void accept_tree_greedy_kernel(AcceptParams p)
 // buffers) and, without replacement, removes x from q' and renormalises.  No
 // child accepted: draw from r; a leaf reached: bonus from p_leaf (slot T - 1).
 __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams p) {
-  __shared__ int first_child[128], next_sib[128], path[128], removed[128];
+  __shared__ int first_child[128], next_sib[128], path[128], removed[128], spar[128];
   __shared__ double shd[16];
   __shared__ float s_M, s_S, s_Zr, s_qmass, s_qtot;
   __shared__ int s_cur, s_acc, s_nrem, s_tok;
@@ -802,8 +851,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
   const float Tt = p.temperature;
   float* rb0 = p.rbuf + (size_t)b * V;
   float* rb1 = p.rbuf + ((size_t)p.B + b) * V;
-  if (threadIdx.x == 0) build_tree(p, b, first_child, next_sib);
-  __syncthreads();
+  build_tree(p, b, first_child, next_sib, spar);
   int v = 0, plen = 1;
   if (threadIdx.x == 0) path[0] = 0;
   while (true) {
@@ -844,22 +892,74 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
       const float qscale = (!p.replacement && nrem > 0) ? 1.0f / (s_qtot - s_qmass) : 1.0f;
       const RowRule rr = row_rule(p, row);
       double zs = 0.0, qs = 0.0;
-      for (int y = threadIdx.x; y < V; y += blockDim.x) {
-        const float ry = cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y] / Zr;
-        float qy = qv[y];
+      // every token as if still in q'; the removed ones are fixed below.  A
+      // thread's RU elements (a workgroup stride apart) are requested at once.
+      constexpr int RU = 8;
+      const float* rsrc = cur < 0 ? z : src;
+      auto resid = [&](float zy, float qy, int y) {
+        const float ry = cur < 0 ? pval(p, rr, zy, y, M, S) : zy / Zr;
         qs += (double)qy;
-        if (!p.replacement) {
-          bool gone = false;
-          for (int i = 0; i < nrem; ++i) gone |= removed[i] == y;
-          if (gone) qy = 0.f;
-        }
         const float d = fmaxf(0.f, ry - qy * qscale);
-        dst[y] = d;
         zs += (double)d;
+        return d;
+      };
+      if ((V & 3) == 0) {
+        // rows are 16-byte aligned: four tokens per load
+        const int V4 = V >> 2;
+        for (int i0 = threadIdx.x; i0 < V4; i0 += RU * blockDim.x) {
+          float4 zr[RU], qr[RU];
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            const int i = min(i0 + u * (int)blockDim.x, V4 - 1);
+            zr[u] = ((const float4*)rsrc)[i];
+            qr[u] = ((const float4*)qv)[i];
+          }
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            const int i = i0 + u * blockDim.x;
+            if (i < V4) {
+              float4 d;
+              d.x = resid(zr[u].x, qr[u].x, 4 * i);
+              d.y = resid(zr[u].y, qr[u].y, 4 * i + 1);
+              d.z = resid(zr[u].z, qr[u].z, 4 * i + 2);
+              d.w = resid(zr[u].w, qr[u].w, 4 * i + 3);
+              ((float4*)dst)[i] = d;
+            }
+          }
+        }
+      } else {
+        for (int y0 = threadIdx.x; y0 < V; y0 += RU * blockDim.x) {
+          float zr[RU], qr[RU];
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            const int yc = min(y0 + u * (int)blockDim.x, V - 1);
+            zr[u] = rsrc[yc];
+            qr[u] = qv[yc];
+          }
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            const int y = y0 + u * blockDim.x;
+            if (y < V) dst[y] = resid(zr[u], qr[u], y);
+          }
+        }
       }
       zs = block_sum(zs, shd);
       qs = block_sum(qs, shd);
       if (threadIdx.x == 0) {
+        if (!p.replacement) {
+          // a removed token has q' = 0: its residual is r itself (each
+          // distinct token once; the pass above wrote r - q' there)
+          for (int i = 0; i < nrem; ++i) {
+            const int x = removed[i];
+            bool seen = false;
+            for (int k = 0; k < i; ++k) seen |= removed[k] == x;
+            if (seen) continue;
+            const float rx = cur < 0 ? pval(p, rr, z[x], x, M, S) : src[x] / Zr;
+            const float dx = fmaxf(0.f, rx - qv[x] * qscale);
+            zs += (double)rx - (double)dx;
+            dst[x] = rx;
+          }
+        }
         if (zs > 0.0) { s_cur = (cur == 0) ? 1 : 0; s_Zr = (float)zs; }
         if (!p.replacement) {
           if (s_qtot < 0.f) s_qtot = (float)qs;
@@ -893,10 +993,51 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
     const float* src = cur == 1 ? rb1 : rb0;
     const float M = s_M, S = s_S;
     const RowRule rr = row_rule(p, row);
-    const int per = (V + blockDim.x - 1) / blockDim.x;
-    const int y0 = threadIdx.x * per, y1 = min(V, y0 + per);
+    const float* vsrc = cur < 0 ? z : src;
+    auto val = [&](float x, int y) { return cur < 0 ? pval(p, rr, x, y, M, S) : x; };
+    // thread chunks of a multiple of 4 tokens when rows are 16-byte aligned
+    const bool vec = (V & 3) == 0;
+    const int per = vec ? 4 * (((V >> 2) + blockDim.x - 1) / blockDim.x) : (V + blockDim.x - 1) / blockDim.x;
+    const int y0 = min(V, (int)threadIdx.x * per), y1 = min(V, y0 + per);
+    // the chunk's values in order, DB loads requested at once; f(y, value)
+    // returns true to stop
+    constexpr int DB = 8;
+    auto walk = [&](auto f) {
+      if (vec) {
+        for (int yb = y0; yb < y1; yb += 4 * DB) {
+          float4 c[DB];
+#pragma unroll
+          for (int u = 0; u < DB; ++u) {
+            const int yy = yb + 4 * u;
+            c[u] = yy < y1 ? *(const float4*)(vsrc + yy) : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < DB; ++u) {
+            const int yy = yb + 4 * u;
+            if (yy < y1) {
+              if (f(yy, val(c[u].x, yy))) return;
+              if (f(yy + 1, val(c[u].y, yy + 1))) return;
+              if (f(yy + 2, val(c[u].z, yy + 2))) return;
+              if (f(yy + 3, val(c[u].w, yy + 3))) return;
+            }
+          }
+        }
+      } else {
+        for (int yb = y0; yb < y1; yb += DB) {
+          float c[DB];
+#pragma unroll
+          for (int u = 0; u < DB; ++u) c[u] = yb + u < y1 ? vsrc[yb + u] : 0.f;
+#pragma unroll
+          for (int u = 0; u < DB; ++u)
+            if (yb + u < y1 && f(yb + u, val(c[u], yb + u))) return;
+        }
+      }
+    };
     double loc = 0.0;
-    for (int y = y0; y < y1; ++y) loc += (double)(cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]);
+    walk([&](int, float v) {
+      loc += (double)v;
+      return false;
+    });
     __shared__ double scan[1024];
     scan[threadIdx.x] = loc;
     if (threadIdx.x == 0) s_tok = 0x7fffffff;
@@ -913,10 +1054,14 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
     const double t = s_t;
     double run = scan[threadIdx.x] - loc;
     if (run <= t && run + loc > t) {
-      for (int y = y0; y < y1; ++y) {
-        run += (double)(cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]);
-        if (run > t) { atomicMin(&s_tok, y); break; }
-      }
+      walk([&](int y, float v) {
+        run += (double)v;
+        if (run > t) {
+          atomicMin(&s_tok, y);
+          return true;
+        }
+        return false;
+      });
     }
     __syncthreads();
     if (s_tok == 0x7fffffff) {

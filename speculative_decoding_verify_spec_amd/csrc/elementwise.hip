@@ -22,49 +22,66 @@ DEVI void check_pages(const PrepParams& p, int b, int n) {
   }
 }
 
-// One workgroup per sequence.  Copies kv_len into the workspace (the later
-// kernels of the step read only the workspace, weights and cache, so their
-// launch sequence can be recorded once and replayed); validates tokens, cache
-// room and the tree;
-// writes each row's clamped token, rotary position (kv_len + i for a chain,
-// kv_len + depth for a tree node), cache slot (kv_len + i), for a tree the
-// ancestor-or-self bitmask used by the attention mask, and gathers the rows'
-// embeddings into the fp32 residual stream x.
+// Workgroup (b, y) prepares rows PREP_ROWS*y .. of sequence b.  The first of
+// a sequence copies kv_len into the workspace (the later kernels of the step
+// read only the workspace, weights and cache, so their launch sequence can be
+// recorded once and replayed) and validates cache room and the tree; every
+// workgroup validates its rows' tokens, writes each row's clamped token,
+// rotary position (kv_len + i for a chain, kv_len + depth for a tree node),
+// cache slot (kv_len + i), for a tree the ancestor-or-self bitmask used by the
+// attention mask, and gathers the rows' embeddings into the fp32 residual
+// stream x.  A tree's depths and masks come from the whole parent array, which
+// each workgroup reads (at most 128 entries).
+constexpr int PREP_ROWS = 8;
 template <typename WT>
 __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
   const int b = blockIdx.x;
   const int T = p.T;
+  const int r0 = blockIdx.y * PREP_ROWS, r1 = min(T, r0 + PREP_ROWS);
+  const bool lead = blockIdx.y == 0;
   __shared__ int depth[128];
   __shared__ uint64_t anc_lo[128], anc_hi[128];
   __shared__ int stok[128];
+  __shared__ int spar[128];
   const int kv = p.kv_len[b];
   const int cap = seq_capacity(p);
-  if (threadIdx.x == 0) {
+  if (lead && threadIdx.x == 0) {
     p.kv_copy[b] = kv;
     if (kv < 0 || kv > cap - T) atomicOr(p.flags, FLAG_KV_OVERFLOW);
     check_pages(p, b, min(cap, (kv < 0 ? 0 : kv) + T));
-    if (p.parent) {
-      const int32_t* par = p.parent + (size_t)b * T;
-      bool bad = par[0] != -1;
-      depth[0] = 0;
-      anc_lo[0] = 1ull;
-      anc_hi[0] = 0ull;
-      for (int i = 1; i < T; ++i) {
-        int pi = par[i];
-        if (pi < 0 || pi >= i) {
-          bad = true;
-          pi = i - 1;  // treat as a chain link so later kernels stay in bounds
-        }
-        depth[i] = depth[pi] + 1;
-        anc_lo[i] = anc_lo[pi] | (i < 64 ? (1ull << i) : 0ull);
-        anc_hi[i] = anc_hi[pi] | (i >= 64 ? (1ull << (i - 64)) : 0ull);
+  }
+  if (p.parent) {
+    // a node's parent must precede it (the root's is -1); a bad link is
+    // flagged and taken as a chain link, so every walk below ends at node 0
+    const int32_t* par = p.parent + (size_t)b * T;
+    bool bad = false;
+    for (int i = threadIdx.x; i < T; i += blockDim.x) {
+      int pi = par[i];
+      if (i == 0 ? pi != -1 : (pi < 0 || pi >= i)) {
+        bad = true;
+        pi = i - 1;
       }
-      if (bad) atomicOr(p.flags, FLAG_TREE);
+      spar[i] = pi;
+    }
+    if (bad && lead) atomicOr(p.flags, FLAG_TREE);
+    __syncthreads();
+    // each node walks to the root: its depth and its ancestor-or-self bits
+    for (int i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
+      int d = 0;
+      uint64_t lo = 0ull, hi = 0ull;
+      for (int c = i;; c = spar[c], ++d) {
+        if (c < 64) lo |= 1ull << c;
+        else hi |= 1ull << (c - 64);
+        if (c == 0) break;
+      }
+      depth[i] = d;
+      anc_lo[i] = lo;
+      anc_hi[i] = hi;
     }
   }
   __syncthreads();
   const int kvc = kv < 0 ? 0 : kv;
-  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+  for (int i = r0 + threadIdx.x; i < r1; i += blockDim.x) {
     const int m = b * T + i;
     int t = p.tokens[m];
     if (t < 0 || t >= p.vocab) {
@@ -86,8 +103,8 @@ __global__ __launch_bounds__(256) void prep_embed_kernel(PrepParams p) {
   // embedding rows, 8 elements per thread per pass
   const WT* E = (const WT*)p.embed;
   const int per_row = p.d / 8;
-  for (int e = threadIdx.x; e < T * per_row; e += blockDim.x) {
-    const int i = e / per_row, c = (e % per_row) * 8;
+  for (int e = threadIdx.x; e < (r1 - r0) * per_row; e += blockDim.x) {
+    const int i = r0 + e / per_row, c = (e % per_row) * 8;
     const WT* src = E + (size_t)stok[i] * p.d + c;
     float* dst = p.x + ((size_t)(b * T + i)) * p.d + c;
     if constexpr (sizeof(WT) == 2) {
@@ -181,10 +198,11 @@ hipError_t launch_prep(const PrepParams& p, hipStream_t s) {
       prep_ragged_kernel<float><<<p.B + 1, 256, 0, s>>>(p);
     return hipGetLastError();
   }
+  const dim3 grid(p.B, (p.T + PREP_ROWS - 1) / PREP_ROWS);
   if (p.wdtype == 1)
-    prep_embed_kernel<uint16_t><<<p.B, 256, 0, s>>>(p);
+    prep_embed_kernel<uint16_t><<<grid, 256, 0, s>>>(p);
   else
-    prep_embed_kernel<float><<<p.B, 256, 0, s>>>(p);
+    prep_embed_kernel<float><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
