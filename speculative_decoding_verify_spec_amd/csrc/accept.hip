@@ -731,67 +731,49 @@ DEVI void build_tree(const AcceptParams& p, int b, int* first_child, int* next_s
   __syncthreads();
 }
 
-// Copy the accepted path's K/V (path[j] -> slot kv_len + j) in ascending j;
-// node path[j] >= j, so no copy overwrites a slot a later copy still reads.
-DEVI void tree_commit(const AcceptParams& p, int b, const int* path, int plen) {
+// The accepted tree path for the commit kernel: the sequence's kv_len, the
+// path length and the path, in the workspace.  Read here, before the commit
+// kernel writes kv_len_out (which may alias kv_len).
+DEVI void stash_tree_path(const AcceptParams& p, int b, const int* path, int plen) {
   if (!p.kv_len_out) return;
-  const int base = p.kv_len[b];
-  if (threadIdx.x == 0) p.kv_len_out[b] = base + plen;
+  int32_t* tp = p.tpath + (size_t)b * TPATH;
+  if (threadIdx.x == 0) {
+    tp[0] = p.kv_len[b];
+    tp[1] = plen;
+  }
+  for (int i = threadIdx.x; i < plen; i += blockDim.x) tp[2 + i] = path[i];
+}
+
+// Tree commit: node path[j] of the accepted path moves to slot kv_len + j,
+// for j in ascending order; node path[j] >= j, so no copy overwrites a slot
+// a later copy still reads.  One workgroup per (layer, KV head) and
+// sequence: the copies (a K row, and one V^T entry per dim, per node) spread
+// over the chip instead of queueing in one CU.  Thread i keeps the same
+// K chunk and V^T row for every j, so no barrier is needed.
+__global__ __launch_bounds__(128) void accept_tree_commit_kernel(AcceptParams p) {
+  const int lh = blockIdx.x, b = blockIdx.y;
+  const int l = lh / p.Hkv, hk = lh % p.Hkv;
+  const int32_t* tp = p.tpath + (size_t)b * TPATH;
+  const int base = tp[0], plen = tp[1];
+  if (lh == 0 && threadIdx.x == 0) p.kv_len_out[b] = base + plen;
   const int cap = p.kvm.table ? min(p.max_ctx, p.kvm.ppseq * KV_PAGE) : p.max_ctx;
-  if (base < 0 || base + p.T > cap) return;
+  if (base < 0 || base + p.T > cap || plen < 1 || plen > p.T) return;
   // one K or V region: [maxB][Hkv][max_ctx][D] dense, [npages][Hkv][page][D] paged
   const size_t per = p.kvm.table ? (size_t)p.kvm.npages * p.Hkv * KV_PAGE * p.D
                                  : (size_t)p.maxB * p.Hkv * p.max_ctx * p.D;
-  // Node path[j] moves to slot base + j, for j in order.  A source slot is
-  // never a slot written earlier (path[j] >= j), and each thread keeps the
-  // same elements for every j, so no barrier is needed.  K rows move in
-  // 16-byte chunks; V^T entries (one slot of a dim row) one by one.  A batch
-  // of CB loads is issued before its stores, since the compiler cannot tell
-  // that sources and destinations differ.
-  constexpr int CB = 16;
-  const int kch = p.D / 8;
-  const int nk = p.L * p.Hkv * kch;   // K chunks per slot
-  const int nv = p.L * p.Hkv * p.D;   // V^T entries per slot
+  uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per;
+  uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
+  const int t = threadIdx.x;
   for (int j = 1; j < plen; ++j) {
-    const int src = path[j];
-    if (src == j) continue;  // uniform: path is shared
-    for (int e0 = threadIdx.x; e0 < nk; e0 += CB * blockDim.x) {
-      uint4 v[CB];
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int e = min(e0 + u * (int)blockDim.x, nk - 1);
-        const int c = e % kch, hk = (e / kch) % p.Hkv, l = e / (kch * p.Hkv);
-        const uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per;
-        v[u] = *(const uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + src) + 8 * c);
-      }
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int e = e0 + u * blockDim.x;
-        if (e < nk) {
-          const int c = e % kch, hk = (e / kch) % p.Hkv, l = e / (kch * p.Hkv);
-          uint16_t* kreg = p.kv_cache + (size_t)(2 * l) * per;
-          *(uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + j) + 8 * c) = v[u];
-        }
-      }
+    const int src = tp[2 + j];
+    if (src == j) continue;  // uniform
+    if (t < p.D / 8) {
+      const uint4 v = *(const uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + src) + 8 * t);
+      *(uint4*)(kreg + kv_k_off(p.kvm, p.Hkv, p.D, b, hk, base + j) + 8 * t) = v;
     }
-    for (int e0 = threadIdx.x; e0 < nv; e0 += CB * blockDim.x) {
-      uint16_t v[CB];
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int e = min(e0 + u * (int)blockDim.x, nv - 1);
-        const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
-        const uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
-        v[u] = vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + src)];
-      }
-#pragma unroll
-      for (int u = 0; u < CB; ++u) {
-        const int e = e0 + u * blockDim.x;
-        if (e < nv) {
-          const int d = e % p.D, hk = (e / p.D) % p.Hkv, l = e / (p.D * p.Hkv);
-          uint16_t* vreg = p.kv_cache + (size_t)(2 * l + 1) * per;
-          vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, d, base + j)] = v[u];
-        }
-      }
+    if (t < p.D) {
+      const uint16_t v = vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, t, base + src)];
+      vreg[kv_v_off(p.kvm, p.Hkv, p.D, b, hk, t, base + j)] = v;
     }
   }
 }
@@ -832,7 +814,7 @@ __global__ __launch_bounds__(128) void accept_tree_greedy_kernel(AcceptParams p)
   }
   __syncthreads();
   write_tree_outputs(p, b, path, s_plen, s_extra);
-  tree_commit(p, b, path, s_plen);
+  stash_tree_path(p, b, path, s_plen);
 }
 
 // Sampled tree walk, one workgroup per sequence.  At node v the running target
@@ -1079,7 +1061,7 @@ __global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams 
     }
   }
   write_tree_outputs(p, b, path, plen, s_tok);
-  tree_commit(p, b, path, plen);
+  stash_tree_path(p, b, path, plen);
 }
 
 // Top-k / top-p selection for all rows, in batches of SEL_ROWS rows, then the
@@ -1118,6 +1100,10 @@ hipError_t launch_accept(const AcceptParams& pin, hipStream_t s) {
   if (p.parent) {
     if (greedy) accept_tree_greedy_kernel<<<p.B, 128, 0, s>>>(p);
     else accept_tree_sampled_kernel<<<p.B, 1024, 0, s>>>(p);
+    if (p.kv_len_out) {
+      if (p.D > 128 || p.T > TPATH - 2 || !p.tpath) return hipErrorInvalidValue;
+      accept_tree_commit_kernel<<<dim3(p.L * p.Hkv, p.B), 128, 0, s>>>(p);
+    }
     return hipGetLastError();
   }
   if (greedy) {

@@ -156,6 +156,7 @@ struct CombineParams {
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- accept
+constexpr int TPATH = 130;  // ints per sequence of AcceptParams::tpath (T <= 128)
 struct AcceptParams {
   const float* logits;     // [B][T][V]
   const float* q;          // chain [B][T-1][V], tree [B][T][V]
@@ -174,6 +175,7 @@ struct AcceptParams {
   float* rsum;             // [B][nch]
   int32_t* nacc;           // [B]
   float* rbuf;             // [2][B][V]
+  int32_t* tpath;          // [B][TPATH]: kv_len, path length, accepted tree path (tree commit)
   uint32_t* flags;
   // cache for the tree commit
   uint16_t* kv_cache;

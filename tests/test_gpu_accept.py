@@ -137,7 +137,8 @@ def test_tree_accept_matches_oracle(V, B, branching, temp, repl):
         T = parent.shape[1]
         assert T == max_rows
         kv_len = torch.full((B,), 100, dtype=torch.int32, device=dev())
-        kv_out = torch.zeros((B,), dtype=torch.int32, device=dev())
+        # odd rounds update the lengths in place (kv_len_out may alias kv_len)
+        kv_out = kv_len if r % 2 else torch.zeros((B,), dtype=torch.int32, device=dev())
         out = torch.full((B, T), -5, dtype=torch.int32, device=dev())
         nacc = torch.full((B,), -5, dtype=torch.int32, device=dev())
         k_before, v_before = synth.kv_views(eng.kv_cache.clone(), _accept_shape(V), 4, 512)
