@@ -38,7 +38,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 PKG_CSRC = os.path.join(ROOT, "speculative_decoding_verify_spec_amd", "csrc")
-GEMM_SOURCES = ("gemm.hip", "common.h", "launch.h")
+# the GEMM kernels' sources: whole files, or (file, first line, end line) for
+# the GEMM section of the shared parameter header
+GEMM_SOURCES = ("gemm.hip", "common.h", ("launch.h", "-- GEMM\n", "-- attention\n"))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama8b_m4_hbm_traffic.txt")
 
 
@@ -50,9 +52,15 @@ def gemm_sources_sha256():
     import re
 
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for src in GEMM_SOURCES:
+        f, first, end = (src, None, None) if isinstance(src, str) else src
         with open(os.path.join(PKG_CSRC, f)) as fh:
             text = fh.read()
+        if first is not None:
+            # the lines from the section banner ending in `first` up to the next
+            # banner ending in `end`
+            a = text.index(first)
+            text = text[a:text.index(end, a)]
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())

@@ -480,11 +480,8 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_lds_kernel(AttnParams p) {
   const int s = u % ncol;
   const int kvh = (u / ncol) % p.Hkv;
   const int b = u / (ncol * p.Hkv);
-  if (s >= p.splits) {
-    const int sw = s - p.splits;
-    const int per = 4 * QT / qpw;
-    if (sw / per > 0) return;
-    attn_suffix<D, QT>(p, kvh, qg, b, sw % per, qpw);
+  if (s >= p.splits) {  // the step's own keys: suffix workgroup s - splits of this query group
+    attn_suffix<D, QT>(p, kvh, qg, b, s - p.splits, qpw);
     return;
   }
   const int rs = p.rstart ? p.rstart[b] : b * p.T;
