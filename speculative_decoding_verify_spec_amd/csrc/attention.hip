@@ -7,14 +7,16 @@
 // The context of a (sequence, KV head) is cut into `splits` workgroups of 4
 // waves; each wave keeps its own online-softmax state (flash-decoding style),
 // the four states are merged in LDS and the workgroup writes one partial
-// (max, sum, unnormalised output) per query.  The products run on bf16 MFMA
-// 16x16x16: S^T = K Q^T with K exact in bf16 and the fp32 queries split into
-// bf16 hi + lo, then O^T += V^T P^T with the fp32 probabilities split the
-// same way; accumulation is fp32.  V is stored transposed in the cache so the
-// key index (the contraction of P V) is contiguous.  A wave's first key
-// blocks (PFB of them) are requested before the queries are prepared, so the
-// cache reads and the query reads overlap, and the block PFB further on is
-// requested as soon as a block is converted into matrix operands.
+// (max, sum, unnormalised output) per query.  The products run on the gfx950
+// bf16 MFMA 16x16x32: S^T = K Q^T with K exact in bf16 and the fp32 queries
+// split into bf16 hi + lo, then O^T += V^T P^T with the fp32 probabilities
+// split the same way; accumulation is fp32.  V is stored transposed in the
+// cache so the key index (the contraction of P V) is contiguous.  A wave's
+// first key blocks (PFB of them) are requested before the queries are
+// prepared, so the cache reads and the query reads overlap, and the block PFB
+// further on is requested as soon as a block's registers are free.  More
+// than 16 queries per KV head at D = 128 take attn_ctx_lds_kernel, which
+// stages the key blocks in LDS instead.
 //
 // Suffix part: more workgroups per (sequence, KV head, query group) attend
 // to the step's own keys in fp32 and write their partials in the slot after
@@ -39,10 +41,12 @@ namespace sv {
 //     blocks are staged in LDS (attn_ctx_lds_kernel below, two workgroups
 //     per CU); at D = 64 two blocks are in flight per wave in registers
 //     (PFB = 2), more than 256 registers per lane: one workgroup per CU;
-//   nq > 64 (token trees): two 16-query groups per workgroup that walk the
-//     same key blocks, two workgroups per CU.  The one-per-CU form would also
-//     run the many suffix workgroups of a tree one per CU (32.1 against
-//     29.9 ms per step at B = 4, tree [4,4,2,2]).
+//   nq > 64 (token trees): at D = 128 the LDS form as above, one 32-query
+//     group per workgroup, the groups of a (sequence, KV head) placed on one
+//     XCD so their key reads after the first hit its L2 (tree [4,4,2,2] at
+//     B = 4: 133 against 269 us per layer); at D = 64 two 16-query groups
+//     per workgroup walk the same key blocks in registers, two workgroups
+//     per CU.
 int attn_query_tiles(int nq, int D) { return (nq > 16 && (D == 128 || nq <= 64)) ? 2 : 1; }
 int attn_groups_per_wg(int nq, int D) { return (D != 128 && nq > 64) ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
