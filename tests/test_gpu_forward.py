@@ -91,6 +91,8 @@ GQA_CASES = [
     (1, 1, [300], None),
     (3, 4, [300, 1, 777], None),
     (2, 8, [1000, 64], None),
+    # a 16-row chain: 64 queries per KV head, the widest chain of the LDS form
+    (2, 16, [997, 33], None),
     (2, 15, [129, 500], [2, 2, 2]),
     (1, 7, [0], None),
     # a deep tree (a 71-node chain, then a fork): nodes with more than 64
