@@ -224,15 +224,17 @@ def main():
     for k in range(a.warmup):
         one_step(k)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the per-step distribution
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for k in range(a.warmup, a.warmup + a.steps):
+    evs[0].record(stream)
+    for i, k in enumerate(range(a.warmup, a.warmup + a.steps)):
         one_step(k)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
+    step_ms = step_percentiles(evs)
     n_timed = nacc_hist[a.warmup:].cpu().numpy()
     tokens_out = int((n_timed + 1).sum())
     value = tokens_out / wall
@@ -316,7 +318,7 @@ def main():
     result = {
         "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
         "value": round(value, 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "step_ms": step_ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32 (bf16 weights, fp32 activations/accum)",
         "data": "synthetic (random-init weights, random bf16 KV context, noisy-target drafts)",
         "config": {"workload": f"llama3-8b-shape chain verify B={B} ctx={ctx} gamma={gamma} "
@@ -398,11 +400,15 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
     for k in range(a.warmup):
         one_step(k)
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     t0 = time.perf_counter()
-    for k in range(a.warmup, a.warmup + a.steps):
+    evs[0].record(stream)
+    for i, k in enumerate(range(a.warmup, a.warmup + a.steps)):
         one_step(k)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = step_percentiles(evs)
     n_timed = nacc_hist[a.warmup:].cpu().numpy()
     tokens_out = int((n_timed + 1).sum())
     ms_per_step = wall * 1000.0 / a.steps
@@ -430,7 +436,8 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
     result = {
         "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s; HBM GB/s vs peak",
         "value": round(tokens_out / wall, 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "step_ms": step_ms, "higher_is_better": True,
+        "scaling": "weak",
         "vs_baseline": None, "dtype": "f32 (bf16 weights, fp32 activations/accum)",
         "data": "synthetic (random-init weights, random bf16 KV context, noisy-target tree drafts)",
         "config": {"workload": f"llama3-8b-shape tree verify B={B} ctx={a.ctx} tree={branching} ({T} nodes) "
@@ -587,6 +594,16 @@ def run_recurrent(a, dev):
                                             f"verify + snapshot commit; {dt:.1f} s"}
     log(f"recurrent: {ms_fused:.4f} ms/step (fused), {ms_replay:.4f} (replay), {ms_snap:.4f} (snapshots)")
     print(json.dumps(result), flush=True)
+
+
+def step_percentiles(evs):
+    """Median, P10 and P90 of the step times between consecutive HIP events
+    recorded on the launch stream (ms)."""
+    import numpy as np
+
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)])
+    return {"median": round(float(np.median(d)), 4), "p10": round(float(np.percentile(d, 10)), 4),
+            "p90": round(float(np.percentile(d, 90)), 4)}
 
 
 def profile_pass(S, eng, one_step, steps):
