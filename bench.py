@@ -669,7 +669,13 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
         toks += int((res["n_accepted"] + 1).sum())
         nrounds += 1
     log(f"cpu baseline: {dt:.1f}s for {nrounds} rounds, {toks} tokens")
-    return {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores,
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores, "cpu_model": cpu_model,
             "kind": "oracle", "sample": f"{nrounds} verify rounds (B={B}, T={a.gamma + 1}, ctx {ctx}, "
                                         f"32 layers, forward + accept) of the same workload; {dt:.1f} s",
             "round_seconds": round(dt / nrounds, 2), "host_cores_visible": cores}
