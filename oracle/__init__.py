@@ -19,10 +19,15 @@ path computes, written from the pages:
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 this package.  It shares no code with the HIP path and imports nothing from it.
 
+Pins: the forward's layer composition agrees with an independent Llama
+decoder implementation (the `transformers` library's, tests/test_oracle_hf_llama.py);
+its components with closed forms and library routines, and the whole forward
+with causal and prefill/decode consistency (tests/test_oracle_model.py); the
+accept rule by exact enumeration of chains and small trees with planted wrong
+variants as negative controls (tests/test_oracle_pins.py).
+
 Parity unpinned: the absolute logit values of the random-init 8B-shaped model
-have no external reference; they are pinned only through the component checks
-in tests/test_oracle_model.py (closed forms, library special cases, causal and
-prefill/decode consistency).  The sibling order of a token tree has no printed
-example; enumeration and sampling pin only losslessness.
+have no external reference beyond those checks.  The sibling order of a token
+tree has no printed example; enumeration pins only losslessness.
 """
 from . import philox, numerics, model, accept, metrics, recurrent  # noqa: F401

@@ -180,7 +180,11 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
     """One sequence with a token tree.  z [T, V] logits per node; q [T, V] the
     draft distribution each node's children were drawn from; tokens [T] node
     tokens (node 0 = pending token); parent [T] (root -1).  u(slot) -> uniform.
-    Returns (path node ids from the root, emitted tokens, margins)."""
+    Returns (path node ids from the root, emitted tokens, margins).
+
+    _variant plants a wrong walk for negative-control tests only:
+    "resample_from_p" keeps r = p_v after rejected siblings; "no_renorm"
+    removes a rejected child from q' without renormalising q'."""
     T = len(tokens)
     children = [[] for _ in range(T)]
     for c in range(1, T):
@@ -224,7 +228,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
             if not replacement:
                 qp[x] = 0.0
                 s = qp.sum()
-                if s > 0.0:
+                if s > 0.0 and _variant != "no_renorm":
                     qp = qp / s
         if accepted is None:
             extra, m = inverse_cdf(r, u(T - 1))

@@ -343,3 +343,58 @@ def test_paged_placement_does_not_change_the_forward():
         outs.append(M.forward(sh, W, toks, kv_len, kg, vg)[0])
     assert np.array_equal(outs[0], outs[1])
     assert np.allclose(outs[0], M.forward(sh, W, toks, kv_len, kd, vd)[0], atol=0)
+
+
+def test_commit_chain_pending_token_convention():
+    """After n accepted drafts the pending token and the n drafts are cached:
+    kv_len grows by n + 1 (CS349E Lecture 6, section 6.2)."""
+    assert list(M.commit_chain([10, 0, 5], [2, 0, 3])) == [13, 1, 9]
+
+
+def test_speculative_greedy_rounds_with_commit_equal_plain_decoding():
+    """Several verify rounds through the oracle's forward, greedy accept and
+    chain commit produce the target's own greedy decoding token for token
+    (CS349E Lecture 6, section 7.4), with the verify window's K/V written at
+    kv_len + i before acceptance and kept only up to the committed length.  An
+    off-by-one in the commit or the window's positions breaks the equality."""
+    from oracle import accept as A
+    sh = _shape(V=37)
+    W = M.Weights(*_weights(sh, seed=12))
+    rng = np.random.default_rng(13)
+    P, n_out, ctx = 6, 24, 64
+    prompt = rng.integers(0, sh.vocab, size=(1, P))
+
+    def prefill():
+        kc, vc = _empty_cache(sh, 1, ctx)
+        z, kn, vn = M.forward(sh, W, prompt, np.zeros(1, int), kc, vc)
+        _store(kc, vc, kn, vn, np.zeros(1, int))
+        return kc, vc, int(np.argmax(z[0, -1]))
+
+    # plain greedy decoding, one row per step
+    kc, vc, pending = prefill()
+    kv, plain = P, [pending]
+    while len(plain) < n_out:
+        z, kn, vn = M.forward(sh, W, np.array([[pending]]), np.array([kv]), kc, vc)
+        _store(kc, vc, kn, vn, np.array([kv]))
+        kv += 1
+        pending = int(np.argmax(z[0, 0]))
+        plain.append(pending)
+
+    # speculative rounds: drafts right about 60% of the time
+    kc, vc, pending = prefill()
+    kv, spec = np.array([P]), [pending]
+    while len(spec) < n_out:
+        gamma = int(rng.integers(1, 5))
+        drafts = []
+        for i in range(gamma):
+            k = len(spec) + i
+            right = plain[k] if k < len(plain) else 0
+            drafts.append(right if rng.random() < 0.6 else int(rng.integers(0, sh.vocab)))
+        toks = np.array([[pending] + drafts])
+        z, kn, vn = M.forward(sh, W, toks, kv, kc, vc)
+        _store(kc, vc, kn, vn, kv)
+        n, out, _ = A.accept_chain_one(z[0], None, toks[0], 0.0, None)
+        kv = M.commit_chain(kv, [n])
+        pending = out[-1]
+        spec += out
+    assert spec[:n_out] == plain

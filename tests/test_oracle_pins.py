@@ -40,12 +40,34 @@ class _Tables:
                 self.q[pre] = _random_dist(rng, V, zeros=1 if (len(pre) % 2) else 0)
 
 
+class _NotConstant(Exception):
+    """The oracle's output changes inside a cell of the rule's partition."""
+
+
+def _constant_on_cell(cells, run):
+    """The oracle's output for uniforms in the box `cells` (slot -> [lo, hi)).
+    It is evaluated at the box's midpoint and just inside its lower and upper
+    corners; each decision is monotone in its uniform (a threshold test, or
+    an inverse CDF), so equal outputs at the three points mean the oracle's
+    own decision boundaries are the rule's: no boundary of the oracle lies
+    inside a cell, and the midpoint's output holds for the whole cell.
+    Raises _NotConstant otherwise."""
+    def at(f):
+        return {s: lo + (hi - lo) * f for s, (lo, hi) in cells.items()}
+    mid = tuple(run(at(0.5)))
+    for f in (1e-9, 1.0 - 1e-9):
+        if tuple(run(at(f))) != mid:
+            raise _NotConstant(cells)
+    return mid
+
+
 def _enumerate_chain(tab, gamma, variant="residual", ztab=None, temperature=1.0, adj=None):
     """Exact distribution of the oracle's emitted tokens, extended to gamma+1
     tokens with the target's own conditionals.  Draft tuples are enumerated
     with weight prod q; every uniform's range is split at the decision
     boundaries implied by the pages' rule (accept iff u < p/q; inverse CDF of
-    the residual) and the oracle is called at each cell's midpoint.
+    the residual) and the oracle's output is taken on each cell after
+    checking that it is constant there (`_constant_on_cell`).
 
     With `ztab` the oracle receives log ztab.p as logits, with `temperature`
     and the sampling adjustments `adj`, while the cells come from tab.p: the
@@ -78,13 +100,13 @@ def _enumerate_chain(tab, gamma, variant="residual", ztab=None, temperature=1.0,
                     p, qq = tab.p[xs[:n]], tab.q[xs[:n]]
                     prefix_w *= min(1.0, p[xs[n]] / qq[xs[n]])
                 continue
-            # accept uniforms for drafts 1..n at their accept-cell midpoints
-            us = {}
+            # accept uniforms for drafts 1..n in their accept cells [0, t)
+            cells = {}
             for i in range(n):
                 p, qq = tab.p[xs[:i]], tab.q[xs[:i]]
-                us[i] = min(1.0, p[xs[i]] / qq[xs[i]]) / 2.0
+                cells[i] = (0.0, min(1.0, p[xs[i]] / qq[xs[i]]))
             if n < gamma:
-                us[n] = rej_mid
+                cells[n] = (2.0 * rej_mid - 1.0, 1.0)
             pn = tab.p[xs[:n]]
             if n < gamma and variant == "residual":
                 r = np.maximum(0.0, pn - tab.q[xs[:n]])
@@ -98,9 +120,11 @@ def _enumerate_chain(tab, gamma, variant="residual", ztab=None, temperature=1.0,
                 if r[y] <= 0:
                     continue
                 lo = c[y - 1] if y else 0.0
-                us[gamma] = (lo + r[y] / 2.0) / R
-                ny, out, _ = acc.accept_chain_one(z, qrows, tokens, temperature, lambda s: us[s],
-                                                  _variant=variant, **adj)
+                cy = dict(cells)
+                cy[gamma] = (lo / R, c[y] / R)
+                out = _constant_on_cell(
+                    cy, lambda u: acc.accept_chain_one(z, qrows, tokens, temperature, lambda s: u[s],
+                                                       _variant=variant, **adj)[1])
                 cell_w = w_draft * w * r[y] / R
                 key = tuple(out)
                 joint[key] = joint.get(key, 0.0) + cell_w
@@ -147,7 +171,10 @@ def test_chain_enumeration_output_is_p(gamma):
 def test_chain_enumeration_wrong_variants_fail(variant):
     """Both wrong implementations of section 7.5 change the output distribution."""
     tab = _Tables(V=8, depth=2, seed=3)
-    got = _enumerate_chain(tab, 2, variant=variant)
+    try:
+        got = _enumerate_chain(tab, 2, variant=variant)
+    except _NotConstant:
+        return
     want = _target_joint(tab, 2)
     assert 0.5 * np.abs(got - want).sum() > 1e-3
 
@@ -285,84 +312,158 @@ def test_tree_all_ones_is_chain():
         assert out_t == out_c
 
 
-def _tree_round_sample(rng, tab, branching, replacement, variant="residual", ztab=None, adj=None):
-    """Draw one token tree from the draft tables (children of a node drawn from
-    q(.|path) with or without replacement), run the oracle's tree accept with
-    fresh uniforms, return the first two emitted tokens.  With `ztab` / `adj`
-    as in _enumerate_chain (tab.p is then the adjusted target)."""
+def _tree_configs(tab, branching, replacement):
+    """Every token tree the draft can produce with the given branching (BFS node
+    order, root = node 0 with an empty prefix), with its probability: a
+    node's children are drawn one after another from q(.|prefix), without
+    replacement (each draw renormalised over the tokens not yet drawn) or
+    with it."""
+    V = tab.V
+
+    def child_lists(qv, k):
+        out = []
+        for xs in itertools.product(range(V), repeat=k):
+            if not replacement and len(set(xs)) < k:
+                continue
+            w, left = 1.0, 1.0
+            for x in xs:
+                w *= qv[x] / left
+                if not replacement:
+                    left -= qv[x]
+            if w > 0.0:
+                out.append((xs, w))
+        return out
+
+    trees = [([-1], [0], [()], 1.0)]
+    level = 1
+    for k in branching:
+        nxt = []
+        for parents, toks, ctx, w in trees:
+            frontier = [v for v in range(len(parents)) if len(ctx[v]) == level - 1]
+            partial = [(parents, toks, ctx, w)]
+            for v in frontier:
+                grown = []
+                for pa, tk, cx, wt in partial:
+                    for xs, wx in child_lists(tab.q[cx[v]], k):
+                        grown.append((pa + [v] * k, tk + list(xs), cx + [cx[v] + (x,) for x in xs], wt * wx))
+                partial = grown
+            nxt += partial
+        trees = nxt
+        level += 1
+    return trees
+
+
+def _enumerate_tree(tab, branching, replacement, variant="residual", ztab=None, adj=None,
+                    oracle_replacement=None):
+    """Exact distribution of the tokens the oracle's tree walk emits, extended to
+    depth+1 tokens with the target's own conditionals.  Every tree the draft
+    can produce is enumerated with its probability; within a tree, every
+    uniform's range is split at the boundaries the rule implies (child c,
+    slot c - 1: accept iff u < r(x)/q'(x), with r and q' updated after each
+    rejected sibling as the residual rule says; the final draw, slot T - 1:
+    inverse CDF of r) and the oracle's output is taken on each cell after
+    checking that it is constant there (`_constant_on_cell`).
+    `ztab` / `adj` as in _enumerate_chain; `oracle_replacement` hands the
+    oracle a different replacement flag than the one the trees were drawn
+    with (a negative control)."""
     V = tab.V
     ztab = tab if ztab is None else ztab
     adj = adj or {}
-    parents, toks, ctx = [-1], [0], [()]
-    level = [0]
-    for k in branching:
-        nxt = []
-        for v in level:
-            qv = tab.q[ctx[v]].copy()
-            chosen = []
-            for _ in range(k):
-                x = int(rng.choice(V, p=qv / qv.sum()))
-                chosen.append(x)
+    orep = replacement if oracle_replacement is None else oracle_replacement
+    depth = len(branching)
+    joint = {}
+    for parents, toks, ctx, w_tree in _tree_configs(tab, branching, replacement):
+        T = len(parents)
+        kids = [[c for c in range(1, T) if parents[c] == v] for v in range(T)]
+        z = np.stack([np.log(np.maximum(ztab.p[c], 1e-300)) for c in ctx])
+        q = np.stack([tab.q[c] if c in tab.q else np.full(V, 1.0 / V) for c in ctx])
+
+        def draw(r, us, w):
+            R = r.sum()
+            c = np.cumsum(r)
+            for y in range(V):
+                if r[y] <= 0:
+                    continue
+                lo = c[y - 1] if y else 0.0
+                cy = dict(us)
+                cy[T - 1] = (lo / R, c[y] / R)
+                key = _constant_on_cell(
+                    cy, lambda u: acc.accept_tree_one(z, q, toks, parents, 1.0, lambda s: u.get(s, 0.5),
+                                                      replacement=orep, _variant=variant, **adj)[1])
+                joint[key] = joint.get(key, 0.0) + w_tree * w * r[y] / R
+
+        def visit(v, us, w):
+            r = tab.p[ctx[v]].copy()
+            if not kids[v]:
+                draw(r, us, w)
+                return
+            qp = tab.q[ctx[v]].copy()
+            for c in kids[v]:
+                x = toks[c]
+                t = 1.0 if qp[x] <= 0 else min(1.0, r[x] / qp[x])
+                if t > 0.0:
+                    visit(c, {**us, c - 1: (0.0, t)}, w * t)
+                if t >= 1.0:
+                    return
+                us = {**us, c - 1: (t, 1.0)}
+                w = w * (1.0 - t)
+                res = np.maximum(0.0, r - qp)
+                if res.sum() > 0.0:
+                    r = res / res.sum()
                 if not replacement:
-                    qv[x] = 0.0
-            for x in chosen:
-                parents.append(v)
-                toks.append(x)
-                ctx.append(ctx[v] + (x,))
-                nxt.append(len(parents) - 1)
-        level = nxt
-    T = len(parents)
-    z = np.stack([np.log(np.maximum(ztab.p[c], 1e-300)) if c in ztab.p else np.zeros(V) for c in ctx])
-    q = np.stack([tab.q[c] if c in tab.q else np.full(V, 1.0 / V) for c in ctx])
-    us = rng.random(T)
-    path, out, _ = acc.accept_tree_one(z, q, toks, parents, 1.0, lambda s: us[s],
-                                       replacement=replacement, _variant=variant, **adj)
-    # continue with the target's own conditionals if only one token came out
-    if len(out) < 2:
-        out = out + [int(rng.choice(V, p=tab.p[tuple(out)]))]
-    return tuple(out[:2])
+                    qp[x] = 0.0
+                    qp = qp / qp.sum()
+            draw(r, us, w)
+
+        visit(0, {}, 1.0)
+    full = np.zeros((V,) * (depth + 1))
+    for out, w in joint.items():
+        k = len(out)
+        for rest in itertools.product(range(V), repeat=depth + 1 - k):
+            seq = out + rest
+            pr = w
+            for j in range(k, depth + 1):
+                pr *= tab.p[seq[:j]][seq[j]]
+            full[seq] += pr
+    return full
 
 
-def _chi2(counts, exp):
-    """Pearson chi-square with cells of expectation < 5 pooled into one."""
-    counts, exp = counts.ravel(), exp.ravel()
-    big = exp >= 5
-    c = list(counts[big]) + [counts[~big].sum()]
-    e = list(exp[big]) + [exp[~big].sum()]
-    c, e = np.array(c), np.array(e)
-    keep = e > 0
-    return float(((c[keep] - e[keep]) ** 2 / e[keep]).sum()), int(keep.sum() - 1)
+TREE_CASES = [(4, [2, 2], False, 21), (4, [2, 2], True, 21), (5, [3, 1], False, 26)]
 
 
-@pytest.mark.parametrize("replacement", [False, True])
-def test_tree_sampled_output_is_p(replacement):
-    """Sampled tree walk: the joint of the first two emitted tokens matches the
-    target's p(y1) p(y2|y1) within sampling error (chi-square)."""
-    V, branching, N = 4, [2, 2], 40000
-    tab = _Tables(V=V, depth=3, seed=21)
-    rng = np.random.default_rng(22)
-    counts = np.zeros((V, V))
-    for _ in range(N):
-        y = _tree_round_sample(rng, tab, branching, replacement)
-        counts[y] += 1
-    want = np.array([[tab.p[()][a] * tab.p[(a,)][b] for b in range(V)] for a in range(V)])
-    chi2, dof = _chi2(counts, want * N)
-    # P(chi2_15 > 50) ~ 1e-5
-    assert chi2 < 50 + 2.5 * (dof - 15), (chi2, dof)
+@pytest.mark.parametrize("V,branching,replacement,seed", TREE_CASES)
+def test_tree_enumeration_output_is_p(V, branching, replacement, seed):
+    """Sampled tree walk, exact: over every tree the draft can produce with the
+    branching and every cell of the uniforms, the joint of the three tokens
+    the round yields (accepted path and extra token, continued with the
+    target's conditionals) is the target's p(y1) p(y2|y1) p(y3|y1,y2) to
+    1e-12, for children drawn with and without replacement, with two and
+    three siblings per node (CS349E Lecture 6, section 7.1, applied per node;
+    section 10.3 for the tree)."""
+    tab = _Tables(V=V, depth=2, seed=seed)
+    got = _enumerate_tree(tab, branching, replacement)
+    want = _target_joint(tab, 2)
+    assert abs(got.sum() - 1.0) < 1e-12
+    assert np.abs(got - want).max() < 1e-12
 
 
-def test_tree_wrong_variant_detected():
-    """Negative control: resampling from p after rejected siblings is biased and
-    the same statistic sees it."""
-    V, branching, N = 4, [2, 2], 40000
-    tab = _Tables(V=V, depth=3, seed=21)
-    rng = np.random.default_rng(23)
-    counts = np.zeros((V, V))
-    for _ in range(N):
-        counts[_tree_round_sample(rng, tab, branching, False, variant="resample_from_p")] += 1
-    want = np.array([[tab.p[()][a] * tab.p[(a,)][b] for b in range(V)] for a in range(V)])
-    chi2, dof = _chi2(counts, want * N)
-    assert chi2 > 200, (chi2, dof)
+@pytest.mark.parametrize("variant,oracle_replacement", [
+    ("resample_from_p", None), ("no_renorm", None), ("residual", True)])
+@pytest.mark.parametrize("V,branching,seed", [(4, [2, 2], 21), (5, [3, 1], 26)])
+def test_tree_enumeration_wrong_walks_fail(variant, oracle_replacement, V, branching, seed):
+    """Negative controls on the same enumeration: keeping r = p after rejected
+    siblings, removing a rejected child from q' without renormalising, and
+    never updating q' for children drawn without replacement each either put
+    a decision boundary inside a cell of the rule's partition or move the
+    output distribution away from p."""
+    tab = _Tables(V=V, depth=2, seed=seed)
+    try:
+        got = _enumerate_tree(tab, branching, False, variant=variant,
+                              oracle_replacement=oracle_replacement)
+    except _NotConstant:
+        return
+    want = _target_joint(tab, 2)
+    assert 0.5 * np.abs(got - want).sum() > 1e-3
 
 
 def test_tree_greedy_walk():
@@ -586,22 +687,20 @@ def test_chain_enumeration_adjusted_output(temperature, top_k, top_p, adjust_q):
     assert 0.5 * np.abs(got - _target_joint(raw, gamma)).sum() > 1e-2
 
 
-def test_tree_sampled_adjusted_output():
-    """Sampled tree walk with top-k and top-p on both sides: the first two
-    emitted tokens follow the adjusted target (chi-square)."""
-    V, branching, N = 5, [2, 2], 40000
-    raw = _Tables(V=V, depth=3, seed=24)
+def test_tree_enumeration_adjusted_output():
+    """Tree walk with top-k and top-p on both sides, exact: the round's output
+    is the adjusted target (section 7.3), and not the unadjusted one."""
+    V = 5
+    raw = _Tables(V=V, depth=2, seed=24)
     adj = dict(top_k=4, top_p=0.8)
     tab = _Tables(V=V, depth=0, seed=0)
     tab.p = {k: _brute_adjust(v, 1.0, **adj) for k, v in raw.p.items()}
     tab.q = {k: _brute_adjust(v, 1.0, **adj) for k, v in raw.q.items()}
-    rng = np.random.default_rng(25)
-    counts = np.zeros((V, V))
-    for _ in range(N):
-        counts[_tree_round_sample(rng, tab, branching, False, ztab=raw, adj=adj)] += 1
-    want = np.array([[tab.p[()][a] * tab.p[(a,)][b] for b in range(V)] for a in range(V)])
-    chi2, dof = _chi2(counts, want * N)
-    assert chi2 < 50 + 2.5 * (dof - 15), (chi2, dof)
+    got = _enumerate_tree(tab, [2, 1], False, ztab=raw, adj=adj)
+    want = _target_joint(tab, 2)
+    assert abs(got.sum() - 1.0) < 1e-12
+    assert np.abs(got - want).max() < 1e-12
+    assert 0.5 * np.abs(got - _target_joint(raw, 2)).sum() > 1e-2
 
 
 # ----------------------------------------------------------------------------
@@ -647,3 +746,44 @@ def test_accept_ragged_caps_and_packing_agree():
     p1 = acc.softmax(z[1, 0], 1.0)
     x, _ = acc.inverse_cdf(p1, U(1, 0))
     assert cap["n_accepted"][1] == 0 and cap["out_tokens"][1, 0] == x
+
+
+# ----------------------------------------------------------------------------
+# margins of the decisions (they decide which GPU/oracle differences are
+# near-ties), against hand-computed cases
+# ----------------------------------------------------------------------------
+
+def test_top2_margin_hand_cases():
+    # gap between the two largest logits over the largest magnitude
+    assert acc.top2_margin(np.array([1.0, 3.0, 2.0])) == pytest.approx(1.0 / 3.0, abs=1e-15)
+    assert acc.top2_margin(np.array([-4.0, 0.5, 0.25])) == pytest.approx(0.25 / 4.0, abs=1e-15)
+    # a tie at the top has margin 0; a single entry has nothing to flip to
+    assert acc.top2_margin(np.array([2.0, 2.0, -1.0])) == 0.0
+    assert acc.top2_margin(np.array([7.0])) == np.inf
+
+
+def test_inverse_cdf_margin_hand_cases():
+    # r = (0.2, 0.3, 0.5), u = 0.45: cumsum (0.2, 0.5, 1.0), u R = 0.45 falls in
+    # token 1's interval [0.2, 0.5); distance to the nearer edge 0.05
+    x, m = acc.inverse_cdf(np.array([0.2, 0.3, 0.5]), 0.45)
+    assert x == 1 and m == pytest.approx(0.05, abs=1e-15)
+    # unnormalised r = (1, 1, 2), R = 4, u = 0.3: u R = 1.2 in [1, 2) -> token 1,
+    # distances 0.2 and 0.8, margin 0.2 / R = 0.05
+    x, m = acc.inverse_cdf(np.array([1.0, 1.0, 2.0]), 0.3)
+    assert x == 1 and m == pytest.approx(0.05, abs=1e-15)
+    # zero-mass entries are never drawn; u = 0 takes the first positive entry
+    x, m = acc.inverse_cdf(np.array([0.0, 0.0, 3.0, 1.0]), 0.0)
+    assert x == 2 and m == 0.0
+    # the strict test: u R exactly on a boundary goes to the next token
+    x, _ = acc.inverse_cdf(np.array([0.25, 0.25, 0.5]), 0.5)
+    assert x == 2
+
+
+def test_accept_margin_hand_case():
+    # p(x) / q(x) = 0.3 / 0.5 = 0.6, u = 0.65: rejected, margin |0.65 - 0.6|
+    z = np.log(np.array([[0.3, 0.7], [0.5, 0.5]]))
+    q = np.array([[0.5, 0.5]])
+    n, out, m = acc.accept_chain_one(z, q, [1, 0], 1.0, lambda s: 0.65 if s == 0 else 0.1)
+    assert n == 0 and m[0] == pytest.approx(0.05, abs=1e-12)
+    # the residual max(0, p - q) = (0, 0.2) leaves token 1 only
+    assert out == [1]
