@@ -25,10 +25,16 @@
  *     when the handle was created); everything else lives on the host.
  *   - `stream` is a hipStream_t passed as void*.  Work is enqueued on it
  *     asynchronously; outputs are valid once the stream has synchronised.
- *     No call synchronises the host except spec_device_errors.
+ *     No call synchronises the host except spec_verify_init (its one table
+ *     upload), spec_device_errors, spec_profile_read, spec_profile_gemm and
+ *     spec_verify_destroy.
  *   - The caller owns every buffer (weights, KV cache, workspace, inputs,
  *     outputs).  The handle only borrows them; they must outlive it.  The
- *     library never allocates or frees device memory.
+ *     library's kernels use only these buffers: it never calls hipMalloc or
+ *     hipFree.  Recording a new shape's launch sequence as a HIP graph (the
+ *     first step of each shape, see spec_verify_step) is the one place where
+ *     the HIP runtime itself may set up internal state; spec_graph_enable(h,
+ *     0) switches recording off.
  *   - Host-detectable errors return a negative spec_status before anything is
  *     enqueued.  Data errors visible only on the device (token id outside
  *     [0, V), bad tree parent, cache overflow) set bits in a sticky flag word
@@ -164,13 +170,13 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
  *   Launches: a prep kernel, the per-layer kernels, the LM head.  The
  *   per-layer kernels read only weights, cache and workspace, so for each
  *   (B, T, chain or tree) their launch sequence is recorded as a HIP graph on
- *   a private stream of the handle and replayed on `stream`: the first step
- *   of a shape launches them directly (choosing library GEMM algorithms for
- *   64+ rows) and then records them, later steps replay (at most 32 shapes
- *   are kept; the least recently used is dropped).  When `stream` is itself
+ *   a private stream of the handle (recording runs nothing) on the first step
+ *   of a shape and replayed on `stream` from then on (at most 32 shapes are
+ *   kept; the least recently used is dropped, and destroyed once its last
+ *   replay has finished, without waiting for it).  When `stream` is itself
  *   being captured by the caller, or graphs are switched off with
- *   spec_graph_enable, the kernels are launched directly.  The HIP runtime
- *   and the GEMM library may allocate internal memory on a shape's first step.
+ *   spec_graph_enable, the kernels are launched directly.  Every projection
+ *   runs in this library's kernels, whatever the row count.
  *   Errors: INVALID_ARG, CAPACITY (B > max_batch, T > max_rows_per_seq,
  *   T < 1), STATE (a paged cache without a block table), DEVICE.
  *   Flags: TOKEN_RANGE, TREE, KV_OVERFLOW, LAYOUT (a paged table entry
@@ -310,8 +316,19 @@ spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int
  * Errors: INVALID_ARG (null handle). */
 spec_status spec_graph_enable(spec_handle* h, int32_t enable);
 
+/* Measurement hook: the tile shape the tiled GEMMs (5 or more rows) use, for
+ * A/B timing and for parity tests of both paths.  route 0: automatic (128-row
+ * x 256-weight-row tiles from 64 rows on, 32-row tiles below); 1: the 32-row
+ * tiles at every row count; 2: the large tiles at every row count the tiled
+ * kernels serve.  Process-wide; results are within the same fp32 tolerance
+ * either way (the sums are taken in a different order).  Takes effect for
+ * launch sequences recorded afterwards (switch graphs off, or use a new
+ * handle, to apply it to shapes already recorded).
+ * Errors: INVALID_ARG (route outside 0..2). */
+spec_status spec_gemm_route(int32_t route);
+
 /* Release the handle: host memory, events, recorded graphs and the private
- * recording stream (waits for the device first when graphs exist). */
+ * recording stream (waits for recorded replays still running). */
 void spec_verify_destroy(spec_handle* h);
 
 /* Static string for a status code. */

@@ -35,7 +35,8 @@ SPEC_FLAG_LAYOUT = 8
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_profile_gemm", "spec_graph_enable", "spec_set_block_table", "spec_verify_destroy", "spec_status_str",
+    "spec_profile_gemm", "spec_graph_enable", "spec_gemm_route", "spec_set_block_table", "spec_verify_destroy",
+    "spec_status_str",
     "spec_recurrent_verify", "spec_recurrent_commit", "spec_recurrent_commit_verify",
 ]
 
@@ -110,6 +111,8 @@ def lib():
     L.spec_profile_gemm.restype = i32
     L.spec_graph_enable.argtypes = [vp, i32]
     L.spec_graph_enable.restype = i32
+    L.spec_gemm_route.argtypes = [i32]
+    L.spec_gemm_route.restype = i32
     L.spec_set_block_table.argtypes = [vp, vp, i32]
     L.spec_set_block_table.restype = i32
     L.spec_verify_destroy.argtypes = [vp]
@@ -260,6 +263,10 @@ def spec_set_block_table(h, table, pages_per_seq: int):
 
 def spec_graph_enable(h, enable: bool):
     _check("spec_graph_enable", lib().spec_graph_enable(h, 1 if enable else 0))
+
+
+def spec_gemm_route(route: int):
+    _check("spec_gemm_route", lib().spec_gemm_route(int(route)))
 
 
 def spec_verify_destroy(h):

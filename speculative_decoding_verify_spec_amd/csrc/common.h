@@ -50,6 +50,15 @@ DEVI floatx4 mfma16x16x32(shortx8 a, shortx8 b, floatx4 c) {
                                                  0, 0);
 }
 
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16): lane l holds
+// A[l%32][8(l/32) + e], B[8(l/32) + e][l%32] (e = 0..7) and D[8(i/4) +
+// 4(l/32) + i%4][l%32] (i = 0..15).
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+DEVI floatx16 mfma32x32x16(shortx8 a, shortx8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
 // --- wave reductions ------------------------------------------------------
 DEVI float wave_sum(float v) {
 #pragma unroll

@@ -669,7 +669,7 @@ __global__ __launch_bounds__(64 * STREAM_WAVES) void gemm_stream_kernel(GemmPara
 }
 
 // ---------------------------------------------------------------- launch
-static int device_cus() {
+int device_cus() {
   static int ncu = 0;
   if (!ncu) {
     int dev = 0;
@@ -717,7 +717,7 @@ bool gemm_use_split(const GemmParams& p) {
 
 bool gemm_takes_xpart(const GemmParams& p) {
   // the k-stationary kernel with a fused norm, one launch of at most 4 rows
-  return p.epi == EPI_QKV && p.norm_g && p.M >= 1 && p.M <= 4 && !gemm_tiled_ok(p) && !gemm_blas_ok(p) &&
+  return p.epi == EPI_QKV && p.norm_g && p.M >= 1 && p.M <= 4 && !gemm_tiled_ok(p) &&
          !gemm_use_mfma(p, p.M) && gemm_is_kstat(p.K) && p.K % 512 == 0;
 }
 

@@ -43,7 +43,8 @@ constexpr int TK = 64;       // k per stage
 constexpr int NPAIR = 32;    // pairs per tile
 constexpr int WROWS = 2 * NPAIR;
 
-template <int EPI>
+// Output pairs of a tile of NP pairs (2 NP weight rows); see the header.
+template <int EPI, int NP>
 DEVI int pair_rows(const GemmParams& p, int j, int& rb) {
   if (EPI == EPI_SWIGLU) {
     rb = p.F + j;
@@ -55,23 +56,23 @@ DEVI int pair_rows(const GemmParams& p, int j, int& rb) {
     rb = a + half;
     return a;
   }
-  const int a = (j / NPAIR) * WROWS + (j % NPAIR);
-  rb = a + NPAIR;
+  const int a = (j / NP) * (2 * NP) + (j % NP);
+  rb = a + NP;
   return a;
 }
 
-template <int EPI>
+template <int EPI, int NP>
 __host__ __device__ int pair_count(const GemmParams& p) {
   if (EPI == EPI_SWIGLU) return p.F;
   if (EPI == EPI_QKV) return p.N / 2;
-  return ((p.N + WROWS - 1) / WROWS) * NPAIR;
+  return ((p.N + 2 * NP - 1) / (2 * NP)) * NP;
 }
 
 // Epilogue of one (row m, pair j) with its two finished sums.
-template <int EPI>
+template <int EPI, int NP>
 DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
   int rb;
-  const int ra = pair_rows<EPI>(p, j, rb);
+  const int ra = pair_rows<EPI, NP>(p, j, rb);
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
     float* o = p.out + (size_t)m * p.ldo;
     if (EPI == EPI_STORE) {
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int p0 = blockIdx.x * NPAIR;
   const int m0 = blockIdx.y * BM;
-  const int npairs = pair_count<EPI>(p);
+  const int npairs = pair_count<EPI, NPAIR>(p);
   const int kext = SPLIT ? p.K / (int)gridDim.z : p.K;
   const int kbeg = SPLIT ? (int)blockIdx.z * kext : 0;
   const int nst = kext / TK;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
     if (r < WROWS) {
       const int j = p0 + (r % NPAIR);
       int rb;
-      const int ra = pair_rows<EPI>(p, j < npairs ? j : 0, rb);
+      const int ra = pair_rows<EPI, NPAIR>(p, j < npairs ? j : 0, rb);
       int row = r < NPAIR ? ra : rb;
       row = (j < npairs && row < p.N) ? row : 0;
       src[i] = (const uint16_t*)p.W + (size_t)row * p.K + kbeg + 8 * q;
@@ -377,16 +378,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(GemmParams p) {
             a *= f;
             b *= f;
           }
-          epilogue_pair<EPI>(p, m, j, a, b);
+          epilogue_pair<EPI, NPAIR>(p, m, j, a, b);
         }
       }
   }
 }
 
 // out = epilogue(sum over the K slices, in slice order)
-template <int EPI, bool NORM>
+template <int EPI, bool NORM, int NP>
 __global__ __launch_bounds__(256) void gemm_tiled_finish_kernel(GemmParams p, int nsplit) {
-  const int npairs = pair_count<EPI>(p);
+  const int npairs = pair_count<EPI, NP>(p);
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (size_t)p.M * npairs) return;
   const int m = (int)(e / npairs), j = (int)(e % npairs);
@@ -401,52 +402,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_finish_kernel(GemmParams p, in
     a *= f;
     b *= f;
   }
-  epilogue_pair<EPI>(p, m, j, a, b);
-}
-
-// Finish of a library GEMM over the stacked planes: d [2M][ldd] holds the
-// products of the hi rows (0 .. M-1) and of the lo rows (M .. 2M-1) with
-// every weight row.  Adds the two, applies the RMSNorm row factor and the
-// epilogue.  One thread per (row, pair).
-template <int EPI, bool NORM>
-__global__ __launch_bounds__(256) void gemm_blas_finish_kernel(GemmParams p, const float* d, int ldd) {
-  const int npairs = pair_count<EPI>(p);
-  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (size_t)p.M * npairs) return;
-  const int m = (int)(e / npairs), j = (int)(e % npairs);
-  int rb;
-  const int ra = pair_rows<EPI>(p, j, rb);
-  const float* hi = d + (size_t)m * ldd;
-  const float* lo = d + (size_t)(p.M + m) * ldd;
-  float a = ra < ldd ? hi[ra] + lo[ra] : 0.f;
-  float b = rb < ldd ? hi[rb] + lo[rb] : 0.f;
-  if (NORM) {
-    const float f = row_factor(p, m);
-    a *= f;
-    b *= f;
-  }
-  epilogue_pair<EPI>(p, m, j, a, b);
-}
-
-template <int EPI>
-static hipError_t launch_blas_finish_epi(const GemmParams& p, const float* d, int ldd, hipStream_t s) {
-  const size_t n = (size_t)p.M * pair_count<EPI>(p);
-  const int blocks = (int)((n + 255) / 256);
-  if (p.norm_g) gemm_blas_finish_kernel<EPI, true><<<blocks, 256, 0, s>>>(p, d, ldd);
-  else gemm_blas_finish_kernel<EPI, false><<<blocks, 256, 0, s>>>(p, d, ldd);
-  return hipGetLastError();
+  epilogue_pair<EPI, NP>(p, m, j, a, b);
 }
 
 template <int MB, int KW, int EPI>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   constexpr int R = 3;
   constexpr int BM = 32 * MB;
-  const int tiles_n = (pair_count<EPI>(p) + NPAIR - 1) / NPAIR;
+  const int tiles_n = (pair_count<EPI, NPAIR>(p) + NPAIR - 1) / NPAIR;
   const int tiles_m = (p.M + BM - 1) / BM;
   // split K while the tiles would not fill the chip, if scratch allows
   int nsplit = 1;
   while (p.part && tiles_n * tiles_m * nsplit < 384 && nsplit < 8 && (p.K / (2 * nsplit)) % TK == 0 &&
-         (size_t)2 * nsplit * p.M * pair_count<EPI>(p) * 2 <= p.part_floats)
+         (size_t)2 * nsplit * p.M * pair_count<EPI, NPAIR>(p) * 2 <= p.part_floats)
     nsplit *= 2;
   const bool norm = p.norm_g != nullptr;
   launch_split_x(p, s);
@@ -457,10 +425,307 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   gemm_tiled_kernel<MB, KW, R, EPI, false, true><<<grid, 256, 0, s>>>(p);
-  const size_t n = (size_t)p.M * pair_count<EPI>(p);
+  const size_t n = (size_t)p.M * pair_count<EPI, NPAIR>(p);
   const int blocks = (int)((n + 255) / 256);
-  if (norm) gemm_tiled_finish_kernel<EPI, true><<<blocks, 256, 0, s>>>(p, nsplit);
-  else gemm_tiled_finish_kernel<EPI, false><<<blocks, 256, 0, s>>>(p, nsplit);
+  if (norm) gemm_tiled_finish_kernel<EPI, true, NPAIR><<<blocks, 256, 0, s>>>(p, nsplit);
+  else gemm_tiled_finish_kernel<EPI, false, NPAIR><<<blocks, 256, 0, s>>>(p, nsplit);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- large tiles
+// Many rows (64 or more: the windows of 16+ sequences, token trees, long
+// verify windows of a batch): the contraction is dense enough that the
+// matrix cores and the LDS, not the weight stream, bound it.  A workgroup of
+// 4 waves owns BIG_BM = 128 activation rows and BIG_NP = 128 pairs (256
+// weight rows); the waves form a 2 x 2 grid of 64 rows x 64 pairs.  Per 16-k
+// step a wave reads 2 + 2 activation fragments (hi, lo) and 4 weight
+// fragments (a and b rows) from LDS and issues 16 32x32x16 products: 512
+// bytes of LDS per 32k flops, half of what the 32-row tiles need, so the LDS
+// read rate stays near 64 B per clock per CU at the matrix-core peak.
+//
+// Stages of 64 k (512 LDS rows of 128 bytes: 256 weight rows, then 128 hi
+// and 128 lo activation rows) are requested two stages ahead into a ring of
+// two register sets (16 chunks of 16 bytes per thread) and written to one of
+// two LDS buffers (128 KB).  The main loop is unrolled by two and
+// branch-free, so every wait names exactly the loads it needs.
+//
+// LDS rows are swizzled so that the 16 rows of one operand read hit distinct
+// banks in groups of 8 lanes (32 banks) and of 16 lanes (64 banks): chunk c
+// of row r sits in slot c ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1).
+//
+// Tiles are numbered so that the hardware's round-robin dispatch over the 8
+// XCDs gives each XCD a contiguous run of them, row tiles fastest: the row
+// tiles of one weight tile run side by side on one XCD and share its weight
+// stream through that XCD's L2.  Launches with fewer tiles than CUs split K
+// into S slices of whole stages; the slices write raw partial sums that
+// gemm_tiled_finish_kernel adds in slice order before the epilogue.
+constexpr int BIG_BM = 128;
+constexpr int BIG_NP = 128;
+constexpr int BIG_WR = 2 * BIG_NP;
+constexpr int BIG_ROWS = BIG_WR + 2 * BIG_BM;  // LDS rows per stage
+constexpr int BIG_CH = BIG_ROWS * 8 / 256;     // 16-byte chunks per thread per stage
+constexpr int BIG_STAGE = BIG_ROWS * 64;       // bf16 elements per LDS stage
+
+DEVI int big_g(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Instruction classes of the scheduler's group barriers, and 8 pairs of
+// products each followed by one instruction of class A and one of class B.
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+template <int A, int B>
+DEVI void sched_pairs8() {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(A, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if constexpr (B != 0) __builtin_amdgcn_sched_group_barrier(B, 1, 0);
+  }
+}
+
+// Buffer resource word 3 of the gfx9 family (raw buffer, 32-bit data format).
+constexpr int BUF_WORD3 = 0x00020000;
+
+template <int EPI, bool NORM, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tiles_m, int nsplit, int ntiles) {
+  // the two stage buffers are separate arrays, so the compiler can tell the
+  // next stage's LDS writes from this stage's reads and interleave them
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[BIG_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[BIG_STAGE];
+  // ---- tile of this workgroup: each XCD takes a contiguous run
+  const int per = (int)gridDim.x / 8;
+  const int tl = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (tl >= ntiles) return;
+  const int mt = tl % tiles_m;
+  const int z = (tl / tiles_m) % nsplit;
+  const int nt = tl / (tiles_m * nsplit);
+  const int p0 = nt * BIG_NP;
+  const int m0 = mt * BIG_BM;
+  const int npairs = pair_count<EPI, BIG_NP>(p);
+  const int nst_all = p.K / TK;
+  const int sbeg = (int)((long long)nst_all * z / nsplit);
+  const int nst = (int)((long long)nst_all * (z + 1) / nsplit) - sbeg;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wp = w >> 1;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // ---- the thread's chunks: stage row r = tid/8 + 32 i, chunk q = tid % 8;
+  // byte offsets of the chunk's first k from the weight base (i < 8) or the
+  // activation planes' base (i >= 8).  32-bit byte offsets let every load
+  // take a scalar base plus a vector offset (weights up to 4 GB).
+  uint32_t off[BIG_CH];
+  const int q = tid & 7;
+#pragma unroll
+  for (int i = 0; i < BIG_CH; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    if (r < BIG_WR) {
+      const int jl = r % BIG_NP;
+      const int j = p0 + jl;
+      int rb;
+      const int ra = pair_rows<EPI, BIG_NP>(p, j < npairs ? j : 0, rb);
+      int row = r < BIG_NP ? ra : rb;
+      row = (j < npairs && row < p.N) ? row : 0;  // rows past the matrix load row 0, never stored
+      off[i] = ((uint32_t)row * (uint32_t)p.K + 8 * q) * 2u;
+    } else {
+      const int rx = r - BIG_WR;
+      const int plane = rx / BIG_BM, ml = rx % BIG_BM;
+      const int m = (m0 + ml < p.M) ? m0 + ml : p.M - 1;  // rows past M: any valid row, never stored
+      off[i] = (((uint32_t)plane * (uint32_t)p.M + (uint32_t)m) * (uint32_t)p.K + 8 * q) * 2u;
+    }
+  }
+  // LDS byte offset of the thread's chunk 0; chunk i is 4096 i further
+  // (g depends on r & 15 only, which is the same for every i)
+  const int r0 = tid >> 3;
+  const int dst0 = r0 * 128 + 16 * (q ^ big_g(r0));
+  // buffer resources over the weight matrix and the two planes: a load is
+  // base + (vector byte offset) + (scalar stage offset), and one outside the
+  // resource's byte range returns zeros instead of faulting
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.W, (short)0, (int)((size_t)p.N * p.K * 2 < 0x7fffffffu ? (size_t)p.N * p.K * 2 : 0x7fffffffu),
+      BUF_WORD3);
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)((size_t)2 * p.M * p.K * 2), BUF_WORD3);
+
+  u32x4 ring[2][BIG_CH];
+  auto fetch = [&](int st, auto sl) {
+    constexpr int S = decltype(sl)::value;
+    const int so = (sbeg + st) * TK * 2;
+#pragma unroll
+    for (int i = 0; i < BIG_CH; ++i) {
+      // plain loads: a weight tile is read by the row tiles running beside it
+      // on the same XCD (a non-temporal hint measured 5-15% slower), the
+      // activation planes by every weight tile
+      if (i < BIG_WR / 32) ring[S][i] = __builtin_amdgcn_raw_buffer_load_b128(wres, off[i], so, 0);
+      else ring[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xres, off[i], so, 0);
+    }
+  };
+  auto buf = [&](auto bf) -> char* {
+    if constexpr (decltype(bf)::value == 0) return (char*)s_b0;
+    else return (char*)s_b1;
+  };
+  auto put = [&](auto sl, auto bf) {
+    constexpr int S = decltype(sl)::value;
+    char* lds = buf(bf);
+#pragma unroll
+    for (int i = 0; i < BIG_CH; ++i) *(u32x4*)(lds + dst0 + 4096 * i) = ring[S][i];
+  };
+
+  // 32x32x16 products: lane l holds operand row (or pair) l % 32 at k
+  // 8 (l / 32) + e of each 16-k sub-step, and result column l % 32 at rows
+  // 8 (i / 4) + 4 (l / 32) + i % 4.  Eight accumulators of 16 floats (rather
+  // than 32 of 4) let the compiler keep every accumulator in place across
+  // the loop.
+  floatx16 acc[2][2][2];  // [row tile of 32][pair block of 32][a, b]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b][0] = acc[a][b][1] = floatx16{};
+
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int gl = big_g(l32);
+  auto mult = [&](auto bf) {
+    const char* base = buf(bf) + l32 * 128;
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+      const char* cb = base + 16 * ((2 * ss + lh) ^ gl);
+      shortx8 ah[2], al[2], ba[2], bb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        ah[t] = *(const shortx8*)(cb + (BIG_WR + 64 * wm + 32 * t) * 128);
+        al[t] = *(const shortx8*)(cb + (BIG_WR + BIG_BM + 64 * wm + 32 * t) * 128);
+        ba[t] = *(const shortx8*)(cb + (64 * wp + 32 * t) * 128);
+        bb[t] = *(const shortx8*)(cb + (BIG_NP + 64 * wp + 32 * t) * 128);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[t][u][0] = mfma32x32x16(ah[t], ba[u], acc[t][u][0]);
+          acc[t][u][1] = mfma32x32x16(ah[t], bb[u], acc[t][u][1]);
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[t][u][0] = mfma32x32x16(al[t], ba[u], acc[t][u][0]);
+          acc[t][u][1] = mfma32x32x16(al[t], bb[u], acc[t][u][1]);
+        }
+    }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  // step st: request stage st + 2 into the ring slot stage st came from,
+  // multiply stage st (LDS buffer st % 2), write stage st + 1 from its ring
+  // slot to the other buffer.  A request past the last stage re-reads it and
+  // a write past it fills a buffer nobody reads, so the steps are branch-free.
+  //
+  // With one wave per SIMD the matrix core idles whenever the wave issues
+  // anything else between two products, so the step's 64 other instructions
+  // (32 operand reads, 16 requests, 16 LDS writes) are placed one after each
+  // product: the reads of sub-step s + 1 during sub-step s, the requests in
+  // the first two sub-steps, the LDS writes (which wait for the requests of
+  // the step before) in the last two.
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);  // operand reads of sub-step 0
+    sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 0: reads of 1, requests
+    sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 1: reads of 2, requests
+    sched_pairs8<SG_DS_READ, SG_DS_WRITE>();    // sub-step 2: reads of 3, LDS writes
+    sched_pairs8<SG_DS_WRITE, 0>();             // sub-step 3: LDS writes
+  };
+  auto step = [&](int st, auto sl, auto sl1) {
+    fetch(min(st + 2, nst - 1), sl);
+    mult(sl);
+    put(sl1, sl1);
+    interleave();
+    lds_barrier();  // orders LDS only: the ring's loads stay in flight
+  };
+  fetch(0, C0{});
+  fetch(min(1, nst - 1), C1{});
+  put(C0{}, C0{});
+  lds_barrier();
+  int st = 0;
+  for (; st + 2 <= nst; st += 2) {
+    step(st, C0{}, C1{});
+    step(st + 1, C1{}, C0{});
+  }
+  if (st < nst) step(st, C0{}, C1{});
+
+  // ---- epilogue: lane l holds pair l % 32 of each pair block, rows
+  // 8 (i / 4) + 4 (l / 32) + i % 4 of each row tile
+  float fac[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + 64 * wm + 32 * t + 8 * (i >> 2) + 4 * lh + (i & 3);
+      fac[t][i] = (NORM && !SPLIT && m < p.M) ? row_factor(p, m) : 1.0f;
+    }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = p0 + 64 * wp + 32 * u + l32;
+    if (j >= npairs) continue;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + 64 * wm + 32 * t + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (m >= p.M) continue;
+        const float a = acc[t][u][0][i], b = acc[t][u][1][i];
+        if constexpr (SPLIT) {
+          float* dst = p.part + (((size_t)z * p.M + m) * npairs + j) * 2;
+          *(float2*)dst = make_float2(a, b);
+        } else {
+          epilogue_pair<EPI, BIG_NP>(p, m, j, a * fac[t][i], b * fac[t][i]);
+        }
+      }
+  }
+}
+
+// K slices for a launch of `tiles` output tiles over `nst` stages.  Time of
+// the slowest CU: rounds of resident workgroups x stages per slice x the time
+// of a stage (~1.7 us: 8.4 MFLOP per tile stage at about half the CU's
+// matrix-core peak), plus, for S > 1, writing and re-reading the partial sums
+// (S x per_split_floats x 4 bytes each way, at ~5 TB/s).  Limited by the
+// scratch.
+int big_splits(int tiles, int nst, int cus, size_t per_split_floats, size_t part_floats) {
+  int best = 1;
+  double best_us = 1e300;
+  for (int S = 1; S <= 8 && S <= nst; ++S) {
+    if (S > 1 && (size_t)S * per_split_floats > part_floats) break;
+    const double rounds = (double)((tiles * S + cus - 1) / cus);
+    double us = rounds * ((nst + S - 1) / S) * 1.7;
+    if (S > 1) us += 2.0 * S * (double)per_split_floats * 4.0 / 5.0e6;
+    if (us < best_us - 1e-9) {
+      best_us = us;
+      best = S;
+    }
+  }
+  return best;
+}
+
+template <int EPI>
+hipError_t launch_big(const GemmParams& p, hipStream_t s) {
+  const int npairs = pair_count<EPI, BIG_NP>(p);
+  const int tiles_n = (npairs + BIG_NP - 1) / BIG_NP;
+  const int tiles_m = (p.M + BIG_BM - 1) / BIG_BM;
+  const int nsplit = p.part ? big_splits(tiles_n * tiles_m, p.K / TK, device_cus(), (size_t)p.M * npairs * 2,
+                                         p.part_floats)
+                            : 1;
+  const int ntiles = tiles_n * tiles_m * nsplit;
+  const int grid = ((ntiles + 7) / 8) * 8;
+  const bool norm = p.norm_g != nullptr;
+  launch_split_x(p, s);
+  if (nsplit == 1) {
+    if (norm) gemm_big_kernel<EPI, true, false><<<grid, 256, 0, s>>>(p, tiles_m, 1, ntiles);
+    else gemm_big_kernel<EPI, false, false><<<grid, 256, 0, s>>>(p, tiles_m, 1, ntiles);
+    return hipGetLastError();
+  }
+  gemm_big_kernel<EPI, false, true><<<grid, 256, 0, s>>>(p, tiles_m, nsplit, ntiles);
+  const size_t n = (size_t)p.M * npairs;
+  const int blocks = (int)((n + 255) / 256);
+  if (norm) gemm_tiled_finish_kernel<EPI, true, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
+  else gemm_tiled_finish_kernel<EPI, false, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
   return hipGetLastError();
 }
 
@@ -469,6 +734,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 // 128 rows).
 template <int EPI>
 hipError_t launch_epi(const GemmParams& p, hipStream_t s) {
+  if (gemm_big_rows(p)) return launch_big<EPI>(p, s);
   if (p.M <= 32) return launch_cfg<1, 2, EPI>(p, s);
   if (p.M <= 64) return launch_cfg<2, 1, EPI>(p, s);
   return launch_cfg<4, 1, EPI>(p, s);
@@ -487,20 +753,23 @@ hipError_t launch_split_x(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_blas_finish(const GemmParams& p, const float* d, int ldd, hipStream_t s) {
-  switch (p.epi) {
-    case EPI_STORE: return launch_blas_finish_epi<EPI_STORE>(p, d, ldd, s);
-    case EPI_RESID: return launch_blas_finish_epi<EPI_RESID>(p, d, ldd, s);
-    case EPI_SWIGLU: return launch_blas_finish_epi<EPI_SWIGLU>(p, d, ldd, s);
-    default: return launch_blas_finish_epi<EPI_QKV>(p, d, ldd, s);
-  }
+size_t gemm_big_part_floats(int M, size_t npairs, int K, int cus) {
+  const int tiles = (int)((npairs + BIG_NP - 1) / BIG_NP) * ((M + BIG_BM - 1) / BIG_BM);
+  const int S = big_splits(tiles, K / TK, cus, (size_t)M * npairs * 2, ~(size_t)0);
+  return S > 1 ? (size_t)S * M * npairs * 2 : 0;
 }
 
-// Between 64 and 128 rows the library GEMM wins on the 4096-deep
-// projections, but the tiled kernel wins on the 14336-deep down projection
-// (128 rows: 69 against 80 us per layer), where the library's product
-// scratch and finish pass cost the most.
-bool gemm_tiled_preferred(const GemmParams& p) { return p.K > 8192 && p.M <= 128 && gemm_tiled_ok(p); }
+// Which tiles serve an M-row launch: the large tiles from 64 rows on, unless
+// a measurement override is set (gemm_route: 1 = 32-row tiles, 2 = large
+// tiles wherever the tiled kernels run).
+int gemm_route = 0;
+bool gemm_big_rows(const GemmParams& p) {
+  // buffer offsets are 32-bit: the weight matrix and the planes stay below 2 GB
+  if ((size_t)p.N * p.K * 2 >= 0x7fffffffu || (size_t)4 * p.M * p.K >= 0x7fffffffu) return false;
+  if (gemm_route == 1) return false;
+  if (gemm_route == 2) return true;
+  return p.M >= 64;
+}
 
 bool gemm_tiled_ok(const GemmParams& p) {
   if (p.wdtype != 1 || p.K % TK || p.K > SSQ_BLK * 1024 || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;

@@ -73,8 +73,6 @@ struct GemmParams {
   float* xs_ssq;          // [M][SSQ_BLK] partial sums of squares per 1024 k
   // QKV epilogue, ragged rows: sequence of each global row (null: row / T)
   const int32_t* seq;
-  // many rows: the library GEMM path (null: not available)
-  struct BlasCtx* blas;
   KvMap kvm;                // cache addressing of the QKV epilogue's writes
   // Activation rows still owed the K-slice partial sums of a split residual
   // GEMM whose reduce was deferred: with xpart set, row m is taken as
@@ -98,24 +96,20 @@ bool gemm_use_split(const GemmParams& p);
 bool gemm_takes_xpart(const GemmParams& p);
 // the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
 bool gemm_tiled_ok(const GemmParams& p);
-// the tiled kernel beats the library GEMM on this launch (deep K, few rows)
-bool gemm_tiled_preferred(const GemmParams& p);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);
-// the activation planes of the tiled kernel ([2][M][K] in p.xs, row sums of
-// squares in p.xs_ssq), and the finish of a library GEMM over them
+// the large-tile kernel serves this launch (64 or more rows, or the override)
+bool gemm_big_rows(const GemmParams& p);
+// measurement override of the tile choice: 0 automatic, 1 the 32-row tiles,
+// 2 the large tiles (set through spec_gemm_route)
+extern int gemm_route;
+// the activation planes of the tiled kernels ([2][M][K] in p.xs, row sums of
+// squares in p.xs_ssq)
 hipError_t launch_split_x(const GemmParams& p, hipStream_t s);
-hipError_t launch_blas_finish(const GemmParams& p, const float* d, int ldd, hipStream_t s);
-// Many-row GEMMs through hipBLASLt (gemm_blas.hip): one plain bf16 GEMM of
-// the stacked hi / lo activation planes against the weights into fp32
-// scratch, then the finish kernel.  blas_create borrows the library's
-// workspace and the fp32 scratch; algorithms are chosen per shape on first
-// use, by timing when `tune` is set (never while the stream is recording).
-struct BlasCtx;
-BlasCtx* blas_create(void* ws, size_t ws_bytes, float* d, size_t d_floats);
-void blas_destroy(BlasCtx* ctx);
-bool gemm_blas_ok(const GemmParams& p);
-bool blas_ready(const BlasCtx* c);  // the library handle exists (created by a tuning call)
-hipError_t launch_gemm_blas(const GemmParams& p, hipStream_t s, bool tune);
+// compute units of the current device
+int device_cus();
+// split-K scratch (floats) the large-tile kernel asks for at M rows of
+// npairs output pairs over K, on a device of `cus` CUs (0: no split)
+size_t gemm_big_part_floats(int M, size_t npairs, int K, int cus);
 
 // ---------------------------------------------------------------- attention
 struct AttnParams {

@@ -67,13 +67,25 @@ int attn_splits(const spec_config& c, int B, int T) {
   return std::max(1, std::min(s, 127));
 }
 
-// Split-K scratch of the GEMMs: the skinny residual GEMM's [4][8][d] and the
-// tiled GEMM's [S <= 8][M <= 64][pairs][2] partial sums (the tiled kernel
-// splits only launches of at most 64 rows, and only while they fit).
+// Split-K scratch of the GEMMs: the skinny residual GEMM's [2][8][d], the
+// 32-row tiled kernel's [S <= 8][M <= 64][pairs][2] partial sums (it splits
+// only launches of at most 64 rows, and only while they fit) and the
+// large-tile kernel's [S][M][pairs][2] for the slices it would choose on a
+// 256-CU device at every row count from 64 to the largest.
 size_t gemm_part_floats(const spec_config& c) {
   const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
-  const size_t pairs = std::max<size_t>((size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim / 2, c.d_model);
-  return std::max((size_t)GEMM_KSPLIT * 8 * c.d_model, 8 * std::min<size_t>(Mmax, 64) * pairs * 2);
+  const size_t qkv_pairs = (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim / 2;
+  const size_t pairs = std::max<size_t>(qkv_pairs, c.d_model);
+  size_t need = std::max((size_t)GEMM_KSPLIT * 8 * c.d_model, 8 * std::min<size_t>(Mmax, 64) * pairs * 2);
+  if (c.weight_dtype == SPEC_DTYPE_BF16) {
+    const int d = c.d_model, F = c.d_ffn, HD = c.n_heads * c.head_dim;
+    auto tile_pairs = [](int n) { return (size_t)((n + 255) / 256) * 128; };
+    const size_t np[5] = {qkv_pairs, tile_pairs(d), (size_t)F, tile_pairs(d), tile_pairs(c.vocab)};
+    const int K[5] = {d, HD, d, F, d};
+    for (size_t M = 64; M <= Mmax; ++M)
+      for (int g = 0; g < 5; ++g) need = std::max(need, gemm_big_part_floats((int)M, np[g], K[g], 256));
+  }
+  return need;
 }
 
 // bf16 hi/lo planes of the widest activation rows the tiled GEMM splits
@@ -81,20 +93,6 @@ size_t gemm_xs_elems(const spec_config& c) {
   const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
   const size_t K = std::max<size_t>(std::max<size_t>(c.d_model, c.d_ffn), (size_t)c.n_heads * c.head_dim);
   return Mmax >= 5 ? 2 * Mmax * K : 0;
-}
-
-// The library GEMM path for 64 or more rows: its workspace and the fp32
-// product scratch [2 rows][weight rows] for up to 256 rows per launch.
-size_t blas_ws_bytes(const spec_config& c) {
-  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
-  return (Mmax >= 64 && c.weight_dtype == SPEC_DTYPE_BF16) ? ((size_t)64 << 20) : 0;
-}
-size_t blas_d_floats(const spec_config& c) {
-  if (!blas_ws_bytes(c)) return 0;
-  const size_t Mmax = (size_t)c.max_batch * c.max_rows_per_seq;
-  const size_t nw = std::max<size_t>(std::max<size_t>(2 * (size_t)c.d_ffn, (size_t)c.vocab),
-                                     (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim);
-  return 2 * std::min<size_t>(Mmax, 256) * nw;
 }
 
 // Shape of one forward: B sequences, T rows each (ragged: at most T, M rows
@@ -109,7 +107,7 @@ struct StepShape {
 
 struct Layout {
   size_t x, x2, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, gbws, gbd, rowstat, rowms, rsum, nacc, rbuf, tpath, fcnt, fmass, fstate, fres,
+  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, tpath, fcnt, fmass, fstate, fres,
       flags, total;
 };
 
@@ -152,8 +150,6 @@ Layout plan(const spec_config& c) {
   L.gpart = take(gemm_part_floats(c) * 4);
   L.gxs = take(gemm_xs_elems(c) * 2);
   L.gssq = take(Mmax * SSQ_BLK * 4);
-  L.gbws = take(blas_ws_bytes(c));
-  L.gbd = take(blas_d_floats(c) * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
@@ -200,14 +196,14 @@ struct spec_handle {
     StepShape sh;
     hipGraphExec_t exec;
     uint64_t used;
+    hipEvent_t done;  // recorded after each replay; null for a shape on direct launches
   };
   bool graphs = true;
-  bool recording = false;     // launches are being recorded: no library tuning
   const int32_t* kv_table = nullptr;  // paged cache: [max_batch][kv_ppseq] page ids
   int kv_ppseq = 0;
-  BlasCtx* blas = nullptr;    // library GEMMs for 64 or more rows
   hipStream_t cap = nullptr;  // private stream used only to record
   std::vector<Graph> gcache;
+  std::vector<Graph> retired;  // evicted recordings whose last replay may still run
   uint64_t gclock = 0;
   int64_t launches[K_N] = {};
   double ms[K_N] = {};
@@ -262,7 +258,6 @@ void gemm_scratch(const spec_handle* h, GemmParams& p) {
   p.xs = h->at<uint16_t>(h->lay.gxs);
   p.xs_elems = gemm_xs_elems(h->cfg);
   p.xs_ssq = h->at<float>(h->lay.gssq);
-  p.blas = h->blas;
 }
 
 hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
@@ -274,14 +269,6 @@ hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s
   {
     GemmParams q = p;
     q.M = M;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    const bool tune = !h->recording && hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
-    if (gemm_blas_ok(q) && !gemm_tiled_preferred(q) && (tune || blas_ready(h->blas))) {
-      // many rows: one library GEMM of the stacked activation planes
-      const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
-                           (double)M * out_cols * 4 * (p.epi == EPI_RESID ? 2 : 1);
-      return timed(h, cls, bytes, s, [&] { return launch_gemm_blas(q, s, tune); });
-    }
     if (gemm_tiled_ok(q)) {
       // many rows: one tiled launch reads the weights once per 128 rows
       const double bytes = (double)nrows * p.K * wbytes + (double)M * p.K * 4 +
@@ -419,15 +406,36 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   return hipSuccess;
 }
 
+// Recordings that left the cache are destroyed once their last replay has
+// finished (its event has completed), never by waiting for it.
+void destroy_graph(spec_handle::Graph& g) {
+  if (g.exec) hipGraphExecDestroy(g.exec);
+  if (g.done) hipEventDestroy(g.done);
+  g.exec = nullptr;
+  g.done = nullptr;
+}
+void sweep_retired(spec_handle* h, bool wait) {
+  for (size_t i = 0; i < h->retired.size();) {
+    spec_handle::Graph& g = h->retired[i];
+    const bool finished = !g.done || (wait ? hipEventSynchronize(g.done) == hipSuccess
+                                           : hipEventQuery(g.done) == hipSuccess);
+    if (!finished && !wait) {
+      ++i;
+      continue;
+    }
+    destroy_graph(g);
+    h->retired.erase(h->retired.begin() + i);
+  }
+}
+void retire_all(spec_handle* h) {
+  for (auto& g : h->gcache) h->retired.push_back(g);
+  h->gcache.clear();
+}
+
 // Replay of the recorded layer sequence for this shape, recorded on first use
 // on the handle's private stream (recording runs nothing).  Returns null when
 // recording or instantiation fails.
 hipGraphExec_t layer_graph(spec_handle* h, const StepShape& sh) {
-  for (auto& g : h->gcache)
-    if (g.sh == sh) {
-      g.used = ++h->gclock;
-      return g.exec;
-    }
   if (!h->cap && hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess) {
     h->cap = nullptr;
     return nullptr;
@@ -444,23 +452,30 @@ hipGraphExec_t layer_graph(spec_handle* h, const StepShape& sh) {
   const hipError_t ie = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
   hipGraphDestroy(graph);
   if (ie != hipSuccess) return nullptr;
+  hipEvent_t done = nullptr;
+  if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess) {
+    hipGraphExecDestroy(ex);
+    return nullptr;
+  }
   if (h->gcache.size() >= kMaxGraphs) {
-    // evict the least recently used shape; it may still be running
+    // the least recently used shape leaves the cache; it may still be running
     size_t old = 0;
     for (size_t i = 1; i < h->gcache.size(); ++i)
       if (h->gcache[i].used < h->gcache[old].used) old = i;
-    if (hipDeviceSynchronize() != hipSuccess) {
-      hipGraphExecDestroy(ex);
-      return nullptr;
-    }
-    if (h->gcache[old].exec) hipGraphExecDestroy(h->gcache[old].exec);
+    h->retired.push_back(h->gcache[old]);
     h->gcache.erase(h->gcache.begin() + old);
   }
-  h->gcache.push_back({sh, ex, ++h->gclock});
+  h->gcache.push_back({sh, ex, ++h->gclock, done});
   return ex;
 }
 
+spec_status replay(spec_handle::Graph& g, hipStream_t s) {
+  if (hipGraphLaunch(g.exec, s) != hipSuccess) return SPEC_ERR_DEVICE;
+  return dev(hipEventRecord(g.done, s));
+}
+
 spec_status run_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
+  sweep_retired(h, false);
   if (h->graphs && !h->prof) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return SPEC_ERR_DEVICE;
@@ -470,21 +485,17 @@ spec_status run_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
         if (g.sh == sh) {
           g.used = ++h->gclock;
           // a shape whose recording failed stays on direct launches
-          return g.exec ? dev(hipGraphLaunch(g.exec, s)) : dev(launch_layers(h, sh, s));
+          return g.exec ? replay(g, s) : dev(launch_layers(h, sh, s));
         }
-      // first step of this shape: launch directly (the library GEMMs of
-      // many-row shapes choose their algorithms here), then record the same
-      // sequence for the next steps; recording runs nothing
-      spec_status st = dev(launch_layers(h, sh, s));
-      if (st != SPEC_OK) return st;
-      h->recording = true;
+      // first step of this shape: record its launch sequence (recording runs
+      // nothing), then replay it
       const hipGraphExec_t ex = layer_graph(h, sh);
-      h->recording = false;
       if (!ex) {
         hipGetLastError();  // clear a capture error; this shape keeps direct launches
-        h->gcache.push_back({sh, nullptr, ++h->gclock});
+        h->gcache.push_back({sh, nullptr, ++h->gclock, nullptr});
+        return dev(launch_layers(h, sh, s));
       }
-      return SPEC_OK;
+      return replay(h->gcache.back(), s);
     }
   }
   return dev(launch_layers(h, sh, s));
@@ -545,8 +556,6 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
   h->kv = (uint16_t*)d_kv_cache;
   h->ws = (char*)d_workspace;
   h->lay = L;
-  if (blas_ws_bytes(*cfg))
-    h->blas = blas_create(h->at<void>(L.gbws), blas_ws_bytes(*cfg), h->at<float>(L.gbd), blas_d_floats(*cfg));
 
   // rotary tables: angle = pos * theta^(-2i/D), evaluated in double
   const int D = cfg->head_dim, half = D / 2;
@@ -565,7 +574,6 @@ spec_status spec_verify_init(const spec_config* cfg, const void* const* d_weight
   if (e == hipSuccess) e = hipMemsetAsync(h->at<uint32_t>(L.flags), 0, 256, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
-    blas_destroy(h->blas);
     delete h;
     return SPEC_ERR_DEVICE;
   }
@@ -814,11 +822,9 @@ void spec_verify_destroy(spec_handle* h) {
     hipEventDestroy(r.b);
   }
   for (auto e : h->pool) hipEventDestroy(e);
-  if (!h->gcache.empty()) hipDeviceSynchronize();  // a replay may still be running
-  for (auto& g : h->gcache)
-    if (g.exec) hipGraphExecDestroy(g.exec);
+  retire_all(h);
+  sweep_retired(h, true);  // a replay may still be running
   if (h->cap) hipStreamDestroy(h->cap);
-  blas_destroy(h->blas);
   delete h;
 }
 
@@ -826,11 +832,10 @@ spec_status spec_set_block_table(spec_handle* h, const int32_t* d_table, int32_t
   if (!h || !d_table || pages_per_seq < 1) return SPEC_ERR_INVALID_ARG;
   if (!h->cfg.kv_page_size) return SPEC_ERR_STATE;
   if (h->kv_table != d_table || h->kv_ppseq != pages_per_seq) {
-    // the recorded launch sequences hold the old table: drop them
-    if (!h->gcache.empty()) hipDeviceSynchronize();
-    for (auto& g : h->gcache)
-      if (g.exec) hipGraphExecDestroy(g.exec);
-    h->gcache.clear();
+    // the recorded launch sequences hold the old table: drop them (each is
+    // destroyed once its last replay has finished)
+    retire_all(h);
+    sweep_retired(h, false);
   }
   h->kv_table = d_table;
   h->kv_ppseq = pages_per_seq;
@@ -840,6 +845,12 @@ spec_status spec_set_block_table(spec_handle* h, const int32_t* d_table, int32_t
 spec_status spec_graph_enable(spec_handle* h, int32_t enable) {
   if (!h) return SPEC_ERR_INVALID_ARG;
   h->graphs = enable != 0;
+  return SPEC_OK;
+}
+
+spec_status spec_gemm_route(int32_t route) {
+  if (route < 0 || route > 2) return SPEC_ERR_INVALID_ARG;
+  sv::gemm_route = route;
   return SPEC_OK;
 }
 

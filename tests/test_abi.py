@@ -146,3 +146,9 @@ def test_recurrent_calls_reject_bad_arguments_without_device():
     assert cv(T=0) == S.SPEC_ERR_INVALID_ARG and cv(out=None) == S.SPEC_ERR_INVALID_ARG
     assert cv(d=S.spec_recurrent_dims(4, 96, 4, 8)) == S.SPEC_ERR_SHAPE
     assert cv(prev=P + 8) == S.SPEC_ERR_INVALID_ARG  # misaligned
+
+
+def test_gemm_route_argument_checked():
+    L = S.lib()
+    assert L.spec_gemm_route(3) == -1 and L.spec_gemm_route(-1) == -1
+    assert L.spec_gemm_route(0) == 0
