@@ -316,6 +316,36 @@ spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int
  * Errors: INVALID_ARG (null handle). */
 spec_status spec_graph_enable(spec_handle* h, int32_t enable);
 
+/* Chain accept that allocates nothing and needs no handle, for callers that
+ * cannot allocate device memory or create a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It computes
+ * what spec_accept computes for a chain (T = gamma + 1 rows per sequence,
+ * d_tree_parent == NULL) with the same kernels, so for the same inputs the
+ * outputs are identical bit for bit; top-k / top-p adjustment is not offered
+ * here (SPEC_ERR_UNSUPPORTED).
+ *   vocab: V of the logits and q rows; the other arguments as in spec_accept.
+ *   d_flags: optional device word that receives the TOKEN_RANGE flag bit
+ *     (ORed in; the caller clears it); NULL discards the flags.
+ *   Scratch: the kernels' row statistics, residual chunk sums and accept
+ *     counts live in a fixed array inside the library (about 2.3 MiB per GPU,
+ *     held until the process ends): at most SPEC_STATIC_MAX_ROWS logits rows
+ *     (B * T), SPEC_STATIC_MAX_SEQS sequences and a vocabulary of
+ *     SPEC_STATIC_MAX_VOCAB.  Every scratch entry a call reads is written
+ *     earlier in that call.  All calls on one GPU share the array: calls that
+ *     overlap on one GPU (two streams, two threads) race; serialise them.
+ *   No hipMalloc, hipFree or allocating library call is made; the first call
+ *   on each device looks up the array's device address once.
+ *   Errors: INVALID_ARG (null pointer, B < 1, T < 1, vocab < 2, bad sampling,
+ *   q missing for a sampled chain), CAPACITY (beyond the limits above, or
+ *   T > 128), UNSUPPORTED (top-k / top-p set), DEVICE. */
+#define SPEC_STATIC_MAX_ROWS 4096
+#define SPEC_STATIC_MAX_SEQS 1024
+#define SPEC_STATIC_MAX_VOCAB 262144
+spec_status spec_accept_chain_static(int32_t B, int32_t T, int32_t vocab, const float* d_logits, const float* d_q,
+                                     const int32_t* d_tokens, const spec_sampling* sampling, int32_t* d_out_tokens,
+                                     int32_t* d_num_accepted, const int32_t* d_kv_len, int32_t* d_kv_len_out,
+                                     uint32_t* d_flags, void* stream);
+
 /* Measurement hook: the tile shape the tiled GEMMs (5 or more rows) use, for
  * A/B timing and for parity tests of both paths.  route 0: automatic (128-row
  * x 256-weight-row tiles from 64 rows on, 32-row tiles below); 1: the 32-row

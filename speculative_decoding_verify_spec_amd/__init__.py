@@ -35,7 +35,7 @@ SPEC_FLAG_LAYOUT = 8
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_profile_gemm", "spec_graph_enable", "spec_gemm_route", "spec_set_block_table", "spec_verify_destroy",
+    "spec_profile_gemm", "spec_graph_enable", "spec_gemm_route", "spec_accept_chain_static", "spec_set_block_table", "spec_verify_destroy",
     "spec_status_str",
     "spec_recurrent_verify", "spec_recurrent_commit", "spec_recurrent_commit_verify",
 ]
@@ -113,6 +113,9 @@ def lib():
     L.spec_graph_enable.restype = i32
     L.spec_gemm_route.argtypes = [i32]
     L.spec_gemm_route.restype = i32
+    L.spec_accept_chain_static.argtypes = [i32, i32, i32, vp, vp, vp, C.POINTER(spec_sampling), vp, vp, vp, vp,
+                                           vp, vp]
+    L.spec_accept_chain_static.restype = i32
     L.spec_set_block_table.argtypes = [vp, vp, i32]
     L.spec_set_block_table.restype = i32
     L.spec_verify_destroy.argtypes = [vp]
@@ -154,6 +157,10 @@ def _check(fn, st):
 
 
 KV_PAGE = 64  # slots per page of a paged cache
+# capacity of spec_accept_chain_static's fixed scratch
+SPEC_STATIC_MAX_ROWS = 4096
+SPEC_STATIC_MAX_SEQS = 1024
+SPEC_STATIC_MAX_VOCAB = 262144
 
 
 def make_config(shape, max_batch, max_ctx, max_rows_per_seq, kv_pages: int = 0) -> spec_config:
@@ -267,6 +274,16 @@ def spec_graph_enable(h, enable: bool):
 
 def spec_gemm_route(route: int):
     _check("spec_gemm_route", lib().spec_gemm_route(int(route)))
+
+
+def spec_accept_chain_static(B, T, vocab, logits, q, tokens, sampling: spec_sampling, out_tokens, num_accepted,
+                             kv_len=None, kv_len_out=None, flags=None, stream=None, check=True):
+    st = lib().spec_accept_chain_static(int(B), int(T), int(vocab), _ptr(logits), _ptr(q), _ptr(tokens),
+                                        C.byref(sampling), _ptr(out_tokens), _ptr(num_accepted), _ptr(kv_len),
+                                        _ptr(kv_len_out), _ptr(flags), _stream(stream))
+    if check:
+        _check("spec_accept_chain_static", st)
+    return st
 
 
 def spec_verify_destroy(h):

@@ -152,3 +152,21 @@ def test_gemm_route_argument_checked():
     L = S.lib()
     assert L.spec_gemm_route(3) == -1 and L.spec_gemm_route(-1) == -1
     assert L.spec_gemm_route(0) == 0
+
+
+def test_static_accept_rejects_before_any_launch():
+    """The allocation-free chain accept checks its arguments and its scratch
+    capacity on the host: nothing is enqueued (no GPU needed here)."""
+    L = S.lib()
+    samp = S.spec_sampling(temperature=1.0, tree_replacement=0, seed=1, round=0, top_k=0, top_p=1.0)
+    fake = C.c_void_p(256)  # never dereferenced: every call below fails its checks first
+    args = lambda B, T, V: (B, T, V, fake, fake, fake, C.byref(samp), fake, fake, None, None, None, None)  # noqa: E731
+    assert L.spec_accept_chain_static(*args(0, 4, 1000)) == -1
+    assert L.spec_accept_chain_static(2, 4, 1000, None, fake, fake, C.byref(samp), fake, fake, None, None, None,
+                                      None) == -1
+    assert L.spec_accept_chain_static(*args(S.SPEC_STATIC_MAX_SEQS + 1, 1, 1000)) == -3
+    assert L.spec_accept_chain_static(*args(64, 65, 1000)) == -3            # 4160 rows > 4096
+    assert L.spec_accept_chain_static(*args(2, 129, 1000)) == -3            # T > 128
+    assert L.spec_accept_chain_static(*args(2, 4, S.SPEC_STATIC_MAX_VOCAB + 1)) == -3
+    samp.top_p = 0.9
+    assert L.spec_accept_chain_static(*args(2, 4, 1000)) == -4              # top-p needs the handle's scratch
