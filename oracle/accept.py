@@ -124,7 +124,7 @@ def inverse_cdf(r: np.ndarray, u: float):
 
 
 def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0, top_p=1.0,
-                     adjust_margins=None):
+                     adjust_margins=None, trace=None):
     """One sequence.  z [gamma+1, V] target logits for the window rows;
     q [gamma, V] draft probabilities (row j: distribution draft j+1 came from);
     tokens [gamma+1] = [pending, x_1 .. x_gamma]; u(slot) -> uniform;
@@ -134,19 +134,27 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
 
     _variant plants one of the two wrong implementations of section 7.5 for
     negative-control tests only: "resample_from_p" draws the extra token from p
-    after a rejection; "deterministic" rejects whenever q > p."""
+    after a rejection; "deterministic" rejects whenever q > p.
+
+    With `trace` (a dict) the decisions' positions are recorded for aligning
+    another implementation's output with this one: trace["depths"][k] is the
+    emitted position decision k (margins[k]) decides, and trace["draw"] is
+    (u * R, cumsum(r)) of the final inverse-CDF draw (sampled mode)."""
     gamma = len(tokens) - 1
     margins = []
+    depths = [] if trace is None else trace.setdefault("depths", [])
     adjust_margins = [] if adjust_margins is None else adjust_margins
     if temperature == 0.0:
         n = 0
         while n < gamma:
             am = argmax_lowest(z[n])
             margins.append(top2_margin(z[n]))
+            depths.append(n)
             if int(tokens[n + 1]) != am:
                 break
             n += 1
         margins.append(top2_margin(z[n]))
+        depths.append(n)
         extra = argmax_lowest(z[n])
         return n, [int(t) for t in tokens[1:n + 1]] + [extra], margins
 
@@ -157,6 +165,7 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
         x = int(tokens[i + 1])
         ui = u(i)
         margins.append(abs(ui - min(1.0, p[x] / q[i][x])) if q[i][x] > 0 else np.inf)
+        depths.append(i)
         ok = (q[i][x] <= p[x]) if _variant == "deterministic" else (ui * q[i][x] < p[x])
         if ok:
             n += 1
@@ -172,11 +181,15 @@ def accept_chain_one(z, q, tokens, temperature, u, _variant="residual", top_k=0,
         r = p
     extra, m = inverse_cdf(r, u(gamma))
     margins.append(m)
+    depths.append(n)
+    if trace is not None:
+        c = np.cumsum(np.asarray(r, dtype=np.float64))
+        trace["draw"] = (u(gamma) * c[-1], c)
     return n, [int(t) for t in tokens[1:n + 1]] + [extra], margins
 
 
 def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _variant="residual",
-                    top_k=0, top_p=1.0, adjust_margins=None):
+                    top_k=0, top_p=1.0, adjust_margins=None, trace=None):
     """One sequence with a token tree.  z [T, V] logits per node; q [T, V] the
     draft distribution each node's children were drawn from; tokens [T] node
     tokens (node 0 = pending token); parent [T] (root -1).  u(slot) -> uniform.
@@ -190,14 +203,25 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
     for c in range(1, T):
         children[int(parent[c])].append(c)
     margins = []
+    depths = [] if trace is None else trace.setdefault("depths", [])
     adjust_margins = [] if adjust_margins is None else adjust_margins
     v = 0
     path = [0]
+
+    def final_draw(r):
+        extra, m = inverse_cdf(r, u(T - 1))
+        margins.append(m)
+        depths.append(len(path) - 1)
+        if trace is not None:
+            c = np.cumsum(np.asarray(r, dtype=np.float64))
+            trace["draw"] = (u(T - 1) * c[-1], c)
+        return extra
 
     if temperature == 0.0:
         while True:
             am = argmax_lowest(z[v])
             margins.append(top2_margin(z[v]))
+            depths.append(len(path) - 1)
             nxt = [c for c in children[v] if int(tokens[c]) == am]
             if not nxt:
                 return path, [int(tokens[c]) for c in path[1:]] + [am], margins
@@ -208,8 +232,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
         r, am = adjust(z[v], temperature, top_k, top_p)
         adjust_margins.append(am)
         if not children[v]:
-            extra, m = inverse_cdf(r, u(T - 1))
-            margins.append(m)
+            extra = final_draw(r)
             return path, [int(tokens[c]) for c in path[1:]] + [extra], margins
         qp = np.asarray(q[v], dtype=np.float64).copy()
         accepted = None
@@ -217,6 +240,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
             x = int(tokens[c])
             uc = u(c - 1)
             margins.append(abs(uc - min(1.0, r[x] / qp[x])) if qp[x] > 0 else np.inf)
+            depths.append(len(path) - 1)
             if uc * qp[x] < r[x]:
                 accepted = c
                 break
@@ -231,8 +255,7 @@ def accept_tree_one(z, q, tokens, parent, temperature, u, replacement=False, _va
                 if s > 0.0 and _variant != "no_renorm":
                     qp = qp / s
         if accepted is None:
-            extra, m = inverse_cdf(r, u(T - 1))
-            margins.append(m)
+            extra = final_draw(r)
             return path, [int(tokens[c]) for c in path[1:]] + [extra], margins
         v = accepted
         path.append(v)
@@ -243,31 +266,35 @@ def accept(logits, q, tokens, temperature, uniforms, tree_parent=None, replaceme
     """Batch driver.  logits [B, T, V]; q [B, T-1, V] (chain) or [B, T, V] (tree);
     tokens [B, T]; uniforms(b, slot) -> float; top_k / top_p as in `adjust`.
     Returns dict with n_accepted [B], out_tokens [B, T] (-1 padded), paths,
-    margins and adjust_margins (lists per sequence)."""
+    margins and adjust_margins (lists per sequence), and traces (per sequence:
+    the emitted position of each margin's decision, and the final draw's
+    u * R and CDF, see accept_chain_one)."""
     logits = np.asarray(logits)
     B, T = np.asarray(tokens).shape
     n_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, T), -1, dtype=np.int64)
-    paths, margins, adj_margins = [], [], []
+    paths, margins, adj_margins, traces = [], [], [], []
     for b in range(B):
         ub = (lambda s, b=b: uniforms(b, s))
         am = []
+        tr = {}
         if tree_parent is None:
             n, toks, m = accept_chain_one(logits[b], None if q is None else q[b], tokens[b],
-                                          temperature, ub, _variant, top_k, top_p, am)
+                                          temperature, ub, _variant, top_k, top_p, am, tr)
             path = list(range(n + 1))
         else:
             path, toks, m = accept_tree_one(logits[b], None if q is None else q[b], tokens[b],
                                             tree_parent[b], temperature, ub, replacement, _variant,
-                                            top_k, top_p, am)
+                                            top_k, top_p, am, tr)
             n = len(path) - 1
+        traces.append(tr)
         n_acc[b] = n
         out[b, : len(toks)] = toks
         paths.append(path)
         margins.append(m)
         adj_margins.append(am)
     return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins,
-            "adjust_margins": adj_margins}
+            "adjust_margins": adj_margins, "traces": traces}
 
 
 def accept_ragged(logits_rows, q_rows, tokens_rows, row_start, lens, q_start, temperature, uniforms,
@@ -283,19 +310,21 @@ def accept_ragged(logits_rows, q_rows, tokens_rows, row_start, lens, q_start, te
     max_len = int(max(lens)) if max_len is None else int(max_len)
     n_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, max_len), -1, dtype=np.int64)
-    margins, adj_margins, paths = [], [], []
+    margins, adj_margins, paths, traces = [], [], [], []
     for b in range(B):
         r0, n_b = int(row_start[b]), int(lens[b])
         z = np.asarray(logits_rows)[r0:r0 + n_b]
         q = None if q_rows is None else np.asarray(q_rows)[int(q_start[b]):int(q_start[b]) + n_b - 1]
         toks = np.asarray(tokens_rows)[r0:r0 + n_b]
         am = []
+        tr = {}
         n, em, m = accept_chain_one(z, q, toks, temperature, (lambda s, b=b: uniforms(b, s)),
-                                    top_k=top_k, top_p=top_p, adjust_margins=am)
+                                    top_k=top_k, top_p=top_p, adjust_margins=am, trace=tr)
+        traces.append(tr)
         n_acc[b] = n
         out[b, :len(em)] = em
         margins.append(m)
         adj_margins.append(am)
         paths.append(list(range(n + 1)))
     return {"n_accepted": n_acc, "out_tokens": out, "paths": paths, "margins": margins,
-            "adjust_margins": adj_margins}
+            "adjust_margins": adj_margins, "traces": traces}

@@ -9,11 +9,18 @@ from oracle.numerics import bf16_bits_to_f64
 from speculative_decoding_verify_spec_amd.engine import VerifyEngine
 
 NEAR_TIE = 1e-4      # decisions this close to their boundary may differ
+# the final draw on shared logits: both sides build the CDF from the same
+# logits, the GPU in fp32 (exp, residual) with fp64 sums, so its CDF sits
+# within a few 1e-7 of the oracle's (relative to the total mass)
+DRAW_BAND_SHARED = 1e-6
 # nucleus cuts this close (in renormalised mass) to top_p may differ: the GPU
 # sums fp32 exp() values in fp64, each within a few 1e-7 of the oracle's fp64
 # exp (the logit / temperature division in fp32 included)
 ADJUST_BAND = 1e-5
-LOGIT_RTOL = 2e-2    # per row: max|z_gpu - z_oracle| / max|z_oracle|
+LOGIT_RTOL = 2e-2    # per row: max|z_gpu - z_oracle| / max|z_oracle|, the contract
+# what the fp32-activation path achieves at the full 8B shape (measured
+# ~5e-5): the full-size tests hold it to this, so a subtle regression shows
+LOGIT_RTOL_FULL = 1e-3
 
 
 def dev():
@@ -46,21 +53,65 @@ def logits_rel_err(z_gpu, z_orc):
     return num / den
 
 
-def compare_decisions(gpu_out, gpu_n, orc, label=""):
-    """Token ids must be equal unless the oracle's decision trace has a margin
-    below NEAR_TIE.  Returns the number of counted near-tie differences."""
+def _first_difference(g_out, g_n, o_out, o_n):
+    """Emitted position of the first decision on which two accept results
+    differ: the first position (up to the shorter result) whose token differs;
+    if the shorter result is a prefix of the longer, the position where one
+    stopped (its test at that position went the other way)."""
+    m = min(g_n, o_n)
+    for j in range(m + 1):
+        if int(g_out[j]) != int(o_out[j]):
+            return j
+    return m
+
+
+def compare_decisions(gpu_out, gpu_n, orc, label="", band=NEAR_TIE, draw_band=NEAR_TIE, cap=None):
+    """Accept results must be equal, except where the first decision on which
+    they differ is a near-tie of the oracle's:
+      * an accept test (or greedy argmax) at that position with margin < band
+        (|u - min(1, p/q)|, or the top-2 gap over max|z|);
+      * the final draw, when the GPU's token lies within draw_band * R of
+        u * R on the oracle's CDF (the two sides' CDFs differ only by their
+        rounding there), i.e. it is the oracle's token or a neighbour across a
+        boundary that close;
+      * a nucleus cut at that position closer than ADJUST_BAND to top_p.
+    Only that first differing decision can excuse a sequence.  Returns the
+    number of excused sequences; `cap` bounds it."""
     near = 0
     for b in range(len(gpu_n)):
-        same = (int(gpu_n[b]) == int(orc["n_accepted"][b])) and \
-            np.array_equal(np.asarray(gpu_out[b]), orc["out_tokens"][b])
-        if same:
+        g_n, o_n = int(gpu_n[b]), int(orc["n_accepted"][b])
+        g_out, o_out = np.asarray(gpu_out[b]), np.asarray(orc["out_tokens"][b])
+        if g_n == o_n and np.array_equal(g_out[:g_n + 1], o_out[:o_n + 1]):
             continue
-        m = min(orc["margins"][b]) if orc["margins"][b] else np.inf
-        am = min(orc.get("adjust_margins", [[]] * len(gpu_n))[b], default=np.inf)
-        assert m < NEAR_TIE or am < ADJUST_BAND, (
-            f"{label} seq {b}: gpu n={gpu_n[b]} out={list(gpu_out[b])} vs oracle "
-            f"n={orc['n_accepted'][b]} out={list(orc['out_tokens'][b])}, min margin {m}, nucleus margin {am}")
+        j = _first_difference(g_out, g_n, o_out, o_n)
+        tr = orc["traces"][b]
+        margins, depths = orc["margins"][b], tr["depths"]
+        has_draw = "draw" in tr
+        draw_k = len(margins) - 1 if has_draw else -1
+        if has_draw and g_n == o_n and j == o_n:
+            # the final draw differs: where does the GPU's token sit on the
+            # oracle's CDF?
+            t, c = tr["draw"]
+            y = int(g_out[j])
+            R = float(c[-1])
+            ok = 0 <= y < len(c)
+            lo = float(c[y - 1]) if ok and y > 0 else 0.0
+            hi = float(c[y]) if ok else 0.0
+            dist = 0.0 if lo <= t < hi else min(abs(t - lo), abs(t - hi))
+            excused = ok and hi > lo and dist <= draw_band * R
+            why = f"draw: gpu token {y} interval [{lo:.6g}, {hi:.6g}) vs u*R {t:.6g} (R {R:.6g})"
+        else:
+            ms = [m for k, (m, d) in enumerate(zip(margins, depths)) if d == j and k != draw_k]
+            excused = min(ms, default=np.inf) < band
+            why = f"decision at position {j}: margins {ms}"
+        am = orc.get("adjust_margins", [[]] * len(gpu_n))[b]
+        if j < len(am) and am[j] < ADJUST_BAND:
+            excused = True
+        assert excused, (
+            f"{label} seq {b}: gpu n={g_n} out={list(g_out)} vs oracle n={o_n} out={list(o_out)}; {why}")
         near += 1
+    if cap is not None:
+        assert near <= cap, f"{label}: {near} near-tie differences, more than {cap}"
     return near
 
 

@@ -9,7 +9,7 @@ import torch
 import synth
 from oracle import accept as OA
 from oracle import philox
-from tests.gpu_util import ADJUST_BAND, compare_decisions, dev
+from tests.gpu_util import ADJUST_BAND, DRAW_BAND_SHARED, compare_decisions, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,9 @@ CHAIN_CASES = [
     (8, 4, 3, 0.0, 1.0),
     (4099, 3, 5, 0.0, 0.3),
     (128256, 2, 3, 0.0, 0.5),
+    # the batch of the largest chain workload: 128 sequences, gamma = 3
+    (128256, 128, 3, 1.0, 1.0),
+    (128256, 128, 3, 0.0, 1.0),
 ]
 
 
@@ -68,8 +71,8 @@ CHAIN_CASES = [
 def test_chain_accept_matches_oracle(V, B, gamma, temp, sigma):
     print(f"[chain accept] V={V} B={B} gamma={gamma} T={temp} sigma={sigma}", flush=True)
     T = gamma + 1
-    eng = _engine(V, 4, 8)
-    near, rounds, n_total = 0, 6, 0
+    eng = _engine(V, max(4, B), 8)
+    near, rounds, n_total = 0, 6 if B <= 8 else 2, 0
     for r in range(rounds):
         seed = 1000 * V % 9973 + 17 * r + gamma
         z, q, tokens = _chain_inputs(B, gamma, V, temp, sigma, seed)
@@ -83,7 +86,7 @@ def test_chain_accept_matches_oracle(V, B, gamma, temp, sigma):
         zn = z.double().cpu().numpy()
         qn = q.double().cpu().numpy() if q is not None else None
         orc = OA.accept(zn, qn, tokens.cpu().numpy(), temp, philox.Uniforms(42 + r, r))
-        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
         assert np.array_equal(kv_out.cpu().numpy(), kv_len.cpu().numpy() + nacc.cpu().numpy() + 1)
         n_total += B
         assert eng.device_errors() == 0
@@ -148,7 +151,7 @@ def test_tree_accept_matches_oracle(V, B, branching, temp, repl):
         orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy() if temp > 0 else None,
                         tokens.cpu().numpy(), temp, philox.Uniforms(7 + r, r),
                         tree_parent=parent.cpu().numpy(), replacement=repl)
-        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
         n_total += B
         assert eng.device_errors() == 0
         # commit: the accepted path's K/V now sit at slots kv_len + 0..n
@@ -213,6 +216,8 @@ ADJ_CHAIN_CASES = [
     (128256, 2, 3, 1.0, 1.0, 50, 0.9, 4.0, False),
     (128256, 1, 5, 1.0, 0.5, 0, 0.95, 4.0, False),
     (128256, 2, 3, 1.0, 1.0, 2000, 1.0, 1.28, False),
+    # 160 logits rows: more than one batch of the selection passes (128 rows)
+    (4099, 40, 3, 1.0, 1.0, 20, 0.9, 4.0, False),
 ]
 
 
@@ -221,7 +226,7 @@ def test_chain_accept_adjusted_matches_oracle(V, B, gamma, temp, sigma, top_k, t
     print(f"[chain accept adjusted] V={V} B={B} gamma={gamma} T={temp} top_k={top_k} top_p={top_p} "
           f"scale={scale} ties={ties}", flush=True)
     T = gamma + 1
-    eng = _engine(V, 4, 8)
+    eng = _engine(V, max(4, B), 8)
     near, n_total = 0, 0
     for r in range(6):
         seed = 777 * V % 9973 + 29 * r + gamma
@@ -240,7 +245,7 @@ def test_chain_accept_adjusted_matches_oracle(V, B, gamma, temp, sigma, top_k, t
         torch.cuda.synchronize()
         orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy(), tokens.cpu().numpy(), temp,
                         philox.Uniforms(42 + r, r), top_k=top_k, top_p=top_p)
-        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
         # the extra token lies in the adjusted support of its row (unless that
         # row's nucleus cut is itself a near-tie)
         for b in range(B):
@@ -296,11 +301,78 @@ def test_tree_accept_adjusted_matches_oracle(V, B, branching, top_k, top_p, adju
         torch.cuda.synchronize()
         orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy(), tokens.cpu().numpy(), 1.0,
                         philox.Uniforms(7 + r, r), tree_parent=parent.cpu().numpy(), top_k=top_k, top_p=top_p)
-        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
         n_total += B
         assert eng.device_errors() == 0
     print(f"  near-ties {near}/{n_total}", flush=True)
     assert near <= max(1, n_total // 10)
+
+
+DEGENERATE = ["q_zero_at_draft", "q_equals_p", "q_twice_p", "one_hot_residual"]
+
+
+@pytest.mark.parametrize("case", DEGENERATE)
+def test_chain_accept_degenerate_probabilities(case):
+    """Edge cases of the rule with probabilities both sides hold exactly
+    (uniform logits over V = 4096: p = 2^-12 in fp32 and fp64), so every
+    decision must agree bit for bit, with no near-tie excuse:
+      q_zero_at_draft  q(x) = 0 at every draft: u * 0 < p(x), always accepted,
+                       then the bonus from p;
+      q_equals_p       q = p: u < 1 always accepts;
+      q_twice_p        q = 2p (unnormalised): accepted iff u < 1/2; after a
+                       rejection max(0, p - q) has no mass and the draw falls
+                       back to p (the reading for a zero-mass residual);
+      one_hot_residual q moves 2^-12 from token y to the draft x: accepted iff
+                       u < 1/2, and a rejection must resample y."""
+    V, B, gamma = 4096, 16, 3
+    T = gamma + 1
+    eng = _engine(V, B, 8)
+    g = torch.Generator().manual_seed(DEGENERATE.index(case))
+    z = torch.zeros((B, T, V), device=dev())
+    tokens = torch.randint(0, V, (B, T), generator=g).to(torch.int32)
+    p = torch.full((B, gamma, V), 1.0 / V)
+    if case == "q_zero_at_draft":
+        q = p.clone()
+        for b in range(B):
+            for i in range(gamma):
+                q[b, i, tokens[b, i + 1]] = 0.0
+    elif case == "q_equals_p":
+        q = p.clone()
+    elif case == "q_twice_p":
+        q = 2.0 * p
+    else:
+        q = p.clone()
+        for b in range(B):
+            for i in range(gamma):
+                x = int(tokens[b, i + 1])
+                y = (x + 1 + int(torch.randint(0, V - 1, (1,), generator=g))) % V
+                q[b, i, x] = 2.0 / V
+                q[b, i, y] = 0.0
+    q, tokens = q.to(dev()), tokens.to(dev())
+    total = np.zeros(T, dtype=int)
+    for r in range(4):
+        kv_len = torch.full((B,), 50, dtype=torch.int32, device=dev())
+        kv_out = torch.zeros_like(kv_len)
+        out = torch.full((B, T), -5, dtype=torch.int32, device=dev())
+        nacc = torch.full((B,), -5, dtype=torch.int32, device=dev())
+        eng.accept(z, q, tokens, out, nacc, kv_len, kv_out, temperature=1.0, seed=99, round_=r)
+        torch.cuda.synchronize()
+        orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy(), tokens.cpu().numpy(), 1.0,
+                        philox.Uniforms(99, r))
+        n = nacc.cpu().numpy()
+        assert np.array_equal(n, orc["n_accepted"]), (case, n, orc["n_accepted"])
+        for b in range(B):
+            assert np.array_equal(out.cpu().numpy()[b, :n[b] + 1], orc["out_tokens"][b, :n[b] + 1]), (case, b)
+        if case in ("q_zero_at_draft", "q_equals_p"):
+            assert np.all(n == gamma)
+        if case == "one_hot_residual":
+            for b in range(B):
+                if n[b] < gamma:  # the resampled token is the one q gave up
+                    assert q[b, n[b], int(out[b, n[b]])] == 0.0
+        np.add.at(total, n, 1)
+        assert eng.device_errors() == 0
+    if case in ("q_twice_p", "one_hot_residual"):
+        assert total[:gamma].sum() > 0 and total.sum() == 4 * B  # rejections happened
 
 
 def test_accept_rejects_bad_adjustment():

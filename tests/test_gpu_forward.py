@@ -137,9 +137,12 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
 
 
 FFN_CASES = [
-    # B, T, ctx lengths: M = 1, 3 and 4 (split-K down whose sum the next QKV
-    # launch adds, matrix-core gate/up), 8 (split-K down + reduce, tiled QKV), 12
+    # B, T, ctx lengths: M = 1, 2 (the 2-row k-stationary and streaming
+    # kernels), 3 and 4 (split-K down whose sum the next QKV launch adds,
+    # matrix-core gate/up), 6 and 8 (split-K down + reduce, tiled QKV), 12
     (1, 1, [700]),
+    (1, 2, [700]),
+    (1, 6, [700]),
     (1, 3, [700]),
     (1, 4, [700]),
     (2, 4, [700, 33]),

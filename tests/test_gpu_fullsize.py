@@ -8,8 +8,9 @@ the launch configurations of the benchmarked workload and the larger ones:
 
 The GPU runs the whole batch; the oracle recomputes the sampled sequences
 (rows of different sequences are independent), so its cost stays bounded.
-Checks per sampled sequence: logits (per-row relative error, the north-star
-bound 2e-2; the path keeps fp32 activations so it lands near 1e-4), the K/V
+Checks per sampled sequence: logits (per-row relative error at most 1e-3,
+what the fp32-activation path achieves with room to spare; the contract
+bound is 2e-2), the K/V
 the step wrote, and the accept decisions on the oracle's own logits (near
 ties counted).  The accept decisions of every sequence are also checked on
 the GPU's logits (shared-logits tier)."""
@@ -24,7 +25,8 @@ from oracle import accept as OA
 from oracle import model as OM
 from oracle import philox
 from speculative_decoding_verify_spec_amd.engine import VerifyEngine
-from tests.gpu_util import LOGIT_RTOL, bf16_close, compare_decisions, dev, logits_rel_err, oracle_weights
+from tests.gpu_util import (DRAW_BAND_SHARED, LOGIT_RTOL_FULL, bf16_close, compare_decisions, dev, logits_rel_err,
+                            oracle_weights)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
@@ -74,13 +76,17 @@ def _tree_drafts(B, branching, V, sigma, seed):
     return tok.to(torch.int32).to(dev()), q, parent
 
 
-def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7):
+def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7, prepare=None):
+    """One verify + accept round on the GPU against the oracle.  `prepare`
+    (engine, kv_len, tokens) -> tokens may run steps first to choose drafts."""
     sh, w, W = model
     max_ctx = ((max(ctx) + T + 63) // 64) * 64
-    print(f"[8b] B={B} T={T} ctx={max(ctx)} tree={parent is not None}: cache", flush=True)
+    print(f"[8b] B={B} T={T} ctx={max(ctx)} tree={parent is not None} temp={temp}: cache", flush=True)
     cache = synth.make_kv_cache(sh, B, max_ctx, ctx, device=dev(), poison_tail=True)
     eng = VerifyEngine(sh, w, cache, B, max_ctx, T)
     kv = torch.tensor(ctx, dtype=torch.int32, device=dev())
+    if prepare is not None:
+        tokens = prepare(eng, kv, tokens)
     z = torch.full((B, T, sh.vocab), float("nan"), device=dev())
     eng.step(tokens, kv, z, tree_parent=parent)
     torch.cuda.synchronize()
@@ -104,7 +110,7 @@ def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7):
 
     # shared-logits tier: the oracle's accept on the GPU's logits, every sequence
     orc = OA.accept(z.double().cpu().numpy(), q_h, tok_h, temp, uni, tree_parent=par_h)
-    near = compare_decisions(out_h, nacc_h, orc, "shared logits")
+    near = compare_decisions(out_h, nacc_h, orc, "shared logits", draw_band=DRAW_BAND_SHARED, cap=max(1, B // 16))
     print(f"  shared-logits near-ties {near}/{B}", flush=True)
 
     for b in sample:
@@ -126,7 +132,7 @@ def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7):
                                 tree_parent=None if par_h is None else par_h[sl])
         err = logits_rel_err(z[b:b + 1].cpu().numpy(), zo)
         print(f"    logits rel err max {err.max():.2e} median {np.median(err):.2e}", flush=True)
-        assert err.max() < LOGIT_RTOL
+        assert err.max() < LOGIT_RTOL_FULL
         ko, vo = kc.copy(), vc.copy()
         OM.write_suffix(ko, vo, kn, vn, np.array(ctx[b:b + 1]))
         s0, s1 = ctx[b], ctx[b] + T
@@ -137,11 +143,12 @@ def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7):
         # end-to-end tier: decisions on the oracle's own logits
         orc_b = OA.accept(zo, None if q_h is None else q_h[sl], tok_h[sl], temp, _shifted(uni, b),
                           tree_parent=None if par_h is None else par_h[sl])
-        nb = compare_decisions(out_h[sl], nacc_h[sl], orc_b, f"sequence {b}")
+        nb = compare_decisions(out_h[sl], nacc_h[sl], orc_b, f"sequence {b}", cap=1)
         print(f"    end-to-end near-ties {nb}", flush=True)
     del eng, cache, z
     gc.collect()
     torch.cuda.empty_cache()
+    return nacc_h
 
 
 class _shifted:
@@ -178,3 +185,68 @@ def test_long_context_gamma7(model8b):
     V = synth.LLAMA8B.vocab
     tokens, q = _chain_drafts(16, 7, V, 1.5, 0.0, seed=404)
     _round(model8b, 16, [32768] * 16, 8, tokens, None, sample=[5], temp=0.0)
+
+
+def test_gamma1_b1(model8b):
+    """B=1, ctx 2048, gamma=1 (two rows: the 2-row GEMM kernels at full width)."""
+    V = synth.LLAMA8B.vocab
+    tokens, q = _chain_drafts(1, 1, V, 1.0, 1.0, seed=111)
+    _round(model8b, 1, [2048], 2, tokens, q, sample=[0])
+
+
+def test_gamma7_b1(model8b):
+    """B=1, ctx 2048, gamma=7 (eight rows), a close draft (sigma 0.5)."""
+    V = synth.LLAMA8B.vocab
+    tokens, q = _chain_drafts(1, 7, V, 0.5, 1.0, seed=121)
+    _round(model8b, 1, [2048], 8, tokens, q, sample=[0])
+
+
+def test_batch32_chain(model8b):
+    """B=32, ctx 1024, gamma=3: 128 rows on the large-tile GEMMs."""
+    V = synth.LLAMA8B.vocab
+    tokens, q = _chain_drafts(32, 3, V, 1.0, 1.0, seed=505)
+    _round(model8b, 32, [1024] * 32, 4, tokens, q, sample=[0, 31])
+
+
+def test_batch128_chain(model8b):
+    """B=128, ctx 1024, gamma=3: 512 rows, the largest chain workload; the
+    shared-logits tier covers all 128 sequences, the oracle's forward two."""
+    V = synth.LLAMA8B.vocab
+    tokens, q = _chain_drafts(128, 3, V, 1.0, 1.0, seed=606)
+    _round(model8b, 128, [1024] * 128, 4, tokens, q, sample=[5, 77])
+
+
+def test_long_context_gamma7_sampled(model8b):
+    """B=16, ctx 32768, gamma=7 at temperature 1 (the long-context workload
+    is reported greedy and sampled)."""
+    V = synth.LLAMA8B.vocab
+    tokens, q = _chain_drafts(16, 7, V, 1.5, 1.0, seed=414)
+    _round(model8b, 16, [32768] * 16, 8, tokens, q, sample=[9])
+
+
+def test_tree_4_4_2_2_greedy(model8b):
+    """B=4, ctx 4096, tree [4,4,2,2], greedy.  Each sequence's first child at
+    every depth is set, depth by depth, to the target's argmax at its parent
+    (a node's logits depend on its ancestors only), so the greedy walk goes
+    down to a leaf instead of stopping at the root."""
+    V = synth.LLAMA8B.vocab
+    tokens, q, parent = _tree_drafts(4, [4, 4, 2, 2], V, 1.0, seed=707)
+    ch = synth.tree_children(parent[0].cpu().tolist())
+
+    def prepare(eng, kv, tok):
+        tok = tok.clone()
+        z = torch.empty((4, 117, V), device=dev())
+        node = [0] * 4
+        for _ in range(4):
+            eng.step(tok, kv, z, tree_parent=parent)
+            torch.cuda.synchronize()
+            for b in range(4):
+                first = ch[node[b]][0]
+                tok[b, first] = int(z[b, node[b]].argmax())
+                node[b] = first
+        return tok
+
+    n = _round(model8b, 4, [4096] * 4, 117, tokens, None, sample=[1], parent=parent, temp=0.0, prepare=prepare)
+    # every first child is its parent's argmax: the walk reaches a leaf
+    # (depth 4), unless an argmax gap is a near-tie the comparison excused
+    assert (n == 4).sum() >= 3, n

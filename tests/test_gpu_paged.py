@@ -12,7 +12,7 @@ from oracle import model as OM
 from oracle import philox
 from oracle.numerics import bf16_bits_to_f64
 from speculative_decoding_verify_spec_amd.engine import VerifyEngine
-from tests.gpu_util import bf16_close, compare_decisions, dev, logits_rel_err, oracle_weights
+from tests.gpu_util import bf16_close, DRAW_BAND_SHARED, compare_decisions, dev, logits_rel_err, oracle_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def test_paged_tree_commit_and_table_edit():
     torch.cuda.synchronize()
     orc = OA.accept(z.double().cpu().numpy(), None, tokens.cpu().numpy(), 0.0, philox.Uniforms(1, 0),
                     tree_parent=parent.cpu().numpy())
-    compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, "paged tree")
+    compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, "paged tree", draw_band=DRAW_BAND_SHARED)
     (k_after, v_after), _ = _gather(pool, sh, table, npages, max_ctx)
     for b in range(B):
         path = orc["paths"][b]

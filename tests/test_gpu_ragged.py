@@ -10,7 +10,7 @@ import synth
 from oracle import accept as OA
 from oracle import model as OM
 from oracle import philox
-from tests.gpu_util import (bf16_close, build_engine, compare_decisions, dev, logits_rel_err, oracle_cache,
+from tests.gpu_util import (bf16_close, build_engine, DRAW_BAND_SHARED, compare_decisions, dev, logits_rel_err, oracle_cache,
                             oracle_weights)
 
 pytestmark = pytest.mark.gpu
@@ -156,7 +156,7 @@ def test_ragged_accept_matches_oracle(V, lens, max_len, temp, top_k, top_p, layo
         torch.cuda.synchronize()
         orc = OA.accept_ragged(zr.double().cpu().numpy(), qr.double().cpu().numpy(), tr.cpu().numpy(), rstart, lens,
                                qstart, temp, philox.Uniforms(3 + r, r), max_len=max_len, top_k=top_k, top_p=top_p)
-        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}")
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
         n = nacc.cpu().numpy()
         assert np.all(n <= np.array(lens) - 1)
         assert np.array_equal(kv_out.cpu().numpy(), kv.cpu().numpy() + n + 1)
