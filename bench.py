@@ -93,7 +93,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=128,
+                    help="timed steps; by default they cover every pre-drafted round once")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--ctx", type=int, default=2048)
@@ -103,7 +104,10 @@ def parse():
     ap.add_argument("--top-k", type=int, default=0, help="top-k adjustment of the target (0: off)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p adjustment of the target (1: off); the synthetic drafts stay unadjusted")
-    ap.add_argument("--rounds", type=int, default=8, help="distinct pre-drafted rounds cycled")
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="distinct pre-drafted rounds cycled (0: enough for 128 sequence-rounds, at least 2)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="B=1 table over gamma in {0,1,3,5,7} x sigma in {0.5,1,2}: c_v, T_verify, tok/s")
     ap.add_argument("--ragged-lens", type=str, default="",
                     help="comma-separated per-sequence verify lengths (one per sequence of --batch): also time "
                          "the compact ragged forward against the fixed-width one")
@@ -145,6 +149,10 @@ def main():
     if a.recurrent:
         return run_recurrent(a, dev)
     sh = synth.LLAMA8B
+    if a.rounds <= 0:
+        a.rounds = max(2, -(-128 // a.batch))
+    if a.sweep:
+        a.gamma = max(SWEEP_GAMMAS)
     B, ctx, gamma, T = a.batch, a.ctx, a.gamma, a.gamma + 1
     if a.tree:
         branching = [int(x) for x in a.tree.split(",")]
@@ -185,29 +193,10 @@ def main():
     pending = synth.make_tokens(B, 1, sh.vocab, seed=synth.SEED_PROMPT, device=dev)
     if a.tree:
         return run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev)
+    if a.sweep:
+        return run_sweep(a, sh, eng, kv_len, pending, dev)
 
-    # ---- pre-draft R rounds from the same state: gamma sequential T=1 decodes
-    # give the target logits z_i of each drafted prefix; q_i = softmax(z_i + eps)
-    rounds = []
-    z1 = torch.empty((B, 1, sh.vocab), device=dev)
-    for r in range(a.rounds):
-        toks = [pending[:, 0]]
-        qs = []
-        for i in range(gamma):
-            tok = toks[-1][:, None].contiguous().to(torch.int32)
-            eng.step(tok, kv_len + i, z1)
-            q, zn = synth.noisy_draft_dist(z1[:, 0], a.sigma, synth.SEED_NOISE * 1000 + r * 16 + i,
-                                           a.temperature if a.temperature > 0 else 1.0)
-            if a.temperature > 0:
-                x = synth.sample_from(q, synth.SEED_DRAFT * 1000 + r * 16 + i)[:, 0]
-            else:
-                x = zn.argmax(-1).to(torch.int32)
-            toks.append(x)
-            qs.append(q)
-        tokens = torch.stack(toks, 1).to(torch.int32).contiguous()
-        qt = torch.stack(qs, 1).contiguous() if gamma else torch.empty((B, 0, sh.vocab), device=dev)
-        rounds.append((tokens, qt))
-    torch.cuda.synchronize()
+    rounds = draft_rounds(eng, sh, B, gamma, a.sigma, a.temperature, a.rounds, kv_len, pending, dev)
     log(f"{a.rounds} draft rounds ready")
 
     logits = torch.empty((B, T, sh.vocab), device=dev)
@@ -239,7 +228,7 @@ def main():
     tokens_out = int((n_timed + 1).sum())
     value = tokens_out / wall
     ms_per_step = wall * 1000.0 / a.steps
-    alpha_hat = float(n_timed.mean()) / gamma if gamma else 0.0
+    acc_stats = acceptance_stats(n_timed, gamma, a.sigma, a.temperature)
     assert eng.device_errors() == 0
     log(f"timed {a.steps} steps: {ms_per_step:.3f} ms/step (events {gpu_ms / a.steps:.3f}), "
         f"{tokens_out} tokens, {value:.1f} tok/s")
@@ -329,16 +318,171 @@ def main():
                    "B": B, "ctx": ctx, "gamma": gamma, "sigma": a.sigma, "temperature": a.temperature,
                    "top_k": a.top_k, "top_p": a.top_p, "parallelism": "single GPU"},
         "c_verify": round(c_v, 4), "t_verify_ms": round(t_verify, 4), "t_decode_ms": round(t_decode, 4),
-        "mean_accepted": round(float(n_timed.mean()), 4), "alpha_hat": round(alpha_hat, 4),
-        "tokens_per_round": round(float((n_timed + 1).mean()), 4),
+        "rounds": {"distinct": a.rounds, "sequences_per_round": B, "timed_sequence_rounds": int(n_timed.size)},
+        **acc_stats,
         "kernels": kernels, "roofline": roofline,
     }
     if ragged is not None:
         result["ragged"] = ragged
 
     if a.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a, kv_len)
+        # the GPU's decisions the oracle leg compares with: every timed step's
+        # logits and accept output (shared-logits tier), and round 0 accepted
+        # with each uniform round the oracle's own forward is used for
+        nk = min(a.steps, 128)
+        shared = []
+        for k in range(a.warmup, a.warmup + nk):
+            one_step(k)
+            tokens, qt = rounds[k % len(rounds)]
+            shared.append((k, tokens.cpu().numpy(), qt.double().cpu().numpy() if gamma else None,
+                           logits.double().cpu().numpy(), out.cpu().numpy(), nacc_hist[k].cpu().numpy()))
+        e2e = []
+        for j in range(3):
+            tokens, qt = rounds[0]
+            eng.step(tokens, kv_len, logits)
+            eng.accept(logits, qt if gamma else None, tokens, out, nacc_hist[0], kv_len, kv_out,
+                       temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=j, top_k=a.top_k, top_p=a.top_p)
+            e2e.append((out.cpu().numpy(), nacc_hist[0].cpu().numpy()))
+        result["cpu_baseline"], result["near_ties"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a,
+                                                                   kv_len, shared, e2e)
     print(json.dumps(result), flush=True)
+
+
+SWEEP_GAMMAS = (0, 1, 3, 5, 7)
+SWEEP_SIGMAS = (0.5, 1.0, 2.0)
+
+
+def draft_rounds(eng, sh, B, gamma, sigma, temperature, R, kv_len, pending, dev):
+    """R rounds pre-drafted from the same state: gamma sequential T=1 decodes
+    give the target logits z_i of each drafted prefix; the noisy-target draft
+    is q_i = softmax(z_i + eps), eps ~ N(0, sigma^2), x_i ~ q_i (argmax of the
+    noisy logits at temperature 0).  Untimed: the draft is synthetic."""
+    import torch
+
+    import synth
+
+    rounds = []
+    z1 = torch.empty((B, 1, sh.vocab), device=dev)
+    for r in range(R):
+        toks = [pending[:, 0]]
+        qs = []
+        for i in range(gamma):
+            tok = toks[-1][:, None].contiguous().to(torch.int32)
+            eng.step(tok, kv_len + i, z1)
+            q, zn = synth.noisy_draft_dist(z1[:, 0], sigma, synth.SEED_NOISE * 1000 + r * 16 + i,
+                                           temperature if temperature > 0 else 1.0)
+            if temperature > 0:
+                x = synth.sample_from(q, synth.SEED_DRAFT * 1000 + r * 16 + i)[:, 0]
+            else:
+                x = zn.argmax(-1).to(torch.int32)
+            toks.append(x)
+            qs.append(q)
+        tokens = torch.stack(toks, 1).to(torch.int32).contiguous()
+        qt = torch.stack(qs, 1).contiguous() if gamma and temperature > 0 else \
+            torch.empty((B, 0, sh.vocab), device=dev)
+        rounds.append((tokens, qt))
+    torch.cuda.synchronize()
+    return rounds
+
+
+def acceptance_stats(n, gamma, sigma, temperature):
+    """Per-position acceptance alpha = tests passed / tests reached (a round
+    that accepted n < gamma drafts reached n + 1 tests, one that accepted all
+    reached gamma), its closed form for the noisy-target draft at temperature
+    1, 2 Phi(-sigma/2) (flat target logits), and tokens per round against
+    eq. (1) of CS349E Lecture 6 section 8.1 at the measured alpha."""
+    import numpy as np
+
+    n = np.asarray(n).ravel()
+    out = {"mean_accepted": round(float(n.mean()), 4), "tokens_per_round": round(float((n + 1).mean()), 4)}
+    if gamma == 0:
+        return out
+    passed = int(n.sum())
+    reached = int(np.minimum(n + 1, gamma).sum())
+    alpha = passed / reached if reached else 0.0
+    out["alpha_per_position"] = round(alpha, 4)
+    out["alpha_se"] = round(math.sqrt(max(alpha * (1 - alpha), 0.0) / max(reached, 1)), 4)
+    if temperature > 0:
+        out["alpha_closed_form"] = round(math.erfc(sigma / 2.0 / math.sqrt(2.0)), 4)  # 2 Phi(-sigma/2)
+    out["tokens_per_round_eq1"] = round((1 - alpha ** (gamma + 1)) / (1 - alpha) if alpha < 1 else gamma + 1.0, 4)
+    out["tokens_per_round_se"] = round(float((n + 1).std(ddof=1) / math.sqrt(n.size)) if n.size > 1 else 0.0, 4)
+    return out
+
+
+def run_sweep(a, sh, eng, kv_len, pending, dev):
+    """The B=1 table over draft length and draft quality: for each gamma, the
+    whole-step T_verify(gamma+1) and c_v = T_verify / T_decode(1); for each
+    (gamma, sigma), accepted tok/s over timed verify + accept steps cycling
+    pre-drafted rounds (the DeepSeek-V4 analysis page's step cost against the
+    verify window; the verify-cost page's decode steps per verify)."""
+    import torch
+
+    import synth
+
+    B, V = a.batch, sh.vocab
+    stream = torch.cuda.current_stream(dev)
+
+    def time_forward(tok, iters=20):
+        lg = torch.empty((B, tok.shape[1], V), device=dev)
+        for _ in range(3):
+            eng.step(tok, kv_len, lg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            eng.step(tok, kv_len, lg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    R = max(16, a.rounds // 2)
+    table = []
+    kv_out = torch.empty_like(kv_len)
+    t_decode = None
+    for gamma in SWEEP_GAMMAS:
+        T = gamma + 1
+        logits = torch.empty((B, T, V), device=dev)
+        out = torch.empty((B, T), dtype=torch.int32, device=dev)
+        for sigma in SWEEP_SIGMAS:
+            rounds = draft_rounds(eng, sh, B, gamma, sigma, a.temperature, R, kv_len, pending, dev)
+            if t_decode is None:
+                t_decode = time_forward(rounds[0][0][:, :1].contiguous())
+            t_verify = time_forward(rounds[0][0])
+            nacc = torch.zeros((2 * R, B), dtype=torch.int32, device=dev)
+
+            def one_step(k):
+                tokens, qt = rounds[k % R]
+                eng.step(tokens, kv_len, logits)
+                eng.accept(logits, qt if gamma and a.temperature > 0 else None, tokens, out, nacc[k], kv_len,
+                           kv_out, temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
+
+            for k in range(4):
+                one_step(k)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(R, 2 * R):
+                one_step(k)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            n = nacc[R:].cpu().numpy()
+            row = {"gamma": gamma, "sigma": sigma, "t_verify_ms": round(t_verify, 4),
+                   "t_decode_ms": round(t_decode, 4), "c_v": round(t_verify / t_decode, 4),
+                   "ms_per_step": round(wall * 1000.0 / R, 4),
+                   "tok_s": round(float((n + 1).sum()) / wall, 2),
+                   **acceptance_stats(n, gamma, sigma, a.temperature)}
+            table.append(row)
+            log(f"gamma {gamma} sigma {sigma}: c_v {row['c_v']}, {row['tok_s']} tok/s, "
+                f"{row['tokens_per_round']} tokens/round")
+    assert eng.device_errors() == 0
+    print(json.dumps({
+        "metric": "verify cost ratio c=T_verify/T_decode; accepted tok/s (sweep)", "unit": "accepted tok/s",
+        "n_gpus": 1, "higher_is_better": True, "vs_baseline": None,
+        "dtype": "f32 (bf16 weights, fp32 activations/accum)",
+        "data": "synthetic (random-init weights, random bf16 KV context, noisy-target drafts)",
+        "config": {"workload": f"llama3-8b-shape chain verify B={B} ctx={a.ctx} gamma x sigma sweep "
+                               f"T={a.temperature}", "B": B, "ctx": a.ctx, "rounds_per_point": R,
+                   "parallelism": "single GPU"},
+        "sweep": table}), flush=True)
 
 
 def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
@@ -371,15 +515,19 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
         q = None
         for lvl in range(len(branching)):
             eng.step(tokens, kv_len, logits, tree_parent=parent)
-            q, _ = synth.noisy_draft_dist(logits, a.sigma, synth.SEED_NOISE * 1000 + r * 16 + lvl,
-                                          a.temperature if a.temperature > 0 else 1.0)
+            q, zn = synth.noisy_draft_dist(logits, a.sigma, synth.SEED_NOISE * 1000 + r * 16 + lvl,
+                                           a.temperature if a.temperature > 0 else 1.0)
             g.manual_seed(synth.SEED_DRAFT * 1000 + r * 16 + lvl)
             qc = q.double().cpu()
+            zc = zn.cpu()
             tk = tokens.cpu()
             for b in range(B):
                 for v in range(T):
                     if depth[v] == lvl and ch[v]:
-                        picks = torch.multinomial(qc[b, v], len(ch[v]), replacement=False, generator=g)
+                        if a.temperature > 0:  # children drawn from q without replacement
+                            picks = torch.multinomial(qc[b, v], len(ch[v]), replacement=False, generator=g)
+                        else:  # greedy: the draft's top-k
+                            picks = torch.topk(zc[b, v], len(ch[v])).indices
                         for c, x in zip(ch[v], picks.tolist()):
                             tk[b, c] = x
             tokens = tk.to(dev)
@@ -394,8 +542,8 @@ def run_tree(a, sh, eng, names, w, cache, kv_len, pending, dev):
     def one_step(k):
         tokens, q = rounds[k % len(rounds)]
         eng.step(tokens, kv_len, logits, tree_parent=parent)
-        eng.accept(logits, q, tokens, out, nacc_hist[k], kv_len, kv_out, tree_parent=parent,
-                   temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
+        eng.accept(logits, q if a.temperature > 0 else None, tokens, out, nacc_hist[k], kv_len, kv_out,
+                   tree_parent=parent, temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=k)
 
     for k in range(a.warmup):
         one_step(k)
@@ -634,9 +782,57 @@ def profile_pass(S, eng, one_step, steps):
     return kernels, roofline
 
 
-def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
+def _first_difference(g_out, g_n, o_out, o_n):
+    m = min(g_n, o_n)
+    for j in range(m + 1):
+        if int(g_out[j]) != int(o_out[j]):
+            return j
+    return m
+
+
+def count_decisions(gpu_out, gpu_n, orc, draw_band, band=1e-4):
+    """The GPU's accept results against the oracle's (same logits, q, drafts
+    and uniforms): decisions taken, sequences that differ only at a near-tie of
+    their first differing decision (an accept test with |u - min(1, p/q)| <
+    band, an argmax with a top-2 gap under band of max|z|, or a final draw
+    whose GPU token sits within draw_band * R of u * R on the oracle's CDF),
+    and sequences that differ otherwise (mismatches, expected 0)."""
+    decisions = near = mismatch = 0
+    for b in range(len(gpu_n)):
+        g_n, o_n = int(gpu_n[b]), int(orc["n_accepted"][b])
+        g_out, o_out = gpu_out[b], orc["out_tokens"][b]
+        decisions += len(orc["margins"][b])
+        if g_n == o_n and all(int(g_out[i]) == int(o_out[i]) for i in range(g_n + 1)):
+            continue
+        j = _first_difference(g_out, g_n, o_out, o_n)
+        tr = orc["traces"][b]
+        draw_k = len(orc["margins"][b]) - 1 if "draw" in tr else -1
+        if "draw" in tr and g_n == o_n and j == o_n:
+            t, c = tr["draw"]
+            y = int(g_out[j])
+            R = float(c[-1])
+            ok = 0 <= y < len(c) and c[y] > (c[y - 1] if y else 0.0)
+            lo, hi = (float(c[y - 1]) if y else 0.0, float(c[y])) if ok else (0.0, 0.0)
+            dist = 0.0 if lo <= t < hi else min(abs(t - lo), abs(t - hi))
+            excused = ok and dist <= draw_band * R
+        else:
+            ms = [m for k, (m, d) in enumerate(zip(orc["margins"][b], tr["depths"])) if d == j and k != draw_k]
+            excused = min(ms, default=float("inf")) < band
+        am = orc["adjust_margins"][b]
+        if j < len(am) and am[j] < 1e-5:
+            excused = True
+        near += int(excused)
+        mismatch += int(not excused)
+    return decisions, near, mismatch
+
+
+def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared, e2e):
     """One verify round (forward over the T rows + accept) of the same workload
-    in the CPU oracle, on this host's cores."""
+    in the CPU oracle, on this host's cores.  The oracle's results also give
+    the decision check the benchmark spec asks to report: the GPU's accept on its
+    own logits against the oracle's accept on the same logits for the timed
+    steps (shared-logits tier), and the GPU's round-0 decisions against the
+    oracle's forward + accept of round 0 (end-to-end tier)."""
     import numpy as np
 
     import synth
@@ -650,7 +846,7 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
     kc, vc = synth.to_numpy_raw(k), synth.to_numpy_raw(v)
     tokens, qt = round0
     tok = tokens.cpu().numpy()
-    qn = qt.double().cpu().numpy()
+    qn = qt.double().cpu().numpy() if a.gamma and a.temperature > 0 else None
     cores = len(os.sched_getaffinity(0))
     threads = None
     try:
@@ -660,6 +856,7 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
         pass
     log(f"cpu baseline: oracle rounds on {cores} cores")
     dt, toks, nrounds = 0.0, 0, 0
+    e2e_counts = [0, 0, 0]
     while nrounds < 3 and (nrounds == 0 or dt < a.cpu_seconds):
         t0 = time.perf_counter()
         z, _, _ = OM.forward(sh, Wn, tok, np.full(B, ctx), kc, vc)
@@ -667,18 +864,36 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len):
                         top_k=a.top_k, top_p=a.top_p)
         dt += time.perf_counter() - t0
         toks += int((res["n_accepted"] + 1).sum())
+        g_out, g_n = e2e[nrounds]
+        for i, x in enumerate(count_decisions(g_out, g_n, res, draw_band=1e-4)):
+            e2e_counts[i] += x
         nrounds += 1
     log(f"cpu baseline: {dt:.1f}s for {nrounds} rounds, {toks} tokens")
+    sh_counts = [0, 0, 0]
+    for kk, tk, qq, zz, g_out, g_n in shared:
+        res = OA.accept(zz, qq, tk, a.temperature, philox.Uniforms(synth.SEED_ACCEPT, kk), top_k=a.top_k,
+                        top_p=a.top_p)
+        for i, x in enumerate(count_decisions(g_out, g_n, res, draw_band=1e-6)):
+            sh_counts[i] += x
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as fh:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores, "cpu_model": cpu_model,
+    base = {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores, "cpu_model": cpu_model,
             "kind": "oracle", "sample": f"{nrounds} verify rounds (B={B}, T={a.gamma + 1}, ctx {ctx}, "
                                         f"32 layers, forward + accept) of the same workload; {dt:.1f} s",
-            "round_seconds": round(dt / nrounds, 2), "host_cores_visible": cores}
+            "round_seconds": round(dt / nrounds, 2), "host_cores_visible": cores,
+            "threads_note": "cores = the BLAS threads the oracle ran on (threadpoolctl), else the visible cores"}
+    near = {"shared_logits": {"sequence_rounds": len(shared) * B, "decisions": sh_counts[0],
+                              "near_tie_differences": sh_counts[1], "mismatches": sh_counts[2],
+                              "draw_band": 1e-6, "band": 1e-4},
+            "end_to_end": {"sequence_rounds": nrounds * B, "decisions": e2e_counts[0],
+                           "near_tie_differences": e2e_counts[1], "mismatches": e2e_counts[2],
+                           "draw_band": 1e-4, "band": 1e-4}}
+    log(f"decisions: shared logits {sh_counts}, end to end {e2e_counts} (decisions, near ties, mismatches)")
+    return base, near
 
 
 if __name__ == "__main__":
