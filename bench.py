@@ -122,6 +122,11 @@ def parse():
                     help="N > 0: time verify + commit of a recurrent (gated delta-rule) layer for N sequences "
                          "instead of the 8B model (32 heads of 128, 4-tap conv, T = gamma + 1)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="1: time the oracle on this host")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the streaming-read ceiling at the 8B GEMMs' weight sizes")
+    ap.add_argument("--gemm-route", type=int, default=0,
+                    help="GEMM kernel override for A/B timing (spec_gemm_route): 0 automatic, 1 32-row tiles, "
+                         "2 large tiles, 3 large tiles in the 4-wave form")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run an fp32 copy of this many MiB three times first (HBM counter calibration)")
@@ -145,9 +150,18 @@ def main():
     from speculative_decoding_verify_spec_amd.engine import VerifyEngine
 
     S.lib()  # fail loudly when the HIP library is missing
+    if a.gemm_route:
+        S.spec_gemm_route(a.gemm_route)
     dev = torch.device("cuda:0")
     if a.recurrent:
         return run_recurrent(a, dev)
+    if a.read_ceiling:
+        sizes = {"o": 4096 * 4096 * 2, "qkv": 6144 * 4096 * 2, "down": 4096 * 14336 * 2,
+                 "gate_up": 28672 * 4096 * 2, "lm_head": 128256 * 4096 * 2}
+        res = read_ceiling(S, dev, sizes)
+        print(json.dumps({"metric": "streaming-read ceiling (launch to end, back to back)", "unit": "us",
+                          "sizes": res}), flush=True)
+        return
     sh = synth.LLAMA8B
     if a.rounds <= 0:
         a.rounds = max(2, -(-128 // a.batch))
@@ -177,13 +191,14 @@ def main():
     log(f"weights + cache ready in {time.time() - t0:.1f}s")
 
     if a.calibrate_copy_mib > 0:
-        # a plain elementwise copy of known size: per dispatch it reads and
+        # a plain elementwise pass of known size: per dispatch it reads and
         # writes exactly n * 4 bytes, which scales the profiler's HBM counters
+        # (a negation, so that its kernel is easy to tell from the others)
         n = a.calibrate_copy_mib * (1 << 20) // 4
         src = torch.ones(n, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.add(src, 0.0, out=dst)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log(f"calibration copy: 3 x {n * 4} bytes read and written")
         del src, dst
@@ -296,6 +311,11 @@ def main():
                 "traffic": committed_traffic(B * T), "algo_bytes_per_launch": gu_bytes_launch,
                 "avg_launch_us": round(gu_avg_s * 1e6, 3), "launches_timed": n_gu}
     log(f"gate/up GEMM: {roofline['avg_launch_us']} us/launch, {roofline['achieved']} GB/s")
+    # the same bytes as one plain streaming read: what a kernel of this size
+    # reaches at best, launch, ramp and tail included
+    rc = read_ceiling(S, dev, {"gate_up": int(gu_bytes_launch) // 16 * 16})["gate_up"]
+    roofline["read_ceiling"] = {**rc, "frac_of_ceiling": round(rc["us"] / roofline["avg_launch_us"], 4)}
+    log(f"read ceiling at {rc['bytes']} B: {rc['us']} us ({rc['GBps']} GB/s)")
 
     # ---- per-kernel-class event timing (a separate profiled pass)
     kernels = {}
@@ -742,6 +762,32 @@ def run_recurrent(a, dev):
                                             f"verify + snapshot commit; {dt:.1f} s"}
     log(f"recurrent: {ms_fused:.4f} ms/step (fused), {ms_replay:.4f} (replay), {ms_snap:.4f} (snapshots)")
     print(json.dumps(result), flush=True)
+
+
+def read_ceiling(S, dev, sizes, iters=None):
+    """Best launch-to-end time of a plain streaming read of each size (bytes)
+    over a few launch shapes, through the library's measurement hook."""
+    import torch
+
+    span = 3 << 30
+    raw = torch.empty(span + 4096, dtype=torch.uint8, device=dev)
+    pad = (-raw.data_ptr()) % 4096
+    buf = raw[pad:pad + span]
+    out = {}
+    for name, nbytes in sizes.items():
+        best = None
+        for grid in (256, 512, 1024, 2048):
+            for unroll in (4, 8):
+                it = iters or (20 if nbytes > (256 << 20) else 100)
+                us = S.spec_profile_stream_read(buf, nbytes, it, grid, unroll)
+                if best is None or us < best[0]:
+                    best = (us, grid, unroll)
+        us, grid, unroll = best
+        out[name] = {"bytes": nbytes, "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1), "grid": grid,
+                     "unroll": unroll}
+    del raw, buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def step_percentiles(evs):

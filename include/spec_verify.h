@@ -309,6 +309,24 @@ int32_t spec_profile_read(spec_handle* h, spec_kernel_stat* out, int32_t max_out
 spec_status spec_profile_gemm(spec_handle* h, const char* cls, int32_t rows, int32_t iters, void* stream,
                               double* ms_out, double* bytes_out);
 
+/* Measurement hook, not part of the verify path: the average launch-to-end
+ * time in microseconds of a plain streaming read of `read_bytes`, launched
+ * `iters` times back to back on `stream` between one pair of HIP events
+ * (after 3 untimed launches).  The read is a grid-stride loop of `grid`
+ * workgroups of 256 threads with `unroll` (4 or 8) 16-byte non-temporal
+ * loads in flight per thread.  Each launch reads the window after the
+ * previous one inside d_buf (wrapping), so that consecutive launches do not
+ * hit the memory-side cache; the buffer's last 16 bytes are a sink the
+ * kernel may write.  It is the practical ceiling of a weight-streaming GEMM
+ * over that many weight bytes, launch, ramp and tail included.  Synchronises
+ * the host (it waits for the end event).
+ * d_buf: device memory, 4096-byte aligned, buf_bytes a multiple of 16 and at
+ * least read_bytes + 8192; read_bytes a multiple of 16.
+ * Errors: SPEC_ERR_INVALID_ARG (null pointer, sizes or alignment as above,
+ * iters or grid < 1, unroll not 4 or 8), SPEC_ERR_DEVICE (a HIP call failed). */
+spec_status spec_profile_stream_read(const void* d_buf, size_t buf_bytes, size_t read_bytes, int32_t iters,
+                                     int32_t grid, int32_t unroll, void* stream, double* us_out);
+
 /* Replay the recorded per-layer launch sequence (enable != 0, the default)
  * or launch every kernel directly (enable == 0).  Both run the same kernels
  * with the same arguments, so the results are identical; replay saves the
@@ -346,15 +364,17 @@ spec_status spec_accept_chain_static(int32_t B, int32_t T, int32_t vocab, const 
                                      int32_t* d_num_accepted, const int32_t* d_kv_len, int32_t* d_kv_len_out,
                                      uint32_t* d_flags, void* stream);
 
-/* Measurement hook: the tile shape the tiled GEMMs (5 or more rows) use, for
- * A/B timing and for parity tests of both paths.  route 0: automatic (128-row
- * x 256-weight-row tiles from 64 rows on, 32-row tiles below); 1: the 32-row
- * tiles at every row count; 2: the large tiles at every row count the tiled
- * kernels serve.  Process-wide; results are within the same fp32 tolerance
- * either way (the sums are taken in a different order).  Takes effect for
- * launch sequences recorded afterwards (switch graphs off, or use a new
- * handle, to apply it to shapes already recorded).
- * Errors: INVALID_ARG (route outside 0..2). */
+/* Measurement hook: the GEMM kernels a launch of 9 or more rows uses, for
+ * A/B timing and for parity tests of every path.  route 0: automatic
+ * (128-row x 256-weight-row tiles from 64 rows on, 32-row tiles for 9-63;
+ * up to 8 rows the weight-streaming kernels); 1: the 32-row tiles at every
+ * row count the tiled kernels serve; 2: the large tiles there; 3: automatic,
+ * with the large tiles in their 4-wave form (one wave per SIMD).
+ * Process-wide; results are within the same fp32 tolerance either way (the
+ * sums are taken in a different order).  Takes effect for launch sequences
+ * recorded afterwards (switch graphs off, or use a new handle, to apply it
+ * to shapes already recorded).
+ * Errors: INVALID_ARG (route outside 0..3). */
 spec_status spec_gemm_route(int32_t route);
 
 /* Release the handle: host memory, events, recorded graphs and the private

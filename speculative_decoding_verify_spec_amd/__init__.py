@@ -35,7 +35,7 @@ SPEC_FLAG_LAYOUT = 8
 EXPORTED = [
     "spec_workspace_bytes", "spec_kv_cache_bytes", "spec_verify_init", "spec_verify_step",
     "spec_verify_step_ragged", "spec_accept", "spec_accept_ragged", "spec_device_errors", "spec_profile_enable", "spec_profile_read",
-    "spec_profile_gemm", "spec_graph_enable", "spec_gemm_route", "spec_accept_chain_static", "spec_set_block_table", "spec_verify_destroy",
+    "spec_profile_gemm", "spec_profile_stream_read", "spec_graph_enable", "spec_gemm_route", "spec_accept_chain_static", "spec_set_block_table", "spec_verify_destroy",
     "spec_status_str",
     "spec_recurrent_verify", "spec_recurrent_commit", "spec_recurrent_commit_verify",
 ]
@@ -109,6 +109,8 @@ def lib():
     L.spec_profile_gemm.argtypes = [vp, C.c_char_p, i32, i32, vp, C.POINTER(C.c_double),
                                     C.POINTER(C.c_double)]
     L.spec_profile_gemm.restype = i32
+    L.spec_profile_stream_read.argtypes = [vp, C.c_size_t, C.c_size_t, i32, i32, i32, vp, C.POINTER(C.c_double)]
+    L.spec_profile_stream_read.restype = i32
     L.spec_graph_enable.argtypes = [vp, i32]
     L.spec_graph_enable.restype = i32
     L.spec_gemm_route.argtypes = [i32]
@@ -262,6 +264,17 @@ def spec_profile_gemm(h, cls: str, rows: int, iters: int, stream=None):
     _check("spec_profile_gemm", lib().spec_profile_gemm(h, cls.encode(), int(rows), int(iters),
                                                         _stream(stream), C.byref(ms), C.byref(nbytes)))
     return ms.value, nbytes.value
+
+
+def spec_profile_stream_read(buf, read_bytes: int, iters: int, grid: int, unroll: int, stream=None):
+    """Average launch-to-end microseconds of a plain streaming read of
+    `read_bytes` from the device buffer `buf` (a tensor), windows rotating
+    through it."""
+    us = C.c_double(0.0)
+    nbytes = buf.numel() * buf.element_size()
+    _check("spec_profile_stream_read", lib().spec_profile_stream_read(
+        _ptr(buf), nbytes, int(read_bytes), int(iters), int(grid), int(unroll), _stream(stream), C.byref(us)))
+    return us.value
 
 
 def spec_set_block_table(h, table, pages_per_seq: int):

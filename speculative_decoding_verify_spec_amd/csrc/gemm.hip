@@ -688,7 +688,9 @@ bool gemm_is_kstat(int K) { return K <= KSTAT_WAVES * KSTAT_SPW * 512; }
 // vector kernel) but slower on small matrices and at M <= 2 (QKV 18.8 vs
 // 16.9 us and O 12.2 vs 10.7 us at M = 4), where its activation prologue is
 // not amortised.  So: matrix cores from M = 5 on, and from M = 3 on for
-// matrices of at least 64 Mi weights (gate/up, LM head).
+// matrices of at least 64 Mi weights (gate/up, LM head).  At 5-8 rows they
+// beat the 32-row tiles on every projection (6 rows: gate/up 45.3 against
+// 53.6 us, LM head 182 against 194, QKV 20.5 against 24.5).
 bool gemm_use_mfma(const GemmParams& p, int rows) {
   if (p.wdtype != 1 || (p.K & 127) || p.K > KSTAT_WAVES * 8 * 128) return false;
   const double elems = (double)(p.epi == EPI_SWIGLU ? 2 * p.F : p.N) * p.K;
@@ -749,12 +751,14 @@ static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
     if (gemm_use_split(p)) return launch_split<MT>(p, s);
   }
   if (gemm_use_mfma(p, p.M)) {
-    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_QKV) {
       // the two largest weight streams take 8 waves of 4 chunks: gate/up
       // with one workgroup per CU (39.6 -> 38.2 us at 4 rows), the LM head
-      // with three (171.6 -> 166 us)
+      // with three (171.6 -> 166 us); QKV (here from 5 rows on) like gate/up:
+      // 20.5 us at 6 rows against 33.9 with 4 waves and 24.5 on the 32-row
+      // tiles
       if (p.K <= 8 * 4 * 128) {
-        const int slots8 = (EPI == EPI_SWIGLU ? 1 : 3) * device_cus();
+        const int slots8 = (EPI == EPI_STORE ? 3 : 1) * device_cus();
         const int rounds8 = (groups + slots8 - 1) / slots8;
         launch_mfma_cpw<MT, EPI, 4, 8>(p, (groups + rounds8 - 1) / rounds8, s);
         return hipGetLastError();

@@ -1,5 +1,5 @@
-// Tiled GEMM for many activation rows (5 or more for the QKV, gate/up and LM
-// head projections, more than 8 for the residual ones):
+// Tiled GEMM for many activation rows (more than 8; up to 8 the
+// weight-streaming kernels are faster on every 8B projection):
 // Y[m][n] = sum_k X[m][k] W[n][k]
 // on the 16x16x32 bf16 matrix instruction, with the fp32 activations split
 // into bf16 hi + lo (two products per tile) so they keep ~2^-16 relative
@@ -165,14 +165,6 @@ __global__ __launch_bounds__(256) void gemm_split_x_kernel(GemmParams p) {
     __syncthreads();
     if (threadIdx.x == 0) p.xs_ssq[m * SSQ_BLK + blk] = red[0] + red[1] + red[2] + red[3];
   }
-}
-
-// RMSNorm factor of activation row m from its partial sums of squares
-DEVI float row_factor(const GemmParams& p, int m) {
-  const int nblk = (p.K + 1023) / 1024;
-  float q = 0.f;
-  for (int b = 0; b < nblk; ++b) q += p.xs_ssq[m * SSQ_BLK + b];
-  return 1.0f / sqrtf(q / (float)p.K + p.eps);
 }
 
 // LDS tile rows are 128 bytes (64 bf16 of k) in eight 16-byte chunks; chunk
@@ -435,19 +427,27 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 // ---------------------------------------------------------------- large tiles
 // Many rows (64 or more: the windows of 16+ sequences, token trees, long
 // verify windows of a batch): the contraction is dense enough that the
-// matrix cores and the LDS, not the weight stream, bound it.  A workgroup of
-// 4 waves owns BIG_BM = 128 activation rows and BIG_NP = 128 pairs (256
-// weight rows); the waves form a 2 x 2 grid of 64 rows x 64 pairs.  Per 16-k
-// step a wave reads 2 + 2 activation fragments (hi, lo) and 4 weight
-// fragments (a and b rows) from LDS and issues 16 32x32x16 products: 512
-// bytes of LDS per 32k flops, half of what the 32-row tiles need, so the LDS
-// read rate stays near 64 B per clock per CU at the matrix-core peak.
+// matrix cores and the LDS, not the weight stream, bound it.  A workgroup
+// owns BIG_BM = 128 activation rows and BIG_NP = 128 pairs (256 weight
+// rows).  Its 8 waves (two per SIMD) form a 2 x 4 grid of 64 rows x 32
+// pairs; per 16-k step a wave reads 2 + 2 activation fragments (hi, lo) and
+// 2 weight fragments (a and b rows) from LDS and issues 8 32x32x16 products.
+// (A 4-wave form, a 2 x 2 grid of 64 x 64 with one wave per SIMD, reads 8
+// fragments per 16 products; it is kept as a measurement option and runs
+// 4-7% slower.)
 //
 // Stages of 64 k (512 LDS rows of 128 bytes: 256 weight rows, then 128 hi
 // and 128 lo activation rows) are requested two stages ahead into a ring of
-// two register sets (16 chunks of 16 bytes per thread) and written to one of
-// two LDS buffers (128 KB).  The main loop is unrolled by two and
-// branch-free, so every wait names exactly the loads it needs.
+// two register sets and written one stage ahead to one of two LDS buffers
+// (128 KB).  The main loop is unrolled by two and branch-free, so every wait
+// names exactly the loads it needs.
+//
+// What bounds it (8B gate/up at 512 rows, measured with parts of the step
+// removed in a copy of this kernel): the products alone take 61% of the full
+// time, and the loads alone hide completely behind them; the LDS traffic is
+// the rest.  LDS moves about 144 bytes per clock per CU for 16-byte reads and
+// about 73 for 16-byte writes, so a stage's 192 KB of operand reads and 64 KB
+// of writes take about as long as its products (2048 clocks per SIMD).
 //
 // LDS rows are swizzled so that the 16 rows of one operand read hit distinct
 // banks in groups of 8 lanes (32 banks) and of 16 lanes (64 banks): chunk c
@@ -463,7 +463,6 @@ constexpr int BIG_BM = 128;
 constexpr int BIG_NP = 128;
 constexpr int BIG_WR = 2 * BIG_NP;
 constexpr int BIG_ROWS = BIG_WR + 2 * BIG_BM;  // LDS rows per stage
-constexpr int BIG_CH = BIG_ROWS * 8 / 256;     // 16-byte chunks per thread per stage
 constexpr int BIG_STAGE = BIG_ROWS * 64;       // bf16 elements per LDS stage
 
 DEVI int big_g(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -485,8 +484,28 @@ DEVI void sched_pairs8() {
 // Buffer resource word 3 of the gfx9 family (raw buffer, 32-bit data format).
 constexpr int BUF_WORD3 = 0x00020000;
 
-template <int EPI, bool NORM, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tiles_m, int nsplit, int ntiles) {
+// Per sub-step of a wave with 8 products: product k is followed by one
+// instruction of class A while k < NA and one of class B while k < NB.
+template <int NA, int A, int NB, int B>
+DEVI void sched_mix8() {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    if constexpr (NA > 0) if (k < NA) __builtin_amdgcn_sched_group_barrier(A, 1, 0);
+    if constexpr (NB > 0) if (k < NB) __builtin_amdgcn_sched_group_barrier(B, 1, 0);
+  }
+}
+
+// NW = 8 (the default): a 2 x 4 grid of 64 rows x 32 pairs, two waves per
+// SIMD, so that one wave's operand reads, requests and LDS writes run while
+// the other's products keep the matrix core busy.  NW = 4: a 2 x 2 grid of
+// 64 rows x 64 pairs, one wave per SIMD.
+template <int EPI, bool NORM, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_big_kernel(GemmParams p, int tiles_m, int nsplit, int ntiles) {
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int RSTEP = NT / 8;               // stage rows between a thread's chunks
+  constexpr int BIG_CH = BIG_ROWS * 8 / NT;   // 16-byte chunks per thread per stage
+  constexpr int UB = NW == 4 ? 2 : 1;         // 32-pair blocks per wave
   // the two stage buffers are separate arrays, so the compiler can tell the
   // next stage's LDS writes from this stage's reads and interleave them
   __shared__ __attribute__((aligned(16))) uint16_t s_b0[BIG_STAGE];
@@ -508,9 +527,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wp = w >> 1;
-  const int l16 = lane & 15, lg = lane >> 4;
 
-  // ---- the thread's chunks: stage row r = tid/8 + 32 i, chunk q = tid % 8;
+  // ---- the thread's chunks: stage row r = tid/8 + RSTEP i, chunk q = tid % 8;
   // byte offsets of the chunk's first k from the weight base (i < 8) or the
   // activation planes' base (i >= 8).  32-bit byte offsets let every load
   // take a scalar base plus a vector offset (weights up to 4 GB).
@@ -518,7 +536,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   const int q = tid & 7;
 #pragma unroll
   for (int i = 0; i < BIG_CH; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = (tid >> 3) + RSTEP * i;
     if (r < BIG_WR) {
       const int jl = r % BIG_NP;
       const int j = p0 + jl;
@@ -534,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
       off[i] = (((uint32_t)plane * (uint32_t)p.M + (uint32_t)m) * (uint32_t)p.K + 8 * q) * 2u;
     }
   }
-  // LDS byte offset of the thread's chunk 0; chunk i is 4096 i further
+  // LDS byte offset of the thread's chunk 0; chunk i is 128 RSTEP i further
   // (g depends on r & 15 only, which is the same for every i)
   const int r0 = tid >> 3;
   const int dst0 = r0 * 128 + 16 * (q ^ big_g(r0));
@@ -547,7 +565,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.xs, (short)0, (int)((size_t)2 * p.M * p.K * 2), BUF_WORD3);
 
-  u32x4 ring[2][BIG_CH];
+  constexpr int R = 2;  // register stages in flight (a third measured 5% slower)
+  u32x4 ring[R][BIG_CH];
   auto fetch = [&](int st, auto sl) {
     constexpr int S = decltype(sl)::value;
     const int so = (sbeg + st) * TK * 2;
@@ -556,7 +575,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
       // plain loads: a weight tile is read by the row tiles running beside it
       // on the same XCD (a non-temporal hint measured 5-15% slower), the
       // activation planes by every weight tile
-      if (i < BIG_WR / 32) ring[S][i] = __builtin_amdgcn_raw_buffer_load_b128(wres, off[i], so, 0);
+      if (i < BIG_WR / RSTEP) ring[S][i] = __builtin_amdgcn_raw_buffer_load_b128(wres, off[i], so, 0);
       else ring[S][i] = __builtin_amdgcn_raw_buffer_load_b128(xres, off[i], so, 0);
     }
   };
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
     constexpr int S = decltype(sl)::value;
     char* lds = buf(bf);
 #pragma unroll
-    for (int i = 0; i < BIG_CH; ++i) *(u32x4*)(lds + dst0 + 4096 * i) = ring[S][i];
+    for (int i = 0; i < BIG_CH; ++i) *(u32x4*)(lds + dst0 + 128 * RSTEP * i) = ring[S][i];
   };
 
   // 32x32x16 products: lane l holds operand row (or pair) l % 32 at k
@@ -576,11 +595,12 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   // 8 (i / 4) + 4 (l / 32) + i % 4.  Eight accumulators of 16 floats (rather
   // than 32 of 4) let the compiler keep every accumulator in place across
   // the loop.
-  floatx16 acc[2][2][2];  // [row tile of 32][pair block of 32][a, b]
+  floatx16 acc[2][UB][2];  // [row tile of 32][pair block of 32][a, b]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b][0] = acc[a][b][1] = floatx16{};
+    for (int b = 0; b < UB; ++b) acc[a][b][0] = acc[a][b][1] = floatx16{};
+  const int pw = 32 * UB * wp;  // the wave's first pair in the tile
 
   const int l32 = lane & 31, lh = lane >> 5;
   const int gl = big_g(l32);
@@ -589,25 +609,28 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
 #pragma unroll
     for (int ss = 0; ss < 4; ++ss) {
       const char* cb = base + 16 * ((2 * ss + lh) ^ gl);
-      shortx8 ah[2], al[2], ba[2], bb[2];
+      shortx8 ah[2], al[2], ba[UB], bb[UB];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         ah[t] = *(const shortx8*)(cb + (BIG_WR + 64 * wm + 32 * t) * 128);
         al[t] = *(const shortx8*)(cb + (BIG_WR + BIG_BM + 64 * wm + 32 * t) * 128);
-        ba[t] = *(const shortx8*)(cb + (64 * wp + 32 * t) * 128);
-        bb[t] = *(const shortx8*)(cb + (BIG_NP + 64 * wp + 32 * t) * 128);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        ba[u] = *(const shortx8*)(cb + (pw + 32 * u) * 128);
+        bb[u] = *(const shortx8*)(cb + (BIG_NP + pw + 32 * u) * 128);
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < UB; ++u) {
           acc[t][u][0] = mfma32x32x16(ah[t], ba[u], acc[t][u][0]);
           acc[t][u][1] = mfma32x32x16(ah[t], bb[u], acc[t][u][1]);
         }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < UB; ++u) {
           acc[t][u][0] = mfma32x32x16(al[t], ba[u], acc[t][u][0]);
           acc[t][u][1] = mfma32x32x16(al[t], bb[u], acc[t][u][1]);
         }
@@ -615,10 +638,12 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  // step st: request stage st + 2 into the ring slot stage st came from,
-  // multiply stage st (LDS buffer st % 2), write stage st + 1 from its ring
-  // slot to the other buffer.  A request past the last stage re-reads it and
-  // a write past it fills a buffer nobody reads, so the steps are branch-free.
+  using C2 = std::integral_constant<int, 2>;
+  // step st: request stage st + R into the ring slot stage st came from
+  // (slot st % R), multiply stage st (LDS buffer st % 2), write stage st + 1
+  // from its ring slot to the other buffer.  A request past the last stage
+  // re-reads it and a write past it fills a buffer nobody reads, so the steps
+  // are branch-free.
   //
   // With one wave per SIMD the matrix core idles whenever the wave issues
   // anything else between two products, so the step's 64 other instructions
@@ -627,29 +652,57 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
   // the first two sub-steps, the LDS writes (which wait for the requests of
   // the step before) in the last two.
   auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);  // operand reads of sub-step 0
-    sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 0: reads of 1, requests
-    sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 1: reads of 2, requests
-    sched_pairs8<SG_DS_READ, SG_DS_WRITE>();    // sub-step 2: reads of 3, LDS writes
-    sched_pairs8<SG_DS_WRITE, 0>();             // sub-step 3: LDS writes
+    if constexpr (NW == 4) {
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);  // operand reads of sub-step 0
+      sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 0: reads of 1, requests
+      sched_pairs8<SG_DS_READ, SG_VMEM_READ>();   // sub-step 1: reads of 2, requests
+      sched_pairs8<SG_DS_READ, SG_DS_WRITE>();    // sub-step 2: reads of 3, LDS writes
+      sched_pairs8<SG_DS_WRITE, 0>();             // sub-step 3: LDS writes
+    } else {
+      // 8 products, 6 operand reads per sub-step; 8 requests and 8 LDS writes
+      // per step
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+      sched_mix8<6, SG_DS_READ, 4, SG_VMEM_READ>();
+      sched_mix8<6, SG_DS_READ, 4, SG_VMEM_READ>();
+      sched_mix8<6, SG_DS_READ, 4, SG_DS_WRITE>();
+      sched_mix8<4, SG_DS_WRITE, 0, 0>();
+    }
   };
-  auto step = [&](int st, auto sl, auto sl1) {
-    fetch(min(st + 2, nst - 1), sl);
-    mult(sl);
-    put(sl1, sl1);
+  auto step = [&](int st, auto sl, auto bf, auto sl1, auto bf1) {
+    fetch(min(st + R, nst - 1), sl);
+    mult(bf);
+    put(sl1, bf1);
     interleave();
     lds_barrier();  // orders LDS only: the ring's loads stay in flight
   };
   fetch(0, C0{});
   fetch(min(1, nst - 1), C1{});
+  if constexpr (R == 3) fetch(min(2, nst - 1), C2{});
   put(C0{}, C0{});
   lds_barrier();
   int st = 0;
-  for (; st + 2 <= nst; st += 2) {
-    step(st, C0{}, C1{});
-    step(st + 1, C1{}, C0{});
+  if constexpr (R == 2) {
+    for (; st + 2 <= nst; st += 2) {
+      step(st, C0{}, C0{}, C1{}, C1{});
+      step(st + 1, C1{}, C1{}, C0{}, C0{});
+    }
+    if (st < nst) step(st, C0{}, C0{}, C1{}, C1{});
+  } else {
+    // (slot, buffer) of stage st repeat every 6 stages
+    for (; st + 6 <= nst; st += 6) {
+      step(st, C0{}, C0{}, C1{}, C1{});
+      step(st + 1, C1{}, C1{}, C2{}, C0{});
+      step(st + 2, C2{}, C0{}, C0{}, C1{});
+      step(st + 3, C0{}, C1{}, C1{}, C0{});
+      step(st + 4, C1{}, C0{}, C2{}, C1{});
+      step(st + 5, C2{}, C1{}, C0{}, C0{});
+    }
+    if (st < nst) step(st, C0{}, C0{}, C1{}, C1{});
+    if (st + 1 < nst) step(st + 1, C1{}, C1{}, C2{}, C0{});
+    if (st + 2 < nst) step(st + 2, C2{}, C0{}, C0{}, C1{});
+    if (st + 3 < nst) step(st + 3, C0{}, C1{}, C1{}, C0{});
+    if (st + 4 < nst) step(st + 4, C1{}, C0{}, C2{}, C1{});
   }
-  if (st < nst) step(st, C0{}, C1{});
 
   // ---- epilogue: lane l holds pair l % 32 of each pair block, rows
   // 8 (i / 4) + 4 (l / 32) + i % 4 of each row tile
@@ -662,8 +715,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p, int tile
       fac[t][i] = (NORM && !SPLIT && m < p.M) ? row_factor(p, m) : 1.0f;
     }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = p0 + 64 * wp + 32 * u + l32;
+  for (int u = 0; u < UB; ++u) {
+    const int j = p0 + pw + 32 * u + l32;
     if (j >= npairs) continue;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -704,6 +757,23 @@ int big_splits(int tiles, int nst, int cus, size_t per_split_floats, size_t part
   return best;
 }
 
+template <int EPI, int NW>
+hipError_t launch_big_nw(const GemmParams& p, hipStream_t s, bool norm, int nsplit, int tiles_m, int ntiles,
+                         int grid) {
+  if (nsplit == 1) {
+    if (norm) gemm_big_kernel<EPI, true, false, NW><<<grid, 64 * NW, 0, s>>>(p, tiles_m, 1, ntiles);
+    else gemm_big_kernel<EPI, false, false, NW><<<grid, 64 * NW, 0, s>>>(p, tiles_m, 1, ntiles);
+    return hipGetLastError();
+  }
+  gemm_big_kernel<EPI, false, true, NW><<<grid, 64 * NW, 0, s>>>(p, tiles_m, nsplit, ntiles);
+  const int npairs = pair_count<EPI, BIG_NP>(p);
+  const size_t n = (size_t)p.M * npairs;
+  const int blocks = (int)((n + 255) / 256);
+  if (norm) gemm_tiled_finish_kernel<EPI, true, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
+  else gemm_tiled_finish_kernel<EPI, false, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_big(const GemmParams& p, hipStream_t s) {
   const int npairs = pair_count<EPI, BIG_NP>(p);
@@ -716,17 +786,8 @@ hipError_t launch_big(const GemmParams& p, hipStream_t s) {
   const int grid = ((ntiles + 7) / 8) * 8;
   const bool norm = p.norm_g != nullptr;
   launch_split_x(p, s);
-  if (nsplit == 1) {
-    if (norm) gemm_big_kernel<EPI, true, false><<<grid, 256, 0, s>>>(p, tiles_m, 1, ntiles);
-    else gemm_big_kernel<EPI, false, false><<<grid, 256, 0, s>>>(p, tiles_m, 1, ntiles);
-    return hipGetLastError();
-  }
-  gemm_big_kernel<EPI, false, true><<<grid, 256, 0, s>>>(p, tiles_m, nsplit, ntiles);
-  const size_t n = (size_t)p.M * npairs;
-  const int blocks = (int)((n + 255) / 256);
-  if (norm) gemm_tiled_finish_kernel<EPI, true, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
-  else gemm_tiled_finish_kernel<EPI, false, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
-  return hipGetLastError();
+  if (gemm_route == 3) return launch_big_nw<EPI, 4>(p, s, norm, nsplit, tiles_m, ntiles, grid);
+  return launch_big_nw<EPI, 8>(p, s, norm, nsplit, tiles_m, ntiles, grid);
 }
 
 // Row blocks by row count: up to 32 rows one block with the waves split over
@@ -742,10 +803,6 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Measured on the 8B layer shapes (back-to-back launches): from 5 rows on the
-// tiled kernel beats the skinny matrix-core kernel on the QKV, gate/up and LM
-// head GEMMs (gate/up 48 vs 58 us at 5..8 rows); the residual GEMMs (O, down)
-// gain only beyond 8 rows.
 hipError_t launch_split_x(const GemmParams& p, hipStream_t s) {
   const dim3 grid((p.K + 1023) / 1024, p.M);
   if (p.norm_g) gemm_split_x_kernel<true><<<grid, 256, 0, s>>>(p);
@@ -761,7 +818,7 @@ size_t gemm_big_part_floats(int M, size_t npairs, int K, int cus) {
 
 // Which tiles serve an M-row launch: the large tiles from 64 rows on, unless
 // a measurement override is set (gemm_route: 1 = 32-row tiles, 2 = large
-// tiles wherever the tiled kernels run).
+// tiles wherever the tiled kernels run, 3 = the large tiles' 4-wave form).
 int gemm_route = 0;
 bool gemm_big_rows(const GemmParams& p) {
   // buffer offsets are 32-bit: the weight matrix and the planes stay below 2 GB
@@ -773,7 +830,7 @@ bool gemm_big_rows(const GemmParams& p) {
 
 bool gemm_tiled_ok(const GemmParams& p) {
   if (p.wdtype != 1 || p.K % TK || p.K > SSQ_BLK * 1024 || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;
-  return p.M > 8 || (p.M >= 5 && p.epi != EPI_RESID);
+  return p.M > 8;
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s) {

@@ -88,19 +88,29 @@ struct GemmParams {
 };
 constexpr int GEMM_KSPLIT = 2;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
+
+// RMSNorm factor of activation row m from the activation split's partial
+// sums of squares (added in a fixed order)
+__device__ __forceinline__ float row_factor(const GemmParams& p, int m) {
+  const int nblk = (p.K + 1023) / 1024;
+  float q = 0.f;
+  for (int b = 0; b < nblk; ++b) q += p.xs_ssq[m * SSQ_BLK + b];
+  return 1.0f / sqrtf(q / (float)p.K + p.eps);
+}
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // the residual GEMM of these parameters runs as K slices + reduce
 bool gemm_use_split(const GemmParams& p);
 // the launch of these parameters can complete its activation rows from
 // deferred partial sums (xpart / xout)
 bool gemm_takes_xpart(const GemmParams& p);
-// the tiled kernel for M > 8 (bf16 weights, K a multiple of 64)
+// the tiled kernels for M > 8 (bf16 weights, K a multiple of 64)
 bool gemm_tiled_ok(const GemmParams& p);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s);
 // the large-tile kernel serves this launch (64 or more rows, or the override)
 bool gemm_big_rows(const GemmParams& p);
 // measurement override of the tile choice: 0 automatic, 1 the 32-row tiles,
-// 2 the large tiles (set through spec_gemm_route)
+// 2 the large tiles, 3 the large tiles' 4-wave form (set through
+// spec_gemm_route)
 extern int gemm_route;
 // the activation planes of the tiled kernels ([2][M][K] in p.xs, row sums of
 // squares in p.xs_ssq)

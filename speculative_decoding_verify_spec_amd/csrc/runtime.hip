@@ -849,7 +849,7 @@ spec_status spec_graph_enable(spec_handle* h, int32_t enable) {
 }
 
 spec_status spec_gemm_route(int32_t route) {
-  if (route < 0 || route > 2) return SPEC_ERR_INVALID_ARG;
+  if (route < 0 || route > 3) return SPEC_ERR_INVALID_ARG;
   sv::gemm_route = route;
   return SPEC_OK;
 }

@@ -150,7 +150,7 @@ def test_recurrent_calls_reject_bad_arguments_without_device():
 
 def test_gemm_route_argument_checked():
     L = S.lib()
-    assert L.spec_gemm_route(3) == -1 and L.spec_gemm_route(-1) == -1
+    assert L.spec_gemm_route(4) == -1 and L.spec_gemm_route(-1) == -1
     assert L.spec_gemm_route(0) == 0
 
 
@@ -170,3 +170,24 @@ def test_static_accept_rejects_before_any_launch():
     assert L.spec_accept_chain_static(*args(2, 4, S.SPEC_STATIC_MAX_VOCAB + 1)) == -3
     samp.top_p = 0.9
     assert L.spec_accept_chain_static(*args(2, 4, 1000)) == -4              # top-p needs the handle's scratch
+
+
+def test_stream_read_hook_rejects_before_any_launch():
+    """The streaming-read measurement hook checks sizes and alignment on the
+    host; an address that is never dereferenced stands in for device memory."""
+    L = S.lib()
+    us = C.c_double(0.0)
+    fake = 1 << 40  # 4096-aligned, never touched: every call below is rejected first
+    bad = [
+        (None, 1 << 20, 4096, 1, 1, 4),          # null buffer
+        (fake, 1 << 20, 4096, 1, 1, 5),          # unroll not 4 or 8
+        (fake + 16, 1 << 20, 4096, 1, 1, 4),     # buffer not 4096-aligned
+        (fake, 1 << 20, 4100, 1, 1, 4),          # read size not a multiple of 16
+        (fake, (1 << 20) + 8, 4096, 1, 1, 4),    # buffer size not a multiple of 16
+        (fake, 8192, 4096, 1, 1, 4),             # buffer below read + 8192
+        (fake, 1 << 20, 4096, 0, 1, 4),          # iters < 1
+        (fake, 1 << 20, 4096, 1, 0, 4),          # grid < 1
+    ]
+    for args in bad:
+        assert L.spec_profile_stream_read(*args, None, C.byref(us)) == S.SPEC_ERR_INVALID_ARG, args
+    assert L.spec_profile_stream_read(fake, 1 << 20, 4096, 1, 1, 4, None, None) == S.SPEC_ERR_INVALID_ARG

@@ -1,7 +1,8 @@
-"""Parity of the tiled GEMM paths (5 or more rows) with the oracle: the
+"""Parity of the tiled GEMM paths (9 or more rows) with the oracle: the
 128-row x 256-weight-row tiles that serve 64 or more rows (with their K
-slices when the tiles do not fill the chip) and the 32-row tiles below, each
-forced onto row counts of the other through spec_gemm_route, on the 8B layer
+slices when the tiles do not fill the chip; 8 waves, and the 4-wave form)
+and the 32-row tiles below, each forced onto row counts of the other through
+spec_gemm_route, and the weight-streaming kernels at 6 and 8 rows, on the 8B layer
 layout (d = 4096, 32 / 8 heads of 128, bf16) with a short and a full-width
 FFN.  Row counts span several tiles and ragged tails (136 = 128 + 8 rows,
 468 = 3 tiles + 84 rows).  Bars: logits per row max|dz| / max|z| <= 1e-3
@@ -19,17 +20,22 @@ from tests.gpu_util import bf16_close, build_engine, dev, logits_rel_err, oracle
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # shape, B, T, tree branching, route (0 automatic, 1 32-row tiles, 2 large tiles)
+    # shape, B, T, tree branching, route (0 automatic, 1 32-row tiles, 2 large
+    # tiles, 3 large tiles in the 4-wave form)
     ("MINI8B", 16, 4, None, 0),     # M = 64: one row tile
     ("MINI8B", 32, 4, None, 0),     # M = 128
     ("MINI8B", 17, 8, None, 0),     # M = 136: a second row tile of 8 rows
     ("MINI8B", 4, 117, [4, 4, 2, 2], 0),  # M = 468: token trees
     ("MINI8B", 128, 4, None, 0),    # M = 512
     ("MINI8B", 10, 4, None, 2),     # M = 40 on the large tiles (one padded row tile)
-    ("MINI8B", 3, 3, None, 2),      # M = 9
+    ("MINI8B", 3, 3, None, 2),      # M = 9 on the large tiles
     ("MINI8B", 32, 4, None, 1),     # M = 128 on the 32-row tiles
     ("FFN8B", 32, 4, None, 0),      # full-width FFN, K = 14336 for the down projection
     ("FFN8B", 20, 7, None, 0),      # M = 140
+    ("MINI8B", 32, 4, None, 3),     # M = 128, 4-wave large tiles
+    ("MINI8B", 17, 8, None, 3),     # M = 136, 4-wave large tiles, ragged row tile
+    ("MINI8B", 1, 6, None, 0),      # M = 6: the weight-streaming kernels (no tiles up to 8 rows)
+    ("MINI8B", 1, 8, None, 0),      # M = 8
 ]
 
 
