@@ -251,31 +251,36 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
       vraw[sl][dt] = (k8 < kend) ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
     }
   };
+  // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
+  // g*DG + 8*ks + e for k-step ks.  Their loads go out before the key block's:
+  // behind it they arrived last and held up the first products (B=1, T=4,
+  // ctx 2048: 8.6 -> 7.3 us with the queries taken out entirely).
+  float4 qraw[QT][DG / 4];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qi = (qg * QT + qt) * 16 + j;
+    const int i = (qi < nqb ? qi : 0) / G, gg = (qi < nqb ? qi : 0) % G;
+    const float* src = p.q + (((size_t)(rs + i)) * p.Hq + kvh * G + gg) * D + g * DG;
+#pragma unroll
+    for (int e = 0; e < DG; e += 4) qraw[qt][e / 4] = *(const float4*)(src + e);
+  }
 #pragma unroll
   for (int sl = 0; sl < PFB; ++sl) {
     const int kb0 = kbeg + 32 * kw + sl * 32 * WPG;
     if (kb0 < kend) load_block(kb0, sl);
   }
 
-  // ---- queries: B operand of S^T = K Q^T; lane (j, g) holds query j's dims
-  // g*DG + 8*ks + e for k-step ks.
   shortx8 qhi[QT][KSTEPS], qlo[QT][KSTEPS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int qi = (qg * QT + qt) * 16 + j;
     float qv[DG];
-    if (qi < nqb) {
-      const int i = qi / G, gg = qi % G;
-      const float* src = p.q + (((size_t)(rs + i)) * p.Hq + kvh * G + gg) * D + g * DG;
+    const float sc = qi < nqb ? p.scale : 0.f;  // queries past the sequence's are zeros
 #pragma unroll
-      for (int e = 0; e < DG; e += 4) {
-        float4 v = *(const float4*)(src + e);
-        qv[e] = v.x * p.scale; qv[e + 1] = v.y * p.scale;
-        qv[e + 2] = v.z * p.scale; qv[e + 3] = v.w * p.scale;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < DG; ++e) qv[e] = 0.f;
+    for (int e = 0; e < DG; e += 4) {
+      const float4 v = qraw[qt][e / 4];
+      qv[e] = v.x * sc; qv[e + 1] = v.y * sc;
+      qv[e + 2] = v.z * sc; qv[e + 3] = v.w * sc;
     }
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -744,12 +749,14 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
 
 // One workgroup per (row i, KV head, sequence); wave gg handles query head
 // kvh * G + gg.  Lanes read the split statistics in parallel (two splits per
-// lane); every split's output is requested before any is weighted, and the
-// weights reach the lanes by shuffles, so the only waits are the loads.
-template <int D>
+// lane) and, in the same round of requests, the outputs of up to NF splits
+// (all of them for NF >= nsplit), so the kernel waits for memory once; the
+// weights reach the lanes by shuffles.  More splits than NF are added in
+// further rounds of U.
+template <int D, int NF>
 __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   constexpr int PL = D / 64;  // dims per lane
-  constexpr int U = 8;        // splits whose outputs are in flight at once
+  constexpr int U = 8;        // splits per round beyond the first NF
   const int i = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, gg = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
@@ -772,6 +779,15 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
       ls[c] = p.part_ml[2 * (sp * stride + q0) + 1];
     }
   }
+  // the first NF splits' outputs, requested with the statistics
+  float v0[NF][PL];
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const int sp = u < ns ? u : ns - 1;
+    const float* src = p.part_o + (sp * stride + q0) * D;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) v0[u][e] = src[lane + 64 * e];
+  }
   float mloc = -INFINITY;
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -788,7 +804,15 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   float acc[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-  for (int sp0 = 0; sp0 < ns; sp0 += U) {
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const float wsp = __shfl(u < 64 ? wt[0] : wt[1], u & 63, 64);
+    if (u < ns) {
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] += wsp * v0[u][e];
+    }
+  }
+  for (int sp0 = NF; sp0 < ns; sp0 += U) {
     float v[U][PL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -817,10 +841,18 @@ hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s) {
   const int G = p.Hq / p.Hkv;
   if (G > 8 || p.nsplit > 128) return hipErrorInvalidValue;
   dim3 grid(p.T, p.Hkv, p.B);
-  if (p.D == 128)
-    attn_combine_kernel<128><<<grid, 64 * G, 0, s>>>(p);
-  else
-    attn_combine_kernel<64><<<grid, 64 * G, 0, s>>>(p);
+  // the splits' outputs all in one round of requests when they fit (32 x 2
+  // floats per lane at D = 128)
+  if (p.D == 128) {
+    if (p.nsplit <= 16) attn_combine_kernel<128, 16><<<grid, 64 * G, 0, s>>>(p);
+    else if (p.nsplit <= 24) attn_combine_kernel<128, 24><<<grid, 64 * G, 0, s>>>(p);
+    else if (p.nsplit <= 32) attn_combine_kernel<128, 32><<<grid, 64 * G, 0, s>>>(p);
+    else attn_combine_kernel<128, 8><<<grid, 64 * G, 0, s>>>(p);
+  } else {
+    if (p.nsplit <= 16) attn_combine_kernel<64, 16><<<grid, 64 * G, 0, s>>>(p);
+    else if (p.nsplit <= 32) attn_combine_kernel<64, 32><<<grid, 64 * G, 0, s>>>(p);
+    else attn_combine_kernel<64, 8><<<grid, 64 * G, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
