@@ -89,7 +89,9 @@ typedef struct spec_config {
   int32_t weight_dtype;
   int32_t max_batch, max_ctx, max_rows_per_seq;
   /* KV cache layout.  kv_page_size 0: dense, per layer K [max_batch][Hkv]
-   * [max_ctx][D] and V [max_batch][Hkv][D][max_ctx].  kv_page_size 64: paged
+   * [max_ctx][D] and V [max_batch][Hkv][max_ctx / 64][D][64] (values
+   * transposed within blocks of 64 slots: the layout of a page, so a block's
+   * values are one contiguous run).  kv_page_size 64: paged
    * (PagedAttention, CS349E Lecture 6's reading list; the page size of the
    * ninfer sweep page), a pool of kv_pages pages shared by all sequences,
    * per layer K [kv_pages][Hkv][64][D] and V [kv_pages][Hkv][D][64]; each
@@ -133,8 +135,9 @@ size_t spec_workspace_bytes(const spec_config* cfg);
 
 /* Bytes of the bf16 KV cache: [L][2][max_batch][Hkv][max_ctx * D].
  * The K half stores each head's keys as [max_ctx][D] (row per position,
- * keys already rotated); the V half stores each head's values transposed,
- * [D][max_ctx].  Returns 0 for an invalid config. */
+ * keys already rotated); the V half stores each head's values transposed
+ * within blocks of 64 positions, [max_ctx / 64][D][64].  Returns 0 for an
+ * invalid config. */
 size_t spec_kv_cache_bytes(const spec_config* cfg);
 
 /* Create a handle.

@@ -19,7 +19,8 @@ Weight order (one device pointer per entry, row-major [out, in]):
 
 KV cache: one bf16 buffer [L][2][max_batch][Hkv][max_ctx * D].  The K half
 holds each head's keys row by row ([max_ctx][D]); the V half holds each
-head's values transposed ([D][max_ctx]).
+head's values transposed within blocks of 64 positions ([max_ctx/64][D][64],
+the layout of a page of the paged cache).
 """
 from __future__ import annotations
 
@@ -162,13 +163,28 @@ def kv_cache_numel(shape: ModelShape, max_batch: int, max_ctx: int) -> int:
     return shape.n_layers * 2 * max_batch * shape.n_kv_heads * max_ctx * shape.head_dim
 
 
+KV_BLOCK = 64  # positions per V block (the page size)
+
+
+def kv_v_blocks(cache: torch.Tensor, shape: ModelShape, max_batch: int, max_ctx: int):
+    """The V half of the flat bf16 cache as stored: [L, B, Hkv, max_ctx/64, D, 64]
+    (a view: writes go to the cache)."""
+    L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    c = cache.view(L, 2, max_batch, H, max_ctx * D)
+    return c[:, 1].view(L, max_batch, H, max_ctx // KV_BLOCK, D, KV_BLOCK)
+
+
 def kv_views(cache: torch.Tensor, shape: ModelShape, max_batch: int, max_ctx: int):
-    """K view [L, B, Hkv, max_ctx, D] and V view [L, B, Hkv, D, max_ctx] of the
-    flat bf16 cache buffer."""
+    """K view [L, B, Hkv, max_ctx, D] of the flat bf16 cache buffer, and V as
+    [L, B, Hkv, D, max_ctx] (values transposed, positions in order).  K is a
+    view of the buffer; V is a copy gathered from its 64-position blocks, for
+    reading (write V through kv_v_blocks)."""
     L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
     c = cache.view(L, 2, max_batch, H, max_ctx * D)
     k = c[:, 0].view(L, max_batch, H, max_ctx, D)
-    v = c[:, 1].view(L, max_batch, H, D, max_ctx)
+    vb = kv_v_blocks(cache, shape, max_batch, max_ctx)
+    v = torch.empty((L, max_batch, H, D, max_ctx), dtype=cache.dtype, device=cache.device)
+    v.view(L, max_batch, H, D, max_ctx // KV_BLOCK, KV_BLOCK).copy_(vb.permute(0, 1, 2, 4, 3, 5))
     return k, v
 
 
@@ -180,7 +196,8 @@ def make_kv_cache(shape: ModelShape, max_batch: int, max_ctx: int, ctx_len, seed
     length show up as non-finite output."""
     n = kv_cache_numel(shape, max_batch, max_ctx)
     cache = torch.full((n,), float("nan") if poison_tail else 0.0, dtype=torch.bfloat16, device=device)
-    k, v = kv_views(cache, shape, max_batch, max_ctx)
+    k, _ = kv_views(cache, shape, max_batch, max_ctx)
+    vb = kv_v_blocks(cache, shape, max_batch, max_ctx)
     g = _gen(seed, device)
     if isinstance(ctx_len, int):
         ctx_len = [ctx_len] * max_batch
@@ -192,7 +209,12 @@ def make_kv_cache(shape: ModelShape, max_batch: int, max_ctx: int, ctx_len, seed
             kk = torch.randn((H, c, D), generator=g, device=device) * KV_STD
             vv = torch.randn((H, D, c), generator=g, device=device) * KV_STD
             k[l, b, :, :c, :] = kk.to(torch.bfloat16)
-            v[l, b, :, :, :c] = vv.to(torch.bfloat16)
+            # positions [0, c) of V into the 64-position blocks (block j holds
+            # positions 64 j .. 64 j + 63 as [D][64])
+            nb = (c + KV_BLOCK - 1) // KV_BLOCK
+            vt = vb[l, b, :, :nb].permute(0, 2, 1, 3).reshape(H, D, nb * KV_BLOCK).clone()  # positions in order
+            vt[:, :, :c] = vv.to(torch.bfloat16)
+            vb[l, b, :, :nb] = vt.view(H, D, nb, KV_BLOCK).permute(0, 2, 1, 3)
     return cache
 
 

@@ -119,6 +119,8 @@ def _round(model, B, ctx, T, tokens, q, sample, parent=None, temp=1.0, seed=7, p
         sl = slice(b, b + 1)
         if parent is not None:
             # the commit copied path node j's K/V to slot kv_len + j, in place
+            # (the views again: V is gathered into a copy when it is taken)
+            k, v = synth.kv_views(cache, sh, B, max_ctx)
             ka = synth.to_numpy_raw(k[:, b:b + 1])
             va = synth.to_numpy_raw(v[:, b:b + 1])
             path = orc["paths"][b] if nacc_h[b] == orc["n_accepted"][b] else None
