@@ -196,21 +196,55 @@ struct QkvStage {
   float sn[MT][64];
 };
 
-template <int MT>
-DEVI void stage_qkv(const GemmParams& p, QkvStage<MT>* st) {
-  const int half = p.D / 2;
-  for (int t = threadIdx.x; t < MT * 64; t += blockDim.x) {
-    const int m = t / 64, i = t % 64;
-    if (m >= p.M) continue;
-    const int mg = p.m0 + m;
-    if (i < half) {
-      const int ps = p.pos[mg];
-      st->cs[m][i] = p.rope_cos[(size_t)ps * half + i];
-      st->sn[m][i] = p.rope_sin[(size_t)ps * half + i];
+// The staging in three steps, for a prologue that must not wait on memory
+// before its weight loads are out: the positions and slots are requested
+// first (pos), the rotary values once the weights have been requested (rope;
+// it waits only for the positions, the oldest loads), and the LDS stores
+// come last (store).  Thread t of NT holds items t, t + NT, ...
+template <int MT, int NT>
+struct QkvPre {
+  static constexpr int IT = (MT * 64 + NT - 1) / NT;
+  int ps[IT], sl[IT];
+  float c[IT], s[IT];
+  DEVI void pos(const GemmParams& p) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int t = threadIdx.x + k * NT, m = t / 64;
+      ps[k] = 0;
+      sl[k] = 0;
+      if (m < MT && m < p.M) {
+        ps[k] = p.pos[p.m0 + m];
+        if (t % 64 == 0) sl[k] = p.slot[p.m0 + m];
+      }
     }
-    if (i == 0) st->slot[m] = p.slot[mg];
   }
-}
+  DEVI void rope(const GemmParams& p) {
+    const int half = p.D / 2;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int t = threadIdx.x + k * NT, m = t / 64, i = t % 64;
+      c[k] = s[k] = 0.f;
+      if (m < MT && m < p.M && i < half) {
+        c[k] = p.rope_cos[(size_t)ps[k] * half + i];
+        s[k] = p.rope_sin[(size_t)ps[k] * half + i];
+      }
+    }
+  }
+  DEVI void store(const GemmParams& p, QkvStage<MT>* st) const {
+    const int half = p.D / 2;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int t = threadIdx.x + k * NT, m = t / 64, i = t % 64;
+      if (m < MT && m < p.M) {
+        if (i < half) {
+          st->cs[m][i] = c[k];
+          st->sn[m][i] = s[k];
+        }
+        if (i == 0) st->slot[m] = sl[k];
+      }
+    }
+  }
+};
 
 // Epilogue for row group rg from the finished sums tot[y * MT + m].  `st`:
 // the QKV stage in LDS, or null to read those inputs from global memory.
@@ -289,7 +323,9 @@ DEVI void epilogue(const GemmParams& p, int rg, const float* tot, const QkvStage
 }
 
 // ---------------------------------------------------------------- k-stationary
-template <int MT, typename WT, int EPI, bool NORM, int NW>
+// XP: the launch completes its activation rows from deferred partial sums
+// (GemmParams::xpart; QKV with the fused norm only).
+template <int MT, typename WT, int EPI, bool NORM, int NW, bool XP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
   constexpr int NVP = MaxPow2<MT>::v;
   constexpr int SPW = KSTAT_WAVES * KSTAT_SPW / NW;  // K steps per wave
@@ -328,7 +364,53 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
   };
   int rg = blockIdx.x;
 
-  if constexpr (EPI == EPI_QKV) stage_qkv<MT>(p, &qst);
+  // ---- prologue.  Everything the first row group needs is requested before
+  // any of it is consumed: the rows' positions (QKV), this wave's activation
+  // slice (with the deferred partial sums), the norm gain, then the first
+  // group's weights, and the rotary values, which need the positions.  A
+  // value consumed in between would make the wave wait for it, and for every
+  // load requested before it, before the weights are even asked for.
+  QkvPre<MT, 64 * NW> qpre;
+  if constexpr (EPI == EPI_QKV) qpre.pos(p);
+  float4 xa[SPW][MT][2];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float* xs = p.X + (size_t)(m < p.M ? m : 0) * p.ldx + kofs[i];
+      xa[i][m][0] = *(const float4*)xs;
+      xa[i][m][1] = *(const float4*)(xs + 4);
+    }
+  // the deferred reduce of the previous residual GEMM
+  constexpr int NSL = XP ? GEMM_KSPLIT : 1;
+  float4 pa[SPW][MT][NSL][2];
+  if constexpr (XP) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          const float* ps = p.xpart + ((size_t)(sl * 8 + (m < p.M ? m : 0))) * p.ldx + kofs[i];
+          pa[i][m][sl][0] = *(const float4*)ps;
+          pa[i][m][sl][1] = *(const float4*)(ps + 4);
+        }
+  }
+  float4 ga[SPW][2];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+      ga[i][0] = *(const float4*)(p.norm_g + kofs[i]);
+      ga[i][1] = *(const float4*)(p.norm_g + kofs[i] + 4);
+    }
+  }
+  // the first row group's weights (a workgroup without a group reads rows
+  // clamped into range and never uses them)
+  load_group(rg);
+  if constexpr (EPI == EPI_QKV) qpre.rope(p);
+  // nothing is scheduled across this point: left alone, the compiler adds the
+  // partial sums (waiting for them) before the weight loads are issued
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- this wave's activation slice, kept in registers
   float xr[SPW][MT][8];
@@ -337,20 +419,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const bool ok = kok[i] && (m < p.M);
-      const int mm = m < p.M ? m : 0;
-      const float* xs = p.X + (size_t)mm * p.ldx + kofs[i];
-      float4 a = *(const float4*)xs;
-      float4 b = *(const float4*)(xs + 4);
-      if (p.xpart) {
-        // the deferred reduce of the previous residual GEMM, in its order
+      float4 a = xa[i][m][0], b = xa[i][m][1];
+      if constexpr (XP) {
+        // the partial sums in slice order, their sum added to the row
         float4 ta = make_float4(0.f, 0.f, 0.f, 0.f), tb = ta;
 #pragma unroll
-        for (int sl = 0; sl < GEMM_KSPLIT; ++sl) {
-          const float* ps = p.xpart + ((size_t)(sl * 8 + mm)) * p.ldx + kofs[i];
-          const float4 pa = *(const float4*)ps;
-          const float4 pb = *(const float4*)(ps + 4);
-          ta.x += pa.x; ta.y += pa.y; ta.z += pa.z; ta.w += pa.w;
-          tb.x += pb.x; tb.y += pb.y; tb.z += pb.z; tb.w += pb.w;
+        for (int sl = 0; sl < NSL; ++sl) {
+          const float4 qa = pa[i][m][sl][0], qb = pa[i][m][sl][1];
+          ta.x += qa.x; ta.y += qa.y; ta.z += qa.z; ta.w += qa.w;
+          tb.x += qb.x; tb.y += qb.y; tb.z += qb.z; tb.w += qb.w;
         }
         a.x += ta.x; a.y += ta.y; a.z += ta.z; a.w += ta.w;
         b.x += tb.x; b.y += tb.y; b.z += tb.z; b.w += tb.w;
@@ -366,9 +443,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
       xr[i][m][6] = ok ? b.z : 0.f; xr[i][m][7] = ok ? b.w : 0.f;
     }
   }
-  // the first row group's weights follow the activation loads, which would
-  // otherwise queue behind them (O at 4 rows: 9.9 -> 9.4 us)
-  if (rg < ngroups) load_group(rg);
   if constexpr (NORM) {
     // RMSNorm of the activation rows: the gain multiplies the registers now;
     // the row factor needs every wave's sum of squares and is applied to the
@@ -385,15 +459,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_kstat_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const float4 ga = *(const float4*)(p.norm_g + kofs[i]);
-      const float4 gb = *(const float4*)(p.norm_g + kofs[i] + 4);
-      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      const float g[8] = {ga[i][0].x, ga[i][0].y, ga[i][0].z, ga[i][0].w,
+                          ga[i][1].x, ga[i][1].y, ga[i][1].z, ga[i][1].w};
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 8; ++e) xr[i][m][e] *= g[e];
     }
   }
+  // the rotary values reach LDS before the first group's reduction barrier
+  if constexpr (EPI == EPI_QKV) qpre.store(p, &qst);
 
   for (; rg < ngroups; rg += gridDim.x) {
     // Each weight register is refilled with the next row group's weights as
@@ -507,7 +582,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_mfma_kernel(Gem
     }
   };
 
-  if constexpr (EPI == EPI_QKV) stage_qkv<MT>(p, &qst);
+  // the rows' positions first (QKV): the rotary loads that need them are
+  // issued after the weights (see QkvPre)
+  QkvPre<MT, 64 * NW> qpre;
+  if constexpr (EPI == EPI_QKV) qpre.pos(p);
   // activations (times the norm gain), split into bf16 hi + lo
   shortx4 xh[CPW][MG][2], xl[CPW][MG][2];
   float ss[MG];
@@ -545,6 +623,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void gemm_mfma_kernel(Gem
   // the first group's weights follow the activation loads, which would
   // otherwise queue behind them (gate/up at 4 rows: 38.5 -> 37.9 us)
   first_group();
+  if constexpr (EPI == EPI_QKV) {
+    qpre.rope(p);
+    qpre.store(p, &qst);  // read after the first group's reduction barrier
+  }
   if constexpr (NORM) {
     // per-wave sums of x^2 of each activation row (lanes with the same r)
 #pragma unroll
@@ -803,11 +885,14 @@ static hipError_t launch_mte(const GemmParams& p, hipStream_t s) {
       const int slots = (EPI == EPI_QKV ? 1 : 2) * device_cus();
       const int rounds8 = (groups + slots - 1) / slots;
       const int grid8 = (groups + rounds8 - 1) / rounds8;
+      const bool xp = EPI == EPI_QKV && p.xpart;
       if (p.wdtype == 1) {
-        if (p.norm_g) gemm_kstat_kernel<MT, uint16_t, EPI, true, 8><<<grid8, 64 * 8, 0, s>>>(p);
+        if (xp) gemm_kstat_kernel<MT, uint16_t, EPI, true, 8, EPI == EPI_QKV><<<grid8, 64 * 8, 0, s>>>(p);
+        else if (p.norm_g) gemm_kstat_kernel<MT, uint16_t, EPI, true, 8><<<grid8, 64 * 8, 0, s>>>(p);
         else gemm_kstat_kernel<MT, uint16_t, EPI, false, 8><<<grid8, 64 * 8, 0, s>>>(p);
       } else {
-        if (p.norm_g) gemm_kstat_kernel<MT, float, EPI, true, 8><<<grid8, 64 * 8, 0, s>>>(p);
+        if (xp) gemm_kstat_kernel<MT, float, EPI, true, 8, EPI == EPI_QKV><<<grid8, 64 * 8, 0, s>>>(p);
+        else if (p.norm_g) gemm_kstat_kernel<MT, float, EPI, true, 8><<<grid8, 64 * 8, 0, s>>>(p);
         else gemm_kstat_kernel<MT, float, EPI, false, 8><<<grid8, 64 * 8, 0, s>>>(p);
       }
     } else if (p.wdtype == 1) {
