@@ -817,251 +817,376 @@ __global__ __launch_bounds__(128) void accept_tree_greedy_kernel(AcceptParams p)
   stash_tree_path(p, b, path, s_plen);
 }
 
-// Sampled tree walk, one workgroup per sequence.  At node v the running target
-// r starts as p_v and the draft q' as q_v.  Child c (token x, uniform slot
-// c - 1) is accepted when u * q'(x) < r(x).  A rejection replaces r by
-// norm(max(0, r - q')) (a pass over the vocabulary into one of two ping-pong
-// buffers) and, without replacement, removes x from q' and renormalises.  No
-// child accepted: draw from r; a leaf reached: bonus from p_leaf (slot T - 1).
-__global__ __launch_bounds__(1024) void accept_tree_sampled_kernel(AcceptParams p) {
-  __shared__ int first_child[128], next_sib[128], path[128], removed[128], spar[128];
+// ---------------------------------------------------------------- sampled tree walk
+// At node v the running target r starts as p_v and the running draft q' as
+// q_v.  Child c (token x, uniform slot c - 1) is accepted when
+// u * q'(x) < r(x).  A rejection replaces r by norm(max(0, r - q')) (kept as
+// it was if that has no mass) and, without replacement, removes x from q'
+// and renormalises it.  No child accepted: draw from r; a leaf reached:
+// bonus from p_leaf (slot T - 1).
+//
+// The residual has a closed form.  With U_0 = p, N_0 = 1 and r_k = U_k / N_k,
+// rejecting under q' = s_k q (s_k = 1, or 1 / the q mass of the tokens not
+// yet removed; removed tokens have q' = 0) gives
+//   U_k(y) = max(0, U_{k-1}(y) - N_{k-1} s_k q(y)),   N_k = sum_y U_k(y).
+// Since max(0, max(0, a - b q) - c q) = max(0, a - (b + c) q) for q >= 0, a
+// token not removed before step k has U_k(y) = max(0, p(y) - A_k q(y)) with
+// A_k = A_{k-1} + N_{k-1} s_k, and a removed token keeps the value it had
+// when it was removed.  So a rejection costs one reduction over the
+// vocabulary, N_k, and nothing is written per token.  The walk runs as a
+// short sequence of launches: each step launch has one workgroup per
+// (vocabulary chunk, sequence); every workgroup first replays the decisions
+// up to the next rejection (a few lookups, identical in all of them), then
+// sums its chunk for that rejection's shift; the next launch combines the
+// chunk sums.  The kernel boundary orders the sums before their use, and
+// the state passes between launches in two alternating copies (chunk 0's
+// workgroup writes the one the next launch reads).  A pick kernel draws the
+// final token from the last pass's chunk sums and a scan of one chunk, and
+// finishes, in one workgroup, a walk that needs more passes than launches.
+constexpr int TW_N = 128;   // nodes per tree
+constexpr int TW_STEPS = 12;  // step launches (a walk passes at most sum of children on its path + 1 times)
+struct TwTree {
+  int first_child[TW_N], next_sib[TW_N];
+};
+struct __align__(16) TwState {
+  int v, plen, child;  // current node, path length, next child to test (-1: none left)
+  int pend;            // 0 decisions to make, 1 rejection pass summed, 2 draw pass wanted, 3 draw pass summed
+  int nrem, pend_x, draw_buf, pad;
+  float M, S;          // softmax statistics of node v's row
+  float A, An;         // residual shift, shift of the summed rejection pass
+  double N, qtot;      // residual mass; q mass of node v's row (-1 until the first pass sums it)
+  int path[TW_N];
+  int rem_tok[TW_N];   // removed tokens (distinct), their p, q and kept residual value
+  float rem_p[TW_N], rem_q[TW_N], rem_val[TW_N];
+};
+struct TwSeq {
+  TwTree tree;
+  TwState st[2];
+};
+// [B] TwSeq, then [2][B][nch] chunk sums (residual mass, q mass)
+size_t tree_walk_bytes(int B, int nch) { return (size_t)B * sizeof(TwSeq) + (size_t)2 * B * nch * sizeof(double2); }
+DEVI TwSeq* tw_seq(const AcceptParams& p, int b) { return (TwSeq*)p.twalk + b; }
+DEVI double2* tw_sums(const AcceptParams& p, int buf, int b) {
+  return (double2*)((char*)p.twalk + (size_t)p.B * sizeof(TwSeq)) + ((size_t)buf * p.B + b) * p.nch;
+}
+// copies of the state between global memory and LDS, 16 bytes per thread
+DEVI void tw_copy(TwState* dst, const TwState* src) {
+  static_assert(sizeof(TwState) % 16 == 0, "state copied in 16-byte words");
+  for (int i = threadIdx.x; i < (int)(sizeof(TwState) / 16); i += blockDim.x) ((uint4*)dst)[i] = ((const uint4*)src)[i];
+}
+
+DEVI int tw_removed(const TwState& s, int x) {
+  for (int i = 0; i < s.nrem; ++i)
+    if (s.rem_tok[i] == x) return i;
+  return -1;
+}
+// the running draft's scale: 1 / the q mass left (0 when none is)
+DEVI float tw_qscale(const AcceptParams& p, const TwState& s) {
+  if (p.replacement || s.nrem == 0) return 1.f;
+  double qm = 0.0;
+  for (int i = 0; i < s.nrem; ++i) qm += (double)s.rem_q[i];
+  const double left = s.qtot - qm;
+  return left > 0.0 ? (float)(1.0 / left) : 0.f;
+}
+
+// Combine the chunk sums of the rejection pass (shift An), then drop the
+// rejected token from the draft.  One thread.
+DEVI void tw_finalize(const AcceptParams& p, int b, TwState& s, const double2* part) {
+  const int row = b * p.T + s.v;
+  double tu = 0.0, tq = 0.0;
+  for (int c0 = 0; c0 < p.nch; c0 += 16) {
+    double2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < p.nch ? part[c0 + i] : make_double2(0.0, 0.0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      tu += v[i].x;
+      tq += v[i].y;
+    }
+  }
+  if (s.qtot < 0.0) s.qtot = tq;
+  // the removed tokens keep their values: take out what the pass counted
+  for (int i = 0; i < s.nrem; ++i)
+    tu += (double)s.rem_val[i] - (double)fmaxf(0.f, s.rem_p[i] - s.An * s.rem_q[i]);
+  if (tu > 0.0) {
+    s.A = s.An;
+    s.N = tu;
+  }
+  const int x = s.pend_x;
+  if (!p.replacement && tw_removed(s, x) < 0) {
+    const float px = pval(p, row_rule(p, row), p.logits[(size_t)row * p.V + x], x, s.M, s.S);
+    const float qx = p.q[(size_t)row * p.V + x];
+    const int n = s.nrem;
+    s.rem_tok[n] = x;
+    s.rem_p[n] = px;
+    s.rem_q[n] = qx;
+    s.rem_val[n] = fmaxf(0.f, px - s.A * qx);
+    s.nrem = n + 1;
+  }
+}
+
+// Test children until a rejection needs a pass (pend 1 after its sum) or the
+// walk ends (pend 2: the draw pass).  One thread.
+DEVI void tw_decide(const AcceptParams& p, int b, TwState& s, const TwTree& tr) {
+  while (s.pend == 0) {
+    const int row = b * p.T + s.v;
+    const int c = s.child;
+    if (c < 0) {  // every child rejected: draw from the residual
+      s.pend = 2;
+      return;
+    }
+    bool bad;
+    const int x = clamp_token(p, p.tokens[b * p.T + c], bad);
+    const float u = philox_uniform(p.seed, p.round, b, c - 1);
+    const float px = pval(p, row_rule(p, row), p.logits[(size_t)row * p.V + x], x, s.M, s.S);
+    const float qraw = p.q[(size_t)row * p.V + x];
+    const int ri = p.replacement ? -1 : tw_removed(s, x);
+    const float rx = (float)((double)(ri >= 0 ? s.rem_val[ri] : fmaxf(0.f, px - s.A * qraw)) / s.N);
+    const bool shrunk = !p.replacement && s.nrem > 0;
+    const float qx = shrunk ? (ri >= 0 ? 0.f : qraw * tw_qscale(p, s)) : qraw;
+    if (!bad && u * qx < rx) {
+      // accepted: node c's own target and draft start afresh
+      s.v = c;
+      s.path[s.plen++] = c;
+      s.A = 0.f;
+      s.N = 1.0;
+      s.nrem = 0;
+      s.qtot = -1.0;
+      float M, S;
+      row_ms(p, b * p.T + c, M, S);
+      s.M = M;
+      s.S = S;
+      s.child = tr.first_child[c];
+      if (s.child < 0) {  // a leaf: bonus from its target
+        s.pend = 2;
+        return;
+      }
+      continue;
+    }
+    s.An = (float)((double)s.A + s.N * (double)(shrunk ? tw_qscale(p, s) : 1.f));
+    s.pend_x = x;
+    s.pend = 1;
+  }
+}
+
+// Sum over tokens [y0, y1) of row `row` of max(0, p(y) - A q(y)) (p(y) itself
+// for A = 0) and, with need_q, of q(y); all threads, ends synchronised.
+DEVI double2 tw_chunk_sum(const AcceptParams& p, int row, float A, bool need_q, float M, float S, int y0, int y1,
+                          double* shd) {
+  const float* z = p.logits + (size_t)row * p.V;
+  const float* qv = p.q + (size_t)row * p.V;
+  const RowRule rr = row_rule(p, row);
+  const bool useq = A != 0.f || need_q;
+  double su = 0.0, sq = 0.0;
+  constexpr int PER = CH / 256;
+  for (int yb = y0; yb < y1; yb += 256 * PER) {
+    float zr[PER], qr[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int y = yb + threadIdx.x + 256 * e;
+      zr[e] = y < y1 ? z[y] : 0.f;
+      qr[e] = (useq && y < y1) ? qv[y] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int y = yb + threadIdx.x + 256 * e;
+      if (y < y1) {
+        su += (double)fmaxf(0.f, pval(p, rr, zr[e], y, M, S) - A * qr[e]);
+        sq += (double)qr[e];
+      }
+    }
+  }
+  su = block_sum(su, shd);
+  sq = block_sum(sq, shd);
+  __syncthreads();
+  return make_double2(su, need_q ? sq : 0.0);
+}
+
+// Child lists and the walk's first state (one workgroup per sequence).
+__global__ __launch_bounds__(128) void accept_tree_init_kernel(AcceptParams p) {
+  __shared__ int first_child[TW_N], next_sib[TW_N], spar[TW_N];
+  const int b = blockIdx.x;
+  build_tree(p, b, first_child, next_sib, spar);
+  TwSeq* sq = tw_seq(p, b);
+  for (int i = threadIdx.x; i < p.T; i += blockDim.x) {
+    sq->tree.first_child[i] = first_child[i];
+    sq->tree.next_sib[i] = next_sib[i];
+  }
+  if (threadIdx.x == 0) {
+    TwState& s = sq->st[0];
+    s.v = 0;
+    s.plen = 1;
+    s.path[0] = 0;
+    s.child = first_child[0];
+    s.pend = s.child < 0 ? 2 : 0;
+    s.nrem = 0;
+    s.pend_x = 0;
+    s.draw_buf = 0;
+    s.A = 0.f;
+    s.An = 0.f;
+    s.N = 1.0;
+    s.qtot = -1.0;
+    float M, S;
+    row_ms(p, b * p.T, M, S);
+    s.M = M;
+    s.S = S;
+  }
+}
+
+// Step k of the walk: grid (chunks, sequences).
+__global__ __launch_bounds__(256) void accept_tree_step_kernel(AcceptParams p, int k) {
+  __shared__ TwState s;
   __shared__ double shd[16];
-  __shared__ float s_M, s_S, s_Zr, s_qmass, s_qtot;
-  __shared__ int s_cur, s_acc, s_nrem, s_tok;
+  const int c = blockIdx.x, b = blockIdx.y;
+  TwSeq* sq = tw_seq(p, b);
+  tw_copy(&s, &sq->st[k & 1]);
+  __syncthreads();
+  if (threadIdx.x == 0 && s.pend < 2) {
+    if (s.pend == 1) {
+      tw_finalize(p, b, s, tw_sums(p, (k - 1) & 1, b));
+      s.child = sq->tree.next_sib[s.child];
+      s.pend = 0;
+    }
+    tw_decide(p, b, s, sq->tree);
+  }
+  __syncthreads();
+  const int pend = s.pend;
+  if (pend == 1 || pend == 2) {
+    const double2 r = tw_chunk_sum(p, b * p.T + s.v, pend == 1 ? s.An : s.A, pend == 1 && s.qtot < 0.0, s.M, s.S,
+                                   c * CH, min(p.V, (c + 1) * CH), shd);
+    if (threadIdx.x == 0) tw_sums(p, k & 1, b)[c] = r;
+  }
+  if (c == 0) {
+    if (threadIdx.x == 0 && pend == 2) {
+      s.pend = 3;
+      s.draw_buf = k & 1;
+    }
+    __syncthreads();
+    tw_copy(&sq->st[(k + 1) & 1], &s);
+  }
+}
+
+// Final draw (one workgroup per sequence), after `nstep` step launches; walks
+// that were not done by then are finished here, one chunk at a time.
+__global__ __launch_bounds__(256) void accept_tree_pick_kernel(AcceptParams p, int nstep) {
+  __shared__ TwState s;
+  __shared__ double shd[16];
+  __shared__ double2 part[64];
+  __shared__ double csum[64];
+  __shared__ double scan[256];
+  __shared__ int s_chunk, s_tok;
   __shared__ double s_t;
   const int b = blockIdx.x, T = p.T, V = p.V;
-  const float Tt = p.temperature;
-  float* rb0 = p.rbuf + (size_t)b * V;
-  float* rb1 = p.rbuf + ((size_t)p.B + b) * V;
-  build_tree(p, b, first_child, next_sib, spar);
-  int v = 0, plen = 1;
-  if (threadIdx.x == 0) path[0] = 0;
-  while (true) {
-    const int row = b * T + v;
-    const float* z = p.logits + (size_t)row * V;
-    const float* qv = p.q + (size_t)row * V;
+  TwSeq* sq = tw_seq(p, b);
+  tw_copy(&s, &sq->st[nstep & 1]);
+  __syncthreads();
+  const double2* src = tw_sums(p, (nstep - 1) & 1, b);
+  while (s.pend != 3) {
     if (threadIdx.x == 0) {
-      float M, S;
-      row_ms(p, row, M, S);
-      s_M = M; s_S = S; s_cur = -1; s_Zr = 1.f; s_nrem = 0; s_qmass = 0.f; s_qtot = -1.f;
+      if (s.pend == 1) {
+        tw_finalize(p, b, s, src);
+        s.child = sq->tree.next_sib[s.child];
+        s.pend = 0;
+      }
+      tw_decide(p, b, s, sq->tree);
     }
     __syncthreads();
-    int c = first_child[v];
-    int accepted = -1;
-    while (c >= 0) {
-      if (threadIdx.x == 0) {
-        bool bad;
-        const int x = clamp_token(p, p.tokens[b * T + c], bad);
-        const float u = philox_uniform(p.seed, p.round, b, c - 1);
-        const float rx = (s_cur < 0) ? pval(p, row_rule(p, row), z[x], x, s_M, s_S) : (s_cur == 0 ? rb0 : rb1)[x] / s_Zr;
-        float qx = qv[x];
-        if (!p.replacement && s_nrem > 0) {
-          bool gone = false;
-          for (int i = 0; i < s_nrem; ++i) gone |= removed[i] == x;
-          qx = gone ? 0.f : qx / (s_qtot - s_qmass);
-        }
-        s_acc = (!bad && u * qx < rx) ? 1 : 0;
-        removed[s_nrem] = x;  // recorded now, counted only after a rejection
-      }
-      __syncthreads();
-      if (s_acc) { accepted = c; break; }
-      // rejection: r <- max(0, r - q') into the other buffer
-      const int cur = s_cur;
-      const float* src = cur == 1 ? rb1 : rb0;
-      float* dst = cur == 0 ? rb1 : rb0;
-      const float M = s_M, S = s_S, Zr = s_Zr;
-      const int nrem = s_nrem;
-      const float qscale = (!p.replacement && nrem > 0) ? 1.0f / (s_qtot - s_qmass) : 1.0f;
-      const RowRule rr = row_rule(p, row);
-      double zs = 0.0, qs = 0.0;
-      // every token as if still in q'; the removed ones are fixed below.  A
-      // thread's RU elements (a workgroup stride apart) are requested at once.
-      constexpr int RU = 8;
-      const float* rsrc = cur < 0 ? z : src;
-      auto resid = [&](float zy, float qy, int y) {
-        const float ry = cur < 0 ? pval(p, rr, zy, y, M, S) : zy / Zr;
-        qs += (double)qy;
-        const float d = fmaxf(0.f, ry - qy * qscale);
-        zs += (double)d;
-        return d;
-      };
-      if ((V & 3) == 0) {
-        // rows are 16-byte aligned: four tokens per load
-        const int V4 = V >> 2;
-        for (int i0 = threadIdx.x; i0 < V4; i0 += RU * blockDim.x) {
-          float4 zr[RU], qr[RU];
-#pragma unroll
-          for (int u = 0; u < RU; ++u) {
-            const int i = min(i0 + u * (int)blockDim.x, V4 - 1);
-            zr[u] = ((const float4*)rsrc)[i];
-            qr[u] = ((const float4*)qv)[i];
-          }
-#pragma unroll
-          for (int u = 0; u < RU; ++u) {
-            const int i = i0 + u * blockDim.x;
-            if (i < V4) {
-              float4 d;
-              d.x = resid(zr[u].x, qr[u].x, 4 * i);
-              d.y = resid(zr[u].y, qr[u].y, 4 * i + 1);
-              d.z = resid(zr[u].z, qr[u].z, 4 * i + 2);
-              d.w = resid(zr[u].w, qr[u].w, 4 * i + 3);
-              ((float4*)dst)[i] = d;
-            }
-          }
-        }
-      } else {
-        for (int y0 = threadIdx.x; y0 < V; y0 += RU * blockDim.x) {
-          float zr[RU], qr[RU];
-#pragma unroll
-          for (int u = 0; u < RU; ++u) {
-            const int yc = min(y0 + u * (int)blockDim.x, V - 1);
-            zr[u] = rsrc[yc];
-            qr[u] = qv[yc];
-          }
-#pragma unroll
-          for (int u = 0; u < RU; ++u) {
-            const int y = y0 + u * blockDim.x;
-            if (y < V) dst[y] = resid(zr[u], qr[u], y);
-          }
-        }
-      }
-      zs = block_sum(zs, shd);
-      qs = block_sum(qs, shd);
-      if (threadIdx.x == 0) {
-        if (!p.replacement) {
-          // a removed token has q' = 0: its residual is r itself (each
-          // distinct token once; the pass above wrote r - q' there)
-          for (int i = 0; i < nrem; ++i) {
-            const int x = removed[i];
-            bool seen = false;
-            for (int k = 0; k < i; ++k) seen |= removed[k] == x;
-            if (seen) continue;
-            const float rx = cur < 0 ? pval(p, rr, z[x], x, M, S) : src[x] / Zr;
-            const float dx = fmaxf(0.f, rx - qv[x] * qscale);
-            zs += (double)rx - (double)dx;
-            dst[x] = rx;
-          }
-        }
-        if (zs > 0.0) { s_cur = (cur == 0) ? 1 : 0; s_Zr = (float)zs; }
-        if (!p.replacement) {
-          if (s_qtot < 0.f) s_qtot = (float)qs;
-          s_qmass += qv[removed[s_nrem]];
-          s_nrem = s_nrem + 1;
-        }
-      }
-      __syncthreads();
-      c = next_sib[c];
+    const int pend = s.pend;
+    for (int c = 0; c < p.nch; ++c) {
+      const double2 r = tw_chunk_sum(p, b * T + s.v, pend == 1 ? s.An : s.A, pend == 1 && s.qtot < 0.0, s.M, s.S,
+                                     c * CH, min(V, (c + 1) * CH), shd);
+      if (threadIdx.x == 0) part[c] = r;
     }
-    if (accepted < 0) break;
-    v = accepted;
-    if (threadIdx.x == 0) path[plen] = v;
-    ++plen;
-    if (first_child[v] < 0) {
-      // leaf: bonus from p_leaf
-      if (threadIdx.x == 0) {
-        float M, S;
-        row_ms(p, b * T + v, M, S);
-        s_M = M; s_S = S; s_cur = -1; s_Zr = 1.f;
+    src = part;
+    if (threadIdx.x == 0 && pend == 2) {
+      s.pend = 3;
+      s.draw_buf = -1;
+    }
+    __syncthreads();
+  }
+  const double2* dsum = s.draw_buf >= 0 ? tw_sums(p, s.draw_buf, b) : part;
+  const int row = b * T + s.v;
+  const float* z = p.logits + (size_t)row * V;
+  const float* qv = p.q + (size_t)row * V;
+  const RowRule rr = row_rule(p, row);
+  const float A = s.A;
+  // value of token y in the final distribution (unnormalised)
+  auto val = [&](float zy, float qy, int y) {
+    for (int i = 0; i < s.nrem; ++i)
+      if (s.rem_tok[i] == y) return s.rem_val[i];
+    return fmaxf(0.f, pval(p, rr, zy, y, s.M, s.S) - A * qy);
+  };
+  if (threadIdx.x == 0) {
+    for (int c = 0; c < p.nch; ++c) csum[c] = dsum[c].x;
+    // the removed tokens keep their values
+    for (int i = 0; i < s.nrem; ++i)
+      csum[s.rem_tok[i] / CH] += (double)s.rem_val[i] - (double)fmaxf(0.f, s.rem_p[i] - A * s.rem_q[i]);
+    double R = 0.0;
+    for (int c = 0; c < p.nch; ++c) R += csum[c];
+    const double t = (double)philox_uniform(p.seed, p.round, b, T - 1) * R;
+    double cum = 0.0;
+    int pick = -1, last = -1;
+    for (int c = 0; c < p.nch; ++c) {
+      if (csum[c] > 0.0) last = c;
+      if (pick < 0 && cum + csum[c] > t) pick = c;
+      if (pick < 0) cum += csum[c];
+    }
+    // rounding left t at or past the total: the last chunk with mass, whose
+    // last token with mass is taken below
+    s_chunk = pick >= 0 ? pick : (last >= 0 ? last : 0);
+    s_t = pick >= 0 ? t - cum : INFINITY;
+    s_tok = 0x7fffffff;
+  }
+  __syncthreads();
+  // inverse CDF inside the chunk: thread i holds tokens y0 + 16 i .. + 15
+  constexpr int PER = CH / 256;
+  const int y0 = s_chunk * CH + PER * threadIdx.x, y1 = min(V, y0 + PER);
+  float vr[PER];
+  double loc = 0.0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int y = y0 + e;
+    const float zy = y < y1 ? z[y] : 0.f;
+    const float qy = (y < y1 && A != 0.f) ? qv[y] : 0.f;
+    vr[e] = y < y1 ? val(zy, qy, y) : 0.f;
+    loc += (double)vr[e];
+  }
+  scan[threadIdx.x] = loc;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const double add = threadIdx.x >= (unsigned)o ? scan[threadIdx.x - o] : 0.0;
+    __syncthreads();
+    scan[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const double t = s_t;
+  double run = scan[threadIdx.x] - loc;
+  if (run <= t && run + loc > t) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      run += (double)vr[e];
+      if (run > t) {
+        atomicMin(&s_tok, y0 + e);
+        break;
       }
-      __syncthreads();
-      break;
     }
   }
-  // final draw from r (s_cur, s_Zr) or p_v (s_cur < 0) at node v, slot T - 1
-  {
-    const int row = b * T + v;
-    const float* z = p.logits + (size_t)row * V;
-    const int cur = s_cur;
-    const float* src = cur == 1 ? rb1 : rb0;
-    const float M = s_M, S = s_S;
-    const RowRule rr = row_rule(p, row);
-    const float* vsrc = cur < 0 ? z : src;
-    auto val = [&](float x, int y) { return cur < 0 ? pval(p, rr, x, y, M, S) : x; };
-    // thread chunks of a multiple of 4 tokens when rows are 16-byte aligned
-    const bool vec = (V & 3) == 0;
-    const int per = vec ? 4 * (((V >> 2) + blockDim.x - 1) / blockDim.x) : (V + blockDim.x - 1) / blockDim.x;
-    const int y0 = min(V, (int)threadIdx.x * per), y1 = min(V, y0 + per);
-    // the chunk's values in order, DB loads requested at once; f(y, value)
-    // returns true to stop
-    constexpr int DB = 8;
-    auto walk = [&](auto f) {
-      if (vec) {
-        for (int yb = y0; yb < y1; yb += 4 * DB) {
-          float4 c[DB];
+  __syncthreads();
+  if (s_tok == 0x7fffffff) {
+    int lastpos = -1;
 #pragma unroll
-          for (int u = 0; u < DB; ++u) {
-            const int yy = yb + 4 * u;
-            c[u] = yy < y1 ? *(const float4*)(vsrc + yy) : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-#pragma unroll
-          for (int u = 0; u < DB; ++u) {
-            const int yy = yb + 4 * u;
-            if (yy < y1) {
-              if (f(yy, val(c[u].x, yy))) return;
-              if (f(yy + 1, val(c[u].y, yy + 1))) return;
-              if (f(yy + 2, val(c[u].z, yy + 2))) return;
-              if (f(yy + 3, val(c[u].w, yy + 3))) return;
-            }
-          }
-        }
-      } else {
-        for (int yb = y0; yb < y1; yb += DB) {
-          float c[DB];
-#pragma unroll
-          for (int u = 0; u < DB; ++u) c[u] = yb + u < y1 ? vsrc[yb + u] : 0.f;
-#pragma unroll
-          for (int u = 0; u < DB; ++u)
-            if (yb + u < y1 && f(yb + u, val(c[u], yb + u))) return;
-        }
-      }
-    };
-    double loc = 0.0;
-    walk([&](int, float v) {
-      loc += (double)v;
-      return false;
-    });
-    __shared__ double scan[1024];
-    scan[threadIdx.x] = loc;
-    if (threadIdx.x == 0) s_tok = 0x7fffffff;
+    for (int e = 0; e < PER; ++e)
+      if (vr[e] > 0.f) lastpos = y0 + e;
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = -1;
     __syncthreads();
-    for (int o = 1; o < (int)blockDim.x; o <<= 1) {
-      double add = threadIdx.x >= o ? scan[threadIdx.x - o] : 0.0;
-      __syncthreads();
-      scan[threadIdx.x] += add;
-      __syncthreads();
-    }
-    const double R = scan[blockDim.x - 1];
-    if (threadIdx.x == 0) s_t = (double)philox_uniform(p.seed, p.round, b, T - 1) * R;
+    if (lastpos >= 0) atomicMax(&s_last, lastpos);
     __syncthreads();
-    const double t = s_t;
-    double run = scan[threadIdx.x] - loc;
-    if (run <= t && run + loc > t) {
-      walk([&](int y, float v) {
-        run += (double)v;
-        if (run > t) {
-          atomicMin(&s_tok, y);
-          return true;
-        }
-        return false;
-      });
-    }
+    if (threadIdx.x == 0) s_tok = s_last >= 0 ? s_last : 0;
     __syncthreads();
-    if (s_tok == 0x7fffffff) {
-      // rounding: take the last token with positive mass
-      int last = -1;
-      for (int y = y0; y < y1; ++y)
-        if ((cur < 0 ? pval(p, rr, z[y], y, M, S) : src[y]) > 0.f) last = y;
-      __shared__ int s_last;
-      if (threadIdx.x == 0) s_last = -1;
-      __syncthreads();
-      if (last >= 0) atomicMax(&s_last, last);
-      __syncthreads();
-      if (threadIdx.x == 0) s_tok = s_last >= 0 ? s_last : 0;
-      __syncthreads();
-    }
   }
-  write_tree_outputs(p, b, path, plen, s_tok);
-  stash_tree_path(p, b, path, plen);
+  write_tree_outputs(p, b, s.path, s.plen, s_tok);
+  stash_tree_path(p, b, s.path, s.plen);
 }
 
 // Top-k / top-p selection for all rows, in batches of SEL_ROWS rows, then the
@@ -1098,8 +1223,15 @@ hipError_t launch_accept(const AcceptParams& pin, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (adjust && (e = launch_select(p, s)) != hipSuccess) return e;
   if (p.parent) {
-    if (greedy) accept_tree_greedy_kernel<<<p.B, 128, 0, s>>>(p);
-    else accept_tree_sampled_kernel<<<p.B, 1024, 0, s>>>(p);
+    if (greedy) {
+      accept_tree_greedy_kernel<<<p.B, 128, 0, s>>>(p);
+    } else {
+      if (p.T > TW_N || p.nch > 64 || !p.twalk) return hipErrorInvalidValue;
+      accept_tree_init_kernel<<<p.B, 128, 0, s>>>(p);
+      const int nstep = p.T < TW_STEPS ? p.T : TW_STEPS;
+      for (int k = 0; k < nstep; ++k) accept_tree_step_kernel<<<dim3(p.nch, p.B), 256, 0, s>>>(p, k);
+      accept_tree_pick_kernel<<<p.B, 256, 0, s>>>(p, nstep);
+    }
     if (p.kv_len_out) {
       if (p.D > 128 || p.T > TPATH - 2 || !p.tpath) return hipErrorInvalidValue;
       accept_tree_commit_kernel<<<dim3(p.L * p.Hkv, p.B), 128, 0, s>>>(p);

@@ -160,6 +160,8 @@ struct CombineParams {
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- accept
+// scratch bytes of the sampled token-tree walk for B sequences of nch chunks
+size_t tree_walk_bytes(int B, int nch);
 constexpr int TPATH = 130;  // ints per sequence of AcceptParams::tpath (T <= 128)
 struct AcceptParams {
   const float* logits;     // [B][T][V]
@@ -178,7 +180,7 @@ struct AcceptParams {
   float* rowms;            // [B*T][2]
   float* rsum;             // [B][nch]
   int32_t* nacc;           // [B]
-  float* rbuf;             // [2][B][V]
+  void* twalk;             // sampled token-tree walk: tree_walk_bytes(B, nch)
   int32_t* tpath;          // [B][TPATH]: kv_len, path length, accepted tree path (tree commit)
   uint32_t* flags;
   // cache for the tree commit

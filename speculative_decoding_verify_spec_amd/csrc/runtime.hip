@@ -107,7 +107,7 @@ struct StepShape {
 
 struct Layout {
   size_t x, x2, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, rbuf, tpath, fcnt, fmass, fstate, fres,
+  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, twalk, tpath, fcnt, fmass, fstate, fres,
       flags, total;
 };
 
@@ -154,7 +154,7 @@ Layout plan(const spec_config& c) {
   L.rowms = take(Mmax * 2 * 4);
   L.rsum = take((size_t)c.max_batch * nch * 4);
   L.nacc = take((size_t)c.max_batch * 4);
-  L.rbuf = take(2 * (size_t)c.max_batch * c.vocab * 4);
+  L.twalk = take(tree_walk_bytes(c.max_batch, nch));
   L.tpath = take((size_t)c.max_batch * TPATH * 4);
   // top-k / top-p selection: histograms and state are indexed by a batch
   // row below SEL_ROWS in each of two alternating buffers
@@ -656,7 +656,7 @@ spec_status accept_impl(spec_handle* h, AcceptParams ap, const spec_sampling* sa
   ap.temperature = temp; ap.replacement = sampling->tree_replacement ? 1 : 0;
   ap.seed = sampling->seed; ap.round = sampling->round;
   ap.rowstat = h->at<float>(L.rowstat); ap.rowms = h->at<float>(L.rowms); ap.rsum = h->at<float>(L.rsum);
-  ap.nacc = h->at<int32_t>(L.nacc); ap.rbuf = h->at<float>(L.rbuf); ap.tpath = h->at<int32_t>(L.tpath); ap.flags = h->at<uint32_t>(L.flags);
+  ap.nacc = h->at<int32_t>(L.nacc); ap.twalk = h->at<char>(L.twalk); ap.tpath = h->at<int32_t>(L.tpath); ap.flags = h->at<uint32_t>(L.flags);
   ap.kv_cache = h->kv; ap.L = c.n_layers; ap.maxB = c.max_batch; ap.Hkv = c.n_kv_heads; ap.D = c.head_dim;
   ap.max_ctx = c.max_ctx; ap.V = c.vocab; ap.nch = accept_chunks(c.vocab);
   ap.top_k = sampling->top_k; ap.top_p = sampling->top_p;

@@ -169,6 +169,41 @@ def test_tree_accept_matches_oracle(V, B, branching, temp, repl):
     assert near <= max(1, n_total // 10)
 
 
+def test_tree_walk_longer_than_its_step_launches():
+    """A root with 16 children drafted from a far-off draft (sigma 4: each is
+    accepted with probability ~2 Phi(-2) ~ 0.05) needs up to 16 rejection
+    passes plus the draw, more than the step launches the walk gets: the pick
+    kernel finishes those walks in one workgroup, against the same oracle."""
+    V, B, branching = 4099, 4, [16, 1]
+    eng = _engine(V, 4, 128, max_ctx=512)
+    near, n_total, long_walks = 0, 0, 0
+    for r in range(3):
+        seed = 977 + r
+        z, q, tokens, parent = _tree_inputs(B, branching, V, 1.0, 4.0, seed, False)
+        T = parent.shape[1]
+        print(f"[tree walk] V={V} B={B} branching={branching} round {r}", flush=True)
+        kv_len = torch.full((B,), 100, dtype=torch.int32, device=dev())
+        out = torch.full((B, T), -5, dtype=torch.int32, device=dev())
+        nacc = torch.full((B,), -5, dtype=torch.int32, device=dev())
+        eng.accept(z, q, tokens, out, nacc, kv_len, None, tree_parent=parent, temperature=1.0, seed=11 + r,
+                   round_=r, replacement=False)
+        torch.cuda.synchronize()
+        orc = OA.accept(z.double().cpu().numpy(), q.double().cpu().numpy(), tokens.cpu().numpy(), 1.0,
+                        philox.Uniforms(11 + r, r), tree_parent=parent.cpu().numpy(), replacement=False)
+        near += compare_decisions(out.cpu().numpy(), nacc.cpu().numpy(), orc, f"round {r}", draw_band=DRAW_BAND_SHARED)
+        n_total += B
+        assert eng.device_errors() == 0
+        # rejections at the root (children are tested in id order): with the
+        # draw pass, 12 or more take more passes than the 12 step launches
+        for b in range(B):
+            path = orc["paths"][b]
+            rejected = path[1] - 1 if len(path) > 1 else 16
+            long_walks += rejected >= 12
+    print(f"  near-ties {near}/{n_total}, walks past 12 rejections {long_walks}", flush=True)
+    assert long_walks > 0, "no walk needed the one-workgroup finish"
+    assert near <= max(1, n_total // 10)
+
+
 def test_accept_flags_bad_draft_token():
     V, B, gamma = 4099, 2, 3
     eng = _engine(V, 4, 8)
