@@ -7,7 +7,7 @@
 // when every draft survived, a bonus token from p_{gamma+1}.  Greedy
 // (section 7.4): longest prefix where draft == argmax, then that argmax.
 // Token trees (section 10.3): walk from the root, testing each node's children
-// in order against a running residual (see accept_tree_sampled_kernel).
+// in order against a running residual (see the sampled tree walk below).
 //
 // The vocabulary is cut into chunks of CH entries so a handful of rows still
 // fills the GPU:
