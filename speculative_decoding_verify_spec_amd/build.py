@@ -52,6 +52,50 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer variant (device code unchanged): every host
+# function of the runtime instrumented, for the CPU checks of the C ABI.  The
+# sanitizer flags apply to the host compilation only.
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_asan(out_dir: str) -> str:
+    """Build <out_dir>/libspec_verify.so with host ASan; skipped when the
+    sources are unchanged since the last such build.  Returns the path."""
+    import hashlib
+
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                  glob.glob(os.path.join(ROOT, "include", "*.h")))
+    h = hashlib.sha256()
+    for f in srcs:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    key = h.hexdigest()
+    lib = os.path.join(out_dir, "libspec_verify.so")
+    stamp = os.path.join(out_dir, "sources.sha256")
+    if os.path.exists(lib) and os.path.exists(stamp) and open(stamp).read().strip() == key:
+        return lib
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, *ASAN_HOST, "-g", "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    hips = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(hips))) as ex:
+        objs = list(ex.map(one, hips))
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    with open(stamp, "w") as fh:
+        fh.write(key + "\n")
+    return lib
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)
