@@ -60,7 +60,10 @@ def test_abi_and_sizing_under_host_asan(tmp_path):
         assert b"__asan_report_load" in fh.read(), "the library is not instrumented"
     drv = tmp_path / "drive.py"
     drv.write_text(DRIVER)
-    env = dict(os.environ, LD_PRELOAD=ASAN_RT[-1], ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+    # the ASan runtime goes first in the preload list; whatever the environment
+    # already preloads stays after it
+    pre = " ".join(x for x in (ASAN_RT[-1], os.environ.get("LD_PRELOAD", "")) if x)
+    env = dict(os.environ, LD_PRELOAD=pre, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
                PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
     r = subprocess.run([sys.executable, str(drv), lib, os.path.join(ROOT, "tests", "test_abi.py")], cwd=ROOT,
                        env=env, capture_output=True, text=True, timeout=600)
