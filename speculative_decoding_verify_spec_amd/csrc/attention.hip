@@ -834,7 +834,18 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(CombineParams p) {
   float* dst = p.out + ((size_t)m * p.Hq + kvh * G + gg) * D;
   const float inv = 1.0f / l;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) dst[lane + 64 * e] = acc[e] * inv;
+  for (int e = 0; e < PL; ++e) {
+    const float v = acc[e] * inv;
+    dst[lane + 64 * e] = v;
+    if (p.xs) {
+      // the O projection's activation planes, as its split would write them
+      const size_t K = (size_t)p.Hq * D, col = (size_t)(kvh * G + gg) * D + lane + 64 * e;
+      short h, lo;
+      split_bf16(v, h, lo);
+      p.xs[(size_t)m * K + col] = (uint16_t)h;
+      p.xs[((size_t)p.M + m) * K + col] = (uint16_t)lo;
+    }
+  }
 }
 
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s) {

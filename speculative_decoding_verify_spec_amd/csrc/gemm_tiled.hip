@@ -83,7 +83,15 @@ DEVI void epilogue_pair(const GemmParams& p, int m, int j, float a, float b) {
       if (rb < p.N) o[rb] += b;
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    p.out[(size_t)m * p.ldo + j] = a / (1.0f + expf(-a)) * b;
+    const float v = a / (1.0f + expf(-a)) * b;
+    p.out[(size_t)m * p.ldo + j] = v;
+    if (p.xs_out) {
+      // the next GEMM's activation planes, as gemm_split_x_kernel writes them
+      short h, l;
+      split_bf16(v, h, l);
+      p.xs_out[(size_t)m * p.ldo + j] = (uint16_t)h;
+      p.xs_out[((size_t)p.M + m) * p.ldo + j] = (uint16_t)l;
+    }
   } else {
     const int D = p.D, half = D / 2;
     const int hh = ra / D, i = ra % D;
@@ -409,7 +417,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
          (size_t)2 * nsplit * p.M * pair_count<EPI, NPAIR>(p) * 2 <= p.part_floats)
     nsplit *= 2;
   const bool norm = p.norm_g != nullptr;
-  launch_split_x(p, s);
+  if (!p.xs_ready) launch_split_x(p, s);
   const dim3 grid(tiles_n, tiles_m, nsplit);
   if (nsplit == 1) {
     if (norm) gemm_tiled_kernel<MB, KW, R, EPI, true, false><<<grid, 256, 0, s>>>(p);
@@ -785,7 +793,7 @@ hipError_t launch_big(const GemmParams& p, hipStream_t s) {
   const int ntiles = tiles_n * tiles_m * nsplit;
   const int grid = ((ntiles + 7) / 8) * 8;
   const bool norm = p.norm_g != nullptr;
-  launch_split_x(p, s);
+  if (!p.xs_ready) launch_split_x(p, s);
   if (gemm_route == 3) return launch_big_nw<EPI, 4>(p, s, norm, nsplit, tiles_m, ntiles, grid);
   return launch_big_nw<EPI, 8>(p, s, norm, nsplit, tiles_m, ntiles, grid);
 }

@@ -85,6 +85,13 @@ struct GemmParams {
   // split residual GEMM: leave the partial sums in `part` for the next
   // GEMM's prologue instead of launching the reduce
   bool defer_reduce;
+  // Activation planes written by the producer: with xs_ready the launch's
+  // planes in `xs` are already there (written by the kernel that produced X,
+  // with the split's arithmetic) and the tiled launch skips its split; only
+  // without a fused norm.  With xs_out a SiLU*up epilogue also writes the
+  // bf16 hi/lo planes [2][M][ldo] of its outputs, for the next GEMM.
+  bool xs_ready;
+  uint16_t* xs_out;
 };
 constexpr int GEMM_KSPLIT = 2;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
@@ -156,6 +163,10 @@ struct CombineParams {
   int B, T, Hq, Hkv, D;
   const int32_t* rstart;   // ragged rows, as in AttnParams
   const int32_t* rlen;
+  // or null: the bf16 hi/lo planes [2][M][Hq*D] of `out` as the tiled GEMMs'
+  // activation split writes them (M = rows of the step)
+  uint16_t* xs;
+  int M;
 };
 hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
 

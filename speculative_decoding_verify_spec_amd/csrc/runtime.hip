@@ -107,7 +107,7 @@ struct StepShape {
 
 struct Layout {
   size_t x, x2, q, ksuf, vsuf, attn, act, part_o, part_ml, rope_cos, rope_sin;
-  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, twalk, tpath, fcnt, fmass, fstate, fres,
+  size_t tok, pos, slot, anc, kvw, rstart, rlen, rseq, gpart, gxs, gssq, rowstat, rowms, rsum, nacc, twalk, tpath, gxs2, fcnt, fmass, fstate, fres,
       flags, total;
 };
 
@@ -149,6 +149,7 @@ Layout plan(const spec_config& c) {
   L.rseq = take(Mmax * 4);
   L.gpart = take(gemm_part_floats(c) * 4);
   L.gxs = take(gemm_xs_elems(c) * 2);
+  L.gxs2 = take(gemm_xs_elems(c) * 2);  // the down projection's planes, written by gate/up
   L.gssq = take(Mmax * SSQ_BLK * 4);
   L.rowstat = take(Mmax * nch * 2 * 4);
   L.rowms = take(Mmax * 2 * 4);
@@ -255,9 +256,17 @@ KvMap kv_map(const spec_handle* h) {
 void gemm_scratch(const spec_handle* h, GemmParams& p) {
   p.part = h->at<float>(h->lay.gpart);
   p.part_floats = gemm_part_floats(h->cfg);
-  p.xs = h->at<uint16_t>(h->lay.gxs);
+  if (!p.xs_ready || !p.xs) p.xs = h->at<uint16_t>(h->lay.gxs);  // a producer's planes stay
   p.xs_elems = gemm_xs_elems(h->cfg);
   p.xs_ssq = h->at<float>(h->lay.gssq);
+}
+
+// The launch of p over M rows runs on the tiled kernels, which read the
+// activation rows as bf16 hi/lo planes.
+bool rows_tiled(const spec_handle* h, GemmParams p, int M) {
+  gemm_scratch(h, p);
+  p.M = M;
+  return gemm_tiled_ok(p);
 }
 
 hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
@@ -381,25 +390,34 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
                   h->at<float>(L.part_ml), B, T, Hq, Hkv, D, c.max_ctx, splits, scale, rstart, rlen, kv_map(h)};
     e = timed(h, K_ATTN, 0, s, [&] { return launch_attention(ap, s); });
     if (e != hipSuccess) return e;
-    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D, rstart, rlen};
-    e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
-    if (e != hipSuccess) return e;
-
     GemmParams go{};
     go.W = wo; go.wdtype = c.weight_dtype; go.X = at; go.ldx = Hq * D; go.N = d; go.K = Hq * D;
     go.epi = EPI_RESID; go.out = nxt; go.ldo = d;
+    // on the tiled kernels the O projection reads its activation planes, which
+    // the combine writes beside its fp32 output (no split launch)
+    go.xs_ready = rows_tiled(h, go, M);
+    CombineParams cp{h->at<float>(L.part_o), h->at<float>(L.part_ml), nsplit, at, B, T, Hq, Hkv, D, rstart, rlen,
+                     go.xs_ready ? h->at<uint16_t>(L.gxs) : nullptr, M};
+    e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
+    if (e != hipSuccess) return e;
     if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return e;
 
     GemmParams gg{};
     gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = nxt; gg.ldx = d; gg.N = 2 * F; gg.K = d;
     gg.norm_g = g2; gg.eps = c.rms_eps;
     gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
-    if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return e;
-
     GemmParams gd{};
     gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
     gd.epi = EPI_RESID; gd.out = nxt; gd.ldo = d;
     gd.defer_reduce = defer && l + 1 < c.n_layers;
+    if (rows_tiled(h, gg, M) && rows_tiled(h, gd, M)) {
+      // the gate/up epilogue writes the down projection's planes into a second
+      // buffer (gate/up is still reading its own from the first)
+      gg.xs_out = h->at<uint16_t>(L.gxs2);
+      gd.xs = gg.xs_out;
+      gd.xs_ready = true;
+    }
+    if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return e;
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
     cur = nxt;
   }
