@@ -803,40 +803,9 @@ def run_toy(a, dev):
     cache = synth.make_kv_cache(sh, 1, max_ctx, 0, device=dev, poison_tail=False)
     eng = VerifyEngine(sh, w, cache, 1, max_ctx, TOY_PROMPT)
     prompt = synth.make_tokens(1, TOY_PROMPT, sh.vocab, seed=synth.SEED_PROMPT, device=dev)
-    z1 = torch.empty((1, 1, sh.vocab), device=dev)
 
     def live(temp):
-        zp = torch.empty((1, TOY_PROMPT, sh.vocab), device=dev)
-        eng.step(prompt, torch.zeros(1, dtype=torch.int32, device=dev), zp)
-        pending = int(zp[0, -1].argmax())
-        kv = TOY_PROMPT
-        recs = []
-        for r in range(R):
-            kvt = torch.tensor([kv], dtype=torch.int32, device=dev)
-            toks, qs = [pending], []
-            for i in range(gamma):
-                eng.step(torch.tensor([[toks[-1]]], dtype=torch.int32, device=dev), kvt + i, z1)
-                q, zn = synth.noisy_draft_dist(z1[:, 0], a.sigma, synth.SEED_NOISE * 1000 + r * 16 + i,
-                                               temp if temp > 0 else 1.0)
-                x = int(synth.sample_from(q, synth.SEED_DRAFT * 1000 + r * 16 + i)[0, 0]) if temp > 0 \
-                    else int(zn[0].argmax())
-                toks.append(x)
-                qs.append(q)
-            tokens = torch.tensor([toks], dtype=torch.int32, device=dev)
-            qt = torch.stack(qs, 1).contiguous() if temp > 0 else None
-            lg = torch.empty((1, T, sh.vocab), device=dev)
-            out = torch.empty((1, T), dtype=torch.int32, device=dev)
-            nacc = torch.empty((1,), dtype=torch.int32, device=dev)
-            kv_out = torch.empty((1,), dtype=torch.int32, device=dev)
-            eng.step(tokens, kvt, lg)
-            eng.accept(lg, qt, tokens, out, nacc, kvt, kv_out, temperature=temp, seed=synth.SEED_ACCEPT, round_=r)
-            n = int(nacc[0])
-            assert int(kv_out[0]) == kv + n + 1
-            recs.append({"kv": kv, "tokens": tokens, "q": qt, "logits": lg, "out": out, "n": n})
-            pending = int(out[0, n])
-            kv += n + 1
-        torch.cuda.synchronize()
-        return pending, recs
+        return toy_live(eng, sh, prompt, R, temp, a.sigma, dev)
 
     def replay(temp, recs, first):
         lg = torch.empty((1, T, sh.vocab), device=dev)
@@ -917,11 +886,53 @@ def run_toy(a, dev):
         "bound": "latency (the whole model, 12.6 MB of fp32 weights, sits in the caches)",
     }
     if a.cpu_baseline:
-        result["cpu_baseline"], result["near_ties"] = toy_oracle(sh, names, w, prompt, modes, a)
+        result["cpu_baseline"], result["near_ties"] = toy_oracle(sh, names, w, prompt, modes)
     print(json.dumps(result), flush=True)
 
 
-def toy_oracle(sh, names, w, prompt, modes, a):
+def toy_live(eng, sh, prompt, R, temp, sigma, dev):
+    """Prefill the prompt with the step itself, then R live rounds of the toy
+    workload (see run_toy); returns the last pending token and the records."""
+    import torch
+
+    import synth
+
+    gamma, T = TOY_GAMMA, TOY_GAMMA + 1
+    z1 = torch.empty((1, 1, sh.vocab), device=dev)
+    zp = torch.empty((1, TOY_PROMPT, sh.vocab), device=dev)
+    eng.step(prompt, torch.zeros(1, dtype=torch.int32, device=dev), zp)
+    pending = int(zp[0, -1].argmax())
+    kv = TOY_PROMPT
+    recs = []
+    for r in range(R):
+        kvt = torch.tensor([kv], dtype=torch.int32, device=dev)
+        toks, qs = [pending], []
+        for i in range(gamma):
+            eng.step(torch.tensor([[toks[-1]]], dtype=torch.int32, device=dev), kvt + i, z1)
+            q, zn = synth.noisy_draft_dist(z1[:, 0], sigma, synth.SEED_NOISE * 1000 + r * 16 + i,
+                                           temp if temp > 0 else 1.0)
+            x = int(synth.sample_from(q, synth.SEED_DRAFT * 1000 + r * 16 + i)[0, 0]) if temp > 0 \
+                else int(zn[0].argmax())
+            toks.append(x)
+            qs.append(q)
+        tokens = torch.tensor([toks], dtype=torch.int32, device=dev)
+        qt = torch.stack(qs, 1).contiguous() if temp > 0 else None
+        lg = torch.empty((1, T, sh.vocab), device=dev)
+        out = torch.empty((1, T), dtype=torch.int32, device=dev)
+        nacc = torch.empty((1,), dtype=torch.int32, device=dev)
+        kv_out = torch.empty((1,), dtype=torch.int32, device=dev)
+        eng.step(tokens, kvt, lg)
+        eng.accept(lg, qt, tokens, out, nacc, kvt, kv_out, temperature=temp, seed=synth.SEED_ACCEPT, round_=r)
+        n = int(nacc[0])
+        assert int(kv_out[0]) == kv + n + 1
+        recs.append({"kv": kv, "tokens": tokens, "q": qt, "logits": lg, "out": out, "n": n})
+        pending = int(out[0, n])
+        kv += n + 1
+    torch.cuda.synchronize()
+    return pending, recs
+
+
+def toy_oracle(sh, names, w, prompt, modes):
     """The oracle's own prefill and rounds, end to end, against the GPU's live
     rounds (same drafted tokens, q and uniforms; the oracle commits its own
     accepted prefix).  Stops at the first round whose results differ."""

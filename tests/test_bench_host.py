@@ -73,8 +73,7 @@ def test_toy_oracle_replay_agrees_with_itself_and_stops_at_a_planted_difference(
     prompt = synth.make_tokens(1, bench.TOY_PROMPT, sh.vocab, seed=synth.SEED_PROMPT)
     R = 3
     modes = {t: {"recs": _oracle_rounds(sh, names, w, prompt, R, t, bench.TOY_GAMMA)} for t in (1.0, 0.0)}
-    a = type("A", (), {})()
-    base, near = bench.toy_oracle(sh, names, w, prompt, modes, a)
+    base, near = bench.toy_oracle(sh, names, w, prompt, modes)
     for key in ("temperature_1", "greedy"):
         rep = near["end_to_end"][key]
         assert rep["rounds_compared"] == R and rep["first_differing_round"] is None, rep
@@ -85,7 +84,7 @@ def test_toy_oracle_replay_agrees_with_itself_and_stops_at_a_planted_difference(
     rc = modes[0.0]["recs"][1]
     rc["out"] = rc["out"].clone()
     rc["out"][0, rc["n"]] = (int(rc["out"][0, rc["n"]]) + 1) % sh.vocab
-    _, near = bench.toy_oracle(sh, names, w, prompt, modes, a)
+    _, near = bench.toy_oracle(sh, names, w, prompt, modes)
     rep = near["end_to_end"]["greedy"]
     assert rep["first_differing_round"] == 1 and rep["rounds_compared"] == 2
     assert rep["near_tie_differences"] + rep["mismatches"] == 1

@@ -140,3 +140,28 @@ def test_speculative_greedy_equals_greedy_decoding():
         if spec[i] != plain[i]:
             assert gaps[i - 1] < 1e-4, (i, spec[:i + 1], plain[:i + 1], gaps[i - 1])
             break
+
+
+def test_live_rounds_match_the_oracle_end_to_end():
+    """30 live rounds on the HIP path (the step's own prefill, gamma T=1
+    draft decodes, verify, accept, commit; gamma = 4, sigma = 1) at
+    temperature 1 and greedy, replayed by the oracle from its own prefill and
+    its own commits with the same drafts, q and uniforms: every round agrees
+    (a near tie, should one occur, ends the comparison and is counted; no
+    mismatch is allowed), and the logits stay within 1e-4 of the oracle's."""
+    import bench
+
+    sh = synth.TOY
+    R = 30
+    print(f"[multiround] toy live rounds against the oracle, R={R}", flush=True)
+    max_ctx = ((bench.TOY_PROMPT + R * (bench.TOY_GAMMA + 1) + bench.TOY_GAMMA + 64) // 64) * 64
+    eng, names, w, _ = build_engine(sh, 1, max_ctx, bench.TOY_PROMPT, ctx_len=[0], poison=False)
+    prompt = synth.make_tokens(1, bench.TOY_PROMPT, sh.vocab, seed=synth.SEED_PROMPT, device=dev())
+    modes = {t: {"recs": bench.toy_live(eng, sh, prompt, R, t, 1.0, dev())[1]} for t in (1.0, 0.0)}
+    assert eng.device_errors() == 0
+    _, near = bench.toy_oracle(sh, names, w, prompt, modes)
+    for key, rep in near["end_to_end"].items():
+        print(f"  {key}: {rep}", flush=True)
+        assert rep["mismatches"] == 0, rep
+        assert rep["rounds_compared"] == R or rep["near_tie_differences"] == 1, rep
+        assert rep["max_logits_rel_err"] < 1e-4, rep
