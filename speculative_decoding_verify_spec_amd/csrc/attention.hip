@@ -50,10 +50,12 @@ namespace sv {
 int attn_query_tiles(int nq, int D) { return (nq > 16 && (D == 128 || nq <= 64)) ? 2 : 1; }
 int attn_groups_per_wg(int nq, int D) { return (D != 128 && nq > 64) ? 2 : 1; }
 int attn_nsplit(int splits) { return splits + 1; }
-// Suffix queries per wave: four for trees and for chains of many
+// Suffix queries per wave: four for trees and for chains of 128 or more
 // (sequence, KV head) pairs, one otherwise (a small batch's suffix must not
-// outlast its context workgroups).
-__host__ __device__ inline int attn_suffix_qpw(bool tree, int pairs) { return (tree || pairs >= 256) ? 4 : 1; }
+// outlast its context workgroups).  Measured at ctx 1024, T = 4: four per
+// wave take B = 16 from 32.5 to 28.5 us per layer, but cost B = 4 and B = 8
+// 2.5 and 1.1 us.
+__host__ __device__ inline int attn_suffix_qpw(bool tree, int pairs) { return (tree || pairs >= 128) ? 4 : 1; }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
 // 4g..4g+3 of both tiles cover keys kb + 8g .. kb + 8g + 7, so one 16-byte
