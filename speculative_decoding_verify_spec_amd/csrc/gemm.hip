@@ -924,9 +924,12 @@ static hipError_t launch_mt(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.xpart && !gemm_takes_xpart(p)) return hipErrorInvalidValue;
-  // planes written by the producer serve only the tiled kernels, and carry no
-  // sums of squares for a fused norm
-  if ((p.xs_ready && (p.norm_g || !gemm_tiled_ok(p))) || (p.xs_out && (p.epi != EPI_SWIGLU || !gemm_tiled_ok(p))))
+  // planes written by the producer serve only the tiled kernels, and a fused
+  // norm needs their sums of squares as well; a finish that prepares the next
+  // launch's planes exists only for K-split residual launches
+  if ((p.xs_ready && ((p.norm_g && !p.ssq_ready) || !gemm_tiled_ok(p))) ||
+      (p.xs_out && (p.epi != EPI_SWIGLU || !gemm_tiled_ok(p))) ||
+      (p.norm_next && (!p.xs_next || !gemm_finish_prepares(p))))
     return hipErrorInvalidValue;
   if (gemm_tiled_ok(p)) return launch_gemm_tiled(p, s);
   if (p.M <= 1) return launch_mt<1>(p, s);

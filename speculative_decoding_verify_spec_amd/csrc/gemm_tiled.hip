@@ -405,17 +405,100 @@ __global__ __launch_bounds__(256) void gemm_tiled_finish_kernel(GemmParams p, in
   epilogue_pair<EPI, NP>(p, m, j, a, b);
 }
 
+// Finish of a K-split residual GEMM that also prepares the next GEMM's
+// activations (norm_next): out = out + (the slices' partial sums, in slice
+// order, as gemm_tiled_finish_kernel adds them), then the bf16 hi/lo planes of
+// out * norm_next into xs_next and the row's sum of squares over each 1024
+// columns into xs_ssq, with the arithmetic of gemm_split_x_kernel.  One
+// workgroup per (1024 columns, row): thread t takes pairs 512 blk + 2t and
+// + 1, whose a and b columns (two adjacent pairs of columns) lie in that
+// block since 1024 is a multiple of a tile's 2 NP columns.
+template <int NP>
+__global__ __launch_bounds__(256) void gemm_finish_norm_kernel(GemmParams p, int nsplit) {
+  static_assert(1024 % (2 * NP) == 0 && NP % 2 == 0, "a workgroup's pairs fill whole tiles");
+  const int blk = blockIdx.x, m = blockIdx.y;
+  const int npairs = pair_count<EPI_RESID, NP>(p);
+  const int j = blk * 512 + 2 * (int)threadIdx.x;
+  float ss = 0.f;
+  if (j < npairs) {
+    float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
+    for (int z = 0; z < nsplit; ++z) {
+      const float4 v = *(const float4*)(p.part + (((size_t)z * p.M + m) * npairs + j) * 2);
+      a0 += v.x;
+      b0 += v.y;
+      a1 += v.z;
+      b1 += v.w;
+    }
+    int rb;
+    const int ra = pair_rows<EPI_RESID, NP>(p, j, rb);
+    float* o = p.out + (size_t)m * p.ldo;
+    uint16_t* hi = p.xs_next + (size_t)m * p.N;
+    uint16_t* lo = hi + (size_t)p.M * p.N;
+    // columns (ra, ra + 1) take a0, a1 and (rb, rb + 1) take b0, b1
+    const int col[2] = {ra, rb};
+    const float add[2][2] = {{a0, a1}, {b0, b1}};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = col[h];
+      if (c + 2 > p.N) continue;  // a tile past the matrix (never for whole tiles)
+      float2 y = *(float2*)(o + c);
+      y.x += add[h][0];
+      y.y += add[h][1];
+      *(float2*)(o + c) = y;
+      const float2 g = *(const float2*)(p.norm_next + c);
+      ss += y.x * y.x;
+      ss += y.y * y.y;
+      short h0, l0, h1, l1;
+      split_bf16(y.x * g.x, h0, l0);
+      split_bf16(y.y * g.y, h1, l1);
+      *(uint32_t*)(hi + c) = (uint32_t)(uint16_t)h0 | ((uint32_t)(uint16_t)h1 << 16);
+      *(uint32_t*)(lo + c) = (uint32_t)(uint16_t)l0 | ((uint32_t)(uint16_t)l1 << 16);
+    }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) p.xs_ssq[m * SSQ_BLK + blk] = red[0] + red[1] + red[2] + red[3];
+}
+
+// The finish of a K-split launch: the plain one, or, for a residual GEMM
+// with norm_next, the one that also writes the next GEMM's planes.
+template <int EPI, int NP>
+void launch_finish(const GemmParams& p, int nsplit, hipStream_t s) {
+  if constexpr (EPI == EPI_RESID) {
+    if (p.norm_next) {
+      gemm_finish_norm_kernel<NP><<<dim3((p.N + 1023) / 1024, p.M), 256, 0, s>>>(p, nsplit);
+      return;
+    }
+  }
+  const size_t n = (size_t)p.M * pair_count<EPI, NP>(p);
+  const int blocks = (int)((n + 255) / 256);
+  if (p.norm_g) gemm_tiled_finish_kernel<EPI, true, NP><<<blocks, 256, 0, s>>>(p, nsplit);
+  else gemm_tiled_finish_kernel<EPI, false, NP><<<blocks, 256, 0, s>>>(p, nsplit);
+}
+
+// K slices of a launch of the 32-row tiles: split while the tiles would not
+// fill the chip, if the scratch allows
+template <int MB, int EPI>
+int cfg_splits(const GemmParams& p) {
+  constexpr int BM = 32 * MB;
+  const int tiles_n = (pair_count<EPI, NPAIR>(p) + NPAIR - 1) / NPAIR;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  int nsplit = 1;
+  while (p.part && tiles_n * tiles_m * nsplit < 384 && nsplit < 8 && (p.K / (2 * nsplit)) % TK == 0 &&
+         (size_t)2 * nsplit * p.M * pair_count<EPI, NPAIR>(p) * 2 <= p.part_floats)
+    nsplit *= 2;
+  return nsplit;
+}
+
 template <int MB, int KW, int EPI>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   constexpr int R = 3;
   constexpr int BM = 32 * MB;
   const int tiles_n = (pair_count<EPI, NPAIR>(p) + NPAIR - 1) / NPAIR;
   const int tiles_m = (p.M + BM - 1) / BM;
-  // split K while the tiles would not fill the chip, if scratch allows
-  int nsplit = 1;
-  while (p.part && tiles_n * tiles_m * nsplit < 384 && nsplit < 8 && (p.K / (2 * nsplit)) % TK == 0 &&
-         (size_t)2 * nsplit * p.M * pair_count<EPI, NPAIR>(p) * 2 <= p.part_floats)
-    nsplit *= 2;
+  const int nsplit = cfg_splits<MB, EPI>(p);
   const bool norm = p.norm_g != nullptr;
   if (!p.xs_ready) launch_split_x(p, s);
   const dim3 grid(tiles_n, tiles_m, nsplit);
@@ -425,10 +508,7 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   gemm_tiled_kernel<MB, KW, R, EPI, false, true><<<grid, 256, 0, s>>>(p);
-  const size_t n = (size_t)p.M * pair_count<EPI, NPAIR>(p);
-  const int blocks = (int)((n + 255) / 256);
-  if (norm) gemm_tiled_finish_kernel<EPI, true, NPAIR><<<blocks, 256, 0, s>>>(p, nsplit);
-  else gemm_tiled_finish_kernel<EPI, false, NPAIR><<<blocks, 256, 0, s>>>(p, nsplit);
+  launch_finish<EPI, NPAIR>(p, nsplit, s);
   return hipGetLastError();
 }
 
@@ -774,12 +854,17 @@ hipError_t launch_big_nw(const GemmParams& p, hipStream_t s, bool norm, int nspl
     return hipGetLastError();
   }
   gemm_big_kernel<EPI, false, true, NW><<<grid, 64 * NW, 0, s>>>(p, tiles_m, nsplit, ntiles);
-  const int npairs = pair_count<EPI, BIG_NP>(p);
-  const size_t n = (size_t)p.M * npairs;
-  const int blocks = (int)((n + 255) / 256);
-  if (norm) gemm_tiled_finish_kernel<EPI, true, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
-  else gemm_tiled_finish_kernel<EPI, false, BIG_NP><<<blocks, 256, 0, s>>>(p, nsplit);
+  launch_finish<EPI, BIG_NP>(p, nsplit, s);
   return hipGetLastError();
+}
+
+template <int EPI>
+int big_nsplit(const GemmParams& p) {
+  const int npairs = pair_count<EPI, BIG_NP>(p);
+  const int tiles_n = (npairs + BIG_NP - 1) / BIG_NP;
+  const int tiles_m = (p.M + BIG_BM - 1) / BIG_BM;
+  return p.part ? big_splits(tiles_n * tiles_m, p.K / TK, device_cus(), (size_t)p.M * npairs * 2, p.part_floats)
+                : 1;
 }
 
 template <int EPI>
@@ -787,9 +872,7 @@ hipError_t launch_big(const GemmParams& p, hipStream_t s) {
   const int npairs = pair_count<EPI, BIG_NP>(p);
   const int tiles_n = (npairs + BIG_NP - 1) / BIG_NP;
   const int tiles_m = (p.M + BIG_BM - 1) / BIG_BM;
-  const int nsplit = p.part ? big_splits(tiles_n * tiles_m, p.K / TK, device_cus(), (size_t)p.M * npairs * 2,
-                                         p.part_floats)
-                            : 1;
+  const int nsplit = big_nsplit<EPI>(p);
   const int ntiles = tiles_n * tiles_m * nsplit;
   const int grid = ((ntiles + 7) / 8) * 8;
   const bool norm = p.norm_g != nullptr;
@@ -839,6 +922,14 @@ bool gemm_big_rows(const GemmParams& p) {
 bool gemm_tiled_ok(const GemmParams& p) {
   if (p.wdtype != 1 || p.K % TK || p.K > SSQ_BLK * 1024 || !p.xs || (size_t)2 * p.M * p.K > p.xs_elems) return false;
   return p.M > 8;
+}
+
+bool gemm_finish_prepares(const GemmParams& p) {
+  if (p.epi != EPI_RESID || !gemm_tiled_ok(p)) return false;
+  if (gemm_big_rows(p)) return big_nsplit<EPI_RESID>(p) > 1;
+  if (p.M <= 32) return cfg_splits<1, EPI_RESID>(p) > 1;
+  if (p.M <= 64) return cfg_splits<2, EPI_RESID>(p) > 1;
+  return cfg_splits<4, EPI_RESID>(p) > 1;
 }
 
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t s) {

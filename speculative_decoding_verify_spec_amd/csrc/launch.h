@@ -92,6 +92,17 @@ struct GemmParams {
   // bf16 hi/lo planes [2][M][ldo] of its outputs, for the next GEMM.
   bool xs_ready;
   uint16_t* xs_out;
+  // ... and xs_ssq holds those rows' sums of squares, so that a launch with a
+  // fused norm may skip its split too
+  bool ssq_ready;
+  // A K-split residual GEMM on the tiled kernels whose finish also prepares
+  // the next GEMM's activations: with norm_next set, the finish (one
+  // workgroup per 1024 output columns of a row) writes the bf16 hi/lo planes
+  // of out * norm_next into xs_next ([2][M][N]) and the rows' sums of squares
+  // per 1024 columns into xs_ssq, as the split of the next launch would.
+  // Only where gemm_finish_prepares holds.
+  const float* norm_next;
+  uint16_t* xs_next;
 };
 constexpr int GEMM_KSPLIT = 2;  // K slices of the skinny residual GEMM
 constexpr int SSQ_BLK = 16;     // 1024-k partial sums of squares per activation row (K <= 16384)
@@ -105,6 +116,10 @@ __device__ __forceinline__ float row_factor(const GemmParams& p, int m) {
   return 1.0f / sqrtf(q / (float)p.K + p.eps);
 }
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// the launch of these parameters (M rows) runs on the tiled kernels as K
+// slices whose finish is a separate kernel: the residual GEMMs where
+// norm_next can take the next launch's split
+bool gemm_finish_prepares(const GemmParams& p);
 // the residual GEMM of these parameters runs as K slices + reduce
 bool gemm_use_split(const GemmParams& p);
 // the launch of these parameters can complete its activation rows from

@@ -269,6 +269,29 @@ bool rows_tiled(const spec_handle* h, GemmParams p, int M) {
   return gemm_tiled_ok(p);
 }
 
+// The launch of p over M rows is a K-split residual GEMM on the tiled kernels
+// whose finish can also write the next GEMM's planes (norm_next).
+bool finish_prepares(const spec_handle* h, GemmParams p, int M) {
+  gemm_scratch(h, p);
+  p.M = M;
+  return gemm_finish_prepares(p);
+}
+
+// The down projection of M rows prepares the next launch's activation planes
+// (the next layer's QKV, or the LM head after the last layer) when its finish
+// can and that launch runs on the tiled kernels too; both take the same
+// activation width d_model.
+bool down_prepares_next(const spec_handle* h, int M) {
+  const spec_config& c = h->cfg;
+  GemmParams gd{};
+  gd.wdtype = c.weight_dtype; gd.N = c.d_model; gd.K = c.d_ffn; gd.epi = EPI_RESID;
+  GemmParams nx{};
+  nx.wdtype = c.weight_dtype; nx.K = c.d_model; nx.N = c.vocab; nx.epi = EPI_STORE;
+  GemmParams nq{};
+  nq.wdtype = c.weight_dtype; nq.K = c.d_model; nq.N = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; nq.epi = EPI_QKV;
+  return finish_prepares(h, gd, M) && rows_tiled(h, nx, M) && rows_tiled(h, nq, M);
+}
+
 hipError_t gemm_rows(spec_handle* h, int cls, GemmParams p, int M, hipStream_t s) {
   const size_t wbytes = h->cfg.weight_dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   const size_t nrows = (p.epi == EPI_SWIGLU) ? (size_t)2 * p.F : (size_t)p.N;
@@ -357,6 +380,9 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   const bool defer = defer_down_reduce(h, M);
   float* x2 = h->at<float>(L.x2);
   float* cur = x;  // residual rows entering the layer
+  // the residual finishes write the next launch's planes and sums of squares
+  // (no split launches in front of QKV, gate/up and the LM head)
+  const bool down_next = down_prepares_next(h, M);
 
   for (int l = 0; l < c.n_layers; ++l) {
     const float* g1 = (const float*)h->W(h->layer_w(l, 0));
@@ -378,6 +404,7 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
       gq.xout = nxt;
     }
     gq.norm_g = g1; gq.eps = c.rms_eps;
+    gq.xs_ready = gq.ssq_ready = down_next && l > 0;
     gq.epi = EPI_QKV; gq.pos = pos; gq.slot = slot;
     gq.rope_cos = h->at<float>(L.rope_cos); gq.rope_sin = h->at<float>(L.rope_sin);
     gq.q_out = q; gq.k_out = ks; gq.v_out = vs; gq.kcache = kreg; gq.vcache = vreg;
@@ -400,12 +427,19 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
                      go.xs_ready ? h->at<uint16_t>(L.gxs) : nullptr, M};
     e = timed(h, K_COMB, 0, s, [&] { return launch_attn_combine(cp, s); });
     if (e != hipSuccess) return e;
-    if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return e;
-
     GemmParams gg{};
     gg.W = wgu; gg.wdtype = c.weight_dtype; gg.X = nxt; gg.ldx = d; gg.N = 2 * F; gg.K = d;
     gg.norm_g = g2; gg.eps = c.rms_eps;
     gg.epi = EPI_SWIGLU; gg.out = act; gg.ldo = F; gg.F = F;
+    if (go.xs_ready && rows_tiled(h, gg, M) && finish_prepares(h, go, M)) {
+      // O's finish writes gate/up's planes (the O launch has read its own
+      // from the same buffer before its finish runs)
+      go.norm_next = g2;
+      go.xs_next = h->at<uint16_t>(L.gxs);
+      gg.xs_ready = gg.ssq_ready = true;
+    }
+    if ((e = gemm_rows(h, K_O, go, M, s)) != hipSuccess) return e;
+
     GemmParams gd{};
     gd.W = wdn; gd.wdtype = c.weight_dtype; gd.X = act; gd.ldx = F; gd.N = d; gd.K = F;
     gd.epi = EPI_RESID; gd.out = nxt; gd.ldo = d;
@@ -416,6 +450,11 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
       gg.xs_out = h->at<uint16_t>(L.gxs2);
       gd.xs = gg.xs_out;
       gd.xs_ready = true;
+    }
+    if (down_next) {
+      // the next layer's attention norm, or the final norm before the LM head
+      gd.norm_next = (const float*)(l + 1 < c.n_layers ? h->W(h->layer_w(l + 1, 0)) : h->W(1 + 6 * (size_t)c.n_layers));
+      gd.xs_next = h->at<uint16_t>(L.gxs);
     }
     if ((e = gemm_rows(h, K_GU, gg, M, s)) != hipSuccess) return e;
     if ((e = gemm_rows(h, K_DOWN, gd, M, s)) != hipSuccess) return e;
@@ -629,6 +668,7 @@ spec_status verify_forward(spec_handle* h, const StepShape& sh, const int32_t* d
   gl.N = V;
   gl.K = d; gl.epi = EPI_STORE; gl.out = d_logits; gl.ldo = V;
   gl.norm_g = gf; gl.eps = c.rms_eps;
+  gl.xs_ready = gl.ssq_ready = down_prepares_next(h, M);  // the last down's finish wrote them
   if ((e = gemm_rows(h, K_LM, gl, M, s)) != hipSuccess) return SPEC_ERR_DEVICE;
   return SPEC_OK;
 }
