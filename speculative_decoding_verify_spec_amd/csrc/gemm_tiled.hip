@@ -479,14 +479,18 @@ void launch_finish(const GemmParams& p, int nsplit, hipStream_t s) {
 }
 
 // K slices of a launch of the 32-row tiles: split while the tiles would not
-// fill the chip, if the scratch allows
+// fill the chip, if the scratch allows, into at most 4 slices (a slice's
+// pipeline of 64-k stages is mostly ramp below ~16 stages: on the 8B shape
+// at 32 rows, 8 slices took the O projection 20.2 and the down projection
+// 37.4 us per launch with their finish, 4 slices 18.5 and 34.6 us; B=8 step
+// 5.07 -> 4.92 ms)
 template <int MB, int EPI>
 int cfg_splits(const GemmParams& p) {
   constexpr int BM = 32 * MB;
   const int tiles_n = (pair_count<EPI, NPAIR>(p) + NPAIR - 1) / NPAIR;
   const int tiles_m = (p.M + BM - 1) / BM;
   int nsplit = 1;
-  while (p.part && tiles_n * tiles_m * nsplit < 384 && nsplit < 8 && (p.K / (2 * nsplit)) % TK == 0 &&
+  while (p.part && tiles_n * tiles_m * nsplit < 384 && nsplit < 4 && (p.K / (2 * nsplit)) % TK == 0 &&
          (size_t)2 * nsplit * p.M * pair_count<EPI, NPAIR>(p) * 2 <= p.part_floats)
     nsplit *= 2;
   return nsplit;
