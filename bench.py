@@ -134,6 +134,9 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run an fp32 copy of this many MiB three times first (HBM counter calibration)")
+    ap.add_argument("--cpu-seqs", type=int, default=0,
+                    help="the oracle leg runs only the first N sequences of the batch (0: all); its tok/s is that "
+                         "subset's own, and the decision checks cover the same sequences")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle rounds are repeated until this much CPU time is spent (at most 3)")
     return ap.parse_args()
@@ -355,22 +358,26 @@ def main():
         # the GPU's decisions the oracle leg compares with: every timed step's
         # logits and accept output (shared-logits tier), and round 0 accepted
         # with each uniform round the oracle's own forward is used for
+        # the oracle's sequences: the first nb of the batch (rows are
+        # independent; the uniforms are indexed by sequence)
+        nb = min(B, a.cpu_seqs) if a.cpu_seqs > 0 else B
         nk = min(a.steps, 128)
         shared = []
         for k in range(a.warmup, a.warmup + nk):
             one_step(k)
             tokens, qt = rounds[k % len(rounds)]
-            shared.append((k, tokens.cpu().numpy(), qt.double().cpu().numpy() if gamma else None,
-                           logits.double().cpu().numpy(), out.cpu().numpy(), nacc_hist[k].cpu().numpy()))
+            shared.append((k, tokens[:nb].cpu().numpy(), qt[:nb].double().cpu().numpy() if gamma else None,
+                           logits[:nb].double().cpu().numpy(), out[:nb].cpu().numpy(),
+                           nacc_hist[k][:nb].cpu().numpy()))
         e2e = []
         for j in range(3):
             tokens, qt = rounds[0]
             eng.step(tokens, kv_len, logits)
             eng.accept(logits, qt if gamma else None, tokens, out, nacc_hist[0], kv_len, kv_out,
                        temperature=a.temperature, seed=synth.SEED_ACCEPT, round_=j, top_k=a.top_k, top_p=a.top_p)
-            e2e.append((out.cpu().numpy(), nacc_hist[0].cpu().numpy()))
+            e2e.append((out[:nb].cpu().numpy(), nacc_hist[0][:nb].cpu().numpy()))
         result["cpu_baseline"], result["near_ties"] = cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, rounds[0], a,
-                                                                   kv_len, shared, e2e)
+                                                                   kv_len, shared, e2e, nb)
     print(json.dumps(result), flush=True)
 
 
@@ -1112,7 +1119,7 @@ def count_decisions(gpu_out, gpu_n, orc, draw_band, band=1e-4):
     return decisions, near, mismatch
 
 
-def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared, e2e):
+def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared, e2e, nb=None):
     """One verify round (forward over the T rows + accept) of the same workload
     in the CPU oracle, on this host's cores.  The oracle's results also give
     the decision check the benchmark spec asks to report: the GPU's accept on its
@@ -1127,12 +1134,14 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared
     from oracle import philox
 
     log("cpu baseline: copying weights and cache to host")
+    nb = B if nb is None else nb
     Wn = OM.Weights(names, [synth.to_numpy_raw(t) for t in w])
-    k, v = synth.kv_views(cache, sh, B, max_ctx)
+    k, v = synth.kv_views(cache, sh, B, max_ctx, seqs=nb)
     kc, vc = synth.to_numpy_raw(k), synth.to_numpy_raw(v)
+    del k, v
     tokens, qt = round0
-    tok = tokens.cpu().numpy()
-    qn = qt.double().cpu().numpy() if a.gamma and a.temperature > 0 else None
+    tok = tokens[:nb].cpu().numpy()
+    qn = qt[:nb].double().cpu().numpy() if a.gamma and a.temperature > 0 else None
     cores = len(os.sched_getaffinity(0))
     threads = None
     try:
@@ -1145,7 +1154,7 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared
     e2e_counts = [0, 0, 0]
     while nrounds < 3 and (nrounds == 0 or dt < a.cpu_seconds):
         t0 = time.perf_counter()
-        z, _, _ = OM.forward(sh, Wn, tok, np.full(B, ctx), kc, vc)
+        z, _, _ = OM.forward(sh, Wn, tok, np.full(nb, ctx), kc, vc)
         res = OA.accept(z, qn, tok, a.temperature, philox.Uniforms(synth.SEED_ACCEPT, nrounds),
                         top_k=a.top_k, top_p=a.top_p)
         dt += time.perf_counter() - t0
@@ -1168,14 +1177,16 @@ def cpu_baseline(sh, names, w, cache, B, max_ctx, ctx, round0, a, kv_len, shared
     except OSError:
         pass
     base = {"value": round(toks / dt, 4), "unit": "accepted tok/s", "cores": threads or cores, "cpu_model": cpu_model,
-            "kind": "oracle", "sample": f"{nrounds} verify rounds (B={B}, T={a.gamma + 1}, ctx {ctx}, "
-                                        f"32 layers, forward + accept) of the same workload; {dt:.1f} s",
+            "kind": "oracle", "sample": f"{nrounds} verify rounds (" + (f"the first {nb} of the B={B} sequences"
+                                                                      if nb < B else f"B={B}")
+                                        + f", T={a.gamma + 1}, ctx {ctx}, 32 layers, forward + accept) of the "
+                                        f"same workload; {dt:.1f} s",
             "round_seconds": round(dt / nrounds, 2), "host_cores_visible": cores,
             "threads_note": "cores = the BLAS threads the oracle ran on (threadpoolctl), else the visible cores"}
-    near = {"shared_logits": {"sequence_rounds": len(shared) * B, "decisions": sh_counts[0],
+    near = {"shared_logits": {"sequence_rounds": len(shared) * nb, "decisions": sh_counts[0],
                               "near_tie_differences": sh_counts[1], "mismatches": sh_counts[2],
                               "draw_band": 1e-6, "band": 1e-4},
-            "end_to_end": {"sequence_rounds": nrounds * B, "decisions": e2e_counts[0],
+            "end_to_end": {"sequence_rounds": nrounds * nb, "decisions": e2e_counts[0],
                            "near_tie_differences": e2e_counts[1], "mismatches": e2e_counts[2],
                            "draw_band": 1e-4, "band": 1e-4}}
     log(f"decisions: shared logits {sh_counts}, end to end {e2e_counts} (decisions, near ties, mismatches)")

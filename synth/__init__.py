@@ -174,17 +174,19 @@ def kv_v_blocks(cache: torch.Tensor, shape: ModelShape, max_batch: int, max_ctx:
     return c[:, 1].view(L, max_batch, H, max_ctx // KV_BLOCK, D, KV_BLOCK)
 
 
-def kv_views(cache: torch.Tensor, shape: ModelShape, max_batch: int, max_ctx: int):
+def kv_views(cache: torch.Tensor, shape: ModelShape, max_batch: int, max_ctx: int, seqs: int = 0):
     """K view [L, B, Hkv, max_ctx, D] of the flat bf16 cache buffer, and V as
     [L, B, Hkv, D, max_ctx] (values transposed, positions in order).  K is a
     view of the buffer; V is a copy gathered from its 64-position blocks, for
-    reading (write V through kv_v_blocks)."""
+    reading (write V through kv_v_blocks).  With seqs > 0 only the first seqs
+    sequences (B = seqs)."""
     L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    nb = seqs if seqs > 0 else max_batch
     c = cache.view(L, 2, max_batch, H, max_ctx * D)
-    k = c[:, 0].view(L, max_batch, H, max_ctx, D)
-    vb = kv_v_blocks(cache, shape, max_batch, max_ctx)
-    v = torch.empty((L, max_batch, H, D, max_ctx), dtype=cache.dtype, device=cache.device)
-    v.view(L, max_batch, H, D, max_ctx // KV_BLOCK, KV_BLOCK).copy_(vb.permute(0, 1, 2, 4, 3, 5))
+    k = c[:, 0].view(L, max_batch, H, max_ctx, D)[:, :nb]
+    vb = kv_v_blocks(cache, shape, max_batch, max_ctx)[:, :nb]
+    v = torch.empty((L, nb, H, D, max_ctx), dtype=cache.dtype, device=cache.device)
+    v.view(L, nb, H, D, max_ctx // KV_BLOCK, KV_BLOCK).copy_(vb.permute(0, 1, 2, 4, 3, 5))
     return k, v
 
 
