@@ -166,6 +166,25 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sub, int 
 
 // PFB: key blocks each wave has in flight.  With PFB = 1 two workgroups fit
 // on a CU; with more, one.
+// Unit u of a launch with `splits` context columns and ncol - splits suffix
+// columns per (KV head, sequence): every context unit comes before every
+// suffix unit in dispatch order, so the short suffix workgroups fill the end
+// of a launch that runs in several rounds of workgroups rather than
+// stretching one of the rounds.
+DEVI void attn_unit(int u, int splits, int ncol, int Hkv, int B, int& s, int& kvh, int& b) {
+  const int nctx = splits * Hkv * B;
+  if (u < nctx) {
+    s = u % splits;
+    kvh = (u / splits) % Hkv;
+    b = u / (splits * Hkv);
+  } else {
+    const int v = u - nctx, nsuf = ncol - splits;
+    s = splits + v % nsuf;
+    kvh = (v / nsuf) % Hkv;
+    b = v / (nsuf * Hkv);
+  }
+}
+
 template <int D, int QT, int QGW, int PFB>
 __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnParams p) {
   constexpr int DG = D / 4;   // dims per lane group
@@ -199,9 +218,8 @@ __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnPara
   const int u = (n / nqw) * 8 + id % 8;
   if (u >= units) return;  // padding of the last XCD round
   const int qgw = n % nqw;
-  const int s = u % ncol;
-  const int kvh = (u / ncol) % p.Hkv;
-  const int b = u / (ncol * p.Hkv);
+  int s, kvh, b;
+  attn_unit(u, p.splits, ncol, p.Hkv, p.B, s, kvh, b);
 
   constexpr int QN = QT * 16;
   constexpr int OS = D + 4;  // padded row stride of the staged outputs
@@ -488,9 +506,8 @@ __global__ __launch_bounds__(256, 2) void attn_ctx_lds_kernel(AttnParams p) {
   const int u = (n / nqw) * 8 + id % 8;
   if (u >= units) return;
   const int qg = n % nqw;
-  const int s = u % ncol;
-  const int kvh = (u / ncol) % p.Hkv;
-  const int b = u / (ncol * p.Hkv);
+  int s, kvh, b;
+  attn_unit(u, p.splits, ncol, p.Hkv, p.B, s, kvh, b);
   if (s >= p.splits) {  // the step's own keys: suffix workgroup s - splits of this query group
     attn_suffix<D, QT>(p, kvh, qg, b, s - p.splits, qpw);
     return;
