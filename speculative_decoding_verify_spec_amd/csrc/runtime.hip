@@ -52,6 +52,12 @@ size_t kv_region_elems(const spec_config& c) {
 // Measured on the 8B shape: B=1, 2K context: 17 (the 128-key bound); B=16,
 // 32K: 32 at T=1, 16 at T=8; B=128, 1K: 2 at T=4 (150 against 212 us for 4),
 // 1 at T=8 (265 against 299 us for 2); tree [4,4,2,2] at B=4, 4K: 4.
+// The 16-query form then takes fewer splits where that makes its context
+// and suffix workgroups one round of the 512 resident ones (the suffix
+// workgroups are dispatched last, so a second round would hold only them)
+// while a workgroup still sees at most 2048 keys: at 1K context B=8 8 -> 4
+// splits, B=16 4 -> 3, B=32 2 -> 1 (attention 16.5 -> 15.2, 29.1 -> 25.3 and
+// 43.0 -> 37.1 us per layer).
 int attn_splits(const spec_config& c, int B, int T) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
   const int QT = attn_query_tiles(nq, c.head_dim), QGW = attn_groups_per_wg(nq, c.head_dim);
@@ -64,6 +70,10 @@ int attn_splits(const spec_config& c, int B, int T) {
   s = std::min(s, (c.max_ctx + 127) / 128);
   const int cap = two_per_cu ? std::max(1, (4096 + units - 1) / units) : std::max(1, 2048 / units);
   s = std::min(s, cap);
+  if (two_per_cu) {
+    const int one = 512 / units - attn_suffix_cols(units, QT, QGW);
+    if (one >= 1 && (c.max_ctx + one - 1) / one <= 2048) s = std::min(s, one);
+  }
   return std::max(1, std::min(s, 127));
 }
 
