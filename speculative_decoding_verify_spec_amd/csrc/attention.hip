@@ -56,9 +56,9 @@ int attn_nsplit(int splits) { return splits + 1; }
 // wave take B = 16 from 32.5 to 28.5 us per layer, but cost B = 4 and B = 8
 // 2.5 and 1.1 us.
 __host__ __device__ inline int attn_suffix_qpw(bool tree, int pairs) { return (tree || pairs >= 128) ? 4 : 1; }
-// Suffix columns of a chain launch with `pairs` (sequence, KV head, query
-// set) units: 4 * QT * QGW query tiles' worth, qpw queries per wave.
-int attn_suffix_cols(int pairs, int QT, int QGW) { return 4 * QT * QGW / attn_suffix_qpw(false, pairs); }
+// Suffix columns of a launch with `pairs` (sequence, KV head, query set)
+// units: 4 * QT * QGW query tiles' worth, qpw queries per wave.
+int attn_suffix_cols(bool tree, int pairs, int QT, int QGW) { return 4 * QT * QGW / attn_suffix_qpw(tree, pairs); }
 
 // Key index held in row r of key tile kt of the 32-key block at kb: rows
 // 4g..4g+3 of both tiles cover keys kb + 8g .. kb + 8g + 7, so one 16-byte

@@ -168,7 +168,7 @@ struct AttnParams {
 int attn_nsplit(int splits);
 int attn_query_tiles(int nq, int D);    // 16-query tiles per wave of the context attention (1 or 2)
 int attn_groups_per_wg(int nq, int D);  // query groups sharing a context workgroup's key blocks (1 or 2)
-int attn_suffix_cols(int pairs, int QT, int QGW);  // suffix workgroups per unit of a chain launch
+int attn_suffix_cols(bool tree, int pairs, int QT, int QGW);  // suffix workgroups per unit
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 struct CombineParams {

@@ -51,14 +51,21 @@ size_t kv_region_elems(const spec_config& c) {
 // form) or ~2048 (the others), and a combine of at most 128 partials.
 // Measured on the 8B shape: B=1, 2K context: 17 (the 128-key bound); B=16,
 // 32K: 32 at T=1, 16 at T=8; B=128, 1K: 2 at T=4 (150 against 212 us for 4),
-// 1 at T=8 (265 against 299 us for 2); tree [4,4,2,2] at B=4, 4K: 4.
-// The 16-query form then takes fewer splits where that makes its context
-// and suffix workgroups one round of the 512 resident ones (the suffix
-// workgroups are dispatched last, so a second round would hold only them)
-// while a workgroup still sees at most 2048 keys: at 1K context B=8 8 -> 4
-// splits, B=16 4 -> 3, B=32 2 -> 1 (attention 16.5 -> 15.2, 29.1 -> 25.3 and
-// 43.0 -> 37.1 us per layer).
-int attn_splits(const spec_config& c, int B, int T) {
+// 1 at T=8 (265 against 299 us for 2).
+// The two forms with two workgroups per CU (16-query tiles, and 32-query
+// tiles in LDS at head width 128) then take
+//   * fewer splits where that makes their context and suffix workgroups one
+//     round of the 512 resident ones (the suffix workgroups are dispatched
+//     last, so a second round would hold only them) while a workgroup still
+//     sees at most 2048 keys (4096 in the LDS form): at 1K context B=8 8 -> 4
+//     splits, B=16 4 -> 3, B=32 2 -> 1 (attention 16.5 -> 15.2, 29.1 -> 25.3
+//     and 43.0 -> 37.1 us per layer); tree [4,4,2,2] at B=1, 4K 4 -> 2
+//     (43.6 -> 40.7 us);
+//   * one split (LDS form) when its units alone number 256 or more and the
+//     context is at most 8K: tree [4,4,2,2] at B=4, 4K (480 units) 1 split
+//     against 4 from the rule above, 114 against 137 us per layer (2: 121,
+//     3: 129, 6: 159).
+int attn_splits(const spec_config& c, int B, int T, bool tree) {
   const int nq = (c.n_heads / c.n_kv_heads) * T;
   const int QT = attn_query_tiles(nq, c.head_dim), QGW = attn_groups_per_wg(nq, c.head_dim);
   const int nqg = (nq + 16 * QT - 1) / (16 * QT);
@@ -70,10 +77,12 @@ int attn_splits(const spec_config& c, int B, int T) {
   s = std::min(s, (c.max_ctx + 127) / 128);
   const int cap = two_per_cu ? std::max(1, (4096 + units - 1) / units) : std::max(1, 2048 / units);
   s = std::min(s, cap);
-  if (two_per_cu) {
-    const int one = 512 / units - attn_suffix_cols(units, QT, QGW);
-    if (one >= 1 && (c.max_ctx + one - 1) / one <= 2048) s = std::min(s, one);
+  const bool lds_form = QT == 2 && c.head_dim == 128;
+  if (two_per_cu || lds_form) {
+    const int one = 512 / units - attn_suffix_cols(tree, units, QT, QGW);
+    if (one >= 1 && (c.max_ctx + one - 1) / one <= (lds_form ? 4096 : 2048)) s = std::min(s, one);
   }
+  if (lds_form && units >= 256 && c.max_ctx <= 8192) s = 1;
   return std::max(1, std::min(s, 127));
 }
 
@@ -127,10 +136,11 @@ Layout plan(const spec_config& c) {
   const size_t D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   size_t part = 0;
   for (int B = 1; B <= c.max_batch; ++B)
-    for (int T = 1; T <= c.max_rows_per_seq; ++T) {
-      const size_t n = (size_t)attn_nsplit(attn_splits(c, B, T)) * B * Hq * T;
-      part = std::max(part, n);
-    }
+    for (int T = 1; T <= c.max_rows_per_seq; ++T)
+      for (int tree = 0; tree < 2; ++tree) {
+        const size_t n = (size_t)attn_nsplit(attn_splits(c, B, T, tree != 0)) * B * Hq * T;
+        part = std::max(part, n);
+      }
   const int nch = accept_chunks(c.vocab);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -384,7 +394,7 @@ hipError_t launch_layers(spec_handle* h, const StepShape& sh, hipStream_t s) {
   const int32_t* kvw = h->at<int32_t>(L.kvw);
   hipError_t e;
   const size_t per_region = kv_region_elems(c);  // elements of one K or V region
-  const int splits = attn_splits(c, B, T);
+  const int splits = attn_splits(c, B, T, tree);
   const int nsplit = attn_nsplit(splits);
   const float scale = 1.0f / std::sqrt((float)D);
   const bool defer = defer_down_reduce(h, M);
