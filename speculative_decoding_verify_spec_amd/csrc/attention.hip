@@ -167,8 +167,6 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sub, int 
   }
 }
 
-// PFB: key blocks each wave has in flight.  With PFB = 1 two workgroups fit
-// on a CU; with more, one.
 // Unit u of a launch with `splits` context columns and ncol - splits suffix
 // columns per (KV head, sequence): every context unit comes before every
 // suffix unit in dispatch order, so the short suffix workgroups fill the end
@@ -188,6 +186,8 @@ DEVI void attn_unit(int u, int splits, int ncol, int Hkv, int B, int& s, int& kv
   }
 }
 
+// PFB: key blocks each wave has in flight.  With PFB = 1 two workgroups fit
+// on a CU; with more, one.
 template <int D, int QT, int QGW, int PFB>
 __global__ __launch_bounds__(256, PFB > 1 ? 1 : 2) void attn_ctx_kernel(AttnParams p) {
   constexpr int DG = D / 4;   // dims per lane group
