@@ -875,9 +875,12 @@ hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s) {
   if (G > 8 || p.nsplit > 128) return hipErrorInvalidValue;
   dim3 grid(p.T, p.Hkv, p.B);
   // the splits' outputs all in one round of requests when they fit (32 x 2
-  // floats per lane at D = 128)
+  // floats per lane at D = 128), and no more requests than splits below 9
+  // (requests past the last split re-read it)
   if (p.D == 128) {
-    if (p.nsplit <= 16) attn_combine_kernel<128, 16><<<grid, 64 * G, 0, s>>>(p);
+    if (p.nsplit <= 4) attn_combine_kernel<128, 4><<<grid, 64 * G, 0, s>>>(p);
+    else if (p.nsplit <= 8) attn_combine_kernel<128, 8><<<grid, 64 * G, 0, s>>>(p);
+    else if (p.nsplit <= 16) attn_combine_kernel<128, 16><<<grid, 64 * G, 0, s>>>(p);
     else if (p.nsplit <= 24) attn_combine_kernel<128, 24><<<grid, 64 * G, 0, s>>>(p);
     else if (p.nsplit <= 32) attn_combine_kernel<128, 32><<<grid, 64 * G, 0, s>>>(p);
     else attn_combine_kernel<128, 8><<<grid, 64 * G, 0, s>>>(p);
