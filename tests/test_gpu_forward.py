@@ -98,6 +98,10 @@ GQA_CASES = [
     # a deep tree (a 71-node chain, then a fork): nodes with more than 64
     # ancestors, several batches of visible suffix rows per query
     (1, 74, [200], [1] * 71 + [2]),
+    # one row at 5000 and 8000 keys: 40 and 60 context splits, so the combine
+    # merges 41 and 61 partials, 8 per round of requests after the first
+    (1, 1, [5000], None),
+    (1, 1, [8000], None),
 ]
 
 
@@ -108,7 +112,7 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
     poisoned tail: logits and written cache slots against the oracle."""
     sh = synth.MINI8B
     print(f"[gqa] B={B} T={T} ctx={ctx} tree={branching}", flush=True)
-    max_ctx = 1088
+    max_ctx = max(1088, (max(ctx) + T + 63) // 64 * 64)
     eng, names, w, cache = build_engine(sh, 4, max_ctx, max(16, T), ctx_len=ctx + [0] * (4 - B))
     W = oracle_weights(names, w)
     kc, vc = oracle_cache(cache, sh, 4, max_ctx)
