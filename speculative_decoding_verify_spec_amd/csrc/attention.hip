@@ -145,6 +145,101 @@ DEVI void attn_suffix_query(const AttnParams& p, int kvh, int b, int qi) {
   }
 }
 
+// NQ consecutive queries qi0 .. qi0 + NQ - 1 of one suffix row (query heads
+// of the same KV head): they see the same rows, so the visibility mask and
+// each batch of keys and values are loaded once for all of them, and the
+// wave waits for memory once per batch instead of once per query.  Each
+// query keeps its own online softmax, in the per-query order above.
+template <int D, int NQ>
+DEVI void attn_suffix_row(const AttnParams& p, int kvh, int b, int qi0) {
+  constexpr int PL = D / 64;
+  constexpr int SB = 8;
+  const int lane = threadIdx.x & 63;
+  const int G = p.Hq / p.Hkv;
+  const int Tb = p.rlen ? p.rlen[b] : p.T;
+  const int rs = p.rstart ? p.rstart[b] : b * p.T;
+  const int nq = G * p.T;
+  const int i = qi0 / G;
+  float qv[NQ][PL];
+  const float* qsrc = p.q + ((size_t)(rs + i) * p.Hq + kvh * G + qi0 % G) * D;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+#pragma unroll
+    for (int e = 0; e < PL; ++e) qv[n][e] = qsrc[n * D + lane + 64 * e] * p.scale;
+  uint64_t lo, hi;
+  if (p.anc) {
+    lo = p.anc[2 * (rs + i)];
+    hi = p.anc[2 * (rs + i) + 1];
+  } else {
+    lo = i >= 63 ? ~0ull : (2ull << i) - 1ull;
+    hi = i < 64 ? 0ull : (i >= 127 ? ~0ull : (2ull << (i - 64)) - 1ull);
+  }
+  if (Tb < 64) lo &= (1ull << Tb) - 1ull;
+  if (Tb <= 64) hi = 0;
+  else if (Tb < 128) hi &= (1ull << (Tb - 64)) - 1ull;
+  float m[NQ], l[NQ], o[NQ][PL];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    m[n] = -INFINITY;
+    l[n] = 0.f;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) o[n][e] = 0.f;
+  }
+  while (lo | hi) {
+    int js[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      int j = -1;
+      if (lo) {
+        j = __builtin_ctzll(lo);
+        lo &= lo - 1ull;
+      } else if (hi) {
+        j = 64 + __builtin_ctzll(hi);
+        hi &= hi - 1ull;
+      }
+      js[k] = j;
+    }
+    float kk[SB][PL], vv[SB][PL];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      const size_t src = ((size_t)(rs + (js[k] < 0 ? 0 : js[k])) * p.Hkv + kvh) * D;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) {
+        kk[k][e] = js[k] >= 0 ? p.k_suf[src + lane + 64 * e] : 0.f;
+        vv[k][e] = js[k] >= 0 ? p.v_suf[src + lane + 64 * e] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (js[k] < 0) break;  // wave-uniform
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) t += qv[n][e] * kk[k][e];
+        const float sc = wave_sum(t);
+        const float mn = fmaxf(m[n], sc);
+        const float f = (m[n] == -INFINITY) ? 0.f : __expf(m[n] - mn);
+        const float pe = __expf(sc - mn);
+        l[n] = l[n] * f + pe;
+        m[n] = mn;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) o[n][e] = o[n][e] * f + pe * vv[k][e];
+      }
+    }
+  }
+  const size_t slot = (((size_t)p.splits * p.B + b) * p.Hkv + kvh) * nq;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+    for (int e = 0; e < PL; ++e) p.part_o[(slot + qi0 + n) * D + lane + 64 * e] = o[n][e];
+    if (lane == 0) {
+      p.part_ml[2 * (slot + qi0 + n)] = m[n];
+      p.part_ml[2 * (slot + qi0 + n) + 1] = l[n];
+    }
+  }
+}
+
 // The step's own keys, in fp32: a chain row i sees rows 0..i; a token-tree
 // node sees itself and its ancestors only (CS349E Lecture 6, section 10.3),
 // a handful of the tree's nodes.  Each wave walks the set bits of its
@@ -160,8 +255,14 @@ DEVI void attn_suffix(const AttnParams& p, int kvh, int qg, int b, int sub, int 
   const int w = threadIdx.x >> 6;
   const int G = p.Hq / p.Hkv;
   const int Tb = p.rlen ? p.rlen[b] : p.T;
+  const int qi0 = qg * QN + 4 * qpw * sub + qpw * w;
+  if (qpw == 4 && G % 4 == 0) {
+    // the wave's four queries (qi0 is a multiple of 4) are heads of one row
+    if (qi0 < G * Tb) attn_suffix_row<D, 4>(p, kvh, b, qi0);
+    return;
+  }
   for (int k = 0; k < qpw; ++k) {
-    const int qi = qg * QN + 4 * qpw * sub + qpw * w + k;
+    const int qi = qi0 + k;
     if (qi >= G * Tb) break;  // wave-uniform
     attn_suffix_query<D>(p, kvh, b, qi);
   }
