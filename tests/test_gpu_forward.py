@@ -110,12 +110,38 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
     """8B-like layout (32 q / 8 kv heads of 128, d=4096, bf16) with two layers,
     a short FFN and vocab, synthetic bf16 cache of ragged lengths with a NaN
     poisoned tail: logits and written cache slots against the oracle."""
-    sh = synth.MINI8B
-    print(f"[gqa] B={B} T={T} ctx={ctx} tree={branching}", flush=True)
+    _gqa_step_case(synth.MINI8B, B, T, ctx, branching)
+
+
+# The same layout with 4 KV heads: 8 query heads per KV head, so a suffix
+# wave's four queries (trees; chains of 128 or more (sequence, KV head)
+# pairs) start at head 0 or head 4 of their row.
+G8 = synth.ModelShape(n_layers=2, d_model=4096, n_heads=32, n_kv_heads=4, head_dim=128,
+                      d_ffn=1024, vocab=8192, rms_eps=1e-5, rope_theta=500000.0, weight_dtype="bf16")
+G8_CASES = [
+    # B, T, ctx lengths, tree branching or None: trees and 32-sequence chains
+    # on the register form (16 queries per KV head) and the LDS form (more)
+    (1, 2, [400], [1]),
+    (2, 15, [300, 57], [2, 2, 2]),
+    (32, 2, [150] * 31 + [3], None),
+    (32, 4, [200] * 31 + [3], None),
+]
+
+
+@pytest.mark.parametrize("B,T,ctx,branching", G8_CASES)
+def test_gqa_group8_step_matches_oracle(B, T, ctx, branching):
+    """8 query heads per KV head: logits and written cache slots against the
+    oracle, on trees and on a chain batch of 128 (sequence, KV head) pairs."""
+    _gqa_step_case(G8, B, T, ctx, branching)
+
+
+def _gqa_step_case(sh, B, T, ctx, branching):
+    print(f"[gqa] G={sh.n_heads // sh.n_kv_heads} B={B} T={T} ctx={ctx} tree={branching}", flush=True)
     max_ctx = max(1088, (max(ctx) + T + 63) // 64 * 64)
-    eng, names, w, cache = build_engine(sh, 4, max_ctx, max(16, T), ctx_len=ctx + [0] * (4 - B))
+    nb = max(4, B)
+    eng, names, w, cache = build_engine(sh, nb, max_ctx, max(16, T), ctx_len=ctx + [0] * (nb - B))
     W = oracle_weights(names, w)
-    kc, vc = oracle_cache(cache, sh, 4, max_ctx)
+    kc, vc = oracle_cache(cache, sh, nb, max_ctx)
     tokens = synth.make_tokens(B, T, sh.vocab, seed=77 + T, device=dev())
     kv = torch.tensor(ctx, dtype=torch.int32, device=dev())
     parent = synth.random_tree(branching, B).to(dev()) if branching else None
@@ -128,7 +154,7 @@ def test_gqa_bf16_step_matches_oracle(B, T, ctx, branching):
     print(f"  logits rel err max {err.max():.2e} median {np.median(err):.2e}", flush=True)
     assert err.max() < 1e-3
     # the step wrote every row's K/V at slot kv_len + i
-    kg, vg = oracle_cache(cache, sh, 4, max_ctx)
+    kg, vg = oracle_cache(cache, sh, nb, max_ctx)
     ko, vo = kc.copy(), vc.copy()
     OM.write_suffix(ko[:, :B], vo[:, :B], kn, vn, np.array(ctx))
     for b in range(B):
